@@ -1,0 +1,239 @@
+"""Decode throughput of the persistent MoE megakernel on one MI355X.
+
+Workload (default): synthetic 30B-total / 3.3B-active MoE decoder (48 layers,
+hidden 2048, 32 q / 4 kv heads of 128, 128 experts top-8 SwiGLU with width
+768, vocab 151936, untied LM head), BF16 weights drawn N(0, 0.02), batch 1
+at 8K context (8192 cached tokens, N(0,1) BF16 KV in 16-token pages), greedy
+decode. A "step" is one whole decode step: embedding through logits, one
+launch of the persistent kernel, plus the caller's greedy argmax.
+
+Prints one JSON line: decode tok/s, the per-op (one launch per operation)
+build of the same tiles in the same harness, the roofline of the megakernel
+(algorithmic bytes per step / measured kernel time vs the 8 TB/s HBM peak) and
+the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at batch 1, 8K ctx + % of HBM speed-of-light (bytes/step÷BW)"
+PEAK_GBS = 8000.0
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def distinct_experts(route_ids: np.ndarray, B: int) -> list:
+    return [len(set(route_ids[l, :B].reshape(-1).tolist())) for l in range(route_ids.shape[0])]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--context", type=int, default=8192)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--no-perop", action="store_true")
+    ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from persistent_megakernel_03_amd import configs, mk, sol, synth
+
+    cfg = configs.A3B
+    B, ctx = args.batch, args.context
+    P = cfg["page_size"]
+    total_tokens = ctx + args.warmup + args.steps + 1
+    pages_per_seq = -(-total_tokens // P)
+    n_pages = pages_per_seq * B + 1
+    t0 = time.time()
+    log(f"generating weights ({cfg['n_layers']} layers) and KV ({n_pages} pages) on device")
+    weights = synth.make_model(cfg, 0, "cuda")
+    k_pool, v_oracle_layout = synth.make_kv_pool(cfg, n_pages, 1, "cuda")
+    v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
+    del v_oracle_layout
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    block_tables = synth.make_block_tables(B, pages_per_seq, n_pages, shuffle=B > 1)
+    tok0 = synth.make_tokens(B, cfg["vocab"], seed=3)
+    results = {}
+
+    def run(mode: int, steps: int, warmup: int, k, v):
+        dec = mk.Decoder(cfg, weights, k, v, max_batch=B, max_pages_per_seq=pages_per_seq, mode=mode,
+                         wg_per_cu=args.wg_per_cu, time_kernels=True)
+        tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
+        logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
+        pos = [ctx] * B
+        stream = torch.cuda.current_stream()
+
+        def one():
+            dec.step(pos, block_tables, tokens, logits)
+            tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+            for b in range(B):
+                pos[b] += 1
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        assert dec.sync_check() == mk.MK_OK
+        start = time.perf_counter()
+        for _ in range(steps):
+            one()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - start
+        st = dec.sync_check()
+        if st != mk.MK_OK:
+            raise RuntimeError(f"device status {st}")
+        # kernel-only time per step: HIP events bracketing the step's kernels,
+        # one step at a time
+        kms = []
+        for _ in range(min(16, steps)):
+            one()
+            kms.append(dec.kernel_ms())
+        dbg = dec.debug()
+        off = dbg.route_ids - dec.workspace.data_ptr()
+        n = cfg["n_layers"] * B * cfg["top_k"]
+        rid = dec.workspace[off:off + 4 * n].view(torch.int32).view(cfg["n_layers"], B, cfg["top_k"]).cpu().numpy()
+        dec.close()
+        return elapsed, float(np.median(kms)), rid, list(pos)
+
+    log(f"megakernel: {args.warmup} warmup + {args.steps} timed steps")
+    k1, v1 = k_pool.clone(), v_pool.clone()
+    el, kms, rid, pos_end = run(mk.MK_MODE_MEGAKERNEL, args.steps, args.warmup, k1, v1)
+    del k1, v1
+    ms_per_step = 1e3 * el / args.steps
+    tok_s = B * args.steps / el
+    # algorithmic bytes of the last timed step (contexts just before it, counted experts)
+    ctx_last = [p - 1 for p in pos_end]
+    bytes_step = sol.step_bytes(cfg, ctx_last, distinct_experts(rid, B), distinct_tokens=B)
+    achieved = bytes_step / (kms * 1e-3) / 1e9
+    log(f"megakernel: {tok_s:.1f} tok/s, {ms_per_step:.3f} ms/step, kernel {kms:.3f} ms, "
+        f"{achieved:.0f} GB/s ({100 * achieved / PEAK_GBS:.1f}% of 8 TB/s)")
+
+    perop = None
+    if not args.no_perop:
+        k2, v2 = k_pool.clone(), v_pool.clone()
+        steps2 = max(8, args.steps // 4)
+        el2, kms2, _, _ = run(mk.MK_MODE_PEROP, steps2, 3, k2, v2)
+        del k2, v2
+        perop = {"value": B * steps2 / el2, "unit": "tok/s", "ms_per_step": 1e3 * el2 / steps2,
+                 "kernel_ms": kms2, "steps": steps2, "kind": "per-op launches, same tiles, eager"}
+        log(f"per-op: {perop['value']:.1f} tok/s, kernels {kms2:.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, args.cpu_steps)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"30B-A3B synthetic MoE decode, batch {B}, {ctx} cached tokens, greedy",
+                   "batch": B, "context": ctx, "layers": cfg["n_layers"], "experts": cfg["n_experts"],
+                   "top_k": cfg["top_k"], "parallelism": "single GPU",
+                   "precision": "BF16 weights and KV, fp32 activations and accumulation"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_persistent (one launch per step)", "bytes_per_launch": bytes_step,
+                     "kernel_ms": round(kms, 4)},
+        "sol": {"bytes_per_step": bytes_step, "sol_tok_s": round(sol.sol_tokens_per_s(bytes_step, B), 1),
+                "pct_sol_step": round(100 * tok_s / sol.sol_tokens_per_s(bytes_step, B), 2)},
+        "perop_baseline": perop,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy of 1 GiB done (3 launches)")
+
+
+def cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, n_steps):
+    """The CPU oracle, as it stands, on the first steps of the same workload:
+    one untimed pass pulls and decodes the weights it touches, then
+    n_steps greedy steps are timed (compute only)."""
+    import torch
+
+    from oracle import DenseModel, PagedKV, decode_step
+    from persistent_megakernel_03_amd import synth
+
+    log("cpu oracle: pulling weights and KV to the host")
+    cache = {}
+
+    def src(name):
+        if name not in weights:
+            return None
+        if name not in cache:
+            cache[name] = synth.bits(weights[name])
+        return cache[name]
+
+    def esrc(layer, kind, e):
+        return synth.bits(weights[f"layers.{layer}.{kind}"][e])
+
+    model = DenseModel(cfg, src, esrc, np.float32)
+    kv = PagedKV(synth.bits(k_pool), synth.bits(v_pool.transpose(-1, -2)), cfg["page_size"])
+    toks = list(int(t) for t in tok0)
+    pos = [ctx] * B
+    # untimed warm pass: decodes dense weights and the first step's experts
+    kv_k, kv_v = kv.k.copy(), kv.v.copy()
+    decode_step(model, PagedKV(kv_k, kv_v, cfg["page_size"]), pos, block_tables, toks)
+    del kv_k, kv_v
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(blas)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        lg, _, _ = decode_step(model, kv, pos, block_tables, toks)
+        toks = [int(np.argmax(lg[b])) for b in range(B)]
+        pos = [p + 1 for p in pos]
+    el = time.perf_counter() - t0
+    log(f"cpu oracle: {B * n_steps / el:.3f} tok/s over {n_steps} steps ({el:.1f}s, {threads} cores)")
+    return {"value": round(B * n_steps / el, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_steps} greedy steps of the same workload from its first position, after one untimed "
+                      f"pass that decodes the touched weights; numpy float32"}
+
+
+if __name__ == "__main__":
+    main()

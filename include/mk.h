@@ -1,0 +1,248 @@
+/*
+ * mk.h -- C ABI of libmk: one decode step of a mixture-of-experts transformer
+ * on one MI355X (gfx950), run either as a single persistent megakernel or as a
+ * per-op chain of kernel launches over the same tiles.
+ *
+ * What the library implements, and where the pages say it:
+ *  - The whole decode step as one persistent kernel, with one resident
+ *    workgroup set per compute unit for the whole step, each walking a list of
+ *    small tasks prepared on the host, and counters in global memory recording
+ *    when a task's inputs are ready ("Cohere Publishes One-Kernel Server for
+ *    North Mini Code, Claims 1.58x vLLM Speedup", section "One resident
+ *    program, many small tasks"; "Inside the Megakernel Serving Engine for
+ *    North Mini Code", paragraph 4).
+ *  - Tile-granular scheduling with backfill, no false dependencies, and weights
+ *    loaded before a task's activation input is ready (first page, section
+ *    "What the scheduling change is meant to avoid").
+ *  - Tiles sharing one calling convention, built from plain tiled
+ *    matrix-vector products and paged attention (first page, section "A
+ *    hand-built approach to a specialized server"; second page, paragraph 5).
+ *  - Continuous batching with ragged sequence lengths over a paged KV cache
+ *    (first page, opening section; "Cohere fuses an entire decode step into
+ *    one GPU program", paragraph 4).
+ *  - The per-op chain is the conventional pipeline the pages contrast it with:
+ *    one launch per operation, each waiting for the previous to drain (first
+ *    page, section "The delay is between operations").
+ *
+ * Conventions for every entry point:
+ *  - Device pointers point into memory of the device given to mk_create; the
+ *    caller owns all of it (weights, KV pools, workspace, tokens, logits) and
+ *    the stream. The library allocates no device memory; it owns only the
+ *    handle and small pinned host staging buffers.
+ *  - Host-detectable errors return synchronously and enqueue nothing.
+ *    Device-detected errors (watchdog timeout, token out of range) are sticky
+ *    and reported by mk_sync_check.
+ *  - No C++ exception crosses this boundary. mk_last_error() returns a
+ *    thread-local message for the last failing call on the calling thread.
+ *  - A handle is used by one host thread and one stream at a time.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MK_OK = 0,
+    MK_ERR_INVALID = -1,     /* bad argument (NULL, negative size, ...) */
+    MK_ERR_UNSUPPORTED = -2, /* model dims or options this build does not handle */
+    MK_ERR_CAPACITY = -3,    /* batch, context, pages or workspace too small */
+    MK_ERR_BAD_PAGE = -4,    /* a block-table entry the step needs is outside the pool */
+    MK_ERR_HIP = -5,         /* a HIP runtime call failed (message has hipGetErrorString) */
+    MK_ERR_TIMEOUT = -6,     /* device watchdog: a dependency wait exceeded its bound */
+    MK_ERR_DEVICE = -7       /* device-detected bad input (token id out of range) */
+} mk_status;
+
+enum {
+    MK_MODE_MEGAKERNEL = 0, /* one persistent cooperative launch per step */
+    MK_MODE_PEROP = 1       /* one launch per operation level, stream-ordered */
+};
+
+/*
+ * Model shape. Pre-norm decoder: RMSNorm, fused QKV projection (no bias),
+ * rotate-half RoPE, grouped-query attention over a paged BF16 KV cache,
+ * output projection, RMSNorm, router (optional fp32 bias) with top-k and a
+ * softmax over the selected logits, SwiGLU experts, final RMSNorm and an
+ * untied LM head. The pages give no architecture; this is the plainest model
+ * that has every operation they name (first page, section "The delay is
+ * between operations"; third page, paragraph 2).
+ */
+typedef struct mk_dims {
+    int32_t n_layers;
+    int32_t hidden;      /* H */
+    int32_t n_q_heads;   /* Hq */
+    int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0, Hq / Hkv <= 16 */
+    int32_t head_dim;    /* D: 64 or 128 */
+    int32_t n_experts;   /* E <= 256 */
+    int32_t top_k;       /* k <= 8 */
+    int32_t moe_inter;   /* I */
+    int32_t vocab;       /* V */
+    int32_t page_size;   /* P: 16 */
+    float rms_eps;
+    float rope_theta;
+    int32_t max_batch;          /* largest B a step may use */
+    int32_t max_pages_per_seq;  /* block-table row length */
+    int64_t n_pages;            /* pages in each layer's pool */
+} mk_dims;
+
+/*
+ * Weights: BF16 device pointers, row-major, rows = output features
+ * ([out][in]). Per-layer entries are host arrays of n_layers device pointers
+ * (copied at mk_create; the pointed-to memory must outlive the handle).
+ *   embed [V][H], lm_head [V][H], final_norm [H]
+ *   attn_norm[l] [H], wqkv[l] [(Hq + 2 Hkv) D][H] (q rows, then k, then v),
+ *   wo[l] [H][Hq D], ffn_norm[l] [H], router[l] [E][H],
+ *   w_gate[l], w_up[l] [E][I][H], w_down[l] [E][H][I],
+ *   router_bias: NULL, or a host array of n_layers device pointers to fp32 [E].
+ */
+typedef struct mk_weights {
+    const void* embed;
+    const void* lm_head;
+    const void* final_norm;
+    const void* const* attn_norm;
+    const void* const* wqkv;
+    const void* const* wo;
+    const void* const* ffn_norm;
+    const void* const* router;
+    const void* const* w_gate;
+    const void* const* w_up;
+    const void* const* w_down;
+    const float* const* router_bias;
+} mk_weights;
+
+typedef struct mk_options {
+    int32_t mode;            /* MK_MODE_MEGAKERNEL or MK_MODE_PEROP */
+    int32_t trace;           /* nonzero: record per-task timestamps (mk_get_trace) */
+    int64_t watchdog_ns;     /* bound on each dependency wait; 0 = 2 s */
+    int32_t wg_per_cu;       /* persistent workgroups per compute unit; 0 = auto */
+    int32_t split_kv_tokens; /* attention chunk length in tokens (multiple of 64); 0 = auto */
+    int32_t n_cu_override;   /* 0 = the device's compute-unit count */
+    int32_t time_kernels;    /* nonzero: bracket each step's kernels with HIP events (mk_kernel_time) */
+    int32_t reserved[4];
+} mk_options;
+
+typedef struct mk_handle mk_handle;
+
+/*
+ * KV pool layout, one K pool and one V pool per model, each n_layers *
+ * n_pages pages of Hkv heads:
+ *   K: [L][n_pages][Hkv][P][D]  BF16 (token-major inside a page)
+ *   V: [L][n_pages][Hkv][D][P]  BF16 (dimension-major inside a page)
+ * Token t of a sequence with block table bt lives in page bt[t / P], slot
+ * t % P (first page, opening section: paged attention). Returns the bytes of
+ * one pool (K and V are the same size).
+ */
+size_t mk_kv_pool_bytes(const mk_dims* dims);
+
+/* Bytes of device workspace mk_create needs for these dims and options
+ * (activations, attention partials, counters, task lists). 0 on bad input. */
+size_t mk_workspace_bytes(const mk_dims* dims, const mk_options* opts);
+
+/*
+ * Create a handle on `device` (HIP ordinal). Validates the dims, queries the
+ * device, carves `workspace` (device memory of at least mk_workspace_bytes,
+ * 256-byte aligned, owned by the caller) and clears its counters with a
+ * synchronous launch on the null stream. Returns MK_ERR_UNSUPPORTED for dims
+ * outside the supported set and MK_ERR_CAPACITY for a short workspace.
+ */
+mk_status mk_create(const mk_dims* dims, const mk_weights* weights, void* k_pool, void* v_pool,
+                    void* workspace, size_t workspace_bytes, const mk_options* opts, int device,
+                    mk_handle** out);
+
+/*
+ * Enqueue one decode step for `batch` sequences on `stream` and return.
+ *   seq_ids      host [B]: distinct ids (tracing only)
+ *   positions    host [B]: tokens already cached; the new token's KV goes to
+ *                that position and attention covers positions 0..positions[b]
+ *   block_tables host [B][max_pages_per_seq]: page ids; entries past
+ *                positions[b] / P are ignored
+ *   tokens       device int32 [B]: input token ids
+ *   logits       device fp32 [B][V]: output
+ * Host errors (bad page, capacity, ...) return before anything is enqueued.
+ * The step is idempotent given (KV pool, positions, block tables, tokens):
+ * it writes its KV slot before reading it.
+ */
+mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids,
+                         const int32_t* positions, const int32_t* block_tables,
+                         const int32_t* tokens, float* logits, void* stream);
+
+/* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PEROP for later steps. */
+mk_status mk_set_mode(mk_handle* h, int32_t mode);
+
+/* Synchronize `stream`, then report and clear the device error word:
+ * MK_OK, MK_ERR_TIMEOUT or MK_ERR_DEVICE. */
+mk_status mk_sync_check(mk_handle* h, void* stream);
+
+/*
+ * Device addresses of per-step results kept in the workspace, for checking
+ * and tracing. Valid until mk_destroy; contents refer to the last step.
+ *   x_layers: fp32 [2L + 1][max_batch][H]: the residual stream; entry 0 is
+ *             the embedding, 2l + 1 the residual after layer l's attention
+ *             block, 2l + 2 after its MoE block
+ *   route_ids: int32 [L][max_batch][k], route_w: fp32 [L][max_batch][k]
+ *   router_logits: fp32 [max_batch][E] (last layer's)
+ */
+typedef struct mk_debug_ptrs {
+    const float* x_layers;
+    const int32_t* route_ids;
+    const float* route_w;
+    const float* router_logits;
+    const uint64_t* trace;   /* see mk_get_trace */
+    int64_t trace_capacity;  /* records */
+} mk_debug_ptrs;
+mk_status mk_get_debug_ptrs(mk_handle* h, mk_debug_ptrs* out);
+
+/*
+ * Task-graph plan of the last step, copied to host memory. Each task record
+ * is 12 int32: {op, layer, a0, a1, a2, a3, pre_ctr, pre_target, ctr, target,
+ * signal, level}; `wg_offsets` has n_wg + 1 entries (CSR: tasks of workgroup
+ * w are [wg_offsets[w], wg_offsets[w + 1])). Pass NULL buffers to query sizes.
+ */
+typedef struct mk_plan_info {
+    int32_t n_wg;
+    int32_t n_tasks;
+    int32_t n_counters;
+    int32_t n_levels;
+    int32_t chunk_tokens;
+    int32_t reserved[3];
+} mk_plan_info;
+
+/*
+ * Build a plan on the host without a device or handle (CPU testing of the
+ * task-graph builder). `n_wg` workgroups; positions host [batch].
+ * `tasks` (12 * n_tasks int32), `wg_offsets` (n_wg + 1 int32) and
+ * `counter_targets` (n_counters int32: the value each counter reaches when
+ * the step completes) may be NULL to query sizes; `cap_tasks` bounds tasks.
+ */
+mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_wg, int32_t batch,
+                        const int32_t* positions, mk_plan_info* info, int32_t* tasks,
+                        int64_t cap_tasks, int32_t* wg_offsets, int32_t* counter_targets);
+
+/*
+ * Per-task timestamps of the last step (when mk_options.trace was set): one
+ * record of 4 uint64 per task, {task index | workgroup << 32, t_start,
+ * t_after_wait, t_end} in the device's constant wall clock (100 MHz ticks).
+ */
+mk_status mk_get_trace(mk_handle* h, void* host_buf, size_t bytes, size_t* written);
+
+/*
+ * Device time of the last step's kernels in milliseconds, from HIP events
+ * recorded on the step's stream immediately before the first and after the
+ * last kernel of the step (per-step staging copies excluded). Needs
+ * mk_options.time_kernels; waits for the step to finish.
+ */
+mk_status mk_kernel_time(mk_handle* h, float* ms);
+
+void mk_destroy(mk_handle* h);
+
+const char* mk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

@@ -1,0 +1,139 @@
+// mk_common.h -- definitions shared by the host task-graph builder and the
+// device code: task records, operation codes, counter layout and the kernel
+// parameter block.
+//
+// A decode step is a DAG of tiles. The host turns it into one task list per
+// persistent workgroup, and global-memory counters record when a tile's
+// inputs are ready ("Cohere Publishes One-Kernel Server for North Mini Code,
+// Claims 1.58x vLLM Speedup", section "One resident program, many small
+// tasks"). Every tile type runs through one calling convention (same page,
+// section "A hand-built approach to a specialized server").
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define MK_HD __host__ __device__
+#else
+#define MK_HD
+#endif
+
+namespace mk {
+
+// Operation codes, in dependency-level order inside a layer.
+enum Op : int32_t {
+    OP_EMBED = 0,  // x0[b] = embedding row of token b
+    OP_QKV = 1,    // fused RMSNorm + QKV rows of one KV group
+    OP_ATTN = 2,   // RoPE (+ KV append) + split-KV attention chunk; last chunk combines
+    OP_OPROJ = 3,  // output projection + residual
+    OP_ROUTER = 4, // fused RMSNorm + router logits
+    OP_GATEUP = 5, // top-k + expert gate/up rows + SwiGLU
+    OP_DOWN = 6,   // top-k + expert down rows + weighted combine + residual
+    OP_LMHEAD = 7, // fused final RMSNorm + LM-head rows
+    OP_COUNT = 8
+};
+
+constexpr int kLevelsPerLayer = 6;  // QKV, ATTN, OPROJ, ROUTER, GATEUP, DOWN
+
+// Dependency level of an op in layer l (0 = embedding, last = LM head).
+inline int op_level(int op, int layer, int n_layers) {
+    if (op == OP_EMBED) return 0;
+    if (op == OP_LMHEAD) return 1 + kLevelsPerLayer * n_layers;
+    return 1 + kLevelsPerLayer * layer + (op - OP_QKV);
+}
+
+// One task: 12 int32, read by a workgroup with scalar loads.
+struct Task {
+    int32_t op;
+    int32_t layer;
+    int32_t a0, a1, a2, a3;   // op-specific tile coordinates
+    int32_t pre_ctr;          // wait before loading weights (-1: none)
+    int32_t pre_target;
+    int32_t ctr;              // wait before computing (-1: none)
+    int32_t target;
+    int32_t signal;           // counter bumped after the tile (-1: none)
+    int32_t level;
+};
+static_assert(sizeof(Task) == 48, "task record is 12 int32");
+
+// Weight table: kinds per layer.
+enum WKind : int32_t {
+    W_ATTN_NORM = 0, W_QKV, W_O, W_FFN_NORM, W_ROUTER, W_GATE, W_UP, W_DOWN, W_RBIAS, W_NKINDS
+};
+
+// Counter bank layout. Main counters sit one per 128-byte line; the attention
+// arrival counters ([L][max_batch][Hkv]) are packed after them.
+constexpr int kCtrStride = 32;  // uint32 words per main counter
+
+struct CounterLayout {
+    int n_layers, n_kv_heads, max_batch;
+    MK_HD int per_layer() const { return n_kv_heads + 5; }
+    MK_HD int embed() const { return 0; }
+    MK_HD int qkv(int l, int g) const { return 1 + l * per_layer() + g; }
+    MK_HD int attn(int l) const { return 1 + l * per_layer() + n_kv_heads; }
+    MK_HD int oproj(int l) const { return attn(l) + 1; }
+    MK_HD int router(int l) const { return attn(l) + 2; }
+    MK_HD int gateup(int l) const { return attn(l) + 3; }
+    MK_HD int down(int l) const { return attn(l) + 4; }
+    MK_HD int n_main() const { return 1 + n_layers * per_layer(); }
+    // word offset of the arrival counters inside a bank
+    MK_HD int64_t arrive_base() const { return (int64_t)n_main() * kCtrStride; }
+    MK_HD int64_t arrive(int l, int b, int g) const {
+        return arrive_base() + ((int64_t)l * max_batch + b) * n_kv_heads + g;
+    }
+    MK_HD int64_t bank_words() const {
+        int64_t w = arrive_base() + (int64_t)n_layers * max_batch * n_kv_heads;
+        return (w + 63) & ~(int64_t)63;
+    }
+};
+
+// Kernel parameter block (passed by value).
+struct Params {
+    // model shape
+    int32_t L, H, Hq, Hkv, D, E, K, I, V, P, G, QKVD;
+    float eps, attn_scale;
+    int32_t max_batch, max_pages, max_chunks;
+    int64_t n_pages;
+    // this step
+    int32_t B, chunk;
+    int32_t perop;      // 1: per-op launches (no counter waits / signals)
+    int32_t trace_on;
+    int64_t watchdog_ticks;
+    // weights
+    const uint16_t* embed;
+    const uint16_t* lm_head;
+    const uint16_t* final_norm;
+    const uint64_t* wtab;  // [L][W_NKINDS] device addresses
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    // step inputs
+    const int32_t* tokens;
+    float* logits;
+    const int32_t* positions;     // [max_batch]
+    const int32_t* block_tables;  // [max_batch][max_pages]
+    const float* rope;            // [max_batch][D/2][2] cos, sin
+    const int32_t* n_chunks;      // [max_batch]
+    // workspace
+    float* x;         // [2L+1][max_batch][H]
+    float* qkv;       // [max_batch][QKVD]
+    float* att_part;  // [max_batch][Hq][max_chunks][D+2]
+    float* att_out;   // [max_batch][Hq*D]
+    float* rlogits;   // [max_batch][E]
+    int32_t* route_ids;  // [L][max_batch][K]
+    float* route_w;      // [L][max_batch][K]
+    float* act;          // [max_batch*K][I]
+    uint32_t* ctr;       // this step's counter bank
+    uint32_t* ctr_other; // the bank the next step uses (cleared by this step)
+    int64_t bank_words;
+    CounterLayout cl;
+    int32_t* err;        // [0]: status code, [1]: detail, [2]: abort flag
+    const Task* tasks;
+    const int32_t* wg_off;
+    uint64_t* trace;     // [n_tasks][4]
+};
+
+// Device error codes (mirror mk_status values).
+constexpr int32_t kErrTimeout = -6;
+constexpr int32_t kErrDevice = -7;
+
+}  // namespace mk

@@ -1,0 +1,365 @@
+// mk_device.h -- device side of the decode step: counter protocol, the
+// streaming matrix-vector engine, and the tile functions.
+//
+// Every tile has the same calling convention, tile_xxx(task, params, lds):
+//   1. issue loads of the tile's immutable inputs (weights, old KV pages)
+//      into registers -- immutable weights start loading before the tile's
+//      activation input is ready ("Cohere Publishes One-Kernel Server for
+//      North Mini Code, Claims 1.58x vLLM Speedup", section "What the
+//      scheduling change is meant to avoid");
+//   2. wait on the task's dependency counter in global memory (agent-scope
+//      acquire; same page, section "One resident program, many small tasks");
+//   3. compute from registers and LDS, write outputs;
+//   4. release the outputs and bump the task's counter.
+// The per-op build runs the same functions with waits and signals switched
+// off; kernel boundaries are then the only ordering.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "mk_common.h"
+
+namespace mk {
+
+constexpr int NT = 256;      // threads per workgroup
+constexpr int NWAVES = NT / 64;
+constexpr int kMaxBatch = 2; // batch handled by the register-resident GEMV tiles
+constexpr int kMaxTopK = 8;
+constexpr int kMaxSlots = kMaxBatch * kMaxTopK;
+constexpr int kSC = 128;     // attention sub-chunk: tokens per MFMA pass
+constexpr int kSPad = kSC + 4;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Thread index through an empty asm barrier: per-lane values derived from it
+// are then computed inside each tile instead of being hoisted out of the task
+// loop, where values from every tile type would stay live at once and raise
+// register pressure for all of them.
+__device__ __forceinline__ int tid_() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// ----------------------------------------------------------------- numerics
+
+__device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> BF16 bits, nearest with ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float dot8(const uint4 w, const float* h, float acc) {
+    acc = fmaf(bflo(w.x), h[0], acc);
+    acc = fmaf(bfhi(w.x), h[1], acc);
+    acc = fmaf(bflo(w.y), h[2], acc);
+    acc = fmaf(bfhi(w.y), h[3], acc);
+    acc = fmaf(bflo(w.z), h[4], acc);
+    acc = fmaf(bfhi(w.z), h[5], acc);
+    acc = fmaf(bflo(w.w), h[6], acc);
+    acc = fmaf(bfhi(w.w), h[7], acc);
+    return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ const uint16_t* wptr(const Params& p, int layer, int kind) {
+    return reinterpret_cast<const uint16_t*>(p.wtab[layer * W_NKINDS + kind]);
+}
+
+// Split an fp32 value into three BF16 parts whose sum reproduces it to about
+// 2^-24 relative. MFMA products of BF16 parts are exact and accumulate in
+// fp32, so three passes give fp32-grade dot products on the matrix cores.
+__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = f2bf(v);
+    const float r1 = v - __uint_as_float(hi << 16);
+    mid = f2bf(r1);
+    const float r2 = r1 - __uint_as_float(mid << 16);
+    lo = f2bf(r2);
+}
+
+// D(16x16) += A(16x32) * B(32x16), BF16 operands, fp32 accumulate.
+// Lane l holds A[l%16][8(l/16) .. +7], B[8(l/16) .. +7][l%16] and
+// D[4(l/16) .. +3][l%16].
+__device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------ counter protocol
+
+__device__ __forceinline__ void raise_error(const Params& p, int32_t code, int32_t detail, bool abort) {
+    int32_t expected = 0;
+    if (__hip_atomic_compare_exchange_strong(p.err, &expected, code, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_store(p.err + 1, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (abort) __hip_atomic_store(p.err + 2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block-wide wait until counter `ctr` reaches `target`. Thread 0 spins with
+// agent-scope loads, then an agent-scope acquire fence makes the producers'
+// writes visible to the whole workgroup after the barrier. Returns false if
+// the step was aborted (watchdog here or elsewhere). Records the time the
+// wait ended in *t_wait (thread 0).
+__device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wait) {
+    if (p.perop || ctr < 0) return true;
+    int ok = 1;
+    if (tid_() == 0) {
+        const uint32_t* c = p.ctr + (int64_t)ctr * kCtrStride;
+        if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)target) {
+            const uint64_t t0 = wall_clock64();
+            uint32_t it = 0;
+            while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)target) {
+                __builtin_amdgcn_s_sleep(1);
+                if ((++it & 31u) == 0) {
+                    if (__hip_atomic_load(p.err + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                        ok = 0;
+                        break;
+                    }
+                    if ((int64_t)(wall_clock64() - t0) > p.watchdog_ticks) {
+                        raise_error(p, kErrTimeout, ctr, true);
+                        ok = 0;
+                        break;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *t_wait = wall_clock64();
+    }
+    return __syncthreads_and(ok) != 0;
+}
+
+// Release this workgroup's writes at agent scope and bump counter `ctr`.
+__device__ void block_signal(const Params& p, int ctr) {
+    if (p.perop || ctr < 0) {
+        __syncthreads();
+        return;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid_() == 0)
+        __hip_atomic_fetch_add(p.ctr + (int64_t)ctr * kCtrStride, 1u, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------ activation slices + norm
+
+// Each lane of each wave holds the activation values at the K positions its
+// weight chunks cover: chunk c of lane l is elements [8(l + 64c), +8).
+// Optionally applies RMSNorm (x / sqrt(mean(x^2) + eps) * gain).
+template <int NCH, int NB>
+__device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, int64_t stride, int nb,
+                                       int K, const uint16_t* gain, float eps) {
+    const int lane = tid_() & 63;
+    const int K8 = K >> 3;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int ch = lane + 64 * c;
+            if (b < nb && ch < K8) {
+                const float4* px = reinterpret_cast<const float4*>(x + b * stride + ch * 8);
+                const float4 u = px[0], v = px[1];
+                h[b][c][0] = u.x; h[b][c][1] = u.y; h[b][c][2] = u.z; h[b][c][3] = u.w;
+                h[b][c][4] = v.x; h[b][c][5] = v.y; h[b][c][6] = v.z; h[b][c][7] = v.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) h[b][c][j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = fmaf(h[b][c][j], h[b][c][j], ss);
+        }
+        if (gain != nullptr) {
+            ss = wave_sum(ss);
+            const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int ch = lane + 64 * c;
+                if (ch < K8) {
+                    const uint4 g = ld16(gain + ch * 8);
+                    const float gv[8] = {bflo(g.x), bfhi(g.x), bflo(g.y), bfhi(g.y),
+                                         bflo(g.z), bfhi(g.z), bflo(g.w), bfhi(g.w)};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) h[b][c][j] = (h[b][c][j] * inv) * gv[j];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------- streaming GEMV
+
+// Load one weight row slice for this lane: chunks lane + 64c of a row with
+// K8 16-byte chunks. A null row loads zeros.
+template <int NCH>
+__device__ __forceinline__ void load_row(uint4 (&w)[NCH], const uint16_t* row, int K8) {
+    const int lane = tid_() & 63;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = lane + 64 * c;
+        if (row != nullptr && ch < K8) w[c] = ld16(row + ch * 8);
+        else w[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Wave-level streaming matrix-vector product. The wave owns `nmine`
+// row-vectors; rowptr(i) returns the i-th. The first PF rows are loaded
+// before ready(h) runs (ready holds the dependency wait and fills the
+// activation slices h); then rows are consumed in order while the row PF
+// places ahead is in flight. reload(i, h) may refresh h before row i;
+// emit(i, acc) receives the wave-reduced dot products (every lane has them).
+template <int NCH, int PF, int NB, class RowPtr, class Ready, class Reload, class Emit>
+__device__ __forceinline__ void gemv_stream(int nmine, int K8, RowPtr rowptr, Ready ready, Reload reload,
+                                            Emit emit) {
+    uint4 buf[PF][NCH];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], s < nmine ? rowptr(s) : nullptr, K8);
+    float h[NB][NCH][8];
+    ready(h);
+    for (int i0 = 0; i0 < nmine; i0 += PF) {
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            const int i = i0 + s;
+            if (i < nmine) {
+                reload(i, h);
+                float acc[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], h[b][c], a);
+                    acc[b] = wave_sum(a);
+                }
+                if (i + PF < nmine) load_row<NCH>(buf[s], rowptr(i + PF), K8);
+                emit(i, acc);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ routing
+
+// Top-k per token and the active-expert slots, in LDS.
+struct RouteLds {
+    int32_t ids[kMaxBatch][kMaxTopK];
+    float w[kMaxBatch][kMaxTopK];
+    int32_t nslots;
+    int32_t slot_e[kMaxSlots];         // expert of each slot, ascending ids
+    int32_t slot_mask[kMaxSlots];      // tokens routed to the slot's expert
+    int8_t slot_rank[kMaxSlots][kMaxBatch]; // rank of the expert in that token's top-k
+};
+
+// Wave 0 computes top-k (logit descending, expert id ascending on ties) and a
+// softmax over the selected logits for each token, then lists the distinct
+// selected experts in ascending order as slots. Ends with a block barrier.
+__device__ __forceinline__ void compute_routing(const Params& p, RouteLds* r) {
+    if (tid_() < 64) {
+        const int lane = tid_();
+        const int E = p.E, K = p.K;
+        uint32_t chosen[4] = {0u, 0u, 0u, 0u};  // per lane: bit b = token b chose expert lane+64i
+        for (int b = 0; b < p.B; ++b) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lane + 64 * i;
+                v[i] = e < E ? p.rlogits[b * E + e] : -INFINITY;
+            }
+            uint32_t taken = 0u;
+            float sel_v[kMaxTopK];
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                sel_v[j] = -INFINITY;
+                if (j < K) {
+                    float bv = -INFINITY;
+                    int bi = 0x7fffffff;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = lane + 64 * i;
+                        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
+                            bv = v[i];
+                            bi = e;
+                        }
+                    }
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) {
+                        const float ov = __shfl_xor(bv, o, 64);
+                        const int oi = __shfl_xor(bi, o, 64);
+                        if (ov > bv || (ov == bv && oi < bi)) {
+                            bv = ov;
+                            bi = oi;
+                        }
+                    }
+                    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+                    sel_v[j] = bv;
+                    if (lane == 0) r->ids[b][j] = bi;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((taken >> i) & 1u) chosen[i] |= 1u << b;
+            // softmax over the selected logits (sel_v[0] is the largest)
+            float ex[kMaxTopK];
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                ex[j] = 0.f;
+                if (j < K) {
+                    ex[j] = expf(sel_v[j] - sel_v[0]);
+                    s += ex[j];
+                }
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < kMaxTopK; ++j)
+                    if (j < K) r->w[b][j] = ex[j] / s;
+            }
+        }
+        // slots: selected experts in ascending id
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t m = __ballot(chosen[i] != 0u);
+            if (chosen[i] != 0u) {
+                const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
+                r->slot_e[slot] = lane + 64 * i;
+                r->slot_mask[slot] = (int32_t)chosen[i];
+            }
+            base += __popcll(m);
+        }
+        if (lane == 0) r->nslots = base;
+    }
+    __syncthreads();
+    // ranks of each slot's expert within each token's selection
+    for (int s = tid_(); s < r->nslots; s += NT) {
+        for (int b = 0; b < kMaxBatch; ++b) {
+            int rank = -1;
+            if (b < p.B)
+                for (int j = 0; j < p.K; ++j)
+                    if (r->ids[b][j] == r->slot_e[s]) rank = j;
+            r->slot_rank[s][b] = (int8_t)rank;
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace mk

@@ -1,0 +1,275 @@
+// mk_plan.cpp -- host task-graph builder (see mk_plan.h).
+#include "mk_plan.h"
+
+#include <algorithm>
+#include <cstdio>
+#include <map>
+#include <queue>
+#include <set>
+#include <tuple>
+
+namespace mk {
+
+namespace {
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+Task make_task(int op, int layer, int a0, int a1, int a2, int a3, int pre_ctr, int pre_target, int ctr,
+               int target, int signal, int level) {
+    Task t;
+    t.op = op;
+    t.layer = layer;
+    t.a0 = a0;
+    t.a1 = a1;
+    t.a2 = a2;
+    t.a3 = a3;
+    t.pre_ctr = pre_ctr;
+    t.pre_target = pre_target;
+    t.ctr = ctr;
+    t.target = target;
+    t.signal = signal;
+    t.level = level;
+    return t;
+}
+
+struct Tile {
+    Task t;
+    double bytes;
+};
+
+}  // namespace
+
+int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested) {
+    int chunk;
+    if (requested > 0) {
+        chunk = ceil_div(requested, 64) * 64;
+    } else {
+        int64_t total = 0;
+        for (int b = 0; b < B; ++b) total += (int64_t)(positions[b] + 1) * s.Hkv;
+        const int64_t per = (total + n_wg - 1) / std::max(1, n_wg);
+        chunk = (int)std::max<int64_t>(128, (per + 127) / 128 * 128);
+    }
+    for (int b = 0; b < B; ++b) {
+        const int need = ceil_div(positions[b] + 1, s.max_chunks);
+        if (need > chunk) chunk = ceil_div(need, 64) * 64;
+    }
+    return chunk;
+}
+
+int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
+    const int G = s.Hq / s.Hkv;
+    const int64_t per_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.rows_qkv) +
+                              (int64_t)s.max_batch * s.Hkv * s.max_chunks + ceil_div(s.H, cfg.rows_o) +
+                              ceil_div(s.E, cfg.rows_router) +
+                              (int64_t)std::min(s.E, s.max_batch * s.K) * ceil_div(s.I, cfg.rows_gateup) +
+                              ceil_div(s.H, cfg.rows_down);
+    return 1 + (int64_t)s.L * per_layer + ceil_div(s.V, cfg.rows_lm);
+}
+
+std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int B, const int32_t* positions,
+                       Plan* out) {
+    if (n_wg <= 0) return "n_wg must be positive";
+    if (B <= 0 || B > s.max_batch) return "batch out of range";
+    const CounterLayout cl{s.L, s.Hkv, s.max_batch};
+    const int G = s.Hq / s.Hkv;
+    Plan& P = *out;
+    P = Plan();
+    P.n_wg = n_wg;
+    P.B = B;
+    P.chunk = choose_chunk(s, n_wg, B, positions, cfg.chunk);
+    P.n_levels = 2 + kLevelsPerLayer * s.L;
+    P.targets.assign(cl.n_main(), 0);
+    P.n_chunks.resize(B);
+    for (int b = 0; b < B; ++b) {
+        if (positions[b] < 0) return "negative position";
+        P.n_chunks[b] = ceil_div(positions[b] + 1, P.chunk);
+        if (P.n_chunks[b] > s.max_chunks) return "attention chunks exceed capacity";
+    }
+
+    std::vector<std::vector<Tile>> levels(P.n_levels);
+    auto add = [&](const Task& t, double bytes) { levels[t.level].push_back({t, bytes}); };
+
+    add(make_task(OP_EMBED, 0, 0, B, 0, 0, -1, 0, -1, 0, cl.embed(), 0), 2.0 * B * s.H);
+    P.targets[cl.embed()] = 1;
+
+    const int grows = (G + 2) * s.D;
+    const int nq = ceil_div(grows, cfg.rows_qkv);
+    const int no = ceil_div(s.H, cfg.rows_o);
+    const int nr = ceil_div(s.E, cfg.rows_router);
+    const int S = std::min(s.E, B * s.K);
+    const int ngu = ceil_div(s.I, cfg.rows_gateup);
+    const int nd = ceil_div(s.H, cfg.rows_down);
+    const int nl = ceil_div(s.V, cfg.rows_lm);
+
+    for (int l = 0; l < s.L; ++l) {
+        const int lv = 1 + kLevelsPerLayer * l;
+        const int in_ctr = l == 0 ? cl.embed() : cl.down(l - 1);
+        const int in_target = l == 0 ? 1 : nd;
+        for (int g = 0; g < s.Hkv; ++g) {
+            for (int i = 0; i < nq; ++i) {
+                const int v0 = i * cfg.rows_qkv, v1 = std::min(grows, v0 + cfg.rows_qkv);
+                add(make_task(OP_QKV, l, g, v0, v1, 0, -1, 0, in_ctr, in_target, cl.qkv(l, g), lv),
+                    2.0 * (v1 - v0) * s.H);
+            }
+            P.targets[cl.qkv(l, g)] = nq;
+        }
+        for (int b = 0; b < B; ++b) {
+            const int n = P.n_chunks[b];
+            for (int g = 0; g < s.Hkv; ++g)
+                for (int c = 0; c < n; ++c) {
+                    const int toks = std::min(P.chunk, positions[b] + 1 - c * P.chunk);
+                    add(make_task(OP_ATTN, l, b, g, c, n, -1, 0, cl.qkv(l, g), nq, cl.attn(l), lv + 1),
+                        4.0 * toks * s.D);
+                }
+        }
+        P.targets[cl.attn(l)] = B * s.Hkv;
+        for (int i = 0; i < no; ++i) {
+            const int r0 = i * cfg.rows_o, r1 = std::min(s.H, r0 + cfg.rows_o);
+            add(make_task(OP_OPROJ, l, r0, r1, 0, 0, -1, 0, cl.attn(l), B * s.Hkv, cl.oproj(l), lv + 2),
+                2.0 * (r1 - r0) * s.Hq * s.D);
+        }
+        P.targets[cl.oproj(l)] = no;
+        for (int i = 0; i < nr; ++i) {
+            const int r0 = i * cfg.rows_router, r1 = std::min(s.E, r0 + cfg.rows_router);
+            add(make_task(OP_ROUTER, l, r0, r1, 0, 0, -1, 0, cl.oproj(l), no, cl.router(l), lv + 3),
+                2.0 * (r1 - r0) * s.H);
+        }
+        P.targets[cl.router(l)] = nr;
+        for (int sl = 0; sl < S; ++sl)
+            for (int i = 0; i < ngu; ++i) {
+                const int r0 = i * cfg.rows_gateup, r1 = std::min(s.I, r0 + cfg.rows_gateup);
+                add(make_task(OP_GATEUP, l, sl, r0, r1, (sl == 0 && i == 0) ? 1 : 0, cl.router(l), nr, -1, 0,
+                              cl.gateup(l), lv + 4),
+                    4.0 * (r1 - r0) * s.H);
+            }
+        P.targets[cl.gateup(l)] = S * ngu;
+        for (int i = 0; i < nd; ++i) {
+            const int r0 = i * cfg.rows_down, r1 = std::min(s.H, r0 + cfg.rows_down);
+            add(make_task(OP_DOWN, l, r0, r1, 0, 0, cl.router(l), nr, cl.gateup(l), S * ngu, cl.down(l), lv + 5),
+                2.0 * S * (r1 - r0) * s.I);
+        }
+        P.targets[cl.down(l)] = nd;
+    }
+    for (int i = 0; i < nl; ++i) {
+        const int r0 = i * cfg.rows_lm, r1 = std::min(s.V, r0 + cfg.rows_lm);
+        add(make_task(OP_LMHEAD, 0, r0, r1, 0, 0, -1, 0, cl.down(s.L - 1), nd, -1, P.n_levels - 1),
+            2.0 * (r1 - r0) * s.H);
+    }
+
+    // Per-op order: level by level.
+    P.level_off.assign(P.n_levels + 1, 0);
+    for (int lv = 0; lv < P.n_levels; ++lv) {
+        P.level_off[lv + 1] = P.level_off[lv] + (int)levels[lv].size();
+        for (const Tile& t : levels[lv]) P.level_tasks.push_back(t.t);
+    }
+
+    // Workgroup lists: level by level, each tile to the least-loaded
+    // workgroup so far (bytes), which backfills workgroups left idle at the
+    // tail of the previous level. Lists stay in level order.
+    std::vector<std::vector<Task>> lists(n_wg);
+    P.wg_bytes.assign(n_wg, 0.0);
+    typedef std::pair<double, int> Slot;
+    std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+    for (int w = 0; w < n_wg; ++w) heap.push({0.0, w});
+    for (int lv = 0; lv < P.n_levels; ++lv) {
+        std::vector<Tile> tiles = levels[lv];
+        std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
+        for (const Tile& t : tiles) {
+            Slot s0 = heap.top();
+            heap.pop();
+            lists[s0.second].push_back(t.t);
+            s0.first += t.bytes + 4096.0;  // small per-task overhead keeps tiny tiles spread
+            P.wg_bytes[s0.second] += t.bytes;
+            heap.push(s0);
+        }
+    }
+    P.wg_off.assign(n_wg + 1, 0);
+    for (int w = 0; w < n_wg; ++w) {
+        P.wg_off[w + 1] = P.wg_off[w] + (int)lists[w].size();
+        P.tasks.insert(P.tasks.end(), lists[w].begin(), lists[w].end());
+    }
+    return std::string();
+}
+
+std::string validate_plan(const ModelShape& s, const Plan& P) {
+    const CounterLayout cl{s.L, s.Hkv, s.max_batch};
+    const int n_main = cl.n_main();
+    char buf[256];
+    if ((int)P.wg_off.size() != P.n_wg + 1) return "wg_off size";
+    if (P.wg_off.back() != (int)P.tasks.size()) return "wg_off end";
+    if (P.level_tasks.size() != P.tasks.size()) return "task count differs between orders";
+    // final counter values and producer levels
+    std::vector<int> final_val(n_main, 0), prod_level(n_main, -1);
+    std::set<std::tuple<int, int, int>> attn_groups;
+    for (const Task& t : P.tasks) {
+        if (t.signal < -1 || t.signal >= n_main) return "signal out of range";
+        if (t.signal < 0) continue;
+        if (t.op == OP_ATTN) {
+            if (attn_groups.insert(std::make_tuple(t.layer, t.a0, t.a1)).second) final_val[t.signal]++;
+        } else {
+            final_val[t.signal]++;
+        }
+        if (prod_level[t.signal] >= 0 && prod_level[t.signal] != t.level) return "counter fed from two levels";
+        prod_level[t.signal] = t.level;
+    }
+    for (int c = 0; c < n_main; ++c)
+        if (final_val[c] != P.targets[c]) {
+            snprintf(buf, sizeof buf, "counter %d reaches %d, target list says %d", c, final_val[c], P.targets[c]);
+            return buf;
+        }
+    for (const Task& t : P.tasks) {
+        const int waits[2][2] = {{t.pre_ctr, t.pre_target}, {t.ctr, t.target}};
+        for (auto& w : waits) {
+            if (w[0] < 0) continue;
+            if (w[0] >= n_main) return "wait counter out of range";
+            if (w[1] != final_val[w[0]] || w[1] <= 0) {
+                snprintf(buf, sizeof buf, "task op %d layer %d waits for %d on counter %d, which reaches %d", t.op,
+                         t.layer, w[1], w[0], final_val[w[0]]);
+                return buf;
+            }
+            if (prod_level[w[0]] >= t.level) return "task waits on a counter of its own or a later level";
+        }
+    }
+    // list order
+    for (int w = 0; w < P.n_wg; ++w)
+        for (int i = P.wg_off[w] + 1; i < P.wg_off[w + 1]; ++i)
+            if (P.tasks[i].level < P.tasks[i - 1].level) return "workgroup list not in level order";
+    // coverage of every operation's output range
+    std::map<std::tuple<int, int, int, int>, std::vector<std::pair<int, int>>> ranges;
+    for (const Task& t : P.tasks) {
+        switch (t.op) {
+            case OP_QKV: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
+            case OP_ATTN: ranges[std::make_tuple(t.op, t.layer, t.a0, t.a1)].push_back({t.a2, t.a2 + 1}); break;
+            case OP_OPROJ:
+            case OP_ROUTER:
+            case OP_DOWN:
+            case OP_LMHEAD: ranges[std::make_tuple(t.op, t.layer, 0, 0)].push_back({t.a0, t.a1}); break;
+            case OP_GATEUP: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
+            default: break;
+        }
+    }
+    const int G = s.Hq / s.Hkv;
+    for (auto& kv : ranges) {
+        auto& v = kv.second;
+        std::sort(v.begin(), v.end());
+        int end = 0;
+        for (auto& r : v) {
+            if (r.first != end) return "tile ranges overlap or leave a gap";
+            end = r.second;
+        }
+        const int op = std::get<0>(kv.first);
+        int want = 0;
+        switch (op) {
+            case OP_QKV: want = (G + 2) * s.D; break;
+            case OP_ATTN: want = P.n_chunks[std::get<2>(kv.first)]; break;
+            case OP_OPROJ: case OP_DOWN: want = s.H; break;
+            case OP_ROUTER: want = s.E; break;
+            case OP_GATEUP: want = s.I; break;
+            case OP_LMHEAD: want = s.V; break;
+        }
+        if (end != want) return "tile ranges do not cover the operation";
+    }
+    return std::string();
+}
+
+}  // namespace mk

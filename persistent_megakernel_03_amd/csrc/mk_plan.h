@@ -1,0 +1,69 @@
+// mk_plan.h -- host task-graph builder for one decode step.
+//
+// The host prepares, for every persistent workgroup, a list of small tasks
+// ("Cohere Publishes One-Kernel Server for North Mini Code, Claims 1.58x vLLM
+// Speedup", section "One resident program, many small tasks"). Operations are
+// cut into tiles so that scheduling works at tile granularity, workgroups
+// idle at the tail of one operation pick up tiles of the next (backfill), and
+// each tile waits only on the tiles it reads ("Inside the Megakernel Serving
+// Engine for North Mini Code", paragraph 4; first page, section "What the
+// scheduling change is meant to avoid").
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "mk_common.h"
+
+namespace mk {
+
+struct ModelShape {
+    int L, H, Hq, Hkv, D, E, K, I, V, P;
+    int max_batch, max_pages;
+    int max_chunks;  // capacity of the attention partial buffer per (b, head)
+};
+
+struct TileConfig {
+    int rows_qkv = 16;
+    int rows_o = 8;
+    int rows_router = 8;
+    int rows_gateup = 16;
+    int rows_down = 4;
+    int rows_lm = 64;
+    int chunk = 0;  // attention chunk in tokens (multiple of 64); 0 = choose
+};
+
+struct Plan {
+    int n_wg = 0;
+    int B = 0;
+    int chunk = 0;
+    int n_levels = 0;
+    std::vector<Task> tasks;          // grouped per workgroup (CSR)
+    std::vector<int32_t> wg_off;      // n_wg + 1
+    std::vector<Task> level_tasks;    // grouped per level (per-op launches)
+    std::vector<int32_t> level_off;   // n_levels + 1
+    std::vector<int32_t> n_chunks;    // per sequence
+    std::vector<int32_t> targets;     // final value of every main counter
+    std::vector<double> wg_bytes;     // bytes streamed per workgroup (balance)
+};
+
+// Attention chunk length for these contexts (tokens, multiple of 64).
+int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested);
+
+// Build the plan. Returns an empty string on success, else a message.
+std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int B,
+                       const int32_t* positions, Plan* out);
+
+// Check the plan's invariants: every task waits only on counters fed by
+// tasks of strictly lower level with targets equal to the producer counts;
+// each workgroup's list is in non-decreasing level order (so with all
+// workgroups co-resident the lowest unfinished task can always run); every
+// tile of the step appears exactly once. Empty string = valid.
+std::string validate_plan(const ModelShape& s, const Plan& plan);
+
+// Upper bound on tasks for any batch <= max_batch.
+int64_t max_tasks(const ModelShape& s, const TileConfig& cfg);
+
+}  // namespace mk

@@ -1,0 +1,705 @@
+// mk_tiles.h -- the tile functions of one decode step and the task
+// dispatcher shared by the persistent megakernel and the per-op kernels.
+//
+// The step is built from plain tiled matrix-vector products and paged
+// attention reorganised to one calling convention ("Cohere Publishes
+// One-Kernel Server for North Mini Code, Claims 1.58x vLLM Speedup", section
+// "A hand-built approach to a specialized server"; "Inside the Megakernel
+// Serving Engine for North Mini Code", paragraph 5): normalization,
+// projections, attention, routing and the experts (first page, section "The
+// delay is between operations").
+#pragma once
+
+#include "mk_device.h"
+
+namespace mk {
+
+// LDS layout (dynamic shared memory), byte offsets.
+//   [0, kLdsRoute)            general region: attention scores/probabilities
+//                             and combine coefficients, or the down tile's
+//                             staged expert activations and outputs
+//   [kLdsRoute, +kLdsRouteSz) routing results
+//   then 512 bytes of per-tile scalars
+constexpr int kLdsRouteSz = 1024;
+constexpr int kMaxDownRows = 64;
+
+struct LdsMap {
+    int route;  // offset of RouteLds
+    int misc;   // offset of scalars
+};
+
+__device__ __forceinline__ RouteLds* route_lds(char* lds, int general_bytes) {
+    return reinterpret_cast<RouteLds*>(lds + general_bytes);
+}
+__device__ __forceinline__ int* misc_lds(char* lds, int general_bytes) {
+    return reinterpret_cast<int*>(lds + general_bytes + kLdsRouteSz);
+}
+
+struct TileCtx {
+    const Params& p;
+    char* lds;
+    int general;      // bytes of the general LDS region
+    uint64_t* t_wait; // trace: when the compute wait ended
+};
+
+__device__ __forceinline__ float* x_at(const Params& p, int idx) {
+    return p.x + (int64_t)idx * p.max_batch * p.H;
+}
+
+// ------------------------------------------------------------------ embed
+
+__device__ __forceinline__ bool tile_embed(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int H8 = p.H >> 3;
+    for (int b = t.a0; b < t.a1; ++b) {
+        int tok = p.tokens[b];
+        if (tok < 0 || tok >= p.V) {
+            if (tid_() == 0) raise_error(p, kErrDevice, tok, false);
+            tok = 0;
+        }
+        const uint16_t* row = p.embed + (int64_t)tok * p.H;
+        float* xo = x_at(p, 0) + (int64_t)b * p.H;
+        for (int i = tid_(); i < H8; i += NT) {
+            const uint4 w = ld16(row + i * 8);
+            float4* o = reinterpret_cast<float4*>(xo + i * 8);
+            o[0] = make_float4(bflo(w.x), bfhi(w.x), bflo(w.y), bfhi(w.y));
+            o[1] = make_float4(bflo(w.z), bfhi(w.z), bflo(w.w), bfhi(w.w));
+        }
+    }
+    block_signal(p, t.signal);
+    return true;
+}
+
+// -------------------------------------------------------------------- QKV
+
+// Rows of one KV group g: the G*D query rows of its heads, then its D key
+// rows, then its D value rows ("virtual rows" a1..a2 of the group).
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, g = t.a0, v0 = t.a1, nrows = t.a2 - t.a1;
+    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
+    const uint16_t* W = wptr(p, l, W_QKV);
+    const int H = p.H, D = p.D, GD = p.G * p.D;
+    auto phys = [&](int v) -> int {
+        if (v < GD) return g * GD + v;
+        if (v < GD + D) return p.Hq * D + g * D + (v - GD);
+        return p.Hq * D + p.Hkv * D + g * D + (v - GD - D);
+    };
+    bool ok = true;
+    gemv_stream<NCH, PF, NB>(
+        nmine, H >> 3, [&](int i) { return W + (int64_t)phys(v0 + wave + i * NWAVES) * H; },
+        [&](float(&h)[NB][NCH][8]) {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, wptr(p, l, W_ATTN_NORM), p.eps);
+        },
+        [&](int, float(&)[NB][NCH][8]) {},
+        [&](int i, const float(&acc)[NB]) {
+            if (lane == 0) {
+                const int row = phys(v0 + wave + i * NWAVES);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b < p.B) p.qkv[(int64_t)b * p.QKVD + row] = acc[b];
+            }
+        });
+    if (!ok) return false;
+    block_signal(p, t.signal);
+    return true;
+}
+
+// -------------------------------------------------------------- attention
+
+// One chunk of split-KV paged attention for sequence b, KV head g, chunk c:
+// tokens [c*chunk, min((c+1)*chunk, pos+1)). The G query heads sharing the KV
+// head form the M dimension of BF16 MFMA tiles (fp32 operands split into
+// three BF16 parts). Old cache pages are loaded before the wait; the chunk
+// holding the new token also applies RoPE to k, rounds k and v to BF16 and
+// writes them into the pool. Writes (m, l, o) partials; the last chunk of
+// (b, g) to finish merges all partials by log-sum-exp.
+template <int D>
+__device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    constexpr int NDB = D / 32;                // QK d-blocks (32 wide)
+    constexpr int NTBW = kSC / 16 / NWAVES;    // 16-token blocks per wave per pass
+    constexpr int NDV = D / 16 / NWAVES;       // PV d-blocks (16 wide) per wave
+    constexpr int NKB = kSC / 32;              // PV k-blocks (32 tokens) per pass
+    const int l = t.layer, b = t.a0, g = t.a1, c = t.a2, nch = t.a3;
+    const int lane = tid_() & 63, wave = tid_() >> 6;
+    const int quad = lane >> 4, col = lane & 15;
+    const int G = p.G;
+    const int pos = p.positions[b];
+    const int t0 = c * p.chunk;
+    const int t1 = min(t0 + p.chunk, pos + 1);
+    const int t_old = min(t1, pos);
+    const bool has_new = (t1 == pos + 1);
+    const int* bt = p.block_tables + (int64_t)b * p.max_pages;
+    const int64_t hstride = (int64_t)16 * D;
+    const int64_t layer_pages = (int64_t)l * p.n_pages;
+
+    float* sS = reinterpret_cast<float*>(cx.lds);      // [16][kSPad] scores
+    float* sP = sS + 16 * kSPad;                         // [16][kSPad] probabilities
+    uint4* sQ = reinterpret_cast<uint4*>(sP + 16 * kSPad); // [3][NDB][64] query A-fragments
+    int* misc = misc_lds(cx.lds, cx.general);
+    float* sM = reinterpret_cast<float*>(misc);          // [16]
+    float* sL = sM + 16;                                 // [16]
+    float* sA = sL + 16;                                 // [16] rescale factors
+    uint16_t* sKn = reinterpret_cast<uint16_t*>(sA + 16); // [D] new key (bf16)
+    uint16_t* sVn = sKn + D;                              // [D] new value (bf16)
+    int* sLast = reinterpret_cast<int*>(sVn + D);
+
+    uint4 kf[NTBW][NDB];
+    uint4 vf[NDV][NKB];
+    auto load_kv = [&](int st0) {
+#pragma unroll
+        for (int i = 0; i < NTBW; ++i) {
+            const int tok = st0 + (wave + NWAVES * i) * 16 + col;
+            if (tok < t_old) {
+                const uint16_t* base = p.k_pool + ((layer_pages + bt[tok >> 4]) * p.Hkv + g) * hstride +
+                                       (tok & 15) * D + quad * 8;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) kf[i][db] = ld16(base + db * 32);
+            } else {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) kf[i][db] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NDV; ++j) {
+            const int d = (wave + NWAVES * j) * 16 + col;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int tv = st0 + kb * 32 + quad * 8;
+                if (tv < t_old) {
+                    vf[j][kb] = ld16(p.v_pool + ((layer_pages + bt[tv >> 4]) * p.Hkv + g) * hstride +
+                                     (int64_t)d * 16 + (tv & 15));
+                } else {
+                    vf[j][kb] = make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+    };
+    // After the loads land: zero tokens past the cached range, insert the new token.
+    auto fix_kv = [&](int st0) {
+#pragma unroll
+        for (int i = 0; i < NTBW; ++i) {
+            const int tok = st0 + (wave + NWAVES * i) * 16 + col;
+            if (has_new && tok == pos) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    kf[i][db] = *reinterpret_cast<const uint4*>(sKn + db * 32 + quad * 8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NDV; ++j) {
+            const int d = (wave + NWAVES * j) * 16 + col;
+            const uint32_t nv = has_new ? (uint32_t)sVn[d] : 0u;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int tv = st0 + kb * 32 + quad * 8;
+                uint32_t w[4] = {vf[j][kb].x, vf[j][kb].y, vf[j][kb].z, vf[j][kb].w};
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int tok = tv + jj;
+                    if (tok >= t_old) {
+                        const uint32_t val = (has_new && tok == pos) ? nv : 0u;
+                        if (jj & 1) w[jj >> 1] = (w[jj >> 1] & 0x0000ffffu) | (val << 16);
+                        else w[jj >> 1] = (w[jj >> 1] & 0xffff0000u) | val;
+                    }
+                }
+                vf[j][kb] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
+
+    load_kv(t0);
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+
+    const float* qkv = p.qkv + (int64_t)b * p.QKVD;
+    const float* rope = p.rope + (int64_t)b * D;  // [D/2][2]
+    // New token: RoPE on k, BF16 rounding of k and v, append to the pool.
+    if (has_new) {
+        for (int i = tid_(); i < D / 2; i += NT) {
+            const float cs = rope[2 * i], sn = rope[2 * i + 1];
+            const float a = qkv[p.Hq * D + g * D + i], bb = qkv[p.Hq * D + g * D + i + D / 2];
+            sKn[i] = (uint16_t)f2bf(a * cs - bb * sn);
+            sKn[i + D / 2] = (uint16_t)f2bf(a * sn + bb * cs);
+        }
+        for (int i = tid_(); i < D; i += NT) sVn[i] = (uint16_t)f2bf(qkv[(p.Hq + p.Hkv) * D + g * D + i]);
+        __syncthreads();
+        const int64_t page = bt[pos >> 4];
+        const int slot = pos & 15;
+        uint16_t* kd = p.k_pool + ((layer_pages + page) * p.Hkv + g) * hstride + slot * D;
+        uint16_t* vd = p.v_pool + ((layer_pages + page) * p.Hkv + g) * hstride + slot;
+        for (int i = tid_(); i < D; i += NT) {
+            kd[i] = sKn[i];
+            vd[(int64_t)i * 16] = sVn[i];
+        }
+    }
+
+    // Queries of the group's heads (rows 0..G-1 of the MFMA A operand), RoPE,
+    // 3-way BF16 split; wave 0 builds the fragments, every wave reads them.
+    if (wave == 0) {
+        float q[NDB][8];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                q[db][jj] = col < G ? qkv[(g * G + col) * D + db * 32 + quad * 8 + jj] : 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int i = db * 32 + quad * 8 + jj;
+                const float cs = rope[2 * i], sn = rope[2 * i + 1];
+                const float a = q[db][jj], bb = q[db + NDB / 2][jj];
+                q[db][jj] = a * cs - bb * sn;
+                q[db + NDB / 2][jj] = a * sn + bb * cs;
+            }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                uint32_t h0, m0, l0, h1, m1, l1;
+                split3(q[db][2 * k2], h0, m0, l0);
+                split3(q[db][2 * k2 + 1], h1, m1, l1);
+                hw[k2] = h0 | (h1 << 16);
+                mw[k2] = m0 | (m1 << 16);
+                lw[k2] = l0 | (l1 << 16);
+            }
+            sQ[(0 * NDB + db) * 64 + lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            sQ[(1 * NDB + db) * 64 + lane] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+            sQ[(2 * NDB + db) * 64 + lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+    }
+    if (tid_() < 16) {
+        sM[tid_()] = -INFINITY;
+        sL[tid_()] = 0.f;
+    }
+    // rows G..15 of the probability tile stay zero
+    for (int i = tid_(); i < (16 - G) * kSPad; i += NT) sP[G * kSPad + i] = 0.f;
+    __syncthreads();
+
+    f32x4_t oacc[NDV];
+#pragma unroll
+    for (int j = 0; j < NDV; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float scale = p.attn_scale;
+
+    for (int st0 = t0; st0 < t1; st0 += kSC) {
+        if (st0 != t0) load_kv(st0);
+        fix_kv(st0);
+        // scores S[h][t] = q_h . k_t * scale
+#pragma unroll
+        for (int i = 0; i < NTBW; ++i) {
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                s = mfma16x16x32(sQ[(0 * NDB + db) * 64 + lane], kf[i][db], s);
+                s = mfma16x16x32(sQ[(1 * NDB + db) * 64 + lane], kf[i][db], s);
+                s = mfma16x16x32(sQ[(2 * NDB + db) * 64 + lane], kf[i][db], s);
+            }
+            const int tl = (wave + NWAVES * i) * 16 + col;
+            const bool valid = st0 + tl < t1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = quad * 4 + r;
+                if (h < G) sS[h * kSPad + tl] = valid ? s[r] * scale : -INFINITY;
+            }
+        }
+        __syncthreads();
+        // online softmax over this pass
+        for (int h = wave; h < G; h += NWAVES) {
+            const float s0 = sS[h * kSPad + lane], s1 = sS[h * kSPad + lane + 64];
+            const float mx = wave_max(fmaxf(s0, s1));
+            const float m_old = sM[h];
+            const float m_new = fmaxf(m_old, mx);
+            const float alpha = expf(m_old - m_new);
+            const float e0 = expf(s0 - m_new), e1 = expf(s1 - m_new);
+            const float sum = wave_sum(e0 + e1);
+            sP[h * kSPad + lane] = e0;
+            sP[h * kSPad + lane + 64] = e1;
+            if (lane == 0) {
+                sM[h] = m_new;
+                sL[h] = sL[h] * alpha + sum;
+                sA[h] = alpha;
+            }
+        }
+        __syncthreads();
+        // o += P V
+#pragma unroll
+        for (int j = 0; j < NDV; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = quad * 4 + r;
+                oacc[j][r] *= (h < G) ? sA[h] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            uint4 pa[3];
+            {
+                const float* pr = sP + col * kSPad + kb * 32 + quad * 8;
+                uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    uint32_t h0, m0, l0, h1, m1, l1;
+                    split3(pr[2 * k2], h0, m0, l0);
+                    split3(pr[2 * k2 + 1], h1, m1, l1);
+                    hw[k2] = h0 | (h1 << 16);
+                    mw[k2] = m0 | (m1 << 16);
+                    lw[k2] = l0 | (l1 << 16);
+                }
+                pa[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                pa[1] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+                pa[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            }
+#pragma unroll
+            for (int j = 0; j < NDV; ++j) {
+                oacc[j] = mfma16x16x32(pa[0], vf[j][kb], oacc[j]);
+                oacc[j] = mfma16x16x32(pa[1], vf[j][kb], oacc[j]);
+                oacc[j] = mfma16x16x32(pa[2], vf[j][kb], oacc[j]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // partials: o (unnormalised), m, l
+    float* part = p.att_part + ((int64_t)b * p.Hq + g * G) * p.max_chunks * (D + 2);
+#pragma unroll
+    for (int j = 0; j < NDV; ++j) {
+        const int d = (wave + NWAVES * j) * 16 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = quad * 4 + r;
+            if (h < G) part[((int64_t)h * p.max_chunks + c) * (D + 2) + d] = oacc[j][r];
+        }
+    }
+    if (tid_() < G) {
+        part[((int64_t)tid_() * p.max_chunks + c) * (D + 2) + D] = sM[tid_()];
+        part[((int64_t)tid_() * p.max_chunks + c) * (D + 2) + D + 1] = sL[tid_()];
+    }
+    // arrival: the last chunk of (b, g) to finish does the merge
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid_() == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(p.ctr + p.cl.arrive(l, b, g), 1u, __ATOMIC_ACQ_REL,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        *sLast = (old + 1u == (uint32_t)nch) ? 1 : 0;
+    }
+    __syncthreads();
+    if (*sLast == 0) return true;
+
+    float* coef = sS;  // [G][nch], reuses the score tiles
+    for (int h = wave; h < G; h += NWAVES) {
+        const float* ph = part + (int64_t)h * p.max_chunks * (D + 2);
+        float mx = -INFINITY;
+        for (int cc = lane; cc < nch; cc += 64) mx = fmaxf(mx, ph[(int64_t)cc * (D + 2) + D]);
+        mx = wave_max(mx);
+        float lsum = 0.f;
+        for (int cc = lane; cc < nch; cc += 64)
+            lsum += expf(ph[(int64_t)cc * (D + 2) + D] - mx) * ph[(int64_t)cc * (D + 2) + D + 1];
+        lsum = wave_sum(lsum);
+        for (int cc = lane; cc < nch; cc += 64) coef[h * nch + cc] = expf(ph[(int64_t)cc * (D + 2) + D] - mx) / lsum;
+    }
+    __syncthreads();
+    float* out = p.att_out + (int64_t)b * p.Hq * D + g * G * D;
+    for (int idx = tid_(); idx < G * D; idx += NT) {
+        const int h = idx / D, d = idx - h * D;
+        const float* ph = part + (int64_t)h * p.max_chunks * (D + 2) + d;
+        float acc = 0.f;
+        for (int cc = 0; cc < nch; ++cc) acc = fmaf(coef[h * nch + cc], ph[(int64_t)cc * (D + 2)], acc);
+        out[idx] = acc;
+    }
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ------------------------------------------------------- output projection
+
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0;
+    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
+    const int K = p.Hq * p.D;
+    const uint16_t* W = wptr(p, l, W_O);
+    const float* xin = x_at(p, 2 * l);
+    float* xmid = x_at(p, 2 * l + 1);
+    bool ok = true;
+    gemv_stream<NCH, PF, NB>(
+        nmine, K >> 3, [&](int i) { return W + (int64_t)(r0 + wave + i * NWAVES) * K; },
+        [&](float(&h)[NB][NCH][8]) {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            load_x<NCH, NB>(h, p.att_out, K, p.B, K, nullptr, 0.f);
+        },
+        [&](int, float(&)[NB][NCH][8]) {},
+        [&](int i, const float(&acc)[NB]) {
+            if (lane == 0) {
+                const int row = r0 + wave + i * NWAVES;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b < p.B) xmid[(int64_t)b * p.H + row] = xin[(int64_t)b * p.H + row] + acc[b];
+            }
+        });
+    if (!ok) return false;
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ------------------------------------------------------------------ router
+
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0;
+    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
+    const int H = p.H;
+    const uint16_t* W = wptr(p, l, W_ROUTER);
+    const float* bias = reinterpret_cast<const float*>(p.wtab[l * W_NKINDS + W_RBIAS]);
+    bool ok = true;
+    gemv_stream<NCH, PF, NB>(
+        nmine, H >> 3, [&](int i) { return W + (int64_t)(r0 + wave + i * NWAVES) * H; },
+        [&](float(&h)[NB][NCH][8]) {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, wptr(p, l, W_FFN_NORM), p.eps);
+        },
+        [&](int, float(&)[NB][NCH][8]) {},
+        [&](int i, const float(&acc)[NB]) {
+            if (lane == 0) {
+                const int row = r0 + wave + i * NWAVES;
+                const float bv = bias != nullptr ? bias[row] : 0.f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b < p.B) p.rlogits[(int64_t)b * p.E + row] = bias != nullptr ? acc[b] + bv : acc[b];
+            }
+        });
+    if (!ok) return false;
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ---------------------------------------------------------- expert gate/up
+
+// Slot a0 (the a0-th distinct selected expert, ascending id), rows a1..a2 of
+// its gate and up matrices; a = SiLU(W_gate h2) * (W_up h2) for every token
+// routed to it. Task a3 != 0: also store the routing of this layer.
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1;
+    const int wave = tid_() >> 6, lane = tid_() & 63;
+    RouteLds* rt = route_lds(cx.lds, cx.general);
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+    compute_routing(p, rt);
+    if (t.a3 != 0) {
+        for (int i = tid_(); i < p.B * p.K; i += NT) {
+            const int b = i / p.K, j = i - b * p.K;
+            p.route_ids[((int64_t)l * p.max_batch + b) * p.K + j] = rt->ids[b][j];
+            p.route_w[((int64_t)l * p.max_batch + b) * p.K + j] = rt->w[b][j];
+        }
+    }
+    if (slot >= rt->nslots) {
+        block_signal(p, t.signal);
+        return true;
+    }
+    const int e = rt->slot_e[slot];
+    const int mask = rt->slot_mask[slot];
+    const int H = p.H;
+    const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * p.I * H;
+    const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * p.I * H;
+    const int npair = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
+    float gate[NB];
+    gemv_stream<NCH, PF, NB>(
+        2 * npair, H >> 3,
+        [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
+        [&](float(&h)[NB][NCH][8]) {
+            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, wptr(p, l, W_FFN_NORM), p.eps);
+        },
+        [&](int, float(&)[NB][NCH][8]) {},
+        [&](int i, const float(&acc)[NB]) {
+            if ((i & 1) == 0) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) gate[b] = acc[b];
+            } else if (lane == 0) {
+                const int row = r0 + wave + (i >> 1) * NWAVES;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < p.B && ((mask >> b) & 1)) {
+                        const float gv = gate[b];
+                        const float a = (gv / (1.0f + expf(-gv))) * acc[b];
+                        p.act[((int64_t)b * p.K + rt->slot_rank[slot][b]) * p.I + row] = a;
+                    }
+                }
+            }
+        });
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ------------------------------------------------------------ expert down
+
+// Rows a0..a1 of the hidden dimension, for every selected expert: y = W_down a,
+// then x_out = x_mid + sum_j w_j y_j in top-k rank order.
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0;
+    const int wave = tid_() >> 6, lane = tid_() & 63;
+    RouteLds* rt = route_lds(cx.lds, cx.general);
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+    compute_routing(p, rt);
+    const int I = p.I, K = p.K, B = p.B;
+    const int nslots = rt->nslots;
+    // wave w takes slots w, w+4, ...; row-vector i -> slot index i / nrows, row i % nrows
+    const int myslots = nslots > wave ? (nslots - wave + NWAVES - 1) / NWAVES : 0;
+    const uint16_t* Wd = wptr(p, l, W_DOWN);
+    float* sAct = reinterpret_cast<float*>(cx.lds);                 // [B*K][I]
+    float* sY = sAct + (int64_t)B * K * I;                          // [B*K][nrows]
+    bool ok = true;
+    const int K8 = I >> 3;
+    gemv_stream<NCH, PF, NB>(
+        myslots * nrows, K8,
+        [&](int i) {
+            const int s = wave + (i / nrows) * NWAVES;
+            return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + (i % nrows)) * I;
+        },
+        [&](float(&)[NB][NCH][8]) {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            const float4* src = reinterpret_cast<const float4*>(p.act);
+            float4* dst = reinterpret_cast<float4*>(sAct);
+            for (int i = tid_(); i < B * K * I / 4; i += NT) dst[i] = src[i];
+            __syncthreads();
+        },
+        [&](int i, float(&h)[NB][NCH][8]) {
+            if (i % nrows == 0) {
+                const int s = wave + (i / nrows) * NWAVES;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) {
+                        const int ch = lane + 64 * c;
+                        if (rank >= 0 && ch < K8) {
+                            const float4* a = reinterpret_cast<const float4*>(sAct + ((int64_t)b * K + rank) * I + ch * 8);
+                            const float4 u = a[0], v = a[1];
+                            h[b][c][0] = u.x; h[b][c][1] = u.y; h[b][c][2] = u.z; h[b][c][3] = u.w;
+                            h[b][c][4] = v.x; h[b][c][5] = v.y; h[b][c][6] = v.z; h[b][c][7] = v.w;
+                        } else {
+#pragma unroll
+                            for (int jj = 0; jj < 8; ++jj) h[b][c][jj] = 0.f;
+                        }
+                    }
+                }
+            }
+        },
+        [&](int i, const float(&acc)[NB]) {
+            if (lane == 0) {
+                const int s = wave + (i / nrows) * NWAVES;
+                const int r = i % nrows;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
+                    if (rank >= 0) sY[((int64_t)b * K + rank) * nrows + r] = acc[b];
+                }
+            }
+        });
+    if (!ok) return false;
+    __syncthreads();
+    const float* xmid = x_at(p, 2 * l + 1);
+    float* xout = x_at(p, 2 * l + 2);
+    for (int idx = tid_(); idx < B * nrows; idx += NT) {
+        const int b = idx / nrows, r = idx - b * nrows;
+        float acc = 0.f;
+        for (int j = 0; j < K; ++j) acc += rt->w[b][j] * sY[((int64_t)b * K + j) * nrows + r];
+        xout[(int64_t)b * p.H + h0 + r] = xmid[(int64_t)b * p.H + h0 + r] + acc;
+    }
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ---------------------------------------------------------------- LM head
+
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int r0 = t.a0, nrows = t.a1 - t.a0;
+    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
+    const int H = p.H;
+    bool ok = true;
+    gemv_stream<NCH, PF, NB>(
+        nmine, H >> 3, [&](int i) { return p.lm_head + (int64_t)(r0 + wave + i * NWAVES) * H; },
+        [&](float(&h)[NB][NCH][8]) {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, p.final_norm, p.eps);
+        },
+        [&](int, float(&)[NB][NCH][8]) {},
+        [&](int i, const float(&acc)[NB]) {
+            if (lane == 0) {
+                const int row = r0 + wave + i * NWAVES;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    if (b < p.B) p.logits[(int64_t)b * p.V + row] = acc[b];
+            }
+        });
+    if (!ok) return false;
+    block_signal(p, t.signal);
+    return true;
+}
+
+// -------------------------------------------------------------- dispatcher
+
+// Compile-time shape of a kernel build: 16-byte chunks per lane per row
+// (ceil(K / 512)) for the three reduction lengths in the model -- hidden
+// size H, attention width Hq*D and expert width I -- and the head size. Each
+// supported model gets its own kernels, so each tile is compiled only for
+// the reduction lengths it actually sees and register allocation is sized
+// per tile, not for every possible shape.
+template <int NCH_H_, int NCH_O_, int NCH_I_, int D_>
+struct Shape {
+    static constexpr int NCH_H = NCH_H_, NCH_O = NCH_O_, NCH_I = NCH_I_, D = D_;
+};
+
+// Rows in flight per wave for a given chunk count and batch.
+template <int NCH, int NB>
+struct Pf {
+    static constexpr int v = NB == 1 ? (NCH <= 2 ? 8 : (NCH <= 4 ? 4 : 2)) : (NCH <= 1 ? 8 : (NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1)));
+};
+
+template <class S, int NB>
+__device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
+    switch (t.op) {
+        case OP_EMBED: return tile_embed(t, cx);
+        case OP_QKV: return tile_qkv<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+        case OP_ATTN: return tile_attn<S::D>(t, cx);
+        case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
+        case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+        case OP_GATEUP: return tile_gateup<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+        case OP_DOWN: return tile_down<S::NCH_I, Pf<S::NCH_I, NB>::v, NB>(t, cx);
+        case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+        default: return false;
+    }
+}
+
+// Run one task; with tracing on, thread 0 records {task | wg << 32, start,
+// end of the compute wait, end}.
+template <class S, int NB>
+__device__ __forceinline__ bool run_task(const Task& t, const Params& p, char* lds, int general, int idx) {
+    uint64_t t_start = 0, t_wait = 0;
+    if (p.trace_on && tid_() == 0) t_start = t_wait = wall_clock64();
+    TileCtx cx{p, lds, general, &t_wait};
+    const bool ok = dispatch_tile<S, NB>(t, cx);
+    if (p.trace_on && tid_() == 0) {
+        uint64_t* rec = p.trace + (int64_t)idx * 4;
+        rec[0] = (uint64_t)(uint32_t)idx | ((uint64_t)blockIdx.x << 32);
+        rec[1] = t_start;
+        rec[2] = t_wait;
+        rec[3] = wall_clock64();
+    }
+    return ok;
+}
+
+}  // namespace mk

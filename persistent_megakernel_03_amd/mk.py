@@ -1,0 +1,310 @@
+"""ctypes binding of libmk (include/mk.h): the same entry points, argument
+marshalling only. Every step of the decode runs in the HIP library; torch is
+used here only to own device memory and streams.
+
+``load()`` must run after ``import torch`` so that torch and libmk share one
+HIP runtime (both name ``libamdhip64.so.7``; the dynamic linker reuses the one
+torch loaded). It raises if the library is missing -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import sys
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK = 0
+MK_ERR_INVALID = -1
+MK_ERR_UNSUPPORTED = -2
+MK_ERR_CAPACITY = -3
+MK_ERR_BAD_PAGE = -4
+MK_ERR_HIP = -5
+MK_ERR_TIMEOUT = -6
+MK_ERR_DEVICE = -7
+MK_MODE_MEGAKERNEL = 0
+MK_MODE_PEROP = 1
+
+STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_CAPACITY",
+                -4: "MK_ERR_BAD_PAGE", -5: "MK_ERR_HIP", -6: "MK_ERR_TIMEOUT", -7: "MK_ERR_DEVICE"}
+
+# Every function declared in include/mk.h.
+EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_set_mode",
+           "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_get_trace", "mk_kernel_time",
+           "mk_destroy", "mk_last_error"]
+
+
+class MkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class mk_dims(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("moe_inter", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("max_batch", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("n_pages", ctypes.c_int64)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class mk_weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("attn_norm", _PP), ("wqkv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("router", _PP),
+                ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP), ("router_bias", _PP)]
+
+
+class mk_options(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("trace", ctypes.c_int32), ("watchdog_ns", ctypes.c_int64),
+                ("wg_per_cu", ctypes.c_int32), ("split_kv_tokens", ctypes.c_int32),
+                ("n_cu_override", ctypes.c_int32), ("time_kernels", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
+
+
+class mk_debug_ptrs(ctypes.Structure):
+    _fields_ = [("x_layers", ctypes.c_void_p), ("route_ids", ctypes.c_void_p), ("route_w", ctypes.c_void_p),
+                ("router_logits", ctypes.c_void_p), ("trace", ctypes.c_void_p),
+                ("trace_capacity", ctypes.c_int64)]
+
+
+class mk_plan_info(ctypes.Structure):
+    _fields_ = [("n_wg", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("n_counters", ctypes.c_int32),
+                ("n_levels", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open libmk.so (built in-tree by persistent_megakernel_03_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if "torch" not in sys.modules:
+        import torch  # noqa: F401  (share torch's HIP runtime)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m persistent_megakernel_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    c = ctypes
+    lib.mk_kv_pool_bytes.argtypes = [c.POINTER(mk_dims)]
+    lib.mk_kv_pool_bytes.restype = c.c_size_t
+    lib.mk_workspace_bytes.argtypes = [c.POINTER(mk_dims), c.POINTER(mk_options)]
+    lib.mk_workspace_bytes.restype = c.c_size_t
+    lib.mk_create.argtypes = [c.POINTER(mk_dims), c.POINTER(mk_weights), c.c_void_p, c.c_void_p, c.c_void_p,
+                              c.c_size_t, c.POINTER(mk_options), c.c_int, c.POINTER(c.c_void_p)]
+    lib.mk_create.restype = c.c_int
+    lib.mk_decode_step.argtypes = [c.c_void_p, c.c_int32, c.POINTER(c.c_int32), c.POINTER(c.c_int32),
+                                   c.POINTER(c.c_int32), c.c_void_p, c.c_void_p, c.c_void_p]
+    lib.mk_decode_step.restype = c.c_int
+    lib.mk_set_mode.argtypes = [c.c_void_p, c.c_int32]
+    lib.mk_set_mode.restype = c.c_int
+    lib.mk_sync_check.argtypes = [c.c_void_p, c.c_void_p]
+    lib.mk_sync_check.restype = c.c_int
+    lib.mk_get_debug_ptrs.argtypes = [c.c_void_p, c.POINTER(mk_debug_ptrs)]
+    lib.mk_get_debug_ptrs.restype = c.c_int
+    lib.mk_plan_build.argtypes = [c.POINTER(mk_dims), c.POINTER(mk_options), c.c_int32, c.c_int32,
+                                  c.POINTER(c.c_int32), c.POINTER(mk_plan_info), c.POINTER(c.c_int32), c.c_int64,
+                                  c.POINTER(c.c_int32), c.POINTER(c.c_int32)]
+    lib.mk_plan_build.restype = c.c_int
+    lib.mk_get_trace.argtypes = [c.c_void_p, c.c_void_p, c.c_size_t, c.POINTER(c.c_size_t)]
+    lib.mk_get_trace.restype = c.c_int
+    lib.mk_kernel_time.argtypes = [c.c_void_p, c.POINTER(c.c_float)]
+    lib.mk_kernel_time.restype = c.c_int
+    lib.mk_destroy.argtypes = [c.c_void_p]
+    lib.mk_destroy.restype = None
+    lib.mk_last_error.argtypes = []
+    lib.mk_last_error.restype = c.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != MK_OK:
+        raise MkError(st, load().mk_last_error().decode())
+
+
+def _i32(a) -> ctypes.Array:
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def make_dims(cfg: dict, max_batch: int, max_pages_per_seq: int, n_pages: int) -> mk_dims:
+    return mk_dims(cfg["n_layers"], cfg["hidden"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                   cfg["n_experts"], cfg["top_k"], cfg["moe_inter"], cfg["vocab"], cfg["page_size"],
+                   cfg.get("rms_eps", 1e-6), cfg.get("rope_theta", 10000.0), max_batch, max_pages_per_seq,
+                   n_pages)
+
+
+def make_options(mode: int = MK_MODE_MEGAKERNEL, trace: bool = False, watchdog_ns: int = 0, wg_per_cu: int = 0,
+                 split_kv_tokens: int = 0, n_cu_override: int = 0, time_kernels: bool = False) -> mk_options:
+    o = mk_options()
+    o.mode, o.trace, o.watchdog_ns = mode, int(bool(trace)), watchdog_ns
+    o.wg_per_cu, o.split_kv_tokens, o.n_cu_override = wg_per_cu, split_kv_tokens, n_cu_override
+    o.time_kernels = int(bool(time_kernels))
+    return o
+
+
+# ----------------------------------------------------------- thin wrappers --
+
+def mk_kv_pool_bytes(dims: mk_dims) -> int:
+    return int(load().mk_kv_pool_bytes(ctypes.byref(dims)))
+
+
+def mk_workspace_bytes(dims: mk_dims, opts: mk_options) -> int:
+    return int(load().mk_workspace_bytes(ctypes.byref(dims), ctypes.byref(opts)))
+
+
+def mk_create(dims: mk_dims, weights: mk_weights, k_pool: int, v_pool: int, workspace: int, workspace_bytes: int,
+              opts: mk_options, device: int = 0) -> int:
+    h = ctypes.c_void_p()
+    _check(load().mk_create(ctypes.byref(dims), ctypes.byref(weights), ctypes.c_void_p(k_pool),
+                            ctypes.c_void_p(v_pool), ctypes.c_void_p(workspace), workspace_bytes,
+                            ctypes.byref(opts), device, ctypes.byref(h)))
+    return h.value
+
+
+def mk_decode_step(h: int, batch: int, seq_ids, positions, block_tables, tokens: int, logits: int,
+                   stream: int) -> None:
+    s_arr, s_p = _i32(seq_ids) if seq_ids is not None else (None, None)
+    p_arr, p_p = _i32(positions)
+    b_arr, b_p = _i32(block_tables)
+    _check(load().mk_decode_step(ctypes.c_void_p(h), batch, s_p, p_p, b_p, ctypes.c_void_p(tokens),
+                                 ctypes.c_void_p(logits), ctypes.c_void_p(stream)))
+
+
+def mk_set_mode(h: int, mode: int) -> None:
+    _check(load().mk_set_mode(ctypes.c_void_p(h), mode))
+
+
+def mk_sync_check(h: int, stream: int) -> int:
+    """Returns the status (MK_OK, MK_ERR_TIMEOUT, MK_ERR_DEVICE) instead of raising for device errors."""
+    st = load().mk_sync_check(ctypes.c_void_p(h), ctypes.c_void_p(stream))
+    if st in (MK_OK, MK_ERR_TIMEOUT, MK_ERR_DEVICE):
+        return st
+    _check(st)
+    return st
+
+
+def mk_get_debug_ptrs(h: int) -> mk_debug_ptrs:
+    out = mk_debug_ptrs()
+    _check(load().mk_get_debug_ptrs(ctypes.c_void_p(h), ctypes.byref(out)))
+    return out
+
+
+def mk_plan_build(dims: mk_dims, opts: mk_options, n_wg: int, positions: Sequence[int]):
+    """Returns (info, tasks [n_tasks][12] int32, wg_offsets, counter_targets)."""
+    lib = load()
+    p_arr, p_p = _i32(positions)
+    info = mk_plan_info()
+    _check(lib.mk_plan_build(ctypes.byref(dims), ctypes.byref(opts), n_wg, len(p_arr), p_p, ctypes.byref(info),
+                             None, 0, None, None))
+    tasks = np.zeros((info.n_tasks, 12), np.int32)
+    offs = np.zeros(info.n_wg + 1, np.int32)
+    targets = np.zeros(info.n_counters, np.int32)
+    _check(lib.mk_plan_build(ctypes.byref(dims), ctypes.byref(opts), n_wg, len(p_arr), p_p, ctypes.byref(info),
+                             tasks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), info.n_tasks,
+                             offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                             targets.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return info, tasks, offs, targets
+
+
+def mk_get_trace(h: int) -> np.ndarray:
+    lib = load()
+    n = ctypes.c_size_t()
+    _check(lib.mk_get_trace(ctypes.c_void_p(h), None, 0, ctypes.byref(n)))
+    buf = np.zeros(n.value // 8, np.uint64)
+    _check(lib.mk_get_trace(ctypes.c_void_p(h), buf.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)))
+    return buf.reshape(-1, 4)
+
+
+def mk_kernel_time(h: int) -> float:
+    ms = ctypes.c_float()
+    _check(load().mk_kernel_time(ctypes.c_void_p(h), ctypes.byref(ms)))
+    return float(ms.value)
+
+
+def mk_destroy(h: int) -> None:
+    load().mk_destroy(ctypes.c_void_p(h))
+
+
+# ------------------------------------------------------------ convenience --
+
+class Decoder:
+    """Owns the torch tensors a handle points into (weights dict, KV pools,
+    workspace) and forwards calls to the C ABI. No arithmetic happens here."""
+
+    def __init__(self, cfg: dict, weights: Dict[str, "torch.Tensor"], k_pool, v_pool, max_batch: int,
+                 max_pages_per_seq: int, mode: int = MK_MODE_MEGAKERNEL, trace: bool = False,
+                 watchdog_ns: int = 0, wg_per_cu: int = 0, split_kv_tokens: int = 0, device: int = 0,
+                 time_kernels: bool = False):
+        import torch
+        self.cfg = dict(cfg)
+        self.dims = make_dims(cfg, max_batch, max_pages_per_seq, k_pool.shape[1])
+        self.opts = make_options(mode, trace, watchdog_ns, wg_per_cu, split_kv_tokens, 0, time_kernels)
+        L = cfg["n_layers"]
+        self._keep: List = [weights, k_pool, v_pool]
+
+        def arr(kind):
+            a = (ctypes.c_void_p * L)(*[weights[f"layers.{l}.{kind}"].data_ptr() for l in range(L)])
+            self._keep.append(a)
+            return ctypes.cast(a, _PP)
+
+        w = mk_weights()
+        w.embed = weights["embed"].data_ptr()
+        w.lm_head = weights["lm_head"].data_ptr()
+        w.final_norm = weights["final_norm"].data_ptr()
+        w.attn_norm, w.wqkv, w.wo = arr("attn_norm"), arr("wqkv"), arr("wo")
+        w.ffn_norm, w.router = arr("ffn_norm"), arr("router")
+        w.w_gate, w.w_up, w.w_down = arr("w_gate"), arr("w_up"), arr("w_down")
+        if f"layers.0.router_bias" in weights:
+            w.router_bias = arr("router_bias")
+        self.weights_struct = w
+        nbytes = mk_workspace_bytes(self.dims, self.opts)
+        if nbytes == 0:
+            raise MkError(MK_ERR_UNSUPPORTED, load().mk_last_error().decode() or "unsupported dims")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=k_pool.device)
+        self.k_pool, self.v_pool = k_pool, v_pool
+        self.handle = mk_create(self.dims, w, k_pool.data_ptr(), v_pool.data_ptr(), self.workspace.data_ptr(),
+                                nbytes, self.opts, device)
+
+    def step(self, positions, block_tables, tokens, logits, stream=None, seq_ids=None):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        positions = np.asarray(positions, np.int32)
+        mk_decode_step(self.handle, len(positions), seq_ids, positions, np.asarray(block_tables, np.int32),
+                       tokens.data_ptr(), logits.data_ptr(), stream)
+
+    def set_mode(self, mode: int):
+        mk_set_mode(self.handle, mode)
+
+    def sync_check(self, stream=None) -> int:
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        return mk_sync_check(self.handle, stream)
+
+    def kernel_ms(self) -> float:
+        return mk_kernel_time(self.handle)
+
+    def debug(self) -> mk_debug_ptrs:
+        return mk_get_debug_ptrs(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            mk_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,137 @@
+"""CPU tests of the C ABI library: it loads, exports every declared entry
+point, and its host task-graph builder produces valid, deadlock-free plans.
+No device code runs here."""
+
+import re
+import os
+import random
+from collections import defaultdict
+
+import numpy as np
+import pytest
+
+from persistent_megakernel_03_amd import configs, mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OP_EMBED, OP_QKV, OP_ATTN, OP_OPROJ, OP_ROUTER, OP_GATEUP, OP_DOWN, OP_LMHEAD = range(8)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = mk.load()
+    names = header_functions()
+    assert set(names) == set(mk.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_and_pool_sizes():
+    d = mk.make_dims(configs.A3B, 1, 520, 520)
+    assert mk.mk_kv_pool_bytes(d) == 48 * 520 * 4 * 16 * 128 * 2
+    ws = mk.mk_workspace_bytes(d, mk.make_options())
+    assert ws > 0
+    # unsupported shapes report 0 bytes
+    bad = dict(configs.A3B, head_dim=96)
+    assert mk.mk_workspace_bytes(mk.make_dims(bad, 1, 520, 520), mk.make_options()) == 0
+
+
+def simulate(tasks, offs, targets, rng):
+    """Run the per-workgroup lists with a random interleaving and the counter
+    protocol; return the final counters, or raise on deadlock."""
+    n_wg = len(offs) - 1
+    ctr = defaultdict(int)
+    arrive = defaultdict(int)
+    nxt = [int(offs[w]) for w in range(n_wg)]
+    stage = [0] * n_wg  # 0: before pre-wait, 1: before compute wait
+    live = [w for w in range(n_wg) if nxt[w] < offs[w + 1]]
+    steps = 0
+    while live:
+        progressed = False
+        rng.shuffle(live)
+        for w in list(live):
+            t = tasks[nxt[w]]
+            op, layer, a0, a1, a2, a3, pre_c, pre_t, c, tg, sig, lvl = [int(v) for v in t]
+            if stage[w] == 0:
+                if pre_c >= 0 and ctr[pre_c] < pre_t:
+                    continue
+                stage[w] = 1
+            if c >= 0 and ctr[c] < tg:
+                continue
+            # run the tile
+            if op == OP_ATTN:
+                arrive[(layer, a0, a1)] += 1
+                if arrive[(layer, a0, a1)] == a3:
+                    ctr[sig] += 1
+            elif sig >= 0:
+                ctr[sig] += 1
+            nxt[w] += 1
+            stage[w] = 0
+            progressed = True
+            steps += 1
+            if nxt[w] >= offs[w + 1]:
+                live.remove(w)
+        if not progressed:
+            raise RuntimeError("deadlock")
+    return ctr, steps
+
+
+@pytest.mark.parametrize("cfg_name,batch,positions,n_wg", [
+    ("TINY", 1, [64], 16),
+    ("TINY", 2, [5, 70], 7),
+    ("TINY", 1, [0], 512),
+    ("A3B", 1, [8192], 512),
+    ("A3B", 2, [100, 3000], 256),
+])
+def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
+    cfg = configs.dims_of(cfg_name)
+    d = mk.make_dims(cfg, 2, 600, 1200)
+    info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), n_wg, positions)
+    assert info.n_tasks == len(tasks) and offs[-1] == len(tasks)
+    # each workgroup list is in non-decreasing dependency level
+    for w in range(n_wg):
+        lv = tasks[offs[w]:offs[w + 1], 11]
+        assert np.all(np.diff(lv) >= 0)
+    # the counters reach exactly their targets, whatever the interleaving
+    for seed in range(2 if cfg_name == "A3B" else 5):
+        ctr, steps = simulate(tasks, offs, targets, random.Random(seed))
+        assert steps == len(tasks)
+        for c, t in enumerate(targets):
+            assert ctr[c] == t, (c, ctr[c], t)
+    # attention chunks cover every cached token plus the new one
+    chunk = info.chunk_tokens
+    for b in range(batch):
+        att = tasks[(tasks[:, 0] == OP_ATTN) & (tasks[:, 2] == b) & (tasks[:, 1] == 0)]
+        n = -(-(positions[b] + 1) // chunk)
+        assert len(att) == cfg["n_kv_heads"] * n
+        assert set(att[:, 5]) == {n}
+
+
+def test_plan_counts_for_the_30b_shape():
+    d = mk.make_dims(configs.A3B, 1, 520, 520)
+    info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192])
+    ops = np.bincount(tasks[:, 0], minlength=8)
+    assert ops[OP_EMBED] == 1
+    assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
+    assert ops[OP_ATTN] == 48 * 4 * 65         # 8193 tokens in 128-token chunks
+    assert ops[OP_OPROJ] == 48 * 256
+    assert ops[OP_ROUTER] == 48 * 16
+    assert ops[OP_GATEUP] == 48 * 8 * 48       # 8 slots x 768 rows / 16
+    assert ops[OP_DOWN] == 48 * 512
+    assert ops[OP_LMHEAD] == -(-151936 // 64)
+    assert info.n_levels == 2 + 6 * 48
+
+
+def test_plan_rejects_bad_input():
+    d = mk.make_dims(configs.TINY, 1, 8, 16)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_build(d, mk.make_options(), 8, [1, 2])   # batch above max_batch
+    assert e.value.status == mk.MK_ERR_CAPACITY
+    bad = mk.make_dims(dict(configs.TINY, page_size=32), 1, 8, 16)
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_build(bad, mk.make_options(), 8, [1])
+    assert e.value.status == mk.MK_ERR_UNSUPPORTED
