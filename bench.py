@@ -66,7 +66,7 @@ def main():
     cfg = configs.A3B
     B, ctx = args.batch, args.context
     P = cfg["page_size"]
-    total_tokens = ctx + args.warmup + args.steps + 1
+    total_tokens = ctx + args.warmup + args.steps + 16 + 1  # + the per-step kernel timing pass
     pages_per_seq = -(-total_tokens // P)
     n_pages = pages_per_seq * B + 1
     t0 = time.time()

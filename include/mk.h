@@ -180,11 +180,13 @@ mk_status mk_sync_check(mk_handle* h, void* stream);
 /*
  * Device addresses of per-step results kept in the workspace, for checking
  * and tracing. Valid until mk_destroy; contents refer to the last step.
- *   x_layers: fp32 [2L + 1][max_batch][H]: the residual stream; entry 0 is
- *             the embedding, 2l + 1 the residual after layer l's attention
- *             block, 2l + 2 after its MoE block
+ * Slices are padded: pad64(n) is n rounded up to a multiple of 64 floats.
+ *   x_layers: fp32 [2L + 1] slices of stride pad64(max_batch * H), each
+ *             [max_batch][H]: the residual stream; slice 0 is the embedding,
+ *             2l + 1 the residual after layer l's attention block, 2l + 2
+ *             after its MoE block
  *   route_ids: int32 [L][max_batch][k], route_w: fp32 [L][max_batch][k]
- *   router_logits: fp32 [max_batch][E] (last layer's)
+ *   router_logits: fp32 [L] slices of stride pad64(max_batch * E)
  */
 typedef struct mk_debug_ptrs {
     const float* x_layers;

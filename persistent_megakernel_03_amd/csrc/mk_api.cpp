@@ -53,7 +53,7 @@ constexpr int kMaxChunksCap = 512;
 constexpr int kStageSlots = 4;
 
 struct Layout {
-    size_t err, banks, x, qkv, att_part, att_out, rlogits, route_ids, route_w, act, wtab, step, tasks, wg_off,
+    size_t err, banks, x, qkv, att_part, att_ml, att_out, rlogits, route_ids, route_w, act, wtab, step, tasks, wg_off,
         level_tasks, trace, total;
     int64_t bank_words;
     int max_chunks;
@@ -130,14 +130,17 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
     };
     L.err = take(256);
     L.banks = take(2 * (size_t)L.bank_words * 4);
-    L.x = take((size_t)(2 * d.n_layers + 1) * B * H * 4);
-    L.qkv = take((size_t)B * QKVD * 4);
-    L.att_part = take((size_t)B * d.n_q_heads * L.max_chunks * (d.head_dim + 2) * 4);
-    L.att_out = take((size_t)B * d.n_q_heads * d.head_dim * 4);
-    L.rlogits = take((size_t)B * d.n_experts * 4);
+    // exchange buffers: one 256-byte-padded slice per layer (see pad64)
+    const size_t Ln = (size_t)d.n_layers;
+    L.x = take((size_t)(2 * d.n_layers + 1) * pad64(B * H) * 4);
+    L.qkv = take(Ln * pad64(B * QKVD) * 4);
+    L.att_part = take(Ln * pad64(B * d.n_q_heads * (int64_t)L.max_chunks * d.head_dim) * 4);
+    L.att_ml = take(Ln * B * d.n_q_heads * pad64(2 * (int64_t)L.max_chunks) * 4);
+    L.att_out = take(Ln * pad64(B * d.n_q_heads * d.head_dim) * 4);
+    L.rlogits = take(Ln * pad64(B * d.n_experts) * 4);
     L.route_ids = take((size_t)d.n_layers * B * d.top_k * 4);
     L.route_w = take((size_t)d.n_layers * B * d.top_k * 4);
-    L.act = take((size_t)B * d.top_k * d.moe_inter * 4);
+    L.act = take(Ln * pad64(B * d.top_k * d.moe_inter) * 4);
     L.wtab = take((size_t)d.n_layers * W_NKINDS * 8);
     // per-step arrays: positions, chunk counts, rotary table, block tables
     L.step_bytes = align256((size_t)B * 4) * 2 + align256((size_t)B * d.head_dim * 4) +
@@ -246,7 +249,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         const int G = d.n_q_heads / d.n_kv_heads;
         const int max_chunks = max_chunks_for(d);
         const size_t attn = (size_t)2 * 16 * (128 + 4) * 4 + (size_t)3 * (d.head_dim / 32) * 64 * 16;
-        const size_t comb = (size_t)G * max_chunks * 4;
+        const size_t comb = (size_t)(16 + max_chunks + 4 + 1024) * 4;
         const size_t down = ((size_t)d.max_batch * d.top_k * d.moe_inter + (size_t)d.max_batch * d.top_k * 64) * 4;
         const size_t general = align256(std::max(attn, std::max(comb, down)));
         h->general = (int)general;
@@ -334,6 +337,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         p.x = reinterpret_cast<float*>(h->ws + h->lay.x);
         p.qkv = reinterpret_cast<float*>(h->ws + h->lay.qkv);
         p.att_part = reinterpret_cast<float*>(h->ws + h->lay.att_part);
+        p.att_ml = reinterpret_cast<float*>(h->ws + h->lay.att_ml);
         p.att_out = reinterpret_cast<float*>(h->ws + h->lay.att_out);
         p.rlogits = reinterpret_cast<float*>(h->ws + h->lay.rlogits);
         p.route_ids = reinterpret_cast<int32_t*>(h->ws + h->lay.route_ids);

@@ -22,18 +22,19 @@ namespace mk {
 
 // Operation codes, in dependency-level order inside a layer.
 enum Op : int32_t {
-    OP_EMBED = 0,  // x0[b] = embedding row of token b
-    OP_QKV = 1,    // fused RMSNorm + QKV rows of one KV group
-    OP_ATTN = 2,   // RoPE (+ KV append) + split-KV attention chunk; last chunk combines
-    OP_OPROJ = 3,  // output projection + residual
-    OP_ROUTER = 4, // fused RMSNorm + router logits
-    OP_GATEUP = 5, // top-k + expert gate/up rows + SwiGLU
-    OP_DOWN = 6,   // top-k + expert down rows + weighted combine + residual
-    OP_LMHEAD = 7, // fused final RMSNorm + LM-head rows
-    OP_COUNT = 8
+    OP_EMBED = 0,   // x0[b] = embedding row of token b
+    OP_QKV = 1,     // fused RMSNorm + QKV rows of one KV group
+    OP_ATTN = 2,    // RoPE (+ KV append) + split-KV attention over one chunk of tokens
+    OP_COMBINE = 3, // merge one query head's chunk partials (log-sum-exp)
+    OP_OPROJ = 4,   // output projection + residual
+    OP_ROUTER = 5,  // fused RMSNorm + router logits
+    OP_GATEUP = 6,  // top-k + expert gate/up rows + SwiGLU
+    OP_DOWN = 7,    // top-k + expert down rows + weighted combine + residual
+    OP_LMHEAD = 8,  // fused final RMSNorm + LM-head rows
+    OP_COUNT = 9
 };
 
-constexpr int kLevelsPerLayer = 6;  // QKV, ATTN, OPROJ, ROUTER, GATEUP, DOWN
+constexpr int kLevelsPerLayer = 7;  // QKV, ATTN, COMBINE, OPROJ, ROUTER, GATEUP, DOWN
 
 // Dependency level of an op in layer l (0 = embedding, last = LM head).
 inline int op_level(int op, int layer, int n_layers) {
@@ -61,31 +62,31 @@ enum WKind : int32_t {
     W_ATTN_NORM = 0, W_QKV, W_O, W_FFN_NORM, W_ROUTER, W_GATE, W_UP, W_DOWN, W_RBIAS, W_NKINDS
 };
 
-// Counter bank layout. Main counters sit one per 128-byte line; the attention
-// arrival counters ([L][max_batch][Hkv]) are packed after them.
-constexpr int kCtrStride = 32;  // uint32 words per main counter
+// Counter bank layout: one counter per 128-byte line. Per layer: one QKV
+// counter and one attention counter per KV group, then the combine, output
+// projection, router, gate/up and down counters.
+constexpr int kCtrStride = 32;  // uint32 words per counter
 
 struct CounterLayout {
     int n_layers, n_kv_heads, max_batch;
-    MK_HD int per_layer() const { return n_kv_heads + 5; }
+    MK_HD int per_layer() const { return 2 * n_kv_heads + 5; }
     MK_HD int embed() const { return 0; }
     MK_HD int qkv(int l, int g) const { return 1 + l * per_layer() + g; }
-    MK_HD int attn(int l) const { return 1 + l * per_layer() + n_kv_heads; }
-    MK_HD int oproj(int l) const { return attn(l) + 1; }
-    MK_HD int router(int l) const { return attn(l) + 2; }
-    MK_HD int gateup(int l) const { return attn(l) + 3; }
-    MK_HD int down(int l) const { return attn(l) + 4; }
+    MK_HD int attn(int l, int g) const { return 1 + l * per_layer() + n_kv_heads + g; }
+    MK_HD int combine(int l) const { return 1 + l * per_layer() + 2 * n_kv_heads; }
+    MK_HD int oproj(int l) const { return combine(l) + 1; }
+    MK_HD int router(int l) const { return combine(l) + 2; }
+    MK_HD int gateup(int l) const { return combine(l) + 3; }
+    MK_HD int down(int l) const { return combine(l) + 4; }
     MK_HD int n_main() const { return 1 + n_layers * per_layer(); }
-    // word offset of the arrival counters inside a bank
-    MK_HD int64_t arrive_base() const { return (int64_t)n_main() * kCtrStride; }
-    MK_HD int64_t arrive(int l, int b, int g) const {
-        return arrive_base() + ((int64_t)l * max_batch + b) * n_kv_heads + g;
-    }
-    MK_HD int64_t bank_words() const {
-        int64_t w = arrive_base() + (int64_t)n_layers * max_batch * n_kv_heads;
-        return (w + 63) & ~(int64_t)63;
-    }
+    MK_HD int64_t bank_words() const { return ((int64_t)n_main() * kCtrStride + 63) & ~(int64_t)63; }
 };
+
+// Exchange buffers are padded so that no 128-byte cache line holds words of
+// two slices with different producers: a consumer may then cache a line
+// only after every word of it has been written (a CU's L1 is not updated by
+// other CUs' stores). pad64 rounds a float count up to 256 bytes.
+MK_HD inline int64_t pad64(int64_t n) { return (n + 63) & ~(int64_t)63; }
 
 // Kernel parameter block (passed by value).
 struct Params {
@@ -113,15 +114,17 @@ struct Params {
     const int32_t* block_tables;  // [max_batch][max_pages]
     const float* rope;            // [max_batch][D/2][2] cos, sin
     const int32_t* n_chunks;      // [max_batch]
-    // workspace
+    // workspace: every buffer exchanged between workgroups has one slice per
+    // layer, so each is written at most once per step
     float* x;         // [2L+1][max_batch][H]
-    float* qkv;       // [max_batch][QKVD]
-    float* att_part;  // [max_batch][Hq][max_chunks][D+2]
-    float* att_out;   // [max_batch][Hq*D]
-    float* rlogits;   // [max_batch][E]
+    float* qkv;       // [L][max_batch][QKVD]
+    float* att_part;  // [L][max_batch][Hq][max_chunks][D] unnormalised outputs
+    float* att_ml;    // [L][max_batch][Hq][pad64(2 max_chunks)] running max and sum
+    float* att_out;   // [L][max_batch][Hq*D]
+    float* rlogits;   // [L][max_batch][E]
     int32_t* route_ids;  // [L][max_batch][K]
     float* route_w;      // [L][max_batch][K]
-    float* act;          // [max_batch*K][I]
+    float* act;          // [L][max_batch*K][I]
     uint32_t* ctr;       // this step's counter bank
     uint32_t* ctr_other; // the bank the next step uses (cleared by this step)
     int64_t bank_words;

@@ -114,11 +114,34 @@ __device__ __forceinline__ void raise_error(const Params& p, int32_t code, int32
     if (abort) __hip_atomic_store(p.err + 2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Data exchanged between workgroups inside a step (activations, attention
+// partials, router logits, expert activations) lives in buffers that are
+// written at most once per step: every buffer has one slice per layer. The
+// producer writes with device-scope (agent) relaxed atomic stores -- plain
+// stores carrying the SC1 cache-policy bit, which gfx950 writes through past
+// the XCD's L2 -- and waits for them to complete before bumping a counter.
+// Consumers read with ordinary cached loads: no XCD can hold a stale copy of
+// a slice, because caches are invalidated at kernel start and no one reads a
+// slice before its producer has finished. Hot activation vectors read by
+// hundreds of workgroups are then served from each XCD's L2 after one miss.
+// The memory model's agent-scope fences would instead write back
+// (buffer_wbl2) or invalidate (buffer_inv) a whole XCD's L2 on every task,
+// which serialises the L2 under thousands of tasks per step.
+__device__ __forceinline__ float ld_dev(const float* p) { return *p; }
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) { return *p; }
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's outstanding memory operations (in particular its
+// device-scope stores) have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Block-wide wait until counter `ctr` reaches `target`. Thread 0 spins with
-// agent-scope loads, then an agent-scope acquire fence makes the producers'
-// writes visible to the whole workgroup after the barrier. Returns false if
-// the step was aborted (watchdog here or elsewhere). Records the time the
-// wait ended in *t_wait (thread 0).
+// device-scope loads; the barrier then orders every thread's later
+// device-scope loads after the observation. Returns false if the step was
+// aborted (watchdog here or elsewhere). Records when the wait ended in
+// *t_wait (thread 0).
 __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wait) {
     if (p.perop || ctr < 0) return true;
     int ok = 1;
@@ -142,33 +165,44 @@ __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wai
                 }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         *t_wait = wall_clock64();
     }
     return __syncthreads_and(ok) != 0;
 }
 
-// Release this workgroup's writes at agent scope and bump counter `ctr`.
+// Complete this workgroup's device-scope stores and bump counter `ctr`.
 __device__ void block_signal(const Params& p, int ctr) {
     if (p.perop || ctr < 0) {
         __syncthreads();
         return;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wait_stores();
     __syncthreads();
     if (tid_() == 0)
-        __hip_atomic_fetch_add(p.ctr + (int64_t)ctr * kCtrStride, 1u, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.ctr + (int64_t)ctr * kCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------ activation slices + norm
 
+// RMSNorm gains for this lane's K positions (chunk c of lane l covers
+// elements [8(l + 64c), +8)). Gains are weights: tiles load them before their
+// dependency wait.
+template <int NCH>
+__device__ __forceinline__ void load_gain(uint4 (&g)[NCH], const uint16_t* gain, int K) {
+    const int lane = tid_() & 63;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = lane + 64 * c;
+        g[c] = ch < (K >> 3) ? ld16(gain + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 // Each lane of each wave holds the activation values at the K positions its
-// weight chunks cover: chunk c of lane l is elements [8(l + 64c), +8).
-// Optionally applies RMSNorm (x / sqrt(mean(x^2) + eps) * gain).
+// weight chunks cover. With `g` non-null applies RMSNorm:
+// x / sqrt(mean(x^2) + eps) * gain.
 template <int NCH, int NB>
 __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, int64_t stride, int nb,
-                                       int K, const uint16_t* gain, float eps) {
+                                       int K, const uint4* g, float eps) {
     const int lane = tid_() & 63;
     const int K8 = K >> 3;
 #pragma unroll
@@ -189,19 +223,16 @@ __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, i
 #pragma unroll
             for (int j = 0; j < 8; ++j) ss = fmaf(h[b][c][j], h[b][c][j], ss);
         }
-        if (gain != nullptr) {
+        if (g != nullptr) {
             ss = wave_sum(ss);
             const float inv = 1.0f / sqrtf(ss / (float)K + eps);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                const int ch = lane + 64 * c;
-                if (ch < K8) {
-                    const uint4 g = ld16(gain + ch * 8);
-                    const float gv[8] = {bflo(g.x), bfhi(g.x), bflo(g.y), bfhi(g.y),
-                                         bflo(g.z), bfhi(g.z), bflo(g.w), bfhi(g.w)};
+                const uint4 gw = g[c];
+                const float gv[8] = {bflo(gw.x), bfhi(gw.x), bflo(gw.y), bfhi(gw.y),
+                                     bflo(gw.z), bfhi(gw.z), bflo(gw.w), bfhi(gw.w)};
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) h[b][c][j] = (h[b][c][j] * inv) * gv[j];
-                }
+                for (int j = 0; j < 8; ++j) h[b][c][j] = (h[b][c][j] * inv) * gv[j];
             }
         }
     }
@@ -272,7 +303,7 @@ struct RouteLds {
 // Wave 0 computes top-k (logit descending, expert id ascending on ties) and a
 // softmax over the selected logits for each token, then lists the distinct
 // selected experts in ascending order as slots. Ends with a block barrier.
-__device__ __forceinline__ void compute_routing(const Params& p, RouteLds* r) {
+__device__ __forceinline__ void compute_routing(const Params& p, const float* rl, RouteLds* r) {
     if (tid_() < 64) {
         const int lane = tid_();
         const int E = p.E, K = p.K;
@@ -282,7 +313,7 @@ __device__ __forceinline__ void compute_routing(const Params& p, RouteLds* r) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = lane + 64 * i;
-                v[i] = e < E ? p.rlogits[b * E + e] : -INFINITY;
+                v[i] = e < E ? ld_dev(rl + b * E + e) : -INFINITY;
             }
             uint32_t taken = 0u;
             float sel_v[kMaxTopK];

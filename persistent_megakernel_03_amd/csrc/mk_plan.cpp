@@ -32,9 +32,14 @@ Task make_task(int op, int layer, int a0, int a1, int a2, int a3, int pre_ctr, i
     return t;
 }
 
+// Tile kinds for the timing model: weights loadable any time, weights known
+// only after routing, inputs produced inside the step.
+enum { kStatic = 0, kRouted = 1, kDynamic = 2 };
+
 struct Tile {
     Task t;
     double bytes;
+    int kind;
 };
 
 }  // namespace
@@ -59,7 +64,8 @@ int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions,
 int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
     const int G = s.Hq / s.Hkv;
     const int64_t per_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.rows_qkv) +
-                              (int64_t)s.max_batch * s.Hkv * s.max_chunks + ceil_div(s.H, cfg.rows_o) +
+                              (int64_t)s.max_batch * s.Hkv * s.max_chunks + (int64_t)s.max_batch * s.Hq +
+                              ceil_div(s.H, cfg.rows_o) +
                               ceil_div(s.E, cfg.rows_router) +
                               (int64_t)std::min(s.E, s.max_batch * s.K) * ceil_div(s.I, cfg.rows_gateup) +
                               ceil_div(s.H, cfg.rows_down);
@@ -87,9 +93,9 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     }
 
     std::vector<std::vector<Tile>> levels(P.n_levels);
-    auto add = [&](const Task& t, double bytes) { levels[t.level].push_back({t, bytes}); };
+    auto add = [&](const Task& t, double bytes, int kind) { levels[t.level].push_back({t, bytes, kind}); };
 
-    add(make_task(OP_EMBED, 0, 0, B, 0, 0, -1, 0, -1, 0, cl.embed(), 0), 2.0 * B * s.H);
+    add(make_task(OP_EMBED, 0, 0, B, 0, 0, -1, 0, -1, 0, cl.embed(), 0), 2.0 * B * s.H, kStatic);
     P.targets[cl.embed()] = 1;
 
     const int grows = (G + 2) * s.D;
@@ -100,6 +106,8 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     const int ngu = ceil_div(s.I, cfg.rows_gateup);
     const int nd = ceil_div(s.H, cfg.rows_down);
     const int nl = ceil_div(s.V, cfg.rows_lm);
+    int total_chunks = 0;
+    for (int b = 0; b < B; ++b) total_chunks += P.n_chunks[b];
 
     for (int l = 0; l < s.L; ++l) {
         const int lv = 1 + kLevelsPerLayer * l;
@@ -109,7 +117,7 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
             for (int i = 0; i < nq; ++i) {
                 const int v0 = i * cfg.rows_qkv, v1 = std::min(grows, v0 + cfg.rows_qkv);
                 add(make_task(OP_QKV, l, g, v0, v1, 0, -1, 0, in_ctr, in_target, cl.qkv(l, g), lv),
-                    2.0 * (v1 - v0) * s.H);
+                    2.0 * (v1 - v0) * s.H, kStatic);
             }
             P.targets[cl.qkv(l, g)] = nq;
         }
@@ -118,42 +126,48 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
             for (int g = 0; g < s.Hkv; ++g)
                 for (int c = 0; c < n; ++c) {
                     const int toks = std::min(P.chunk, positions[b] + 1 - c * P.chunk);
-                    add(make_task(OP_ATTN, l, b, g, c, n, -1, 0, cl.qkv(l, g), nq, cl.attn(l), lv + 1),
-                        4.0 * toks * s.D);
+                    add(make_task(OP_ATTN, l, b, g, c, n, -1, 0, cl.qkv(l, g), nq, cl.attn(l, g), lv + 1),
+                        4.0 * toks * s.D, kStatic);
                 }
         }
-        P.targets[cl.attn(l)] = B * s.Hkv;
+        for (int g = 0; g < s.Hkv; ++g) P.targets[cl.attn(l, g)] = total_chunks;
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < s.Hq; ++h)
+                add(make_task(OP_COMBINE, l, b, h, P.n_chunks[b], 0, -1, 0, cl.attn(l, h / G), total_chunks,
+                              cl.combine(l), lv + 2),
+                    4.0 * P.n_chunks[b] * (s.D + 2), kDynamic);
+        P.targets[cl.combine(l)] = B * s.Hq;
         for (int i = 0; i < no; ++i) {
             const int r0 = i * cfg.rows_o, r1 = std::min(s.H, r0 + cfg.rows_o);
-            add(make_task(OP_OPROJ, l, r0, r1, 0, 0, -1, 0, cl.attn(l), B * s.Hkv, cl.oproj(l), lv + 2),
-                2.0 * (r1 - r0) * s.Hq * s.D);
+            add(make_task(OP_OPROJ, l, r0, r1, 0, 0, -1, 0, cl.combine(l), B * s.Hq, cl.oproj(l), lv + 3),
+                2.0 * (r1 - r0) * s.Hq * s.D, kStatic);
         }
         P.targets[cl.oproj(l)] = no;
         for (int i = 0; i < nr; ++i) {
             const int r0 = i * cfg.rows_router, r1 = std::min(s.E, r0 + cfg.rows_router);
-            add(make_task(OP_ROUTER, l, r0, r1, 0, 0, -1, 0, cl.oproj(l), no, cl.router(l), lv + 3),
-                2.0 * (r1 - r0) * s.H);
+            add(make_task(OP_ROUTER, l, r0, r1, 0, 0, -1, 0, cl.oproj(l), no, cl.router(l), lv + 4),
+                2.0 * (r1 - r0) * s.H, kStatic);
         }
         P.targets[cl.router(l)] = nr;
         for (int sl = 0; sl < S; ++sl)
             for (int i = 0; i < ngu; ++i) {
                 const int r0 = i * cfg.rows_gateup, r1 = std::min(s.I, r0 + cfg.rows_gateup);
                 add(make_task(OP_GATEUP, l, sl, r0, r1, (sl == 0 && i == 0) ? 1 : 0, cl.router(l), nr, -1, 0,
-                              cl.gateup(l), lv + 4),
-                    4.0 * (r1 - r0) * s.H);
+                              cl.gateup(l), lv + 5),
+                    4.0 * (r1 - r0) * s.H, kRouted);
             }
         P.targets[cl.gateup(l)] = S * ngu;
         for (int i = 0; i < nd; ++i) {
             const int r0 = i * cfg.rows_down, r1 = std::min(s.H, r0 + cfg.rows_down);
-            add(make_task(OP_DOWN, l, r0, r1, 0, 0, cl.router(l), nr, cl.gateup(l), S * ngu, cl.down(l), lv + 5),
-                2.0 * S * (r1 - r0) * s.I);
+            add(make_task(OP_DOWN, l, r0, r1, 0, 0, cl.router(l), nr, cl.gateup(l), S * ngu, cl.down(l), lv + 6),
+                2.0 * S * (r1 - r0) * s.I, kRouted);
         }
         P.targets[cl.down(l)] = nd;
     }
     for (int i = 0; i < nl; ++i) {
         const int r0 = i * cfg.rows_lm, r1 = std::min(s.V, r0 + cfg.rows_lm);
         add(make_task(OP_LMHEAD, 0, r0, r1, 0, 0, -1, 0, cl.down(s.L - 1), nd, -1, P.n_levels - 1),
-            2.0 * (r1 - r0) * s.H);
+            2.0 * (r1 - r0) * s.H, kStatic);
     }
 
     // Per-op order: level by level.
@@ -163,26 +177,48 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         for (const Tile& t : levels[lv]) P.level_tasks.push_back(t.t);
     }
 
-    // Workgroup lists: level by level, each tile to the least-loaded
-    // workgroup so far (bytes), which backfills workgroups left idle at the
-    // tail of the previous level. Lists stay in level order.
+    // Workgroup lists by list scheduling over a simple timing model. Each
+    // workgroup runs its tasks in order; a task's weights start loading when
+    // the workgroup is free (and, for expert tiles, once the routing is
+    // known), and it computes once its inputs are ready:
+    //   finish = max(max(free, weights_ready) + bytes / bw, inputs_ready) + overhead.
+    // Tiles go, level by level and largest first, to the workgroup that is
+    // free earliest, so workgroups idle at the tail of one operation take the
+    // next one's tiles (backfill) and no workgroup queues a tile behind a late
+    // one when another is free. Lists stay in level order (deadlock freedom).
+    const double bw = cfg.model_bw_bytes_per_us / n_wg;   // bytes per microsecond per workgroup
+    const double overhead = cfg.model_task_us, sync = cfg.model_sync_us;
     std::vector<std::vector<Task>> lists(n_wg);
     P.wg_bytes.assign(n_wg, 0.0);
     typedef std::pair<double, int> Slot;
     std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
     for (int w = 0; w < n_wg; ++w) heap.push({0.0, w});
+    std::vector<double> level_end(P.n_levels, 0.0);
+    auto producer_end = [&](int lv) { return lv > 0 ? level_end[lv - 1] + sync : 0.0; };
     for (int lv = 0; lv < P.n_levels; ++lv) {
         std::vector<Tile> tiles = levels[lv];
         std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
+        const int op = tiles.empty() ? -1 : tiles[0].t.op;
+        // inputs ready: the previous level; weights of routed tiles: the router level
+        const double ready = producer_end(lv);
+        double wready = 0.0;
+        if (op == OP_GATEUP) wready = producer_end(lv);
+        if (op == OP_DOWN) wready = producer_end(lv - 1);
+        double end = 0.0;
         for (const Tile& t : tiles) {
             Slot s0 = heap.top();
             heap.pop();
+            const double wr = t.kind == kDynamic ? ready : wready;
+            const double fin = std::max(std::max(s0.first, wr) + t.bytes / bw, ready) + overhead;
             lists[s0.second].push_back(t.t);
-            s0.first += t.bytes + 4096.0;  // small per-task overhead keeps tiny tiles spread
             P.wg_bytes[s0.second] += t.bytes;
+            s0.first = fin;
+            end = std::max(end, fin);
             heap.push(s0);
         }
+        level_end[lv] = end;
     }
+    P.model_us = level_end.back();
     P.wg_off.assign(n_wg + 1, 0);
     for (int w = 0; w < n_wg; ++w) {
         P.wg_off[w + 1] = P.wg_off[w] + (int)lists[w].size();
@@ -200,15 +236,10 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
     if (P.level_tasks.size() != P.tasks.size()) return "task count differs between orders";
     // final counter values and producer levels
     std::vector<int> final_val(n_main, 0), prod_level(n_main, -1);
-    std::set<std::tuple<int, int, int>> attn_groups;
     for (const Task& t : P.tasks) {
         if (t.signal < -1 || t.signal >= n_main) return "signal out of range";
         if (t.signal < 0) continue;
-        if (t.op == OP_ATTN) {
-            if (attn_groups.insert(std::make_tuple(t.layer, t.a0, t.a1)).second) final_val[t.signal]++;
-        } else {
-            final_val[t.signal]++;
-        }
+        final_val[t.signal]++;
         if (prod_level[t.signal] >= 0 && prod_level[t.signal] != t.level) return "counter fed from two levels";
         prod_level[t.signal] = t.level;
     }
@@ -245,6 +276,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
             case OP_DOWN:
             case OP_LMHEAD: ranges[std::make_tuple(t.op, t.layer, 0, 0)].push_back({t.a0, t.a1}); break;
             case OP_GATEUP: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
+            case OP_COMBINE: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a1 + 1}); break;
             default: break;
         }
     }
@@ -262,6 +294,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         switch (op) {
             case OP_QKV: want = (G + 2) * s.D; break;
             case OP_ATTN: want = P.n_chunks[std::get<2>(kv.first)]; break;
+            case OP_COMBINE: want = s.Hq; break;
             case OP_OPROJ: case OP_DOWN: want = s.H; break;
             case OP_ROUTER: want = s.E; break;
             case OP_GATEUP: want = s.I; break;

@@ -33,6 +33,10 @@ struct TileConfig {
     int rows_down = 4;
     int rows_lm = 64;
     int chunk = 0;  // attention chunk in tokens (multiple of 64); 0 = choose
+    // timing model used to place tiles on workgroups
+    double model_bw_bytes_per_us = 5.6e6;  // whole-device HBM bandwidth
+    double model_task_us = 2.5;            // fixed cost of a task after its inputs are ready
+    double model_sync_us = 1.0;            // producer signal to consumer start
 };
 
 struct Plan {
@@ -47,6 +51,7 @@ struct Plan {
     std::vector<int32_t> n_chunks;    // per sequence
     std::vector<int32_t> targets;     // final value of every main counter
     std::vector<double> wg_bytes;     // bytes streamed per workgroup (balance)
+    double model_us = 0.0;            // modelled step time
 };
 
 // Attention chunk length for these contexts (tokens, multiple of 64).

@@ -42,8 +42,29 @@ struct TileCtx {
     uint64_t* t_wait; // trace: when the compute wait ended
 };
 
+// Per-layer slices of the exchange buffers, each padded to 256 bytes.
 __device__ __forceinline__ float* x_at(const Params& p, int idx) {
-    return p.x + (int64_t)idx * p.max_batch * p.H;
+    return p.x + (int64_t)idx * pad64((int64_t)p.max_batch * p.H);
+}
+__device__ __forceinline__ float* qkv_at(const Params& p, int l) {
+    return p.qkv + (int64_t)l * pad64((int64_t)p.max_batch * p.QKVD);
+}
+__device__ __forceinline__ float* part_at(const Params& p, int l) {
+    return p.att_part + (int64_t)l * pad64((int64_t)p.max_batch * p.Hq * p.max_chunks * p.D);
+}
+// (max, sum) pairs: one padded row of max_chunks pairs per (sequence, head)
+__device__ __forceinline__ int64_t ml_row(const Params& p) { return pad64(2 * (int64_t)p.max_chunks); }
+__device__ __forceinline__ float* ml_at(const Params& p, int l) {
+    return p.att_ml + (int64_t)l * p.max_batch * p.Hq * ml_row(p);
+}
+__device__ __forceinline__ float* attout_at(const Params& p, int l) {
+    return p.att_out + (int64_t)l * pad64((int64_t)p.max_batch * p.Hq * p.D);
+}
+__device__ __forceinline__ float* rlogits_at(const Params& p, int l) {
+    return p.rlogits + (int64_t)l * pad64((int64_t)p.max_batch * p.E);
+}
+__device__ __forceinline__ float* act_at(const Params& p, int l) {
+    return p.act + (int64_t)l * pad64((int64_t)p.max_batch * p.K * p.I);
 }
 
 // ------------------------------------------------------------------ embed
@@ -61,9 +82,10 @@ __device__ __forceinline__ bool tile_embed(const Task& t, TileCtx& cx) {
         float* xo = x_at(p, 0) + (int64_t)b * p.H;
         for (int i = tid_(); i < H8; i += NT) {
             const uint4 w = ld16(row + i * 8);
-            float4* o = reinterpret_cast<float4*>(xo + i * 8);
-            o[0] = make_float4(bflo(w.x), bfhi(w.x), bflo(w.y), bfhi(w.y));
-            o[1] = make_float4(bflo(w.z), bfhi(w.z), bflo(w.w), bfhi(w.w));
+            const float v[8] = {bflo(w.x), bfhi(w.x), bflo(w.y), bfhi(w.y),
+                                bflo(w.z), bfhi(w.z), bflo(w.w), bfhi(w.w)};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) st_dev(xo + i * 8 + j, v[j]);
         }
     }
     block_signal(p, t.signal);
@@ -91,8 +113,10 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
     gemv_stream<NCH, PF, NB>(
         nmine, H >> 3, [&](int i) { return W + (int64_t)phys(v0 + wave + i * NWAVES) * H; },
         [&](float(&h)[NB][NCH][8]) {
+            uint4 gn[NCH];
+            load_gain<NCH>(gn, wptr(p, l, W_ATTN_NORM), H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, wptr(p, l, W_ATTN_NORM), p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, gn, p.eps);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -100,7 +124,7 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
                 const int row = phys(v0 + wave + i * NWAVES);
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    if (b < p.B) p.qkv[(int64_t)b * p.QKVD + row] = acc[b];
+                    if (b < p.B) st_dev(qkv_at(p, l) + (int64_t)b * p.QKVD + row, acc[b]);
             }
         });
     if (!ok) return false;
@@ -146,7 +170,6 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     float* sA = sL + 16;                                 // [16] rescale factors
     uint16_t* sKn = reinterpret_cast<uint16_t*>(sA + 16); // [D] new key (bf16)
     uint16_t* sVn = sKn + D;                              // [D] new value (bf16)
-    int* sLast = reinterpret_cast<int*>(sVn + D);
 
     uint4 kf[NTBW][NDB];
     uint4 vf[NDV][NKB];
@@ -215,17 +238,17 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     load_kv(t0);
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
 
-    const float* qkv = p.qkv + (int64_t)b * p.QKVD;
+    const float* qkv = qkv_at(p, l) + (int64_t)b * p.QKVD;
     const float* rope = p.rope + (int64_t)b * D;  // [D/2][2]
     // New token: RoPE on k, BF16 rounding of k and v, append to the pool.
     if (has_new) {
         for (int i = tid_(); i < D / 2; i += NT) {
             const float cs = rope[2 * i], sn = rope[2 * i + 1];
-            const float a = qkv[p.Hq * D + g * D + i], bb = qkv[p.Hq * D + g * D + i + D / 2];
+            const float a = ld_dev(qkv + p.Hq * D + g * D + i), bb = ld_dev(qkv + p.Hq * D + g * D + i + D / 2);
             sKn[i] = (uint16_t)f2bf(a * cs - bb * sn);
             sKn[i + D / 2] = (uint16_t)f2bf(a * sn + bb * cs);
         }
-        for (int i = tid_(); i < D; i += NT) sVn[i] = (uint16_t)f2bf(qkv[(p.Hq + p.Hkv) * D + g * D + i]);
+        for (int i = tid_(); i < D; i += NT) sVn[i] = (uint16_t)f2bf(ld_dev(qkv + (p.Hq + p.Hkv) * D + g * D + i));
         __syncthreads();
         const int64_t page = bt[pos >> 4];
         const int slot = pos & 15;
@@ -245,7 +268,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj)
-                q[db][jj] = col < G ? qkv[(g * G + col) * D + db * 32 + quad * 8 + jj] : 0.f;
+                q[db][jj] = col < G ? ld_dev(qkv + (g * G + col) * D + db * 32 + quad * 8 + jj) : 0.f;
 #pragma unroll
         for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
@@ -364,52 +387,91 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
         __syncthreads();
     }
 
-    // partials: o (unnormalised), m, l
-    float* part = p.att_part + ((int64_t)b * p.Hq + g * G) * p.max_chunks * (D + 2);
+    // partials: o (unnormalised) and (m, l) per head for this chunk
+    float* part = part_at(p, l) + ((int64_t)b * p.Hq + g * G) * p.max_chunks * D;
+    float* ml = ml_at(p, l) + ((int64_t)b * p.Hq + g * G) * ml_row(p);
 #pragma unroll
     for (int j = 0; j < NDV; ++j) {
         const int d = (wave + NWAVES * j) * 16 + col;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int h = quad * 4 + r;
-            if (h < G) part[((int64_t)h * p.max_chunks + c) * (D + 2) + d] = oacc[j][r];
+            if (h < G) st_dev(part + ((int64_t)h * p.max_chunks + c) * D + d, oacc[j][r]);
         }
     }
     if (tid_() < G) {
-        part[((int64_t)tid_() * p.max_chunks + c) * (D + 2) + D] = sM[tid_()];
-        part[((int64_t)tid_() * p.max_chunks + c) * (D + 2) + D + 1] = sL[tid_()];
+        st_dev(ml + (int64_t)tid_() * ml_row(p) + 2 * c, sM[tid_()]);
+        st_dev(ml + (int64_t)tid_() * ml_row(p) + 2 * c + 1, sL[tid_()]);
     }
-    // arrival: the last chunk of (b, g) to finish does the merge
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid_() == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(p.ctr + p.cl.arrive(l, b, g), 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        *sLast = (old + 1u == (uint32_t)nch) ? 1 : 0;
-    }
-    __syncthreads();
-    if (*sLast == 0) return true;
+    (void)nch;
+    block_signal(p, t.signal);
+    return true;
+}
 
-    float* coef = sS;  // [G][nch], reuses the score tiles
-    for (int h = wave; h < G; h += NWAVES) {
-        const float* ph = part + (int64_t)h * p.max_chunks * (D + 2);
-        float mx = -INFINITY;
-        for (int cc = lane; cc < nch; cc += 64) mx = fmaxf(mx, ph[(int64_t)cc * (D + 2) + D]);
-        mx = wave_max(mx);
-        float lsum = 0.f;
-        for (int cc = lane; cc < nch; cc += 64)
-            lsum += expf(ph[(int64_t)cc * (D + 2) + D] - mx) * ph[(int64_t)cc * (D + 2) + D + 1];
-        lsum = wave_sum(lsum);
-        for (int cc = lane; cc < nch; cc += 64) coef[h * nch + cc] = expf(ph[(int64_t)cc * (D + 2) + D] - mx) / lsum;
-    }
+// Merge the chunk partials of one query head a1 of sequence a0:
+// o = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c with M = max_c m_c
+// (the softmax over all cached tokens, split by chunks). Each thread sums a
+// fixed set of chunks for four dimensions, then the sets are added in a fixed
+// order, so the result does not depend on timing.
+template <int D>
+__device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, b = t.a0, h = t.a1, nch = t.a2;
+    const int tid = tid_(), lane = tid & 63, wave = tid >> 6;
+    constexpr int NQ = D / 4;          // float4 columns
+    constexpr int NPH = NT / NQ;       // chunk phases
+    float* sred = reinterpret_cast<float*>(cx.lds);           // [NWAVES][2] reductions
+    float* coef = sred + 16;                                  // [nch]
+    float* sacc = coef + ((p.max_chunks + 3) & ~3);           // [NPH][D]
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    const int64_t row = (int64_t)b * p.Hq + h;
+    const float* ml = ml_at(p, l) + row * ml_row(p);
+    const float* po = part_at(p, l) + row * p.max_chunks * D;
+    // M = max_c m_c
+    float mx = -INFINITY;
+    for (int c = tid; c < nch; c += NT) mx = fmaxf(mx, ml[2 * c]);
+    mx = wave_max(mx);
+    if (lane == 0) sred[wave] = mx;
     __syncthreads();
-    float* out = p.att_out + (int64_t)b * p.Hq * D + g * G * D;
-    for (int idx = tid_(); idx < G * D; idx += NT) {
-        const int h = idx / D, d = idx - h * D;
-        const float* ph = part + (int64_t)h * p.max_chunks * (D + 2) + d;
-        float acc = 0.f;
-        for (int cc = 0; cc < nch; ++cc) acc = fmaf(coef[h * nch + cc], ph[(int64_t)cc * (D + 2)], acc);
-        out[idx] = acc;
+    mx = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
+    // L = sum_c exp(m_c - M) l_c
+    float ls = 0.f;
+    for (int c = tid; c < nch; c += NT) {
+        const float e = expf(ml[2 * c] - mx);
+        coef[c] = e;
+        ls += e * ml[2 * c + 1];
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) sred[NWAVES + wave] = ls;
+    __syncthreads();
+    const float inv = 1.0f / (((sred[NWAVES] + sred[NWAVES + 1]) + sred[NWAVES + 2]) + sred[NWAVES + 3]);
+    // o[d] = sum_c coef_c o_c[d] * inv
+    const int q = tid % NQ, ph = tid / NQ;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int c = ph;
+    for (; c + 3 * NPH < nch; c += 4 * NPH) {
+        const float4 v0 = *reinterpret_cast<const float4*>(po + (int64_t)c * D + 4 * q);
+        const float4 v1 = *reinterpret_cast<const float4*>(po + (int64_t)(c + NPH) * D + 4 * q);
+        const float4 v2 = *reinterpret_cast<const float4*>(po + (int64_t)(c + 2 * NPH) * D + 4 * q);
+        const float4 v3 = *reinterpret_cast<const float4*>(po + (int64_t)(c + 3 * NPH) * D + 4 * q);
+        const float w0 = coef[c], w1 = coef[c + NPH], w2 = coef[c + 2 * NPH], w3 = coef[c + 3 * NPH];
+        acc.x = fmaf(w0, v0.x, acc.x); acc.y = fmaf(w0, v0.y, acc.y); acc.z = fmaf(w0, v0.z, acc.z); acc.w = fmaf(w0, v0.w, acc.w);
+        acc.x = fmaf(w1, v1.x, acc.x); acc.y = fmaf(w1, v1.y, acc.y); acc.z = fmaf(w1, v1.z, acc.z); acc.w = fmaf(w1, v1.w, acc.w);
+        acc.x = fmaf(w2, v2.x, acc.x); acc.y = fmaf(w2, v2.y, acc.y); acc.z = fmaf(w2, v2.z, acc.z); acc.w = fmaf(w2, v2.w, acc.w);
+        acc.x = fmaf(w3, v3.x, acc.x); acc.y = fmaf(w3, v3.y, acc.y); acc.z = fmaf(w3, v3.z, acc.z); acc.w = fmaf(w3, v3.w, acc.w);
+    }
+    for (; c < nch; c += NPH) {
+        const float4 v = *reinterpret_cast<const float4*>(po + (int64_t)c * D + 4 * q);
+        const float w = coef[c];
+        acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y); acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(sacc)[ph * NQ + q] = acc;
+    __syncthreads();
+    float* out = attout_at(p, l) + row * D;
+    for (int d = tid; d < D; d += NT) {
+        float s = 0.f;
+        for (int k = 0; k < NPH; ++k) s += sacc[k * D + d];
+        st_dev(out + d, s * inv);
     }
     block_signal(p, t.signal);
     return true;
@@ -432,7 +494,7 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
         nmine, K >> 3, [&](int i) { return W + (int64_t)(r0 + wave + i * NWAVES) * K; },
         [&](float(&h)[NB][NCH][8]) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, p.att_out, K, p.B, K, nullptr, 0.f);
+            load_x<NCH, NB>(h, attout_at(p, l), K, p.B, K, nullptr, 0.f);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -440,7 +502,7 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
                 const int row = r0 + wave + i * NWAVES;
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    if (b < p.B) xmid[(int64_t)b * p.H + row] = xin[(int64_t)b * p.H + row] + acc[b];
+                    if (b < p.B) st_dev(xmid + (int64_t)b * p.H + row, ld_dev(xin + (int64_t)b * p.H + row) + acc[b]);
             }
         });
     if (!ok) return false;
@@ -463,8 +525,10 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
     gemv_stream<NCH, PF, NB>(
         nmine, H >> 3, [&](int i) { return W + (int64_t)(r0 + wave + i * NWAVES) * H; },
         [&](float(&h)[NB][NCH][8]) {
+            uint4 gn[NCH];
+            load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, wptr(p, l, W_FFN_NORM), p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -473,7 +537,7 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
                 const float bv = bias != nullptr ? bias[row] : 0.f;
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    if (b < p.B) p.rlogits[(int64_t)b * p.E + row] = bias != nullptr ? acc[b] + bv : acc[b];
+                    if (b < p.B) st_dev(rlogits_at(p, l) + (int64_t)b * p.E + row, bias != nullptr ? acc[b] + bv : acc[b]);
             }
         });
     if (!ok) return false;
@@ -492,8 +556,10 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1;
     const int wave = tid_() >> 6, lane = tid_() & 63;
     RouteLds* rt = route_lds(cx.lds, cx.general);
+    uint4 gn[NCH];
+    load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), p.H);
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
-    compute_routing(p, rt);
+    compute_routing(p, rlogits_at(p, l), rt);
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
             const int b = i / p.K, j = i - b * p.K;
@@ -516,7 +582,7 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
         2 * npair, H >> 3,
         [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
         [&](float(&h)[NB][NCH][8]) {
-            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, wptr(p, l, W_FFN_NORM), p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -530,7 +596,7 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
                     if (b < p.B && ((mask >> b) & 1)) {
                         const float gv = gate[b];
                         const float a = (gv / (1.0f + expf(-gv))) * acc[b];
-                        p.act[((int64_t)b * p.K + rt->slot_rank[slot][b]) * p.I + row] = a;
+                        st_dev(act_at(p, l) + ((int64_t)b * p.K + rt->slot_rank[slot][b]) * p.I + row, a);
                     }
                 }
             }
@@ -550,7 +616,7 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const int wave = tid_() >> 6, lane = tid_() & 63;
     RouteLds* rt = route_lds(cx.lds, cx.general);
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
-    compute_routing(p, rt);
+    compute_routing(p, rlogits_at(p, l), rt);
     const int I = p.I, K = p.K, B = p.B;
     const int nslots = rt->nslots;
     // wave w takes slots w, w+4, ...; row-vector i -> slot index i / nrows, row i % nrows
@@ -568,7 +634,7 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
         },
         [&](float(&)[NB][NCH][8]) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            const float4* src = reinterpret_cast<const float4*>(p.act);
+            const float4* src = reinterpret_cast<const float4*>(act_at(p, l));
             float4* dst = reinterpret_cast<float4*>(sAct);
             for (int i = tid_(); i < B * K * I / 4; i += NT) dst[i] = src[i];
             __syncthreads();
@@ -614,7 +680,7 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
         const int b = idx / nrows, r = idx - b * nrows;
         float acc = 0.f;
         for (int j = 0; j < K; ++j) acc += rt->w[b][j] * sY[((int64_t)b * K + j) * nrows + r];
-        xout[(int64_t)b * p.H + h0 + r] = xmid[(int64_t)b * p.H + h0 + r] + acc;
+        st_dev(xout + (int64_t)b * p.H + h0 + r, ld_dev(xmid + (int64_t)b * p.H + h0 + r) + acc);
     }
     block_signal(p, t.signal);
     return true;
@@ -633,8 +699,10 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
     gemv_stream<NCH, PF, NB>(
         nmine, H >> 3, [&](int i) { return p.lm_head + (int64_t)(r0 + wave + i * NWAVES) * H; },
         [&](float(&h)[NB][NCH][8]) {
+            uint4 gn[NCH];
+            load_gain<NCH>(gn, p.final_norm, H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, p.final_norm, p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, gn, p.eps);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -675,6 +743,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
         case OP_EMBED: return tile_embed(t, cx);
         case OP_QKV: return tile_qkv<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         case OP_ATTN: return tile_attn<S::D>(t, cx);
+        case OP_COMBINE: return tile_combine<S::D>(t, cx);
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
         case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         case OP_GATEUP: return tile_gateup<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);

@@ -72,11 +72,17 @@ def workspace_view(dec: mk.Decoder, ptr: int, count: int, dtype) -> torch.Tensor
     return dec.workspace[off:off + count * item].view(dtype)
 
 
+def pad64(n: int) -> int:
+    return (n + 63) // 64 * 64
+
+
 def x_layers(dec: mk.Decoder) -> torch.Tensor:
     c = dec.cfg
     B = dec.dims.max_batch
-    n = (2 * c["n_layers"] + 1) * B * c["hidden"]
-    return workspace_view(dec, dec.debug().x_layers, n, torch.float32).view(2 * c["n_layers"] + 1, B, c["hidden"])
+    stride = pad64(B * c["hidden"])
+    n = (2 * c["n_layers"] + 1) * stride
+    v = workspace_view(dec, dec.debug().x_layers, n, torch.float32).view(2 * c["n_layers"] + 1, stride)
+    return v[:, :B * c["hidden"]].reshape(2 * c["n_layers"] + 1, B, c["hidden"])
 
 
 def route_ids(dec: mk.Decoder) -> torch.Tensor:

@@ -13,7 +13,7 @@ import pytest
 from persistent_megakernel_03_amd import configs, mk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OP_EMBED, OP_QKV, OP_ATTN, OP_OPROJ, OP_ROUTER, OP_GATEUP, OP_DOWN, OP_LMHEAD = range(8)
+OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_ROUTER, OP_GATEUP, OP_DOWN, OP_LMHEAD = range(9)
 
 
 def header_functions():
@@ -45,7 +45,6 @@ def simulate(tasks, offs, targets, rng):
     protocol; return the final counters, or raise on deadlock."""
     n_wg = len(offs) - 1
     ctr = defaultdict(int)
-    arrive = defaultdict(int)
     nxt = [int(offs[w]) for w in range(n_wg)]
     stage = [0] * n_wg  # 0: before pre-wait, 1: before compute wait
     live = [w for w in range(n_wg) if nxt[w] < offs[w + 1]]
@@ -63,11 +62,7 @@ def simulate(tasks, offs, targets, rng):
             if c >= 0 and ctr[c] < tg:
                 continue
             # run the tile
-            if op == OP_ATTN:
-                arrive[(layer, a0, a1)] += 1
-                if arrive[(layer, a0, a1)] == a3:
-                    ctr[sig] += 1
-            elif sig >= 0:
+            if sig >= 0:
                 ctr[sig] += 1
             nxt[w] += 1
             stage[w] = 0
@@ -114,16 +109,17 @@ def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
 def test_plan_counts_for_the_30b_shape():
     d = mk.make_dims(configs.A3B, 1, 520, 520)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192])
-    ops = np.bincount(tasks[:, 0], minlength=8)
+    ops = np.bincount(tasks[:, 0], minlength=9)
     assert ops[OP_EMBED] == 1
     assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
     assert ops[OP_ATTN] == 48 * 4 * 65         # 8193 tokens in 128-token chunks
+    assert ops[OP_COMBINE] == 48 * 32          # one merge per query head
     assert ops[OP_OPROJ] == 48 * 256
     assert ops[OP_ROUTER] == 48 * 16
     assert ops[OP_GATEUP] == 48 * 8 * 48       # 8 slots x 768 rows / 16
     assert ops[OP_DOWN] == 48 * 512
     assert ops[OP_LMHEAD] == -(-151936 // 64)
-    assert info.n_levels == 2 + 6 * 48
+    assert info.n_levels == 2 + 7 * 48
 
 
 def test_plan_rejects_bad_input():
