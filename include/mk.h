@@ -122,7 +122,8 @@ typedef struct mk_options {
     int32_t split_kv_tokens; /* attention chunk length in tokens (multiple of 64); 0 = auto */
     int32_t n_cu_override;   /* 0 = the device's compute-unit count */
     int32_t time_kernels;    /* nonzero: bracket each step's kernels with HIP events (mk_kernel_time) */
-    int32_t reserved[4];
+    int32_t down_lookahead;  /* nonzero: gate/up tiles stage the next down tile's weights in LDS */
+    int32_t reserved[3];
 } mk_options;
 
 typedef struct mk_handle mk_handle;
@@ -226,8 +227,9 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
 
 /*
  * Per-task timestamps of the last step (when mk_options.trace was set): one
- * record of 4 uint64 per task, {task index | workgroup << 32, t_start,
- * t_after_wait, t_end} in the device's constant wall clock (100 MHz ticks).
+ * record of 8 uint64 per task, {task index | workgroup << 32, t_start,
+ * t_after_wait, four phase stamps inside the tile (0 if unused), t_end}, in
+ * the device's constant wall clock (100 MHz ticks).
  */
 mk_status mk_get_trace(mk_handle* h, void* host_buf, size_t bytes, size_t* written);
 

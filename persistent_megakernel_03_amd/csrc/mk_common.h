@@ -98,6 +98,7 @@ struct Params {
     // this step
     int32_t B, chunk;
     int32_t perop;      // 1: per-op launches (no counter waits / signals)
+    int32_t la_bytes;   // LDS lookahead capacity for down-projection weights (0: off)
     int32_t trace_on;
     int64_t watchdog_ticks;
     // weights

@@ -67,16 +67,53 @@ __device__ __forceinline__ float dot8(const uint4 w, const float* h, float acc) 
     return acc;
 }
 
+// DPP move within rows of 16 lanes (compile-time control word).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float readlane(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Wave-wide sum, the same in every lane: pairs, quads (quad_perm), half rows
+// (row_half_mirror), rows of 16 (row_mirror), then the four row sums. All
+// steps are DPP or lane reads, so there is no LDS round trip.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
+
+// Wave-wide maximum of 64-bit unsigned keys (DPP on both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_mov64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_mov64<0xB1>(v));
+    v = max_u64(v, dpp_mov64<0x4E>(v));
+    v = max_u64(v, dpp_mov64<0x141>(v));
+    v = max_u64(v, dpp_mov64<0x140>(v));
+    return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -85,15 +122,19 @@ __device__ __forceinline__ const uint16_t* wptr(const Params& p, int layer, int 
     return reinterpret_cast<const uint16_t*>(p.wtab[layer * W_NKINDS + kind]);
 }
 
-// Split an fp32 value into three BF16 parts whose sum reproduces it to about
-// 2^-24 relative. MFMA products of BF16 parts are exact and accumulate in
-// fp32, so three passes give fp32-grade dot products on the matrix cores.
+// Split a finite fp32 value into three BF16 parts whose sum reproduces it to
+// about 2^-24 relative: each part keeps the top bits of what the previous
+// parts left (truncation; the remainders are exact in fp32). MFMA products
+// of BF16 parts are exact and accumulate in fp32, so three passes give
+// fp32-grade dot products on the matrix cores.
 __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    hi = f2bf(v);
-    const float r1 = v - __uint_as_float(hi << 16);
-    mid = f2bf(r1);
-    const float r2 = r1 - __uint_as_float(mid << 16);
-    lo = f2bf(r2);
+    const uint32_t u = __float_as_uint(v);
+    hi = u >> 16;
+    const float r1 = v - __uint_as_float(u & 0xffff0000u);
+    const uint32_t u1 = __float_as_uint(r1);
+    mid = u1 >> 16;
+    const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+    lo = __float_as_uint(r2) >> 16;
 }
 
 // D(16x16) += A(16x32) * B(32x16), BF16 operands, fp32 accumulate.
@@ -171,12 +212,14 @@ __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wai
 }
 
 // Complete this workgroup's device-scope stores and bump counter `ctr`.
-__device__ void block_signal(const Params& p, int ctr) {
+// `drained`: every wave has already waited for its stores (and may have
+// issued loads since, which must not delay the signal).
+__device__ void block_signal(const Params& p, int ctr, bool drained = false) {
     if (p.perop || ctr < 0) {
         __syncthreads();
         return;
     }
-    wait_stores();
+    if (!drained) wait_stores();
     __syncthreads();
     if (tid_() == 0)
         __hip_atomic_fetch_add(p.ctr + (int64_t)ctr * kCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -259,14 +302,18 @@ __device__ __forceinline__ void load_row(uint4 (&w)[NCH], const uint16_t* row, i
 // activation slices h); then rows are consumed in order while the row PF
 // places ahead is in flight. reload(i, h) may refresh h before row i;
 // emit(i, acc) receives the wave-reduced dot products (every lane has them).
-template <int NCH, int PF, int NB, class RowPtr, class Ready, class Reload, class Emit>
+// With XFIRST, ready(h) runs before the first rows are loaded instead (for
+// tiles whose weights are known only after the wait: the small activation
+// load then does not queue behind the weight stream).
+template <int NCH, int PF, int NB, bool XFIRST = false, class RowPtr, class Ready, class Reload, class Emit>
 __device__ __forceinline__ void gemv_stream(int nmine, int K8, RowPtr rowptr, Ready ready, Reload reload,
                                             Emit emit) {
+    float h[NB][NCH][8];
+    if (XFIRST) ready(h);
     uint4 buf[PF][NCH];
 #pragma unroll
     for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], s < nmine ? rowptr(s) : nullptr, K8);
-    float h[NB][NCH][8];
-    ready(h);
+    if (!XFIRST) ready(h);
     for (int i0 = 0; i0 < nmine; i0 += PF) {
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
@@ -315,34 +362,35 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
                 const int e = lane + 64 * i;
                 v[i] = e < E ? ld_dev(rl + b * E + e) : -INFINITY;
             }
+            // top-k by repeated wave-wide maximum of 64-bit keys (logit in an
+            // order-preserving unsigned form, then the inverted expert id):
+            // the largest key is the largest logit, ties to the lowest id
             uint32_t taken = 0u;
+            uint64_t key[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lane + 64 * i;
+                uint32_t u = __float_as_uint(v[i]);
+                u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+                key[i] = e < E ? (((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+            }
             float sel_v[kMaxTopK];
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) {
                 sel_v[j] = -INFINITY;
                 if (j < K) {
-                    float bv = -INFINITY;
-                    int bi = 0x7fffffff;
+                    uint64_t kb = key[0];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int e = lane + 64 * i;
-                        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
-                            bv = v[i];
-                            bi = e;
-                        }
-                    }
+                    for (int i = 1; i < 4; ++i) kb = key[i] > kb ? key[i] : kb;
+                    const uint64_t km = wave_max_u64(kb);
+                    const int best = (int)(0xffffffffu - (uint32_t)km);
+                    const uint32_t uh = (uint32_t)(km >> 32);
+                    sel_v[j] = __uint_as_float((uh & 0x80000000u) ? (uh ^ 0x80000000u) : ~uh);
 #pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) {
-                        const float ov = __shfl_xor(bv, o, 64);
-                        const int oi = __shfl_xor(bi, o, 64);
-                        if (ov > bv || (ov == bv && oi < bi)) {
-                            bv = ov;
-                            bi = oi;
-                        }
-                    }
-                    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-                    sel_v[j] = bv;
-                    if (lane == 0) r->ids[b][j] = bi;
+                    for (int i = 0; i < 4; ++i)
+                        if (key[i] == km) key[i] = 0ull;   // taken (keys are unique)
+                    if (lane == 0) r->ids[b][j] = best;
+                    if ((best & 63) == lane) taken |= 1u << (best >> 6);
                 }
             }
 #pragma unroll

@@ -40,7 +40,14 @@ struct TileCtx {
     char* lds;
     int general;      // bytes of the general LDS region
     uint64_t* t_wait; // trace: when the compute wait ended
+    uint64_t* marks;  // trace: four phase stamps inside the tile
+    const Task* next; // the workgroup's next task (persistent mode), else null
 };
+
+// Trace stamp k (0..3) of the current tile (thread 0, tracing on).
+__device__ __forceinline__ void mark(TileCtx& cx, int k) {
+    if (cx.p.trace_on && tid_() == 0) cx.marks[k] = wall_clock64();
+}
 
 // Per-layer slices of the exchange buffers, each padded to 256 bytes.
 __device__ __forceinline__ float* x_at(const Params& p, int idx) {
@@ -117,6 +124,7 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
             load_gain<NCH>(gn, wptr(p, l, W_ATTN_NORM), H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, gn, p.eps);
+            mark(cx, 0);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -128,6 +136,7 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
             }
         });
     if (!ok) return false;
+    mark(cx, 1);
     block_signal(p, t.signal);
     return true;
 }
@@ -164,6 +173,8 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     float* sS = reinterpret_cast<float*>(cx.lds);      // [16][kSPad] scores
     float* sP = sS + 16 * kSPad;                         // [16][kSPad] probabilities
     uint4* sQ = reinterpret_cast<uint4*>(sP + 16 * kSPad); // [3][NDB][64] query A-fragments
+    float* sQf = reinterpret_cast<float*>(sQ + 3 * NDB * 64); // [G][D] queries before RoPE
+    float* sRope = sQf + 16 * D;                               // [D/2][2] cos, sin
     int* misc = misc_lds(cx.lds, cx.general);
     float* sM = reinterpret_cast<float*>(misc);          // [16]
     float* sL = sM + 16;                                 // [16]
@@ -236,45 +247,59 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     };
 
     load_kv(t0);
+    // the rotary table is a host input: load it before the wait
+    const int tid = tid_();
+    const float rope_v = tid < D ? p.rope[(int64_t)b * D + tid] : 0.f;
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
 
     const float* qkv = qkv_at(p, l) + (int64_t)b * p.QKVD;
-    const float* rope = p.rope + (int64_t)b * D;  // [D/2][2]
+    // queries of the group's heads (G x D floats) and the rotary table into LDS
+    for (int i = tid * 4; i < G * D; i += NT * 4)
+        *reinterpret_cast<float4*>(sQf + i) = *reinterpret_cast<const float4*>(qkv + (int64_t)g * G * D + i);
+    if (tid < D) sRope[tid] = rope_v;
+    __syncthreads();
     // New token: RoPE on k, BF16 rounding of k and v, append to the pool.
     if (has_new) {
-        for (int i = tid_(); i < D / 2; i += NT) {
-            const float cs = rope[2 * i], sn = rope[2 * i + 1];
+        for (int i = tid; i < D / 2; i += NT) {
+            const float cs = sRope[2 * i], sn = sRope[2 * i + 1];
             const float a = ld_dev(qkv + p.Hq * D + g * D + i), bb = ld_dev(qkv + p.Hq * D + g * D + i + D / 2);
             sKn[i] = (uint16_t)f2bf(a * cs - bb * sn);
             sKn[i + D / 2] = (uint16_t)f2bf(a * sn + bb * cs);
         }
-        for (int i = tid_(); i < D; i += NT) sVn[i] = (uint16_t)f2bf(ld_dev(qkv + (p.Hq + p.Hkv) * D + g * D + i));
+        for (int i = tid; i < D; i += NT) sVn[i] = (uint16_t)f2bf(ld_dev(qkv + (p.Hq + p.Hkv) * D + g * D + i));
         __syncthreads();
         const int64_t page = bt[pos >> 4];
         const int slot = pos & 15;
         uint16_t* kd = p.k_pool + ((layer_pages + page) * p.Hkv + g) * hstride + slot * D;
         uint16_t* vd = p.v_pool + ((layer_pages + page) * p.Hkv + g) * hstride + slot;
-        for (int i = tid_(); i < D; i += NT) {
+        for (int i = tid; i < D; i += NT) {
             kd[i] = sKn[i];
             vd[(int64_t)i * 16] = sVn[i];
         }
     }
 
-    // Queries of the group's heads (rows 0..G-1 of the MFMA A operand), RoPE,
-    // 3-way BF16 split; wave 0 builds the fragments, every wave reads them.
+    // Query fragments (rows 0..G-1 of the MFMA A operand): RoPE, then the
+    // 3-way BF16 split; wave 0 builds them, every wave reads them.
     if (wave == 0) {
         float q[NDB][8];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db) {
+            if (col < G) {
+                const float4 u = *reinterpret_cast<const float4*>(sQf + col * D + db * 32 + quad * 8);
+                const float4 w = *reinterpret_cast<const float4*>(sQf + col * D + db * 32 + quad * 8 + 4);
+                q[db][0] = u.x; q[db][1] = u.y; q[db][2] = u.z; q[db][3] = u.w;
+                q[db][4] = w.x; q[db][5] = w.y; q[db][6] = w.z; q[db][7] = w.w;
+            } else {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                q[db][jj] = col < G ? ld_dev(qkv + (g * G + col) * D + db * 32 + quad * 8 + jj) : 0.f;
+                for (int jj = 0; jj < 8; ++jj) q[db][jj] = 0.f;
+            }
+        }
 #pragma unroll
         for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int i = db * 32 + quad * 8 + jj;
-                const float cs = rope[2 * i], sn = rope[2 * i + 1];
+                const float cs = sRope[2 * i], sn = sRope[2 * i + 1];
                 const float a = q[db][jj], bb = q[db + NDB / 2][jj];
                 q[db][jj] = a * cs - bb * sn;
                 q[db + NDB / 2][jj] = a * sn + bb * cs;
@@ -303,6 +328,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     // rows G..15 of the probability tile stay zero
     for (int i = tid_(); i < (16 - G) * kSPad; i += NT) sP[G * kSPad + i] = 0.f;
     __syncthreads();
+    mark(cx, 0);
 
     f32x4_t oacc[NDV];
 #pragma unroll
@@ -349,6 +375,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
             }
         }
         __syncthreads();
+        mark(cx, 1);
         // o += P V
 #pragma unroll
         for (int j = 0; j < NDV; ++j) {
@@ -387,6 +414,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
         __syncthreads();
     }
 
+    mark(cx, 2);
     // partials: o (unnormalised) and (m, l) per head for this chunk
     float* part = part_at(p, l) + ((int64_t)b * p.Hq + g * G) * p.max_chunks * D;
     float* ml = ml_at(p, l) + ((int64_t)b * p.Hq + g * G) * ml_row(p);
@@ -404,6 +432,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
         st_dev(ml + (int64_t)tid_() * ml_row(p) + 2 * c + 1, sL[tid_()]);
     }
     (void)nch;
+    mark(cx, 3);
     block_signal(p, t.signal);
     return true;
 }
@@ -445,6 +474,7 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     if (lane == 0) sred[NWAVES + wave] = ls;
     __syncthreads();
     const float inv = 1.0f / (((sred[NWAVES] + sred[NWAVES + 1]) + sred[NWAVES + 2]) + sred[NWAVES + 3]);
+    mark(cx, 0);
     // o[d] = sum_c coef_c o_c[d] * inv
     const int q = tid % NQ, ph = tid / NQ;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -467,6 +497,7 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     }
     reinterpret_cast<float4*>(sacc)[ph * NQ + q] = acc;
     __syncthreads();
+    mark(cx, 1);
     float* out = attout_at(p, l) + row * D;
     for (int d = tid; d < D; d += NT) {
         float s = 0.f;
@@ -506,6 +537,7 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
             }
         });
     if (!ok) return false;
+    mark(cx, 1);
     block_signal(p, t.signal);
     return true;
 }
@@ -541,11 +573,14 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
             }
         });
     if (!ok) return false;
+    mark(cx, 1);
     block_signal(p, t.signal);
     return true;
 }
 
 // ---------------------------------------------------------- expert gate/up
+
+__device__ __forceinline__ void issue_down_lookahead(TileCtx& cx, const Task& nt, const RouteLds* rt);
 
 // Slot a0 (the a0-th distinct selected expert, ascending id), rows a1..a2 of
 // its gate and up matrices; a = SiLU(W_gate h2) * (W_up h2) for every token
@@ -560,6 +595,8 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), p.H);
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     compute_routing(p, rlogits_at(p, l), rt);
+    mark(cx, 0);
+    const bool lookahead = cx.next != nullptr && cx.next->op == OP_DOWN && cx.next->layer == l;
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
             const int b = i / p.K, j = i - b * p.K;
@@ -568,7 +605,9 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
         }
     }
     if (slot >= rt->nslots) {
-        block_signal(p, t.signal);
+        wait_stores();
+        if (lookahead) issue_down_lookahead(cx, *cx.next, rt);
+        block_signal(p, t.signal, true);
         return true;
     }
     const int e = rt->slot_e[slot];
@@ -578,11 +617,12 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * p.I * H;
     const int npair = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     float gate[NB];
-    gemv_stream<NCH, PF, NB>(
+    gemv_stream<NCH, PF, NB, true>(
         2 * npair, H >> 3,
         [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
         [&](float(&h)[NB][NCH][8]) {
             load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
+            mark(cx, 1);
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
@@ -601,79 +641,148 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
                 }
             }
         });
-    block_signal(p, t.signal);
+    mark(cx, 2);
+    // Drain this wave's stores first, so the lookahead loads issued next do
+    // not delay the signal (vmcnt counts loads and stores together).
+    wait_stores();
+    if (lookahead) issue_down_lookahead(cx, *cx.next, rt);
+    block_signal(p, t.signal, true);
     return true;
 }
 
 // ------------------------------------------------------------ expert down
 
+// Down-projection lookahead. Expert weights are known once the routing is,
+// which is long before the gate/up outputs a down tile needs are. A gate/up
+// tile whose workgroup runs a down tile of the same layer next streams that
+// tile's weights straight into LDS (direct global-to-LDS loads) while its own
+// gate/up rows stream into registers; the down tile then computes from LDS.
+// Layout: per selected expert (slot), its nrows rows of I BF16, slot-major.
+__device__ __forceinline__ int down_tag(const Task& t) { return (t.layer << 16) | t.a0; }
+constexpr int kLaTag = 60;  // int slot in the per-tile scalar area
+
+__device__ __forceinline__ void issue_down_lookahead(TileCtx& cx, const Task& nt, const RouteLds* rt) {
+    const Params& p = cx.p;
+    int* tag = misc_lds(cx.lds, cx.general) + kLaTag;
+    const int nrows = nt.a1 - nt.a0;
+    const int64_t slot_bytes = (int64_t)nrows * p.I * 2;
+    const int64_t total = (int64_t)rt->nslots * slot_bytes;
+    const int64_t n_inst = (total + 1023) / 1024;   // 64 lanes x 16 bytes per load
+    if (n_inst * 1024 > p.la_bytes || (slot_bytes & 15) != 0 || p.perop) return;
+    const int tid = tid_(), lane = tid & 63, wave = tid >> 6;
+    const uint16_t* Wd = wptr(p, nt.layer, W_DOWN);
+    for (int64_t q = wave; q < n_inst; q += NWAVES) {
+        int64_t off = (q * 64 + lane) * 16;
+        if (off >= total) off = 0;   // tail lanes reload the first chunk into padding
+        const int s = (int)(off / slot_bytes);
+        const int64_t within = off - s * slot_bytes;
+        const char* src = reinterpret_cast<const char*>(Wd + ((int64_t)rt->slot_e[s] * p.H + nt.a0) * p.I) + within;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(cx.lds + q * 1024), 16, 0, 0);
+    }
+    if (tid == 0) *tag = down_tag(nt);
+}
+
 // Rows a0..a1 of the hidden dimension, for every selected expert: y = W_down a,
-// then x_out = x_mid + sum_j w_j y_j in top-k rank order.
+// then x_out = x_mid + sum_j w_j y_j in top-k rank order. Weights come from
+// the LDS lookahead when the previous task loaded them, else from registers.
 template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0;
     const int wave = tid_() >> 6, lane = tid_() & 63;
     RouteLds* rt = route_lds(cx.lds, cx.general);
+    int* tag = misc_lds(cx.lds, cx.general) + kLaTag;
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     compute_routing(p, rlogits_at(p, l), rt);
+    mark(cx, 0);
+    const bool la = *tag == down_tag(t);
     const int I = p.I, K = p.K, B = p.B;
     const int nslots = rt->nslots;
     // wave w takes slots w, w+4, ...; row-vector i -> slot index i / nrows, row i % nrows
     const int myslots = nslots > wave ? (nslots - wave + NWAVES - 1) / NWAVES : 0;
     const uint16_t* Wd = wptr(p, l, W_DOWN);
-    float* sAct = reinterpret_cast<float*>(cx.lds);                 // [B*K][I]
-    float* sY = sAct + (int64_t)B * K * I;                          // [B*K][nrows]
-    bool ok = true;
+    float* sY = reinterpret_cast<float*>(cx.lds + cx.general) - kMaxBatch * kMaxTopK * kMaxDownRows;  // [B*K][nrows]
+    const float* act = act_at(p, l);
     const int K8 = I >> 3;
-    gemv_stream<NCH, PF, NB>(
-        myslots * nrows, K8,
-        [&](int i) {
+    auto load_act = [&](int s, float(&h)[NB][NCH][8]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int ch = lane + 64 * c;
+                if (rank >= 0 && ch < K8) {
+                    const float4* a = reinterpret_cast<const float4*>(act + ((int64_t)b * K + rank) * I + ch * 8);
+                    const float4 u = a[0], v = a[1];
+                    h[b][c][0] = u.x; h[b][c][1] = u.y; h[b][c][2] = u.z; h[b][c][3] = u.w;
+                    h[b][c][4] = v.x; h[b][c][5] = v.y; h[b][c][6] = v.z; h[b][c][7] = v.w;
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) h[b][c][jj] = 0.f;
+                }
+            }
+        }
+    };
+    auto emit = [&](int i, const float(&acc)[NB]) {
+        if (lane == 0) {
             const int s = wave + (i / nrows) * NWAVES;
-            return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + (i % nrows)) * I;
-        },
-        [&](float(&)[NB][NCH][8]) {
-            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            const float4* src = reinterpret_cast<const float4*>(act_at(p, l));
-            float4* dst = reinterpret_cast<float4*>(sAct);
-            for (int i = tid_(); i < B * K * I / 4; i += NT) dst[i] = src[i];
-            __syncthreads();
-        },
-        [&](int i, float(&h)[NB][NCH][8]) {
-            if (i % nrows == 0) {
-                const int s = wave + (i / nrows) * NWAVES;
+            const int r = i % nrows;
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
-#pragma unroll
-                    for (int c = 0; c < NCH; ++c) {
-                        const int ch = lane + 64 * c;
-                        if (rank >= 0 && ch < K8) {
-                            const float4* a = reinterpret_cast<const float4*>(sAct + ((int64_t)b * K + rank) * I + ch * 8);
-                            const float4 u = a[0], v = a[1];
-                            h[b][c][0] = u.x; h[b][c][1] = u.y; h[b][c][2] = u.z; h[b][c][3] = u.w;
-                            h[b][c][4] = v.x; h[b][c][5] = v.y; h[b][c][6] = v.z; h[b][c][7] = v.w;
-                        } else {
-#pragma unroll
-                            for (int jj = 0; jj < 8; ++jj) h[b][c][jj] = 0.f;
-                        }
-                    }
-                }
+            for (int b = 0; b < NB; ++b) {
+                const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
+                if (rank >= 0) sY[((int64_t)b * K + rank) * nrows + r] = acc[b];
             }
-        },
-        [&](int i, const float(&acc)[NB]) {
-            if (lane == 0) {
-                const int s = wave + (i / nrows) * NWAVES;
-                const int r = i % nrows;
+        }
+    };
+    bool ok = true;
+    if (la) {
+        ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's lookahead loads have landed
+        __syncthreads();                                   // and every wave's
+        mark(cx, 1);
+        const uint16_t* la_w = reinterpret_cast<const uint16_t*>(cx.lds);
+        float h[NB][NCH][8];
+        for (int i = 0; i < myslots * nrows; ++i) {
+            const int s = wave + (i / nrows) * NWAVES;
+            if (i % nrows == 0) load_act(s, h);
+            const uint16_t* row = la_w + ((int64_t)s * nrows + (i % nrows)) * I;
+            uint4 w[NCH];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
-                    if (rank >= 0) sY[((int64_t)b * K + rank) * nrows + r] = acc[b];
-                }
+            for (int c = 0; c < NCH; ++c) {
+                const int ch = lane + 64 * c;
+                w[c] = ch < K8 ? *reinterpret_cast<const uint4*>(row + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
             }
-        });
+            float acc[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float a = 0.f;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) a = dot8(w[c], h[b][c], a);
+                acc[b] = wave_sum(a);
+            }
+            emit(i, acc);
+        }
+    } else {
+        gemv_stream<NCH, PF, NB>(
+            myslots * nrows, K8,
+            [&](int i) {
+                const int s = wave + (i / nrows) * NWAVES;
+                return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + (i % nrows)) * I;
+            },
+            [&](float(&)[NB][NCH][8]) {
+                ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+                mark(cx, 1);
+            },
+            [&](int i, float(&h)[NB][NCH][8]) {
+                if (i % nrows == 0) load_act(wave + (i / nrows) * NWAVES, h);
+            },
+            emit);
+    }
     if (!ok) return false;
     __syncthreads();
+    mark(cx, 2);
+    if (tid_() == 0) *tag = -1;
     const float* xmid = x_at(p, 2 * l + 1);
     float* xout = x_at(p, 2 * l + 2);
     for (int idx = tid_(); idx < B * nrows; idx += NT) {
@@ -714,6 +823,7 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
             }
         });
     if (!ok) return false;
+    mark(cx, 1);
     block_signal(p, t.signal);
     return true;
 }
@@ -746,7 +856,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
         case OP_COMBINE: return tile_combine<S::D>(t, cx);
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
         case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
-        case OP_GATEUP: return tile_gateup<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+        case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 8 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
         case OP_DOWN: return tile_down<S::NCH_I, Pf<S::NCH_I, NB>::v, NB>(t, cx);
         case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         default: return false;
@@ -754,19 +864,25 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
 }
 
 // Run one task; with tracing on, thread 0 records {task | wg << 32, start,
-// end of the compute wait, end}.
+// end of the compute wait, four phase stamps, end}.
 template <class S, int NB>
-__device__ __forceinline__ bool run_task(const Task& t, const Params& p, char* lds, int general, int idx) {
+__device__ __forceinline__ bool run_task(const Task& t, const Task* next, const Params& p, char* lds, int general,
+                                         int idx) {
     uint64_t t_start = 0, t_wait = 0;
+    uint64_t marks[4] = {0, 0, 0, 0};
     if (p.trace_on && tid_() == 0) t_start = t_wait = wall_clock64();
-    TileCtx cx{p, lds, general, &t_wait};
+    TileCtx cx{p, lds, general, &t_wait, marks, next};
     const bool ok = dispatch_tile<S, NB>(t, cx);
     if (p.trace_on && tid_() == 0) {
-        uint64_t* rec = p.trace + (int64_t)idx * 4;
+        uint64_t* rec = p.trace + (int64_t)idx * 8;
         rec[0] = (uint64_t)(uint32_t)idx | ((uint64_t)blockIdx.x << 32);
         rec[1] = t_start;
         rec[2] = t_wait;
-        rec[3] = wall_clock64();
+        rec[3] = marks[0];
+        rec[4] = marks[1];
+        rec[5] = marks[2];
+        rec[6] = marks[3];
+        rec[7] = wall_clock64();
     }
     return ok;
 }
