@@ -36,6 +36,35 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_source_sha256() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "persistent_megakernel_03_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(batch: int, ctx: int):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    summary for this workload, or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    if batch != 1 or ctx != 8192:
+        return None
+    path = os.path.join(ROOT, "profiles", "k_persistent_a3b_b1_ctx8192_hbm_counters.md")
+    try:
+        text = open(path).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("source_sha256") != kernel_source_sha256():
+        return None
+    return int(data["traffic_bytes_per_launch"])
+
+
 def distinct_experts(route_ids: np.ndarray, B: int) -> list:
     return [len(set(route_ids[l, :B].reshape(-1).tolist())) for l in range(route_ids.shape[0])]
 
@@ -48,7 +77,7 @@ def main():
     ap.add_argument("--context", type=int, default=8192)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-perop", action="store_true")
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--down-lookahead", action="store_true")
@@ -167,7 +196,7 @@ def main():
                    "top_k": cfg["top_k"], "parallelism": "single GPU",
                    "precision": "BF16 weights and KV, fp32 activations and accumulation"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(B, ctx),
                      "kernel": "k_persistent (one launch per step)", "bytes_per_launch": bytes_step,
                      "kernel_ms": round(kms, 4)},
         "sol": {"bytes_per_step": bytes_step, "sol_tok_s": round(sol.sol_tokens_per_s(bytes_step, B), 1),
