@@ -80,7 +80,6 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-perop", action="store_true")
     ap.add_argument("--wg-per-cu", type=int, default=0)
-    ap.add_argument("--down-lookahead", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -114,7 +113,7 @@ def main():
 
     def run(mode: int, steps: int, warmup: int, k, v):
         dec = mk.Decoder(cfg, weights, k, v, max_batch=B, max_pages_per_seq=pages_per_seq, mode=mode,
-                         wg_per_cu=args.wg_per_cu, time_kernels=True, down_lookahead=args.down_lookahead)
+                         wg_per_cu=args.wg_per_cu, time_kernels=True)
         tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
         logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
         pos = [ctx] * B

@@ -122,8 +122,7 @@ typedef struct mk_options {
     int32_t split_kv_tokens; /* attention chunk length in tokens (multiple of 64); 0 = auto */
     int32_t n_cu_override;   /* 0 = the device's compute-unit count */
     int32_t time_kernels;    /* nonzero: bracket each step's kernels with HIP events (mk_kernel_time) */
-    int32_t down_lookahead;  /* nonzero: gate/up tiles stage the next down tile's weights in LDS */
-    int32_t reserved[3];
+    int32_t reserved[4];
 } mk_options;
 
 typedef struct mk_handle mk_handle;

@@ -167,7 +167,6 @@ struct mk_handle {
     KernelPair kern[kMaxBatchValu + 1];
     size_t lds_bytes = 0;
     int general = 0;
-    int la_bytes = 0;
     Layout lay;
     char* ws = nullptr;
     int bank = 0;
@@ -252,17 +251,13 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         const size_t attn = (size_t)2 * 16 * (128 + 4) * 4 + (size_t)3 * (d.head_dim / 32) * 64 * 16 +
                             (size_t)16 * d.head_dim * 4 + (size_t)d.head_dim * 4;
         const size_t comb = (size_t)(16 + max_chunks + 4 + 1024) * 4;
-        // down tile: output staging at the end of the general region; the
-        // lookahead (its weights, loaded by the preceding gate/up tile) at the
-        // start, when it fits next to the attention tiles' needs
+        // down tile: its gate/up activations [B][k][I] fp32 at the start of
+        // the general region, its output staging at the end
         const size_t ystage = (size_t)2 * 8 * 64 * 4;
-        const size_t la_need = ((size_t)std::min(d.n_experts, d.max_batch * d.top_k) * 4 * d.moe_inter * 2 + 1023) / 1024 * 1024;
-        size_t general = align256(std::max(attn, comb) + ystage);
-        if (la_need + ystage <= (size_t)64 * 1024) general = std::max(general, align256(la_need + ystage));
-        const size_t la_bytes = (o.down_lookahead && general - ystage >= la_need) ? la_need : 0;
+        const size_t act = (size_t)d.max_batch * d.top_k * d.moe_inter * 4;
+        const size_t general = align256(std::max(std::max(attn, comb), act) + ystage);
         h->general = (int)general;
         h->lds_bytes = general + 1024 + 1024;
-        h->la_bytes = (int)la_bytes;
         if (h->lds_bytes > (size_t)prop.sharedMemPerBlock && h->lds_bytes > 160 * 1024)
             return fail(MK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", h->lds_bytes);
         for (int nb = 1; nb <= kMaxBatchValu; ++nb) MK_HIP(set_kernel_attributes(h->kern[nb], h->lds_bytes));
@@ -329,7 +324,6 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         p.max_chunks = max_chunks;
         p.n_pages = d.n_pages;
         p.trace_on = o.trace ? 1 : 0;
-        p.la_bytes = h->la_bytes;
         const int64_t wd_ns = o.watchdog_ns > 0 ? o.watchdog_ns : 2000000000LL;
         p.watchdog_ticks = wd_ns / 10;  // 100 MHz constant clock
         p.embed = static_cast<const uint16_t*>(w->embed);

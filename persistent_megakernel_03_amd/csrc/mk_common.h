@@ -65,7 +65,11 @@ enum WKind : int32_t {
 // Counter bank layout: one counter per 128-byte line. Per layer: one QKV
 // counter and one attention counter per KV group, then the combine, output
 // projection, router, gate/up and down counters.
-constexpr int kCtrStride = 32;  // uint32 words per counter
+constexpr int kCtrStride = 32;  // uint32 words per counter line
+// Each counter is split over kCtrSub lines: a producer bumps the line of its
+// workgroup index modulo kCtrSub and a consumer sums them, so the hundreds of
+// tiles of a wide level do not queue on one address.
+constexpr int kCtrSub = 8;
 
 struct CounterLayout {
     int n_layers, n_kv_heads, max_batch;
@@ -79,7 +83,7 @@ struct CounterLayout {
     MK_HD int gateup(int l) const { return combine(l) + 3; }
     MK_HD int down(int l) const { return combine(l) + 4; }
     MK_HD int n_main() const { return 1 + n_layers * per_layer(); }
-    MK_HD int64_t bank_words() const { return ((int64_t)n_main() * kCtrStride + 63) & ~(int64_t)63; }
+    MK_HD int64_t bank_words() const { return ((int64_t)n_main() * kCtrSub * kCtrStride + 63) & ~(int64_t)63; }
 };
 
 // Exchange buffers are padded so that no 128-byte cache line holds words of
@@ -98,7 +102,6 @@ struct Params {
     // this step
     int32_t B, chunk;
     int32_t perop;      // 1: per-op launches (no counter waits / signals)
-    int32_t la_bytes;   // LDS lookahead capacity for down-projection weights (0: off)
     int32_t trace_on;
     int64_t watchdog_ticks;
     // weights

@@ -116,7 +116,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Loads through global-address-space pointers. Weight pointers come from a
+// table in memory, so the compiler cannot tell they are global and would emit
+// FLAT loads, which also count against the LDS wait counter: every later LDS
+// access would then wait for all weight rows in flight, serialising the
+// prefetch. All buffers here are device memory.
+// (The casts go through clang's native vector types: a load through the HIP
+// vector classes would still be generic.)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+#define MK_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ float ldg(const float* p) { return *(const MK_GLOBAL float*)p; }
+__device__ __forceinline__ int32_t ldg(const int32_t* p) { return *(const MK_GLOBAL int32_t*)p; }
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    const u32x4_t v = *(const MK_GLOBAL u32x4_t*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ldf4(const float* p) {
+    const f32x4v_t v = *(const MK_GLOBAL f32x4v_t*)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ const uint16_t* wptr(const Params& p, int layer, int kind) {
     return reinterpret_cast<const uint16_t*>(p.wtab[layer * W_NKINDS + kind]);
@@ -168,8 +187,8 @@ __device__ __forceinline__ void raise_error(const Params& p, int32_t code, int32
 // The memory model's agent-scope fences would instead write back
 // (buffer_wbl2) or invalidate (buffer_inv) a whole XCD's L2 on every task,
 // which serialises the L2 under thousands of tasks per step.
-__device__ __forceinline__ float ld_dev(const float* p) { return *p; }
-__device__ __forceinline__ int32_t ld_dev(const int32_t* p) { return *p; }
+__device__ __forceinline__ float ld_dev(const float* p) { return ldg(p); }
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) { return ldg(p); }
 __device__ __forceinline__ void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -178,20 +197,29 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 // device-scope stores) have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Block-wide wait until counter `ctr` reaches `target`. Thread 0 spins with
-// device-scope loads; the barrier then orders every thread's later
-// device-scope loads after the observation. Returns false if the step was
-// aborted (watchdog here or elsewhere). Records when the wait ended in
-// *t_wait (thread 0).
+// Block-wide wait until counter `ctr` (the sum of its kCtrSub lines) reaches
+// `target`. Lanes 0..kCtrSub-1 of wave 0 poll one line each with
+// device-scope loads; the barrier then orders every thread's later loads
+// after the observation. Returns false if the step was aborted (watchdog
+// here or elsewhere). Records when the wait ended in *t_wait (thread 0).
+__device__ __forceinline__ uint32_t counter_sum(const Params& p, int ctr) {
+    const int lane = tid_() & 63;
+    const uint32_t* c = p.ctr + ((int64_t)ctr * kCtrSub + (lane & (kCtrSub - 1))) * kCtrStride;
+    const uint32_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kCtrSub; ++j) s += (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+    return s;
+}
+
 __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wait) {
     if (p.perop || ctr < 0) return true;
     int ok = 1;
-    if (tid_() == 0) {
-        const uint32_t* c = p.ctr + (int64_t)ctr * kCtrStride;
-        if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)target) {
+    if (tid_() < 64) {
+        if (counter_sum(p, ctr) < (uint32_t)target) {
             const uint64_t t0 = wall_clock64();
             uint32_t it = 0;
-            while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)target) {
+            while (counter_sum(p, ctr) < (uint32_t)target) {
                 __builtin_amdgcn_s_sleep(1);
                 if ((++it & 31u) == 0) {
                     if (__hip_atomic_load(p.err + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -199,21 +227,21 @@ __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wai
                         break;
                     }
                     if ((int64_t)(wall_clock64() - t0) > p.watchdog_ticks) {
-                        raise_error(p, kErrTimeout, ctr, true);
+                        if (tid_() == 0) raise_error(p, kErrTimeout, ctr, true);
                         ok = 0;
                         break;
                     }
                 }
             }
         }
-        *t_wait = wall_clock64();
+        if (tid_() == 0) *t_wait = wall_clock64();
     }
     return __syncthreads_and(ok) != 0;
 }
 
-// Complete this workgroup's device-scope stores and bump counter `ctr`.
-// `drained`: every wave has already waited for its stores (and may have
-// issued loads since, which must not delay the signal).
+// Complete this workgroup's device-scope stores and bump counter `ctr` (the
+// line of this workgroup). `drained`: every wave has already waited for its
+// stores (and may have issued loads since, which must not delay the signal).
 __device__ void block_signal(const Params& p, int ctr, bool drained = false) {
     if (p.perop || ctr < 0) {
         __syncthreads();
@@ -222,7 +250,8 @@ __device__ void block_signal(const Params& p, int ctr, bool drained = false) {
     if (!drained) wait_stores();
     __syncthreads();
     if (tid_() == 0)
-        __hip_atomic_fetch_add(p.ctr + (int64_t)ctr * kCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.ctr + ((int64_t)ctr * kCtrSub + (blockIdx.x & (kCtrSub - 1))) * kCtrStride, 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------ activation slices + norm
@@ -255,8 +284,7 @@ __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, i
         for (int c = 0; c < NCH; ++c) {
             const int ch = lane + 64 * c;
             if (b < nb && ch < K8) {
-                const float4* px = reinterpret_cast<const float4*>(x + b * stride + ch * 8);
-                const float4 u = px[0], v = px[1];
+                const float4 u = ldf4(x + b * stride + ch * 8), v = ldf4(x + b * stride + ch * 8 + 4);
                 h[b][c][0] = u.x; h[b][c][1] = u.y; h[b][c][2] = u.z; h[b][c][3] = u.w;
                 h[b][c][4] = v.x; h[b][c][5] = v.y; h[b][c][6] = v.z; h[b][c][7] = v.w;
             } else {
@@ -284,55 +312,70 @@ __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, i
 // ------------------------------------------------------- streaming GEMV
 
 // Load one weight row slice for this lane: chunks lane + 64c of a row with
-// K8 16-byte chunks. A null row loads zeros.
+// K8 16-byte chunks. Branch-free: lanes past the row's end re-read its last
+// chunk (already being fetched), so every call issues exactly NCH loads and
+// the compiler can wait for each row precisely. Their activation slices are
+// zero (load_x and the tiles' loaders zero them), so the duplicate finite
+// weights add nothing to the dot products.
 template <int NCH>
 __device__ __forceinline__ void load_row(uint4 (&w)[NCH], const uint16_t* row, int K8) {
     const int lane = tid_() & 63;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
-        if (row != nullptr && ch < K8) w[c] = ld16(row + ch * 8);
-        else w[c] = make_uint4(0u, 0u, 0u, 0u);
+        w[c] = ld16(row + (ch < K8 ? ch : K8 - 1) * 8);
     }
 }
 
-// Wave-level streaming matrix-vector product. The wave owns `nmine`
-// row-vectors; rowptr(i) returns the i-th. The first PF rows are loaded
-// before ready(h) runs (ready holds the dependency wait and fills the
-// activation slices h); then rows are consumed in order while the row PF
-// places ahead is in flight. reload(i, h) may refresh h before row i;
-// emit(i, acc) receives the wave-reduced dot products (every lane has them).
-// With XFIRST, ready(h) runs before the first rows are loaded instead (for
-// tiles whose weights are known only after the wait: the small activation
-// load then does not queue behind the weight stream).
-template <int NCH, int PF, int NB, bool XFIRST = false, class RowPtr, class Ready, class Reload, class Emit>
-__device__ __forceinline__ void gemv_stream(int nmine, int K8, RowPtr rowptr, Ready ready, Reload reload,
-                                            Emit emit) {
-    float h[NB][NCH][8];
-    if (XFIRST) ready(h);
+// Wave-level streaming matrix-vector product over activation slices h that
+// the caller holds. The wave owns `nmine` row-vectors; rowptr(i) returns the
+// i-th. The first PF rows are loaded before ready() runs (ready holds the
+// dependency wait); then rows are consumed in order while the row PF places
+// ahead is in flight. reload(i, h) may refresh h before row i; emit(i, acc)
+// receives the wave-reduced dot products (every lane has them). Loads are
+// unconditional (slots past the last row re-read the last row, which is in
+// flight already), so the wait before each row covers that row only and the
+// stream stays PF rows deep.
+template <int NCH, int PF, int NB, class RowPtr, class Ready, class Reload, class Emit>
+__device__ __forceinline__ void gemv_rows(float (&h)[NB][NCH][8], int nmine, int K8, RowPtr rowptr, Ready ready,
+                                          Reload reload, Emit emit) {
+    if (nmine <= 0) {
+        ready();
+        return;
+    }
     uint4 buf[PF][NCH];
+    const int last = nmine - 1;
 #pragma unroll
-    for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], s < nmine ? rowptr(s) : nullptr, K8);
-    if (!XFIRST) ready(h);
+    for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], rowptr(s < last ? s : last), K8);
+    ready();
     for (int i0 = 0; i0 < nmine; i0 += PF) {
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
             const int i = i0 + s;
-            if (i < nmine) {
-                reload(i, h);
-                float acc[NB];
+            const bool live = i < nmine;
+            if (live) reload(i, h);
+            float acc[NB];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    float a = 0.f;
+            for (int b = 0; b < NB; ++b) {
+                float a = 0.f;
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], h[b][c], a);
-                    acc[b] = wave_sum(a);
-                }
-                if (i + PF < nmine) load_row<NCH>(buf[s], rowptr(i + PF), K8);
-                emit(i, acc);
+                for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], h[b][c], a);
+                acc[b] = wave_sum(a);
             }
+            const int nx = i + PF;
+            if (i0 + PF < nmine) load_row<NCH>(buf[s], rowptr(nx < last ? nx : last), K8);
+            if (live) emit(i, acc);
         }
     }
+}
+
+// The same with the activation slices owned here: ready(h) holds the
+// dependency wait and fills h.
+template <int NCH, int PF, int NB, class RowPtr, class Ready, class Reload, class Emit>
+__device__ __forceinline__ void gemv_stream(int nmine, int K8, RowPtr rowptr, Ready ready, Reload reload,
+                                            Emit emit) {
+    float h[NB][NCH][8];
+    gemv_rows<NCH, PF, NB>(h, nmine, K8, rowptr, [&]() { ready(h); }, reload, emit);
 }
 
 // ------------------------------------------------------------ routing
@@ -350,7 +393,7 @@ struct RouteLds {
 // Wave 0 computes top-k (logit descending, expert id ascending on ties) and a
 // softmax over the selected logits for each token, then lists the distinct
 // selected experts in ascending order as slots. Ends with a block barrier.
-__device__ __forceinline__ void compute_routing(const Params& p, const float* rl, RouteLds* r) {
+__device__ __forceinline__ void compute_routing(const Params& p, const float* rl, RouteLds* r, uint64_t* mk = nullptr) {
     if (tid_() < 64) {
         const int lane = tid_();
         const int E = p.E, K = p.K;
@@ -365,6 +408,7 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
             // top-k by repeated wave-wide maximum of 64-bit keys (logit in an
             // order-preserving unsigned form, then the inverted expert id):
             // the largest key is the largest logit, ties to the lowest id
+            if (mk && p.trace_on && lane == 0) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); mk[0] = wall_clock64(); }
             uint32_t taken = 0u;
             uint64_t key[4];
 #pragma unroll
@@ -374,10 +418,9 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
                 u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
                 key[i] = e < E ? (((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
             }
-            float sel_v[kMaxTopK];
-#pragma unroll
+            float top_v = -INFINITY;
+#pragma unroll 1
             for (int j = 0; j < kMaxTopK; ++j) {
-                sel_v[j] = -INFINITY;
                 if (j < K) {
                     uint64_t kb = key[0];
 #pragma unroll
@@ -385,7 +428,9 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
                     const uint64_t km = wave_max_u64(kb);
                     const int best = (int)(0xffffffffu - (uint32_t)km);
                     const uint32_t uh = (uint32_t)(km >> 32);
-                    sel_v[j] = __uint_as_float((uh & 0x80000000u) ? (uh ^ 0x80000000u) : ~uh);
+                    const float vj = __uint_as_float((uh & 0x80000000u) ? (uh ^ 0x80000000u) : ~uh);
+                    if (j == 0) top_v = vj;
+                    if (lane == 0) r->w[b][j] = vj;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (key[i] == km) key[i] = 0ull;   // taken (keys are unique)
@@ -393,24 +438,18 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
                     if ((best & 63) == lane) taken |= 1u << (best >> 6);
                 }
             }
+            if (mk && p.trace_on && lane == 0) mk[1] = wall_clock64();
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if ((taken >> i) & 1u) chosen[i] |= 1u << b;
-            // softmax over the selected logits (sel_v[0] is the largest)
-            float ex[kMaxTopK];
-            float s = 0.f;
-#pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) {
-                ex[j] = 0.f;
-                if (j < K) {
-                    ex[j] = expf(sel_v[j] - sel_v[0]);
-                    s += ex[j];
-                }
-            }
+            // softmax over the selected logits (the first is the largest);
+            // lane 0 holds them in r->w[b][..] and replaces them by weights
             if (lane == 0) {
-#pragma unroll
-                for (int j = 0; j < kMaxTopK; ++j)
-                    if (j < K) r->w[b][j] = ex[j] / s;
+                float sum = 0.f;
+#pragma unroll 1
+                for (int j = 0; j < K; ++j) sum += expf(r->w[b][j] - top_v);
+#pragma unroll 1
+                for (int j = 0; j < K; ++j) r->w[b][j] = expf(r->w[b][j] - top_v) / sum;
             }
         }
         // slots: selected experts in ascending id

@@ -22,7 +22,6 @@ __global__ void __launch_bounds__(NT, 2) k_persistent(Params p, int general) {
     // Clear the counter bank the next step will use (disjoint slice per workgroup).
     for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < p.bank_words; i += (int64_t)gridDim.x * NT)
         p.ctr_other[i] = 0u;
-    if (threadIdx.x == 0) misc_lds(lds, general)[kLaTag] = -1;
     __syncthreads();
     const int beg = p.wg_off[blockIdx.x], end = p.wg_off[blockIdx.x + 1];
     for (int i = beg; i < end; ++i) {
@@ -37,7 +36,6 @@ __global__ void __launch_bounds__(NT, 2) k_perop(Params p, int general, int firs
     extern __shared__ __align__(16) char lds[];
     const int i = first + blockIdx.x;
     const Task t = p.tasks[i];
-    if (threadIdx.x == 0) misc_lds(lds, general)[kLaTag] = -1;
     __syncthreads();
     run_task<S, NB>(t, nullptr, p, lds, general, i);
 }

@@ -44,6 +44,22 @@ struct Tile {
 
 }  // namespace
 
+void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down) {
+    *rows_gu = cfg.rows_gateup;
+    *rows_down = cfg.rows_down;
+    // A down tile keeps all its weight rows (S experts x rows) in registers,
+    // at most 16 row-vectors per wave.
+    const int rd = std::min(64, 64 / std::max(1, S));
+    if (rd < cfg.rows_down) return;
+    const int n_down = ceil_div(s.H, rd);
+    const int per_slot = (n_wg - n_down) / std::max(1, S);
+    if (per_slot < 1) return;
+    int rg = std::max(cfg.rows_gateup, ceil_div(s.I, per_slot));
+    rg = ceil_div(rg, 4) * 4;
+    *rows_gu = rg;
+    *rows_down = rd;
+}
+
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested) {
     int chunk;
     if (requested > 0) {
@@ -103,8 +119,10 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     const int no = ceil_div(s.H, cfg.rows_o);
     const int nr = ceil_div(s.E, cfg.rows_router);
     const int S = std::min(s.E, B * s.K);
-    const int ngu = ceil_div(s.I, cfg.rows_gateup);
-    const int nd = ceil_div(s.H, cfg.rows_down);
+    int rows_gu = 0, rows_down = 0;
+    expert_rows(s, cfg, n_wg, S, &rows_gu, &rows_down);
+    const int ngu = ceil_div(s.I, rows_gu);
+    const int nd = ceil_div(s.H, rows_down);
     const int nl = ceil_div(s.V, cfg.rows_lm);
     int total_chunks = 0;
     for (int b = 0; b < B; ++b) total_chunks += P.n_chunks[b];
@@ -139,7 +157,7 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         P.targets[cl.combine(l)] = B * s.Hq;
         for (int i = 0; i < no; ++i) {
             const int r0 = i * cfg.rows_o, r1 = std::min(s.H, r0 + cfg.rows_o);
-            add(make_task(OP_OPROJ, l, r0, r1, 0, 0, -1, 0, cl.combine(l), B * s.Hq, cl.oproj(l), lv + 3),
+            add(make_task(OP_OPROJ, l, r0, r1, 0, 0, in_ctr, in_target, cl.combine(l), B * s.Hq, cl.oproj(l), lv + 3),
                 2.0 * (r1 - r0) * s.Hq * s.D, kStatic);
         }
         P.targets[cl.oproj(l)] = no;
@@ -151,14 +169,14 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         P.targets[cl.router(l)] = nr;
         for (int sl = 0; sl < S; ++sl)
             for (int i = 0; i < ngu; ++i) {
-                const int r0 = i * cfg.rows_gateup, r1 = std::min(s.I, r0 + cfg.rows_gateup);
-                add(make_task(OP_GATEUP, l, sl, r0, r1, (sl == 0 && i == 0) ? 1 : 0, cl.router(l), nr, -1, 0,
-                              cl.gateup(l), lv + 5),
+                const int r0 = i * rows_gu, r1 = std::min(s.I, r0 + rows_gu);
+                add(make_task(OP_GATEUP, l, sl, r0, r1, (sl == 0 && i == 0) ? 1 : 0, cl.oproj(l), no, cl.router(l),
+                              nr, cl.gateup(l), lv + 5),
                     4.0 * (r1 - r0) * s.H, kRouted);
             }
         P.targets[cl.gateup(l)] = S * ngu;
         for (int i = 0; i < nd; ++i) {
-            const int r0 = i * cfg.rows_down, r1 = std::min(s.H, r0 + cfg.rows_down);
+            const int r0 = i * rows_down, r1 = std::min(s.H, r0 + rows_down);
             add(make_task(OP_DOWN, l, r0, r1, 0, 0, cl.router(l), nr, cl.gateup(l), S * ngu, cl.down(l), lv + 6),
                 2.0 * S * (r1 - r0) * s.I, kRouted);
         }

@@ -54,6 +54,13 @@ struct Plan {
     double model_us = 0.0;            // modelled step time
 };
 
+// Rows per gate/up tile and per down tile. When the step's distinct experts
+// allow it, down tiles are sized so that each holds all its weights in
+// registers and gate/up tiles so that both kinds fit on the workgroups at
+// once: the down weights then stream alongside the gate/up weights instead of
+// after them. Otherwise the configured sizes.
+void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down);
+
 // Attention chunk length for these contexts (tokens, multiple of 64).
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested);
 

@@ -255,7 +255,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     const float* qkv = qkv_at(p, l) + (int64_t)b * p.QKVD;
     // queries of the group's heads (G x D floats) and the rotary table into LDS
     for (int i = tid * 4; i < G * D; i += NT * 4)
-        *reinterpret_cast<float4*>(sQf + i) = *reinterpret_cast<const float4*>(qkv + (int64_t)g * G * D + i);
+        *reinterpret_cast<float4*>(sQf + i) = ldf4(qkv + (int64_t)g * G * D + i);
     if (tid < D) sRope[tid] = rope_v;
     __syncthreads();
     // New token: RoPE on k, BF16 rounding of k and v, append to the pool.
@@ -458,7 +458,7 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     const float* po = part_at(p, l) + row * p.max_chunks * D;
     // M = max_c m_c
     float mx = -INFINITY;
-    for (int c = tid; c < nch; c += NT) mx = fmaxf(mx, ml[2 * c]);
+    for (int c = tid; c < nch; c += NT) mx = fmaxf(mx, ld_dev(ml + 2 * c));
     mx = wave_max(mx);
     if (lane == 0) sred[wave] = mx;
     __syncthreads();
@@ -466,9 +466,9 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     // L = sum_c exp(m_c - M) l_c
     float ls = 0.f;
     for (int c = tid; c < nch; c += NT) {
-        const float e = expf(ml[2 * c] - mx);
+        const float e = expf(ld_dev(ml + 2 * c) - mx);
         coef[c] = e;
-        ls += e * ml[2 * c + 1];
+        ls += e * ld_dev(ml + 2 * c + 1);
     }
     ls = wave_sum(ls);
     if (lane == 0) sred[NWAVES + wave] = ls;
@@ -480,10 +480,10 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int c = ph;
     for (; c + 3 * NPH < nch; c += 4 * NPH) {
-        const float4 v0 = *reinterpret_cast<const float4*>(po + (int64_t)c * D + 4 * q);
-        const float4 v1 = *reinterpret_cast<const float4*>(po + (int64_t)(c + NPH) * D + 4 * q);
-        const float4 v2 = *reinterpret_cast<const float4*>(po + (int64_t)(c + 2 * NPH) * D + 4 * q);
-        const float4 v3 = *reinterpret_cast<const float4*>(po + (int64_t)(c + 3 * NPH) * D + 4 * q);
+        const float4 v0 = ldf4(po + (int64_t)c * D + 4 * q);
+        const float4 v1 = ldf4(po + (int64_t)(c + NPH) * D + 4 * q);
+        const float4 v2 = ldf4(po + (int64_t)(c + 2 * NPH) * D + 4 * q);
+        const float4 v3 = ldf4(po + (int64_t)(c + 3 * NPH) * D + 4 * q);
         const float w0 = coef[c], w1 = coef[c + NPH], w2 = coef[c + 2 * NPH], w3 = coef[c + 3 * NPH];
         acc.x = fmaf(w0, v0.x, acc.x); acc.y = fmaf(w0, v0.y, acc.y); acc.z = fmaf(w0, v0.z, acc.z); acc.w = fmaf(w0, v0.w, acc.w);
         acc.x = fmaf(w1, v1.x, acc.x); acc.y = fmaf(w1, v1.y, acc.y); acc.z = fmaf(w1, v1.z, acc.z); acc.w = fmaf(w1, v1.w, acc.w);
@@ -491,7 +491,7 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
         acc.x = fmaf(w3, v3.x, acc.x); acc.y = fmaf(w3, v3.y, acc.y); acc.z = fmaf(w3, v3.z, acc.z); acc.w = fmaf(w3, v3.w, acc.w);
     }
     for (; c < nch; c += NPH) {
-        const float4 v = *reinterpret_cast<const float4*>(po + (int64_t)c * D + 4 * q);
+        const float4 v = ldf4(po + (int64_t)c * D + 4 * q);
         const float w = coef[c];
         acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y); acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
     }
@@ -518,8 +518,18 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
     const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     const int K = p.Hq * p.D;
     const uint16_t* W = wptr(p, l, W_O);
-    const float* xin = x_at(p, 2 * l);
     float* xmid = x_at(p, 2 * l + 1);
+    // residual: lane i holds the layer input at this wave's i-th row; the
+    // layer input is complete long before the attention output (pre counter),
+    // so it is loaded before the main wait
+    float xres[NB];
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+    {
+        const float* xin = x_at(p, 2 * l);
+        const int row = r0 + wave + (lane < nmine ? lane : 0) * NWAVES;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xres[b] = (b < p.B && lane < nmine) ? ld_dev(xin + (int64_t)b * p.H + row) : 0.f;
+    }
     bool ok = true;
     gemv_stream<NCH, PF, NB>(
         nmine, K >> 3, [&](int i) { return W + (int64_t)(r0 + wave + i * NWAVES) * K; },
@@ -529,11 +539,11 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
         },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
-            if (lane == 0) {
+            if (lane == i) {
                 const int row = r0 + wave + i * NWAVES;
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    if (b < p.B) st_dev(xmid + (int64_t)b * p.H + row, ld_dev(xin + (int64_t)b * p.H + row) + acc[b]);
+                    if (b < p.B) st_dev(xmid + (int64_t)b * p.H + row, xres[b] + acc[b]);
             }
         });
     if (!ok) return false;
@@ -566,7 +576,7 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
                 const int row = r0 + wave + i * NWAVES;
-                const float bv = bias != nullptr ? bias[row] : 0.f;
+                const float bv = bias != nullptr ? ldg(bias + row) : 0.f;
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     if (b < p.B) st_dev(rlogits_at(p, l) + (int64_t)b * p.E + row, bias != nullptr ? acc[b] + bv : acc[b]);
@@ -580,23 +590,30 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
 
 // ---------------------------------------------------------- expert gate/up
 
-__device__ __forceinline__ void issue_down_lookahead(TileCtx& cx, const Task& nt, const RouteLds* rt);
-
 // Slot a0 (the a0-th distinct selected expert, ascending id), rows a1..a2 of
 // its gate and up matrices; a = SiLU(W_gate h2) * (W_up h2) for every token
-// routed to it. Task a3 != 0: also store the routing of this layer.
+// routed to it. The post-attention residual is ready one level before the
+// router logits, so the tile waits for it first (pre counter), normalizes it,
+// then waits for the logits (main counter) and computes the routing; only
+// then are the expert's rows known and streamed. Task a3 != 0: also store the
+// routing of this layer.
 template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1;
     const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int H = p.H;
     RouteLds* rt = route_lds(cx.lds, cx.general);
-    uint4 gn[NCH];
-    load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), p.H);
-    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
-    compute_routing(p, rlogits_at(p, l), rt);
-    mark(cx, 0);
-    const bool lookahead = cx.next != nullptr && cx.next->op == OP_DOWN && cx.next->layer == l;
+    float h[NB][NCH][8];
+    {
+        uint4 gn[NCH];
+        load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), H);
+        if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+        load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
+    }
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    compute_routing(p, rlogits_at(p, l), rt, cx.marks);
+    mark(cx, 2);
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
             const int b = i / p.K, j = i - b * p.K;
@@ -605,25 +622,19 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
         }
     }
     if (slot >= rt->nslots) {
-        wait_stores();
-        if (lookahead) issue_down_lookahead(cx, *cx.next, rt);
-        block_signal(p, t.signal, true);
+        block_signal(p, t.signal);
         return true;
     }
     const int e = rt->slot_e[slot];
     const int mask = rt->slot_mask[slot];
-    const int H = p.H;
     const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * p.I * H;
     const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * p.I * H;
     const int npair = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     float gate[NB];
-    gemv_stream<NCH, PF, NB, true>(
-        2 * npair, H >> 3,
+    gemv_rows<NCH, PF, NB>(
+        h, 2 * npair, H >> 3,
         [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
-        [&](float(&h)[NB][NCH][8]) {
-            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
-            mark(cx, 1);
-        },
+        [&]() { mark(cx, 3); },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if ((i & 1) == 0) {
@@ -641,155 +652,96 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
                 }
             }
         });
-    mark(cx, 2);
-    // Drain this wave's stores first, so the lookahead loads issued next do
-    // not delay the signal (vmcnt counts loads and stores together).
-    wait_stores();
-    if (lookahead) issue_down_lookahead(cx, *cx.next, rt);
-    block_signal(p, t.signal, true);
+    block_signal(p, t.signal);
     return true;
 }
 
 // ------------------------------------------------------------ expert down
 
-// Down-projection lookahead. Expert weights are known once the routing is,
-// which is long before the gate/up outputs a down tile needs are. A gate/up
-// tile whose workgroup runs a down tile of the same layer next streams that
-// tile's weights straight into LDS (direct global-to-LDS loads) while its own
-// gate/up rows stream into registers; the down tile then computes from LDS.
-// Layout: per selected expert (slot), its nrows rows of I BF16, slot-major.
-__device__ __forceinline__ int down_tag(const Task& t) { return (t.layer << 16) | t.a0; }
-constexpr int kLaTag = 60;  // int slot in the per-tile scalar area
-
-__device__ __forceinline__ void issue_down_lookahead(TileCtx& cx, const Task& nt, const RouteLds* rt) {
-    const Params& p = cx.p;
-    int* tag = misc_lds(cx.lds, cx.general) + kLaTag;
-    const int nrows = nt.a1 - nt.a0;
-    const int64_t slot_bytes = (int64_t)nrows * p.I * 2;
-    const int64_t total = (int64_t)rt->nslots * slot_bytes;
-    const int64_t n_inst = (total + 1023) / 1024;   // 64 lanes x 16 bytes per load
-    if (n_inst * 1024 > p.la_bytes || (slot_bytes & 15) != 0 || p.perop) return;
-    const int tid = tid_(), lane = tid & 63, wave = tid >> 6;
-    const uint16_t* Wd = wptr(p, nt.layer, W_DOWN);
-    for (int64_t q = wave; q < n_inst; q += NWAVES) {
-        int64_t off = (q * 64 + lane) * 16;
-        if (off >= total) off = 0;   // tail lanes reload the first chunk into padding
-        const int s = (int)(off / slot_bytes);
-        const int64_t within = off - s * slot_bytes;
-        const char* src = reinterpret_cast<const char*>(Wd + ((int64_t)rt->slot_e[s] * p.H + nt.a0) * p.I) + within;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(cx.lds + q * 1024), 16, 0, 0);
-    }
-    if (tid == 0) *tag = down_tag(nt);
-}
-
 // Rows a0..a1 of the hidden dimension, for every selected expert: y = W_down a,
-// then x_out = x_mid + sum_j w_j y_j in top-k rank order. Weights come from
-// the LDS lookahead when the previous task loaded them, else from registers.
+// then x_out = x_mid + sum_j w_j y_j in top-k rank order. The routing (and so
+// the expert rows) is known once the router logits are (pre counter): the
+// tile computes it and starts every row of its weights streaming into
+// registers while the gate/up tiles are still running, then waits for them
+// (main counter) and reads their activations once, into LDS.
 template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0;
-    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int tid = tid_(), wave = tid >> 6, lane = tid & 63;
     RouteLds* rt = route_lds(cx.lds, cx.general);
-    int* tag = misc_lds(cx.lds, cx.general) + kLaTag;
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     compute_routing(p, rlogits_at(p, l), rt);
     mark(cx, 0);
-    const bool la = *tag == down_tag(t);
     const int I = p.I, K = p.K, B = p.B;
     const int nslots = rt->nslots;
+    // residual slice: ready since the output projection
+    const float* xmid = x_at(p, 2 * l + 1);
+    const float xres = tid < B * nrows ? xmid[(int64_t)(tid / nrows) * p.H + h0 + tid % nrows] : 0.f;
     // wave w takes slots w, w+4, ...; row-vector i -> slot index i / nrows, row i % nrows
     const int myslots = nslots > wave ? (nslots - wave + NWAVES - 1) / NWAVES : 0;
     const uint16_t* Wd = wptr(p, l, W_DOWN);
+    float* sAct = reinterpret_cast<float*>(cx.lds);   // [B][K][I] gate/up outputs
     float* sY = reinterpret_cast<float*>(cx.lds + cx.general) - kMaxBatch * kMaxTopK * kMaxDownRows;  // [B*K][nrows]
-    const float* act = act_at(p, l);
     const int K8 = I >> 3;
-    auto load_act = [&](int s, float(&h)[NB][NCH][8]) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int ch = lane + 64 * c;
-                if (rank >= 0 && ch < K8) {
-                    const float4* a = reinterpret_cast<const float4*>(act + ((int64_t)b * K + rank) * I + ch * 8);
-                    const float4 u = a[0], v = a[1];
-                    h[b][c][0] = u.x; h[b][c][1] = u.y; h[b][c][2] = u.z; h[b][c][3] = u.w;
-                    h[b][c][4] = v.x; h[b][c][5] = v.y; h[b][c][6] = v.z; h[b][c][7] = v.w;
-                } else {
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) h[b][c][jj] = 0.f;
-                }
-            }
-        }
-    };
-    auto emit = [&](int i, const float(&acc)[NB]) {
-        if (lane == 0) {
+    const float* act = act_at(p, l);
+    bool ok = true;
+    float h[NB][NCH][8];
+    gemv_rows<NCH, PF, NB>(
+        h, myslots * nrows, K8,
+        [&](int i) {
             const int s = wave + (i / nrows) * NWAVES;
-            const int r = i % nrows;
+            return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + (i % nrows)) * I;
+        },
+        [&]() {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            const int n4 = (B * K * I) >> 2;
+            for (int i = tid; i < n4; i += NT)
+                reinterpret_cast<float4*>(sAct)[i] = ldf4(act + 4 * i);
+            __syncthreads();
+            mark(cx, 1);
+        },
+        [&](int i, float(&hh)[NB][NCH][8]) {
+            if (i % nrows != 0) return;
+            const int s = wave + (i / nrows) * NWAVES;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
-                if (rank >= 0) sY[((int64_t)b * K + rank) * nrows + r] = acc[b];
-            }
-        }
-    };
-    bool ok = true;
-    if (la) {
-        ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's lookahead loads have landed
-        __syncthreads();                                   // and every wave's
-        mark(cx, 1);
-        const uint16_t* la_w = reinterpret_cast<const uint16_t*>(cx.lds);
-        float h[NB][NCH][8];
-        for (int i = 0; i < myslots * nrows; ++i) {
-            const int s = wave + (i / nrows) * NWAVES;
-            if (i % nrows == 0) load_act(s, h);
-            const uint16_t* row = la_w + ((int64_t)s * nrows + (i % nrows)) * I;
-            uint4 w[NCH];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int ch = lane + 64 * c;
-                w[c] = ch < K8 ? *reinterpret_cast<const uint4*>(row + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
-            }
-            float acc[NB];
+                for (int c = 0; c < NCH; ++c) {
+                    const int ch = lane + 64 * c;
+                    if (rank >= 0 && ch < K8) {
+                        const float4* a = reinterpret_cast<const float4*>(sAct + (b * K + rank) * I + ch * 8);
+                        const float4 u = a[0], v = a[1];
+                        hh[b][c][0] = u.x; hh[b][c][1] = u.y; hh[b][c][2] = u.z; hh[b][c][3] = u.w;
+                        hh[b][c][4] = v.x; hh[b][c][5] = v.y; hh[b][c][6] = v.z; hh[b][c][7] = v.w;
+                    } else {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                float a = 0.f;
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) a = dot8(w[c], h[b][c], a);
-                acc[b] = wave_sum(a);
+                        for (int jj = 0; jj < 8; ++jj) hh[b][c][jj] = 0.f;
+                    }
+                }
             }
-            emit(i, acc);
-        }
-    } else {
-        gemv_stream<NCH, PF, NB>(
-            myslots * nrows, K8,
-            [&](int i) {
+        },
+        [&](int i, const float(&acc)[NB]) {
+            if (lane == 0) {
                 const int s = wave + (i / nrows) * NWAVES;
-                return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + (i % nrows)) * I;
-            },
-            [&](float(&)[NB][NCH][8]) {
-                ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-                mark(cx, 1);
-            },
-            [&](int i, float(&h)[NB][NCH][8]) {
-                if (i % nrows == 0) load_act(wave + (i / nrows) * NWAVES, h);
-            },
-            emit);
-    }
+                const int r = i % nrows;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
+                    if (rank >= 0) sY[(b * K + rank) * nrows + r] = acc[b];
+                }
+            }
+        });
     if (!ok) return false;
     __syncthreads();
     mark(cx, 2);
-    if (tid_() == 0) *tag = -1;
-    const float* xmid = x_at(p, 2 * l + 1);
     float* xout = x_at(p, 2 * l + 2);
-    for (int idx = tid_(); idx < B * nrows; idx += NT) {
-        const int b = idx / nrows, r = idx - b * nrows;
+    if (tid < B * nrows) {
+        const int b = tid / nrows, r = tid - b * nrows;
         float acc = 0.f;
-        for (int j = 0; j < K; ++j) acc += rt->w[b][j] * sY[((int64_t)b * K + j) * nrows + r];
-        st_dev(xout + (int64_t)b * p.H + h0 + r, ld_dev(xmid + (int64_t)b * p.H + h0 + r) + acc);
+        for (int j = 0; j < K; ++j) acc += rt->w[b][j] * sY[(b * K + j) * nrows + r];
+        st_dev(xout + (int64_t)b * p.H + h0 + r, xres + acc);
     }
     block_signal(p, t.signal);
     return true;
@@ -857,7 +809,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
         case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 8 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
-        case OP_DOWN: return tile_down<S::NCH_I, Pf<S::NCH_I, NB>::v, NB>(t, cx);
+        case OP_DOWN: return tile_down<S::NCH_I, (NB == 1 && S::NCH_I <= 2 ? 16 : Pf<S::NCH_I, NB>::v), NB>(t, cx);
         case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         default: return false;
     }

@@ -116,8 +116,8 @@ def test_plan_counts_for_the_30b_shape():
     assert ops[OP_COMBINE] == 48 * 32          # one merge per query head
     assert ops[OP_OPROJ] == 48 * 256
     assert ops[OP_ROUTER] == 48 * 16
-    assert ops[OP_GATEUP] == 48 * 8 * 48       # 8 slots x 768 rows / 16
-    assert ops[OP_DOWN] == 48 * 512
+    assert ops[OP_GATEUP] == 48 * 8 * 32       # 8 slots x 768 rows / 24 (gate/up and down fit 512 workgroups)
+    assert ops[OP_DOWN] == 48 * 256            # 2048 rows / 8: 8 experts x 8 rows per tile held in registers
     assert ops[OP_LMHEAD] == -(-151936 // 64)
     assert info.n_levels == 2 + 7 * 48
 
