@@ -390,67 +390,75 @@ struct RouteLds {
     int8_t slot_rank[kMaxSlots][kMaxBatch]; // rank of the expert in that token's top-k
 };
 
-// Wave 0 computes top-k (logit descending, expert id ascending on ties) and a
-// softmax over the selected logits for each token, then lists the distinct
-// selected experts in ascending order as slots. Ends with a block barrier.
-__device__ __forceinline__ void compute_routing(const Params& p, const float* rl, RouteLds* r, uint64_t* mk = nullptr) {
+// Order-preserving map of a float to an unsigned key (larger float, larger
+// key); no finite float or infinity maps to 0, which marks "no candidate".
+__device__ __forceinline__ uint32_t fkey(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unkey(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Wave 0 computes, per token, the top-k experts (logit descending, expert id
+// ascending on ties) by k rounds of a wave-wide maximum over order-preserving
+// keys; the lowest id holding the maximum is found with ballots. Then the
+// softmax over the selected logits (lane j holds the j-th), and the distinct
+// selected experts in ascending id as slots, with each token's rank of the
+// slot's expert. Ends with a block barrier.
+__device__ __forceinline__ void compute_routing(const Params& p, const float* rl, RouteLds* r) {
     if (tid_() < 64) {
         const int lane = tid_();
         const int E = p.E, K = p.K;
-        uint32_t chosen[4] = {0u, 0u, 0u, 0u};  // per lane: bit b = token b chose expert lane+64i
+        uint32_t chosen[4] = {0u, 0u, 0u, 0u};  // bit b: token b chose expert lane + 64i
+        uint32_t rank[4] = {~0u, ~0u, ~0u, ~0u}; // byte b: its rank in token b's top-k
         for (int b = 0; b < p.B; ++b) {
-            float v[4];
+            uint32_t u[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = lane + 64 * i;
-                v[i] = e < E ? ld_dev(rl + b * E + e) : -INFINITY;
+                u[i] = e < E ? fkey(ld_dev(rl + b * E + e)) : 0u;
             }
-            // top-k by repeated wave-wide maximum of 64-bit keys (logit in an
-            // order-preserving unsigned form, then the inverted expert id):
-            // the largest key is the largest logit, ties to the lowest id
-            if (mk && p.trace_on && lane == 0) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); mk[0] = wall_clock64(); }
-            uint32_t taken = 0u;
-            uint64_t key[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = lane + 64 * i;
-                uint32_t u = __float_as_uint(v[i]);
-                u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-                key[i] = e < E ? (((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
-            }
-            float top_v = -INFINITY;
+            float top = 0.f, sel = 0.f;
 #pragma unroll 1
-            for (int j = 0; j < kMaxTopK; ++j) {
-                if (j < K) {
-                    uint64_t kb = key[0];
+            for (int j = 0; j < K; ++j) {
+                const uint32_t m = wave_max_u32(max(max(u[0], u[1]), max(u[2], u[3])));
+                int best = -1;
 #pragma unroll
-                    for (int i = 1; i < 4; ++i) kb = key[i] > kb ? key[i] : kb;
-                    const uint64_t km = wave_max_u64(kb);
-                    const int best = (int)(0xffffffffu - (uint32_t)km);
-                    const uint32_t uh = (uint32_t)(km >> 32);
-                    const float vj = __uint_as_float((uh & 0x80000000u) ? (uh ^ 0x80000000u) : ~uh);
-                    if (j == 0) top_v = vj;
-                    if (lane == 0) r->w[b][j] = vj;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (key[i] == km) key[i] = 0ull;   // taken (keys are unique)
-                    if (lane == 0) r->ids[b][j] = best;
-                    if ((best & 63) == lane) taken |= 1u << (best >> 6);
+                for (int i = 3; i >= 0; --i) {
+                    const uint64_t bal = __ballot(u[i] == m);
+                    if (bal != 0ull) best = 64 * i + (int)__builtin_ctzll(bal);
                 }
-            }
-            if (mk && p.trace_on && lane == 0) mk[1] = wall_clock64();
+                const float v = unkey(m);
+                if (j == 0) top = v;
+                if (lane == j) sel = v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if ((taken >> i) & 1u) chosen[i] |= 1u << b;
-            // softmax over the selected logits (the first is the largest);
-            // lane 0 holds them in r->w[b][..] and replaces them by weights
-            if (lane == 0) {
-                float sum = 0.f;
-#pragma unroll 1
-                for (int j = 0; j < K; ++j) sum += expf(r->w[b][j] - top_v);
-#pragma unroll 1
-                for (int j = 0; j < K; ++j) r->w[b][j] = expf(r->w[b][j] - top_v) / sum;
+                for (int i = 0; i < 4; ++i) {
+                    if (64 * i + lane == best) {
+                        u[i] = 0u;
+                        chosen[i] |= 1u << b;
+                        rank[i] = (rank[i] & ~(0xffu << (8 * b))) | ((uint32_t)j << (8 * b));
+                    }
+                }
+                if (lane == 0) r->ids[b][j] = best;
             }
+            // softmax over the selected logits (the first is the largest)
+            const float ex = lane < K ? expf(sel - top) : 0.f;
+            const float sum = wave_sum(ex);
+            if (lane < K) r->w[b][lane] = ex / sum;
         }
         // slots: selected experts in ascending id
         int base = 0;
@@ -461,21 +469,15 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
                 const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
                 r->slot_e[slot] = lane + 64 * i;
                 r->slot_mask[slot] = (int32_t)chosen[i];
+#pragma unroll
+                for (int b = 0; b < kMaxBatch; ++b) {
+                    const uint32_t rk = (rank[i] >> (8 * b)) & 0xffu;
+                    r->slot_rank[slot][b] = (int8_t)(rk == 0xffu ? -1 : (int)rk);
+                }
             }
             base += __popcll(m);
         }
         if (lane == 0) r->nslots = base;
-    }
-    __syncthreads();
-    // ranks of each slot's expert within each token's selection
-    for (int s = tid_(); s < r->nslots; s += NT) {
-        for (int b = 0; b < kMaxBatch; ++b) {
-            int rank = -1;
-            if (b < p.B)
-                for (int j = 0; j < p.K; ++j)
-                    if (r->ids[b][j] == r->slot_e[s]) rank = j;
-            r->slot_rank[s][b] = (int8_t)rank;
-        }
     }
     __syncthreads();
 }

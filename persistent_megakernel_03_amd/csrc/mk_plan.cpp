@@ -49,7 +49,7 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
     *rows_down = cfg.rows_down;
     // A down tile keeps all its weight rows (S experts x rows) in registers,
     // at most 16 row-vectors per wave.
-    const int rd = std::min(64, 64 / std::max(1, S));
+    const int rd = std::min(64, 64 / std::max(1, S)) & ~1;   // even: the down tile takes rows in pairs
     if (rd < cfg.rows_down) return;
     const int n_down = ceil_div(s.H, rd);
     const int per_slot = (n_wg - n_down) / std::max(1, S);

@@ -612,8 +612,8 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
         load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
     }
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
-    compute_routing(p, rlogits_at(p, l), rt, cx.marks);
-    mark(cx, 2);
+    compute_routing(p, rlogits_at(p, l), rt);
+    mark(cx, 0);
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
             const int b = i / p.K, j = i - b * p.K;
@@ -634,7 +634,7 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     gemv_rows<NCH, PF, NB>(
         h, 2 * npair, H >> 3,
         [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
-        [&]() { mark(cx, 3); },
+        [&]() { mark(cx, 1); },
         [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if ((i & 1) == 0) {
@@ -652,6 +652,7 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
                 }
             }
         });
+    mark(cx, 2);
     block_signal(p, t.signal);
     return true;
 }
@@ -661,10 +662,16 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
 // Rows a0..a1 of the hidden dimension, for every selected expert: y = W_down a,
 // then x_out = x_mid + sum_j w_j y_j in top-k rank order. The routing (and so
 // the expert rows) is known once the router logits are (pre counter): the
-// tile computes it and starts every row of its weights streaming into
-// registers while the gate/up tiles are still running, then waits for them
-// (main counter) and reads their activations once, into LDS.
-template <int NCH, int PF, int NB>
+// tile computes it and starts its weights streaming into registers while the
+// gate/up tiles are still running, then waits for them (main counter) and
+// reads their activations once, into LDS.
+//
+// Rows are taken in pairs: two consecutive rows of an expert are contiguous,
+// so a pair of I-wide rows is 2I/8 16-byte chunks that NCHP full-wave loads
+// cover (I = 768: three loads, where one row alone would need one full and
+// one half-empty load). Lane l's chunk c is chunk f = 64c + l of the pair:
+// row f / (I/8), column f % (I/8).
+template <int NCHP, int PF, int NB>
 __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0;
@@ -674,67 +681,106 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     compute_routing(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     const int I = p.I, K = p.K, B = p.B;
+    const int K8 = I >> 3;
     const int nslots = rt->nslots;
     // residual slice: ready since the output projection
     const float* xmid = x_at(p, 2 * l + 1);
-    const float xres = tid < B * nrows ? xmid[(int64_t)(tid / nrows) * p.H + h0 + tid % nrows] : 0.f;
-    // wave w takes slots w, w+4, ...; row-vector i -> slot index i / nrows, row i % nrows
+    const float xres = tid < B * nrows ? ldg(xmid + (int64_t)(tid / nrows) * p.H + h0 + tid % nrows) : 0.f;
+    // wave w takes slots w, w+4, ...; pair-vector q -> slot index q / npps, rows 2(q % npps) + {0, 1}
+    const int npps = nrows >> 1;
     const int myslots = nslots > wave ? (nslots - wave + NWAVES - 1) / NWAVES : 0;
+    const int nmine = myslots * npps;
     const uint16_t* Wd = wptr(p, l, W_DOWN);
     float* sAct = reinterpret_cast<float*>(cx.lds);   // [B][K][I] gate/up outputs
     float* sY = reinterpret_cast<float*>(cx.lds + cx.general) - kMaxBatch * kMaxTopK * kMaxDownRows;  // [B*K][nrows]
-    const int K8 = I >> 3;
     const float* act = act_at(p, l);
-    bool ok = true;
-    float h[NB][NCH][8];
-    gemv_rows<NCH, PF, NB>(
-        h, myslots * nrows, K8,
-        [&](int i) {
-            const int s = wave + (i / nrows) * NWAVES;
-            return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + (i % nrows)) * I;
-        },
-        [&]() {
-            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            const int n4 = (B * K * I) >> 2;
-            for (int i = tid; i < n4; i += NT)
-                reinterpret_cast<float4*>(sAct)[i] = ldf4(act + 4 * i);
-            __syncthreads();
-            mark(cx, 1);
-        },
-        [&](int i, float(&hh)[NB][NCH][8]) {
-            if (i % nrows != 0) return;
-            const int s = wave + (i / nrows) * NWAVES;
+    auto pairptr = [&](int q) {
+        const int s = wave + (q / npps) * NWAVES;
+        return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + 2 * (q % npps)) * I;
+    };
+    // every wave runs the same barriers; waves without slots only help copy
+    uint4 buf[PF][NCHP];
+    const int last = nmine > 0 ? nmine - 1 : 0;
+    if (nmine > 0) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
+        for (int s = 0; s < PF; ++s) load_row<NCHP>(buf[s], pairptr(s < last ? s : last), 2 * K8);
+    }
+    bool ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+    if (ok) {
+        // all loads of a batch in flight before the LDS writes
+        const int n4 = (B * K * I) >> 2;
+        for (int i0 = 0; i0 < n4; i0 += 6 * NT) {
+            float4 v[6];
 #pragma unroll
-                for (int c = 0; c < NCH; ++c) {
-                    const int ch = lane + 64 * c;
-                    if (rank >= 0 && ch < K8) {
-                        const float4* a = reinterpret_cast<const float4*>(sAct + (b * K + rank) * I + ch * 8);
-                        const float4 u = a[0], v = a[1];
-                        hh[b][c][0] = u.x; hh[b][c][1] = u.y; hh[b][c][2] = u.z; hh[b][c][3] = u.w;
-                        hh[b][c][4] = v.x; hh[b][c][5] = v.y; hh[b][c][6] = v.z; hh[b][c][7] = v.w;
-                    } else {
+            for (int k = 0; k < 6; ++k) {
+                const int i = i0 + k * NT + tid;
+                v[k] = ldf4(act + 4 * (i < n4 ? i : 0));
+            }
 #pragma unroll
-                        for (int jj = 0; jj < 8; ++jj) hh[b][c][jj] = 0.f;
+            for (int k = 0; k < 6; ++k) {
+                const int i = i0 + k * NT + tid;
+                if (i < n4) reinterpret_cast<float4*>(sAct)[i] = v[k];
+            }
+        }
+    }
+    __syncthreads();
+    mark(cx, 1);
+    if (ok && nmine > 0) {
+        float hp[NB][NCHP][8];
+        for (int q0 = 0; q0 < nmine; q0 += PF) {
+#pragma unroll
+            for (int s = 0; s < PF; ++s) {
+                const int q = q0 + s;
+                const int sl = wave + (q / npps) * NWAVES;
+                if (q < nmine && q % npps == 0) {
+                    // this slot's activations at the columns of this lane's chunks
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const int rank = (b < B) ? rt->slot_rank[sl][b] : -1;
+#pragma unroll
+                        for (int c = 0; c < NCHP; ++c) {
+                            const int f = lane + 64 * c;
+                            const int col = f < K8 ? f : f - K8;
+                            if (rank >= 0 && f < 2 * K8) {
+                                const float* a = sAct + (b * K + rank) * I + col * 8;
+                                const float4 u = *reinterpret_cast<const float4*>(a);
+                                const float4 v = *reinterpret_cast<const float4*>(a + 4);
+                                hp[b][c][0] = u.x; hp[b][c][1] = u.y; hp[b][c][2] = u.z; hp[b][c][3] = u.w;
+                                hp[b][c][4] = v.x; hp[b][c][5] = v.y; hp[b][c][6] = v.z; hp[b][c][7] = v.w;
+                            } else {
+#pragma unroll
+                                for (int jj = 0; jj < 8; ++jj) hp[b][c][jj] = 0.f;
+                            }
+                        }
+                    }
+                }
+                float y0[NB], y1[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                    for (int c = 0; c < NCHP; ++c) {
+                        const float d = dot8(buf[s][c], hp[b][c], 0.f);
+                        if (lane + 64 * c < K8) a0 += d;
+                        else a1 += d;
+                    }
+                    y0[b] = wave_sum(a0);
+                    y1[b] = wave_sum(a1);
+                }
+                const int nx = q + PF;
+                if (q0 + PF < nmine) load_row<NCHP>(buf[s], pairptr(nx < last ? nx : last), 2 * K8);
+                if (q < nmine && lane < 2) {
+                    const int r = 2 * (q % npps) + lane;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const int rank = (b < B) ? rt->slot_rank[sl][b] : -1;
+                        if (rank >= 0) sY[(b * K + rank) * nrows + r] = lane == 0 ? y0[b] : y1[b];
                     }
                 }
             }
-        },
-        [&](int i, const float(&acc)[NB]) {
-            if (lane == 0) {
-                const int s = wave + (i / nrows) * NWAVES;
-                const int r = i % nrows;
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int rank = (b < B) ? rt->slot_rank[s][b] : -1;
-                    if (rank >= 0) sY[(b * K + rank) * nrows + r] = acc[b];
-                }
-            }
-        });
-    if (!ok) return false;
-    __syncthreads();
+        }
+    }
+    if (!__syncthreads_and(ok)) return false;
     mark(cx, 2);
     float* xout = x_at(p, 2 * l + 2);
     if (tid < B * nrows) {
@@ -788,9 +834,9 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
 // supported model gets its own kernels, so each tile is compiled only for
 // the reduction lengths it actually sees and register allocation is sized
 // per tile, not for every possible shape.
-template <int NCH_H_, int NCH_O_, int NCH_I_, int D_>
+template <int NCH_H_, int NCH_O_, int NCH_I_, int D_, int NCHP_I_>
 struct Shape {
-    static constexpr int NCH_H = NCH_H_, NCH_O = NCH_O_, NCH_I = NCH_I_, D = D_;
+    static constexpr int NCH_H = NCH_H_, NCH_O = NCH_O_, NCH_I = NCH_I_, D = D_, NCHP_I = NCHP_I_;
 };
 
 // Rows in flight per wave for a given chunk count and batch.
@@ -809,7 +855,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
         case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 8 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
-        case OP_DOWN: return tile_down<S::NCH_I, (NB == 1 && S::NCH_I <= 2 ? 16 : Pf<S::NCH_I, NB>::v), NB>(t, cx);
+        case OP_DOWN: return tile_down<S::NCHP_I, (NB == 1 ? 8 : 4), NB>(t, cx);
         case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         default: return false;
     }
