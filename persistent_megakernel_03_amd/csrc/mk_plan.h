@@ -26,7 +26,7 @@ struct ModelShape {
 };
 
 struct TileConfig {
-    int rows_qkv = 16;
+    int rows_qkv = 24;
     int rows_o = 8;
     int rows_router = 8;
     int rows_gateup = 16;

@@ -849,7 +849,7 @@ template <class S, int NB>
 __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
     switch (t.op) {
         case OP_EMBED: return tile_embed(t, cx);
-        case OP_QKV: return tile_qkv<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+        case OP_QKV: return tile_qkv<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 6 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
         case OP_ATTN: return tile_attn<S::D>(t, cx);
         case OP_COMBINE: return tile_combine<S::D>(t, cx);
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);

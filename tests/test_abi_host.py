@@ -111,7 +111,7 @@ def test_plan_counts_for_the_30b_shape():
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192])
     ops = np.bincount(tasks[:, 0], minlength=9)
     assert ops[OP_EMBED] == 1
-    assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
+    assert ops[OP_QKV] == 48 * 4 * 54          # 1280 rows per KV group, 24 per tile
     assert ops[OP_ATTN] == 48 * 4 * 65         # 8193 tokens in 128-token chunks
     assert ops[OP_COMBINE] == 48 * 32          # one merge per query head
     assert ops[OP_OPROJ] == 48 * 256
