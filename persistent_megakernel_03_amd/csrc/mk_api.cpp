@@ -248,8 +248,8 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         // routing results, per-tile scalars.
         const int G = d.n_q_heads / d.n_kv_heads;
         const int max_chunks = max_chunks_for(d);
-        const size_t attn = (size_t)2 * 16 * (128 + 4) * 4 + (size_t)3 * (d.head_dim / 32) * 64 * 16 +
-                            (size_t)16 * d.head_dim * 4 + (size_t)d.head_dim * 4;
+        // attention: the new token's k and v (bf16), per-wave (m, l) and o^T
+        const size_t attn = (size_t)4 * d.head_dim + (size_t)2 * 4 * 16 * 4 + (size_t)4 * 16 * (d.head_dim + 1) * 4;
         const size_t comb = (size_t)(16 + max_chunks + 4 + 1024) * 4;
         // down tile: its gate/up activations [B][k][I] fp32 at the start of
         // the general region, its output staging at the end

@@ -132,6 +132,11 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
     const u32x4_t v = *(const MK_GLOBAL u32x4_t*)p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 ld8(const void* p) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = *(const MK_GLOBAL u32x2_t*)p;
+    return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ float4 ldf4(const float* p) {
     const f32x4v_t v = *(const MK_GLOBAL f32x4v_t*)p;
     return make_float4(v.x, v.y, v.z, v.w);
@@ -154,6 +159,16 @@ __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uin
     mid = u1 >> 16;
     const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
     lo = __float_as_uint(r2) >> 16;
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16x16) * B(16x16), BF16 operands, fp32 accumulate.
+// Lane l holds A[l%16][4(l/16) .. +3], B[4(l/16) .. +3][l%16] and
+// D[4(l/16) .. +3][l%16].
+__device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                     0, 0, 0);
 }
 
 // D(16x16) += A(16x32) * B(32x16), BF16 operands, fp32 accumulate.

@@ -144,21 +144,25 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
 // -------------------------------------------------------------- attention
 
 // One chunk of split-KV paged attention for sequence b, KV head g, chunk c:
-// tokens [c*chunk, min((c+1)*chunk, pos+1)). The G query heads sharing the KV
-// head form the M dimension of BF16 MFMA tiles (fp32 operands split into
-// three BF16 parts). Old cache pages are loaded before the wait; the chunk
-// holding the new token also applies RoPE to k, rounds k and v to BF16 and
-// writes them into the pool. Writes (m, l, o) partials; the last chunk of
-// (b, g) to finish merges all partials by log-sum-exp.
+// tokens [c*chunk, min((c+1)*chunk, pos+1)). Each wave owns 16-token blocks
+// of the chunk (one cache page each) and runs a complete online softmax over
+// them on the matrix cores: scores transposed, S^T = K Q^T (BF16 MFMA
+// 16x16x32, the G query heads of the KV head as the N dimension), then
+// O^T += V^T P^T (MFMA 16x16x16), where the probabilities P^T already sit in
+// the B-operand layout the score tile was produced in, so nothing is
+// exchanged between waves until the four per-wave (m, l, o) are merged in
+// LDS at the end. fp32 operands (queries, probabilities) are split into three
+// BF16 parts. Cache pages are loaded before the wait; the chunk holding the
+// new token also applies RoPE to k, rounds k and v to BF16 and writes them
+// into the pool. Writes the chunk's (m, l, o) partials.
 template <int D>
 __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     constexpr int NDB = D / 32;                // QK d-blocks (32 wide)
+    constexpr int NDV = D / 16;                // PV d-blocks (16 wide)
     constexpr int NTBW = kSC / 16 / NWAVES;    // 16-token blocks per wave per pass
-    constexpr int NDV = D / 16 / NWAVES;       // PV d-blocks (16 wide) per wave
-    constexpr int NKB = kSC / 32;              // PV k-blocks (32 tokens) per pass
-    const int l = t.layer, b = t.a0, g = t.a1, c = t.a2, nch = t.a3;
-    const int lane = tid_() & 63, wave = tid_() >> 6;
+    const int l = t.layer, b = t.a0, g = t.a1, c = t.a2;
+    const int tid = tid_(), lane = tid & 63, wave = tid >> 6;
     const int quad = lane >> 4, col = lane & 15;
     const int G = p.G;
     const int pos = p.positions[b];
@@ -170,46 +174,37 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     const int64_t hstride = (int64_t)16 * D;
     const int64_t layer_pages = (int64_t)l * p.n_pages;
 
-    float* sS = reinterpret_cast<float*>(cx.lds);      // [16][kSPad] scores
-    float* sP = sS + 16 * kSPad;                         // [16][kSPad] probabilities
-    uint4* sQ = reinterpret_cast<uint4*>(sP + 16 * kSPad); // [3][NDB][64] query A-fragments
-    float* sQf = reinterpret_cast<float*>(sQ + 3 * NDB * 64); // [G][D] queries before RoPE
-    float* sRope = sQf + 16 * D;                               // [D/2][2] cos, sin
-    int* misc = misc_lds(cx.lds, cx.general);
-    float* sM = reinterpret_cast<float*>(misc);          // [16]
-    float* sL = sM + 16;                                 // [16]
-    float* sA = sL + 16;                                 // [16] rescale factors
-    uint16_t* sKn = reinterpret_cast<uint16_t*>(sA + 16); // [D] new key (bf16)
-    uint16_t* sVn = sKn + D;                              // [D] new value (bf16)
+    // LDS: new token (bf16), then the per-wave results for the merge
+    uint16_t* sKn = reinterpret_cast<uint16_t*>(cx.lds);        // [D]
+    uint16_t* sVn = sKn + D;                                      // [D]
+    float* sM = reinterpret_cast<float*>(cx.lds + 4 * D);         // [NWAVES][16]
+    float* sL = sM + NWAVES * 16;                                 // [NWAVES][16]
+    float* sO = sL + NWAVES * 16;                                 // [NWAVES][16][D + 1]
 
-    uint4 kf[NTBW][NDB];
-    uint4 vf[NDV][NKB];
+    uint4 kf[NTBW][NDB];   // A operand of S^T: token col of the block, dims 32db + 8quad..+7
+    uint2 vf[NTBW][NDV];   // A operand of O^T: dim 16dv + col, tokens 4quad..+3 of the block
     auto load_kv = [&](int st0) {
 #pragma unroll
         for (int i = 0; i < NTBW; ++i) {
-            const int tok = st0 + (wave + NWAVES * i) * 16 + col;
-            if (tok < t_old) {
-                const uint16_t* base = p.k_pool + ((layer_pages + bt[tok >> 4]) * p.Hkv + g) * hstride +
-                                       (tok & 15) * D + quad * 8;
+            const int blk = st0 + (wave + NWAVES * i) * 16;     // first token of the block
+            const int64_t page = (layer_pages + bt[min(blk, t_old > 0 ? t_old - 1 : 0) >> 4]) * p.Hkv + g;
+            const int tk = blk + col;
+            if (tk < t_old) {
+                const uint16_t* kb = p.k_pool + page * hstride + (tk & 15) * D + quad * 8;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) kf[i][db] = ld16(base + db * 32);
+                for (int db = 0; db < NDB; ++db) kf[i][db] = ld16(kb + db * 32);
             } else {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) kf[i][db] = make_uint4(0u, 0u, 0u, 0u);
             }
-        }
+            const int tv = blk + 4 * quad;
+            if (tv < t_old) {
+                const uint16_t* vb = p.v_pool + page * hstride + (tv & 15);
 #pragma unroll
-        for (int j = 0; j < NDV; ++j) {
-            const int d = (wave + NWAVES * j) * 16 + col;
+                for (int dv = 0; dv < NDV; ++dv) vf[i][dv] = ld8(vb + (int64_t)(dv * 16 + col) * 16);
+            } else {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const int tv = st0 + kb * 32 + quad * 8;
-                if (tv < t_old) {
-                    vf[j][kb] = ld16(p.v_pool + ((layer_pages + bt[tv >> 4]) * p.Hkv + g) * hstride +
-                                     (int64_t)d * 16 + (tv & 15));
-                } else {
-                    vf[j][kb] = make_uint4(0u, 0u, 0u, 0u);
-                }
+                for (int dv = 0; dv < NDV; ++dv) vf[i][dv] = make_uint2(0u, 0u);
             }
         }
     };
@@ -217,51 +212,64 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     auto fix_kv = [&](int st0) {
 #pragma unroll
         for (int i = 0; i < NTBW; ++i) {
-            const int tok = st0 + (wave + NWAVES * i) * 16 + col;
-            if (has_new && tok == pos) {
+            const int blk = st0 + (wave + NWAVES * i) * 16;
+            if (has_new && blk + col == pos) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     kf[i][db] = *reinterpret_cast<const uint4*>(sKn + db * 32 + quad * 8);
             }
-        }
+            const int tv = blk + 4 * quad;
 #pragma unroll
-        for (int j = 0; j < NDV; ++j) {
-            const int d = (wave + NWAVES * j) * 16 + col;
-            const uint32_t nv = has_new ? (uint32_t)sVn[d] : 0u;
+            for (int dv = 0; dv < NDV; ++dv) {
+                uint32_t w[2] = {vf[i][dv].x, vf[i][dv].y};
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const int tv = st0 + kb * 32 + quad * 8;
-                uint32_t w[4] = {vf[j][kb].x, vf[j][kb].y, vf[j][kb].z, vf[j][kb].w};
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
+                for (int jj = 0; jj < 4; ++jj) {
                     const int tok = tv + jj;
                     if (tok >= t_old) {
-                        const uint32_t val = (has_new && tok == pos) ? nv : 0u;
+                        const uint32_t val = (has_new && tok == pos) ? (uint32_t)sVn[dv * 16 + col] : 0u;
                         if (jj & 1) w[jj >> 1] = (w[jj >> 1] & 0x0000ffffu) | (val << 16);
                         else w[jj >> 1] = (w[jj >> 1] & 0xffff0000u) | val;
                     }
                 }
-                vf[j][kb] = make_uint4(w[0], w[1], w[2], w[3]);
+                vf[i][dv] = make_uint2(w[0], w[1]);
             }
         }
     };
 
     load_kv(t0);
-    // the rotary table is a host input: load it before the wait
-    const int tid = tid_();
-    const float rope_v = tid < D ? p.rope[(int64_t)b * D + tid] : 0.f;
+    // queries: lane (quad, col) holds head col's dims 32db + 8quad..+7 (zero
+    // for col >= G); the rotary factors of those dims are a host input, so
+    // both are fetched before the wait where possible
+    float rc[NDB / 2][8], rs[NDB / 2][8];
+#pragma unroll
+    for (int db = 0; db < NDB / 2; ++db) {
+        const float* rp = p.rope + (int64_t)b * D + 2 * (db * 32 + quad * 8);
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const float4 v = ldf4(rp + 4 * k4);
+            rc[db][2 * k4] = v.x; rs[db][2 * k4] = v.y; rc[db][2 * k4 + 1] = v.z; rs[db][2 * k4 + 1] = v.w;
+        }
+    }
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
 
     const float* qkv = qkv_at(p, l) + (int64_t)b * p.QKVD;
-    // queries of the group's heads (G x D floats) and the rotary table into LDS
-    for (int i = tid * 4; i < G * D; i += NT * 4)
-        *reinterpret_cast<float4*>(sQf + i) = ldf4(qkv + (int64_t)g * G * D + i);
-    if (tid < D) sRope[tid] = rope_v;
-    __syncthreads();
+    float q[NDB][8];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        if (col < G) {
+            const float* qp = qkv + (int64_t)(g * G + col) * D + db * 32 + quad * 8;
+            const float4 u = ldf4(qp), w = ldf4(qp + 4);
+            q[db][0] = u.x; q[db][1] = u.y; q[db][2] = u.z; q[db][3] = u.w;
+            q[db][4] = w.x; q[db][5] = w.y; q[db][6] = w.z; q[db][7] = w.w;
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) q[db][jj] = 0.f;
+        }
+    }
     // New token: RoPE on k, BF16 rounding of k and v, append to the pool.
     if (has_new) {
         for (int i = tid; i < D / 2; i += NT) {
-            const float cs = sRope[2 * i], sn = sRope[2 * i + 1];
+            const float cs = ldg(p.rope + (int64_t)b * D + 2 * i), sn = ldg(p.rope + (int64_t)b * D + 2 * i + 1);
             const float a = ld_dev(qkv + p.Hq * D + g * D + i), bb = ld_dev(qkv + p.Hq * D + g * D + i + D / 2);
             sKn[i] = (uint16_t)f2bf(a * cs - bb * sn);
             sKn[i + D / 2] = (uint16_t)f2bf(a * sn + bb * cs);
@@ -277,161 +285,141 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
             vd[(int64_t)i * 16] = sVn[i];
         }
     }
-
-    // Query fragments (rows 0..G-1 of the MFMA A operand): RoPE, then the
-    // 3-way BF16 split; wave 0 builds them, every wave reads them.
-    if (wave == 0) {
-        float q[NDB][8];
+    // RoPE on the queries (pairs d, d + D/2 sit in blocks db, db + NDB/2 of
+    // this lane), then the three-way BF16 split: B operand of S^T
+    uint4 qf[3][NDB];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            if (col < G) {
-                const float4 u = *reinterpret_cast<const float4*>(sQf + col * D + db * 32 + quad * 8);
-                const float4 w = *reinterpret_cast<const float4*>(sQf + col * D + db * 32 + quad * 8 + 4);
-                q[db][0] = u.x; q[db][1] = u.y; q[db][2] = u.z; q[db][3] = u.w;
-                q[db][4] = w.x; q[db][5] = w.y; q[db][6] = w.z; q[db][7] = w.w;
-            } else {
+    for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) q[db][jj] = 0.f;
-            }
+        for (int jj = 0; jj < 8; ++jj) {
+            const float cs = rc[db][jj], sn = rs[db][jj];
+            const float a = q[db][jj], bb = q[db + NDB / 2][jj];
+            q[db][jj] = a * cs - bb * sn;
+            q[db + NDB / 2][jj] = a * sn + bb * cs;
         }
 #pragma unroll
-        for (int db = 0; db < NDB / 2; ++db)
+    for (int db = 0; db < NDB; ++db) {
+        uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int i = db * 32 + quad * 8 + jj;
-                const float cs = sRope[2 * i], sn = sRope[2 * i + 1];
-                const float a = q[db][jj], bb = q[db + NDB / 2][jj];
-                q[db][jj] = a * cs - bb * sn;
-                q[db + NDB / 2][jj] = a * sn + bb * cs;
-            }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            uint32_t hw[4], mw[4], lw[4];
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
-                uint32_t h0, m0, l0, h1, m1, l1;
-                split3(q[db][2 * k2], h0, m0, l0);
-                split3(q[db][2 * k2 + 1], h1, m1, l1);
-                hw[k2] = h0 | (h1 << 16);
-                mw[k2] = m0 | (m1 << 16);
-                lw[k2] = l0 | (l1 << 16);
-            }
-            sQ[(0 * NDB + db) * 64 + lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            sQ[(1 * NDB + db) * 64 + lane] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-            sQ[(2 * NDB + db) * 64 + lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        for (int k2 = 0; k2 < 4; ++k2) {
+            uint32_t h0, m0, l0, h1, m1, l1;
+            split3(q[db][2 * k2], h0, m0, l0);
+            split3(q[db][2 * k2 + 1], h1, m1, l1);
+            hw[k2] = h0 | (h1 << 16);
+            mw[k2] = m0 | (m1 << 16);
+            lw[k2] = l0 | (l1 << 16);
         }
+        qf[0][db] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        qf[1][db] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+        qf[2][db] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
-    if (tid_() < 16) {
-        sM[tid_()] = -INFINITY;
-        sL[tid_()] = 0.f;
-    }
-    // rows G..15 of the probability tile stay zero
-    for (int i = tid_(); i < (16 - G) * kSPad; i += NT) sP[G * kSPad + i] = 0.f;
-    __syncthreads();
     mark(cx, 0);
 
+    // per-wave online softmax state for head col (the same in the four lane groups)
+    float m_run = -INFINITY, l_run = 0.f;
     f32x4_t oacc[NDV];
 #pragma unroll
-    for (int j = 0; j < NDV; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dv = 0; dv < NDV; ++dv) oacc[dv] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float scale = p.attn_scale;
 
     for (int st0 = t0; st0 < t1; st0 += kSC) {
         if (st0 != t0) load_kv(st0);
         fix_kv(st0);
-        // scores S[h][t] = q_h . k_t * scale
+        // S^T[token][head] for this wave's blocks: lane (quad, col) holds
+        // tokens 4quad..+3 of each block for head col
+        float sc[NTBW][4];
+        float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NTBW; ++i) {
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                s = mfma16x16x32(sQ[(0 * NDB + db) * 64 + lane], kf[i][db], s);
-                s = mfma16x16x32(sQ[(1 * NDB + db) * 64 + lane], kf[i][db], s);
-                s = mfma16x16x32(sQ[(2 * NDB + db) * 64 + lane], kf[i][db], s);
+                s4 = mfma16x16x32(kf[i][db], qf[0][db], s4);
+                s4 = mfma16x16x32(kf[i][db], qf[1][db], s4);
+                s4 = mfma16x16x32(kf[i][db], qf[2][db], s4);
             }
-            const int tl = (wave + NWAVES * i) * 16 + col;
-            const bool valid = st0 + tl < t1;
+            const int blk = st0 + (wave + NWAVES * i) * 16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int h = quad * 4 + r;
-                if (h < G) sS[h * kSPad + tl] = valid ? s[r] * scale : -INFINITY;
+                sc[i][r] = (blk + 4 * quad + r < t1) ? s4[r] * scale : -INFINITY;
+                mx = fmaxf(mx, sc[i][r]);
             }
         }
-        __syncthreads();
-        // online softmax over this pass
-        for (int h = wave; h < G; h += NWAVES) {
-            const float s0 = sS[h * kSPad + lane], s1 = sS[h * kSPad + lane + 64];
-            const float mx = wave_max(fmaxf(s0, s1));
-            const float m_old = sM[h];
-            const float m_new = fmaxf(m_old, mx);
-            const float alpha = expf(m_old - m_new);
-            const float e0 = expf(s0 - m_new), e1 = expf(s1 - m_new);
-            const float sum = wave_sum(e0 + e1);
-            sP[h * kSPad + lane] = e0;
-            sP[h * kSPad + lane + 64] = e1;
-            if (lane == 0) {
-                sM[h] = m_new;
-                sL[h] = sL[h] * alpha + sum;
-                sA[h] = alpha;
-            }
-        }
-        __syncthreads();
-        mark(cx, 1);
-        // o += P V
+        // maximum over the wave's tokens: across the four lane groups
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
+        float ps = 0.f;
 #pragma unroll
-        for (int j = 0; j < NDV; ++j) {
+        for (int i = 0; i < NTBW; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int h = quad * 4 + r;
-                oacc[j][r] *= (h < G) ? sA[h] : 0.f;
+                sc[i][r] = m_new == -INFINITY ? 0.f : expf(sc[i][r] - m_new);
+                ps += sc[i][r];
+            }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+#pragma unroll
+        for (int dv = 0; dv < NDV; ++dv)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[dv][r] *= alpha;
+        // O^T[d][head] += V^T[d][token] P^T[token][head]; P^T is this lane's
+        // four probabilities, split in three BF16 parts
+#pragma unroll
+        for (int i = 0; i < NTBW; ++i) {
+            uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+            split3(sc[i][0], h0, m0, l0);
+            split3(sc[i][1], h1, m1, l1);
+            split3(sc[i][2], h2, m2, l2);
+            split3(sc[i][3], h3, m3, l3);
+            const uint2 ph = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            const uint2 pm = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
+            const uint2 pl = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+#pragma unroll
+            for (int dv = 0; dv < NDV; ++dv) {
+                oacc[dv] = mfma16x16x16(vf[i][dv], ph, oacc[dv]);
+                oacc[dv] = mfma16x16x16(vf[i][dv], pm, oacc[dv]);
+                oacc[dv] = mfma16x16x16(vf[i][dv], pl, oacc[dv]);
             }
         }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            uint4 pa[3];
-            {
-                const float* pr = sP + col * kSPad + kb * 32 + quad * 8;
-                uint32_t hw[4], mw[4], lw[4];
-#pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) {
-                    uint32_t h0, m0, l0, h1, m1, l1;
-                    split3(pr[2 * k2], h0, m0, l0);
-                    split3(pr[2 * k2 + 1], h1, m1, l1);
-                    hw[k2] = h0 | (h1 << 16);
-                    mw[k2] = m0 | (m1 << 16);
-                    lw[k2] = l0 | (l1 << 16);
-                }
-                pa[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                pa[1] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-                pa[2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-            }
-#pragma unroll
-            for (int j = 0; j < NDV; ++j) {
-                oacc[j] = mfma16x16x32(pa[0], vf[j][kb], oacc[j]);
-                oacc[j] = mfma16x16x32(pa[1], vf[j][kb], oacc[j]);
-                oacc[j] = mfma16x16x32(pa[2], vf[j][kb], oacc[j]);
-            }
-        }
-        __syncthreads();
     }
+    mark(cx, 1);
 
+    // merge the four waves: lane (quad, col) holds O^T[16dv + 4quad + r][col]
+#pragma unroll
+    for (int dv = 0; dv < NDV; ++dv)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sO[(wave * 16 + col) * (D + 1) + dv * 16 + 4 * quad + r] = oacc[dv][r];
+    if (quad == 0) {
+        sM[wave * 16 + col] = m_run;
+        sL[wave * 16 + col] = l_run;
+    }
+    __syncthreads();
     mark(cx, 2);
-    // partials: o (unnormalised) and (m, l) per head for this chunk
     float* part = part_at(p, l) + ((int64_t)b * p.Hq + g * G) * p.max_chunks * D;
     float* ml = ml_at(p, l) + ((int64_t)b * p.Hq + g * G) * ml_row(p);
+    for (int i = tid; i < G * D; i += NT) {
+        const int h = i / D, d = i - h * D;
+        float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NDV; ++j) {
-        const int d = (wave + NWAVES * j) * 16 + col;
+        for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, sM[w * 16 + h]);
+        float o = 0.f, L = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = quad * 4 + r;
-            if (h < G) st_dev(part + ((int64_t)h * p.max_chunks + c) * D + d, oacc[j][r]);
+        for (int w = 0; w < NWAVES; ++w) {
+            const float mw = sM[w * 16 + h];
+            const float e = mw == -INFINITY ? 0.f : expf(mw - M);
+            o += e * sO[(w * 16 + h) * (D + 1) + d];
+            L += e * sL[w * 16 + h];
+        }
+        st_dev(part + ((int64_t)h * p.max_chunks + c) * D + d, o);
+        if (d == 0) {
+            st_dev(ml + (int64_t)h * ml_row(p) + 2 * c, M);
+            st_dev(ml + (int64_t)h * ml_row(p) + 2 * c + 1, L);
         }
     }
-    if (tid_() < G) {
-        st_dev(ml + (int64_t)tid_() * ml_row(p) + 2 * c, sM[tid_()]);
-        st_dev(ml + (int64_t)tid_() * ml_row(p) + 2 * c + 1, sL[tid_()]);
-    }
-    (void)nch;
     mark(cx, 3);
     block_signal(p, t.signal);
     return true;
