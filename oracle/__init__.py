@@ -4,14 +4,14 @@ TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
 execute anything in this package: only the tests, the smoke check and the
 benchmark's CPU-baseline leg use it. It shares no code with the HIP library.
 
-The pages on the decode megakernel describe it as a scheduling change, not a
-change of the arithmetic: a "serving-system change, not a new model" built
-from "ordinary tiled matrix multiplications and paged attention" with no
-accuracy loss ("Cohere Publishes One-Kernel Server for North Mini Code,
-Claims 1.58x vLLM Speedup", opening section and section "A hand-built
-approach to a specialized server"). So the oracle is the plain sequential
-definition of a decode step, one sequence at a time, in float32 over BF16
-weights (float64 on request), with rotary angles in float64.
+The pages on the decode megakernel present it as a change to how a serving
+system schedules work, not a new model: it is assembled from plain tiled
+matrix products and paged attention and loses no accuracy ("Cohere Publishes
+One-Kernel Server for North Mini Code, Claims 1.58x vLLM Speedup", opening
+section and section "A hand-built approach to a specialized server"). So the
+oracle is the plain sequential definition of a decode step, one sequence at a
+time, in float32 over BF16 weights (float64 on request), with rotary angles
+in float64.
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by a test under tests/ (invariant, closed form, library
@@ -27,7 +27,11 @@ from .decode import (  # noqa: F401
     gather_pages,
     attention_decode,
     route_topk,
+    route_weights,
     swiglu_expert,
+    attention_block,
+    moe_block,
+    final_logits,
     moe_combine,
     DenseModel,
     PagedKV,

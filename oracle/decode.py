@@ -135,18 +135,23 @@ def attention_decode(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
     return out
 
 
+def route_weights(logits: np.ndarray, ids: Sequence[int], dtype=np.float32) -> np.ndarray:
+    """Routing weights of the selected experts ``ids`` (in that order): a
+    softmax over their logits, which equals the full softmax renormalised
+    over the selection."""
+    sel = np.asarray(logits, dtype=dtype)[np.asarray(ids, dtype=np.int64)]
+    e = np.exp(sel - np.max(sel))
+    return (e / np.sum(e, dtype=dtype)).astype(dtype)
+
+
 def route_topk(logits: np.ndarray, k: int, dtype=np.float32):
     """Top-k expert selection and routing weights.
 
     Selection order is (logit descending, expert index ascending), so ties go
-    to the lower index. The weights are a softmax over the k selected logits,
-    which equals the full softmax renormalised over the selection."""
+    to the lower index; the weights are route_weights of the selection."""
     r = np.asarray(logits, dtype=dtype)
     order = np.argsort(-r, kind="stable")[:k]
-    sel = r[order]
-    e = np.exp(sel - np.max(sel))
-    w = e / np.sum(e, dtype=dtype)
-    return order.astype(np.int32), w.astype(dtype)
+    return order.astype(np.int32), route_weights(r, order, dtype)
 
 
 def swiglu_expert(h: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
@@ -320,52 +325,82 @@ class SeqTrace:
     x_final: np.ndarray = None
 
 
+def attention_block(model: DenseModel, kv: PagedKV, l: int, x: np.ndarray, pos: int, block_table,
+                    cos: np.ndarray, sin: np.ndarray, dtype=np.float32) -> Tuple[np.ndarray, LayerTrace]:
+    """Layer l's attention block for one sequence: RMSNorm, QKV projection,
+    RoPE at position pos, append of the new K/V (BF16) to the paged cache,
+    attention over positions 0..pos, output projection plus residual.
+    Returns the residual after the block and a trace with the KV slot."""
+    d = model.dims
+    hq, hkv, D = d.n_q_heads, d.n_kv_heads, d.head_dim
+    qd, kvd = hq * D, hkv * D
+    lt = LayerTrace()
+    pre = f"layers.{l}."
+    h = rms_norm(x, model.tensor(pre + "attn_norm"), d.rms_eps, dtype)
+    qkv = model.tensor(pre + "wqkv") @ h
+    q = qkv[:qd].reshape(hq, D)
+    k = qkv[qd:qd + kvd].reshape(hkv, D)
+    v = qkv[qd + kvd:qd + 2 * kvd].reshape(hkv, D)
+    q = rope_rotate(q, cos, sin)
+    k = rope_rotate(k, cos, sin)
+    kv.append(l, block_table, pos, f32_to_bf16_rne(k.astype(np.float32)),
+              f32_to_bf16_rne(v.astype(np.float32)))
+    lt.kv_page, lt.kv_slot = int(block_table[pos // d.page_size]), pos % d.page_size
+    keys, vals = kv.read(l, block_table, pos + 1)
+    o = attention_decode(q, keys, vals, dtype)
+    x = x + model.tensor(pre + "wo") @ o.reshape(qd)
+    lt.x_attn = x.copy()
+    return x, lt
+
+
+def moe_block(model: DenseModel, l: int, x: np.ndarray, lt: LayerTrace, dtype=np.float32,
+              force_ids: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Layer l's mixture-of-experts block for one sequence: RMSNorm, router
+    (plus bias), top-k routing, SwiGLU experts combined in rank order, plus
+    residual. ``force_ids`` replaces the top-k selection by the given
+    experts (in that order; weights by route_weights), for comparisons that
+    adopt another implementation's routing. Fills lt and returns the new
+    residual."""
+    d = model.dims
+    pre = f"layers.{l}."
+    h2 = rms_norm(x, model.tensor(pre + "ffn_norm"), d.rms_eps, dtype)
+    r = model.tensor(pre + "router") @ h2
+    bias = model.router_bias(l)
+    if bias is not None:
+        r = r + bias
+    if force_ids is None:
+        ids, w = route_topk(r, d.top_k, dtype)
+    else:
+        ids = np.asarray(force_ids, dtype=np.int32)
+        w = route_weights(r, ids, dtype)
+    ys = []
+    for e in ids:
+        wg, wu, wd = model.expert(l, int(e))
+        ys.append(swiglu_expert(h2, wg, wu, wd, dtype))
+    x = x + moe_combine(ys, w, dtype)
+    lt.x_out = x.copy()
+    lt.h2, lt.router_logits, lt.ids, lt.weights = h2, r, ids, w
+    return x
+
+
+def final_logits(model: DenseModel, x: np.ndarray, dtype=np.float32) -> np.ndarray:
+    """Final RMSNorm and LM head."""
+    hf = rms_norm(x, model.tensor("final_norm"), model.dims.rms_eps, dtype)
+    return (model.tensor("lm_head") @ hf).astype(dtype)
+
+
 def _decode_one(model: DenseModel, kv: PagedKV, pos: int, block_table, token: int,
                 dtype) -> Tuple[np.ndarray, SeqTrace]:
     d = model.dims
-    H, hq, hkv, D = d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim
-    qd, kvd = hq * D, hkv * D
     tr = SeqTrace()
-
     x = model.rows("embed", token).astype(dtype)
-    cos, sin = rope_cos_sin(pos, D, d.rope_theta, dtype)
+    cos, sin = rope_cos_sin(pos, d.head_dim, d.rope_theta, dtype)
     for l in range(d.n_layers):
-        lt = LayerTrace()
-        pre = f"layers.{l}."
-        # attention block
-        h = rms_norm(x, model.tensor(pre + "attn_norm"), d.rms_eps, dtype)
-        qkv = model.tensor(pre + "wqkv") @ h
-        q = qkv[:qd].reshape(hq, D)
-        k = qkv[qd:qd + kvd].reshape(hkv, D)
-        v = qkv[qd + kvd:qd + 2 * kvd].reshape(hkv, D)
-        q = rope_rotate(q, cos, sin)
-        k = rope_rotate(k, cos, sin)
-        kv.append(l, block_table, pos, f32_to_bf16_rne(k.astype(np.float32)),
-                  f32_to_bf16_rne(v.astype(np.float32)))
-        lt.kv_page, lt.kv_slot = int(block_table[pos // d.page_size]), pos % d.page_size
-        keys, vals = kv.read(l, block_table, pos + 1)
-        o = attention_decode(q, keys, vals, dtype)
-        x = x + model.tensor(pre + "wo") @ o.reshape(qd)
-        lt.x_attn = x.copy()
-        # mixture-of-experts block
-        h2 = rms_norm(x, model.tensor(pre + "ffn_norm"), d.rms_eps, dtype)
-        r = model.tensor(pre + "router") @ h2
-        bias = model.router_bias(l)
-        if bias is not None:
-            r = r + bias
-        ids, w = route_topk(r, d.top_k, dtype)
-        ys = []
-        for e in ids:
-            wg, wu, wd = model.expert(l, int(e))
-            ys.append(swiglu_expert(h2, wg, wu, wd, dtype))
-        x = x + moe_combine(ys, w, dtype)
-        lt.x_out = x.copy()
-        lt.h2, lt.router_logits, lt.ids, lt.weights = h2, r, ids, w
+        x, lt = attention_block(model, kv, l, x, pos, block_table, cos, sin, dtype)
+        x = moe_block(model, l, x, lt, dtype)
         tr.layers.append(lt)
     tr.x_final = x.copy()
-    hf = rms_norm(x, model.tensor("final_norm"), d.rms_eps, dtype)
-    logits = model.tensor("lm_head") @ hf
-    return logits.astype(dtype), tr
+    return final_logits(model, x, dtype), tr
 
 
 def decode_step(model: DenseModel, kv: PagedKV, positions: Sequence[int],

@@ -13,7 +13,9 @@ import struct
 import numpy as np
 import pytest
 
-from oracle import DenseModel, PagedKV, bf16_to_f32, decode_sequence, decode_step
+from oracle import (DenseModel, PagedKV, attention_block, bf16_to_f32, decode_sequence, decode_step, final_logits,
+                    moe_block, rope_cos_sin, route_weights)
+from oracle.decode import LayerTrace
 from persistent_megakernel_03_amd import configs, sol, synth
 
 
@@ -238,6 +240,38 @@ def test_routing_weights_sum_to_one_and_ids_distinct(tiny):
         for lt in tr.layers:
             assert abs(float(np.sum(lt.weights, dtype=np.float64)) - 1.0) < 1e-6
             assert len(set(lt.ids.tolist())) == d["top_k"]
+
+
+def test_blocks_compose_to_the_step_and_forced_routing_reproduces_top_k(tiny):
+    """The per-block entry points (used to adopt another implementation's
+    routing) are the step: composing them with the oracle's own top-k ids
+    forced gives the step's logits bit for bit."""
+    d, tensors = tiny
+    P, T = d["page_size"], 40
+    bt = [3, 0, 2]
+    kp, vp = _np_pool(d, 4, seed=1)
+    model = DenseModel.from_dict(d, tensors)
+    want, tr, _ = decode_step(model, PagedKV(kp.copy(), vp.copy(), P), [T], [bt], [21])
+    kv = PagedKV(kp.copy(), vp.copy(), P)
+    cos, sin = rope_cos_sin(T, d["head_dim"], d["rope_theta"])
+    x = model.rows("embed", 21).astype(np.float32)
+    for l in range(d["n_layers"]):
+        x, lt = attention_block(model, kv, l, x, T, bt, cos, sin)
+        x = moe_block(model, l, x, lt, force_ids=tr[0].layers[l].ids)
+        assert np.array_equal(lt.weights, tr[0].layers[l].weights)
+    assert np.array_equal(final_logits(model, x), want[0])
+
+
+def test_route_weights_is_the_renormalised_full_softmax():
+    rng = np.random.default_rng(5)
+    r = rng.normal(size=32).astype(np.float32)
+    ids = [7, 3, 30, 12]
+    full = np.exp(r.astype(np.float64) - r.max()) / np.sum(np.exp(r.astype(np.float64) - r.max()))
+    want = full[ids] / full[ids].sum()
+    got = route_weights(r, ids)
+    assert np.allclose(got, want, rtol=1e-6, atol=0)
+    # the order of ids is the order of the weights
+    assert np.allclose(route_weights(r, ids[::-1]), want[::-1], rtol=1e-6, atol=0)
 
 
 # ----------------------------------------------------------------- bytes ----
