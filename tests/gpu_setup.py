@@ -15,11 +15,11 @@ class Setup:
     oracle's pool with each page stored dimension-major (the library's V
     layout); everything else is bit-identical."""
 
-    def __init__(self, cfg: dict, n_pages: int, seed: int = 0, device_gen: bool = False):
+    def __init__(self, cfg: dict, n_pages: int, seed: int = 0, device_gen: bool = False, weights=None):
         self.cfg = cfg
         self.n_pages = n_pages
         if device_gen:
-            self.w_dev = synth.make_model(cfg, seed, "cuda")
+            self.w_dev = weights if weights is not None else synth.make_model(cfg, seed, "cuda")
             k, v = synth.make_kv_pool(cfg, n_pages, seed + 1, "cuda")
         else:
             w_cpu = synth.make_model(cfg, seed, "cpu")
@@ -27,8 +27,8 @@ class Setup:
             k, v = synth.make_kv_pool(cfg, n_pages, seed + 1, "cpu")
             k, v = k.cuda(), v.cuda()
         self.k0 = k                                   # [L][N][Hkv][P][D]
-        self.v0_oracle_layout = v
         self.v0 = v.transpose(-1, -2).contiguous()    # [L][N][Hkv][D][P]
+        del v
 
     def fresh_pools(self):
         return self.k0.clone(), self.v0.clone()

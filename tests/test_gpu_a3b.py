@@ -23,7 +23,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_block, bf16_to_f32, final_logits, moe_block, rope_cos_sin, route_topk
+from oracle import PagedKV, attention_block, bf16_to_f32, final_logits, moe_block, rope_cos_sin, route_topk
 from oracle.decode import LayerTrace
 from persistent_megakernel_03_amd import configs, mk, synth
 from tests.gpu_setup import Setup, rel_l2, route_ids, x_layers
@@ -31,29 +31,38 @@ from tests.gpu_setup import Setup, rel_l2, route_ids, x_layers
 pytestmark = pytest.mark.gpu
 
 CFG = configs.A3B
-CTX = 8192
 P = CFG["page_size"]
-PAGES_PER_SEQ = CTX // P + 2
-N_PAGES = PAGES_PER_SEQ + 7
 SAMPLED = (0, 1, 23, 46, 47)
 
 
 @pytest.fixture(scope="module")
-def big():
-    print("a3b: generating weights and cache on the device", flush=True)
-    s = Setup(CFG, n_pages=N_PAGES, seed=0, device_gen=True)
-    bt = [int(x) for x in synth.make_block_tables(1, PAGES_PER_SEQ, N_PAGES, shuffle=True)[0]]
+def weights():
+    print("a3b: generating weights on the device", flush=True)
+    return synth.make_model(CFG, 0, "cuda")
+
+
+def _case(weights, ctx):
+    pages = ctx // P + 2
+    n_pages = pages + 7
+    print(f"a3b: cache for {ctx} tokens ({n_pages} pages)", flush=True)
+    s = Setup(CFG, n_pages=n_pages, seed=0, device_gen=True, weights=weights)
+    bt = [int(x) for x in synth.make_block_tables(1, pages, n_pages, shuffle=True)[0]]
     tok = int(synth.make_tokens(1, CFG["vocab"], seed=11)[0])
-    return s, bt, tok
+    return s, bt, tok, pages
 
 
-def _run(s, bt, tok, mode):
+@pytest.fixture(scope="module")
+def big(weights):
+    return _case(weights, 8192)
+
+
+def _run(s, bt, tok, mode, ctx=8192, pages=8192 // 16 + 2):
     k, v = s.fresh_pools()
-    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=1, max_pages_per_seq=PAGES_PER_SEQ, mode=mode)
+    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=1, max_pages_per_seq=pages, mode=mode)
     tokens = torch.tensor([tok], dtype=torch.int32, device="cuda")
     logits = torch.empty(1, CFG["vocab"], dtype=torch.float32, device="cuda")
-    print(f"a3b: one step, mode {mode}", flush=True)
-    dec.step([CTX], [bt], tokens, logits)
+    print(f"a3b: one step at {ctx} cached tokens, mode {mode}", flush=True)
+    dec.step([ctx], [bt], tokens, logits)
     assert dec.sync_check() == mk.MK_OK
     out = dict(logits=logits.cpu().numpy()[0], xs=x_layers(dec).cpu().numpy()[:, 0],
                ids=route_ids(dec).cpu().numpy()[:, 0], k=k, v=v)
@@ -67,36 +76,48 @@ def _margin(r, a, b):
     return abs(r[a] - r[b])
 
 
-def test_a3b_step_matches_oracle(big):
-    s, bt, tok = big
-    g = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL)
+def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True):
+    """end_to_end: the whole step with the device's routing adopted, then the
+    sampled layers teacher-forced. Otherwise (very long caches, to bound host
+    memory) layer 0 teacher-forced only."""
     L = CFG["n_layers"]
     model = s.oracle_model(lazy_experts=True)
     cos, sin = rope_cos_sin(CTX, CFG["head_dim"], CFG["rope_theta"])
+    page, slot = bt[CTX // P], CTX % P
 
-    # end to end, the device's routing adopted
-    kv = s.oracle_kv()
-    x = model.rows("embed", tok).astype(np.float32)
-    flips = 0
-    for l in range(L):
-        x, lt = attention_block(model, kv, l, x, CTX, bt, cos, sin)
-        assert rel_l2(x, g["xs"][2 * l + 1]) <= 1e-2, ("after attention", l, rel_l2(x, g["xs"][2 * l + 1]))
-        x = moe_block(model, l, x, lt, force_ids=g["ids"][l])
-        assert rel_l2(x, g["xs"][2 * l + 2]) <= 1e-2, ("after experts", l, rel_l2(x, g["xs"][2 * l + 2]))
-        own, _ = route_topk(lt.router_logits, CFG["top_k"])
-        if set(own.tolist()) != set(g["ids"][l].tolist()):
-            flips += 1
-            tol = 1e-2 * max(1.0, float(np.max(np.abs(lt.router_logits))))
-            kth = np.sort(np.asarray(lt.router_logits, np.float64))[::-1]
-            assert kth[CFG["top_k"] - 1] - kth[CFG["top_k"]] < tol, ("routing", l, own, g["ids"][l])
-    ol = final_logits(model, x)
-    err = float(np.max(np.abs(ol - g["logits"])))
-    print(f"a3b: logits max-abs {err:.3e}, selection flips vs the oracle's own top-k: {flips}", flush=True)
-    assert err <= 5e-2
+    if end_to_end:
+        kv = s.oracle_kv()
+        x = model.rows("embed", tok).astype(np.float32)
+        flips = 0
+        for l in range(L):
+            x, lt = attention_block(model, kv, l, x, CTX, bt, cos, sin)
+            assert rel_l2(x, g["xs"][2 * l + 1]) <= 1e-2, ("after attention", l, rel_l2(x, g["xs"][2 * l + 1]))
+            x = moe_block(model, l, x, lt, force_ids=g["ids"][l])
+            assert rel_l2(x, g["xs"][2 * l + 2]) <= 1e-2, ("after experts", l, rel_l2(x, g["xs"][2 * l + 2]))
+            own, _ = route_topk(lt.router_logits, CFG["top_k"])
+            if set(own.tolist()) != set(g["ids"][l].tolist()):
+                flips += 1
+                tol = 1e-2 * max(1.0, float(np.max(np.abs(lt.router_logits))))
+                kth = np.sort(np.asarray(lt.router_logits, np.float64))[::-1]
+                assert kth[CFG["top_k"] - 1] - kth[CFG["top_k"]] < tol, ("routing", l, own, g["ids"][l])
+        ol = final_logits(model, x)
+        err = float(np.max(np.abs(ol - g["logits"])))
+        print(f"a3b: logits max-abs {err:.3e}, selection flips vs the oracle's own top-k: {flips}", flush=True)
+        assert err <= 5e-2
+        for l in range(L):
+            ks = synth.bits(g["k"][l, page, :, slot, :])
+            vs = synth.bits(g["v"][l, page, :, :, slot])
+            assert rel_l2(bf16_to_f32(ks), bf16_to_f32(kv.k[l, page, :, slot, :])) <= 1e-2
+            assert rel_l2(bf16_to_f32(vs), bf16_to_f32(kv.v[l, page, :, slot, :])) <= 1e-2
+        del kv
+        kv2, layers = s.oracle_kv(), SAMPLED
+    else:
+        # a one-layer cache for layer 0
+        kv2 = PagedKV(synth.bits(s.k0[0:1]), synth.bits(s.v0[0:1].transpose(-1, -2)), P)
+        layers = (0,)
 
     # sampled layers teacher-forced from the device's residuals
-    kv2 = s.oracle_kv()
-    for l in SAMPLED:
+    for l in layers:
         xa, lt = attention_block(model, kv2, l, g["xs"][2 * l].astype(np.float32), CTX, bt, cos, sin)
         assert rel_l2(xa, g["xs"][2 * l + 1]) <= 1e-3, ("teacher-forced attention", l)
         lt2 = LayerTrace()
@@ -109,37 +130,51 @@ def test_a3b_step_matches_oracle(big):
                     assert _margin(r, a, b) < 1e-4 * max(1.0, float(np.max(np.abs(r)))), ("routing", l, j, a, b)
         xo = moe_block(model, l, g["xs"][2 * l + 1].astype(np.float32), LayerTrace(), force_ids=g["ids"][l])
         assert rel_l2(xo, g["xs"][2 * l + 2]) <= 1e-3, ("teacher-forced experts", l)
-
-    # the cache: exactly the new slot of every layer, within one BF16 ulp of the oracle's values
-    kb, vb = synth.bits(s.k0), synth.bits(s.v0)
-    ka, va = synth.bits(g["k"]), synth.bits(g["v"])
-    page, slot = bt[CTX // P], CTX % P
-    ck = {tuple(int(t) for t in x) for x in np.argwhere(np.any(ka != kb, axis=(2, 4)))}
-    cv = {tuple(int(t) for t in x) for x in np.argwhere(np.any(va != vb, axis=(2, 3)))}
-    want = {(l, page, slot) for l in range(L)}
-    assert ck == want and cv == want
-    # values: at the sampled layers, the teacher-forced oracle's BF16 rounding
-    # of the same products, to within one BF16 ulp wherever the value is not
-    # tiny (fp32 summation-order differences can move a near-zero value by
-    # more ulps than that) and to BF16 noise overall; close to the
-    # free-running oracle's at every layer
-    for l in SAMPLED:
-        for got, want in ((ka[l, page, :, slot, :], kv2.k[l, page, :, slot, :]),
-                          (va[l, page, :, :, slot], kv2.v[l, page, :, slot, :])):
+        # the new entries: the teacher-forced oracle's BF16 rounding of the
+        # same products, to within one BF16 ulp wherever the value is not
+        # tiny (fp32 summation-order differences can move a near-zero value
+        # by more ulps than that) and to BF16 noise overall
+        for got, want in ((synth.bits(g["k"][l, page, :, slot, :]), kv2.k[l, page, :, slot, :]),
+                          (synth.bits(g["v"][l, page, :, :, slot]), kv2.v[l, page, :, slot, :])):
             gf, wf = bf16_to_f32(got), bf16_to_f32(want)
             big_ = np.abs(wf) >= 0.1 * np.max(np.abs(wf))
             assert np.abs(got.astype(np.int32) - want.astype(np.int32))[big_].max() <= 1
             assert rel_l2(gf, wf) <= 5e-3
-    for l in range(L):
-        assert rel_l2(bf16_to_f32(ka[l, page, :, slot, :]), bf16_to_f32(kv.k[l, page, :, slot, :])) <= 1e-2
-        assert rel_l2(bf16_to_f32(va[l, page, :, :, slot]), bf16_to_f32(kv.v[l, page, :, slot, :])) <= 1e-2
+
+    # the cache changed exactly at the new slot of every layer (compared on the device)
+    ck = {tuple(int(t) for t in x) for x in torch.nonzero(torch.any(g["k"] != s.k0, dim=4).any(dim=2)).tolist()}
+    cv = {tuple(int(t) for t in x) for x in torch.nonzero(torch.any(g["v"] != s.v0, dim=3).any(dim=2)).tolist()}
+    want = {(l, page, slot) for l in range(L)}
+    assert ck == want and cv == want
+
+
+def test_a3b_step_matches_oracle(big):
+    s, bt, tok, pages = big
+    g = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL, 8192, pages)
+    _check_against_oracle(s, bt, tok, g, 8192)
 
 
 def test_a3b_megakernel_equals_perop_bitwise(big):
-    s, bt, tok = big
-    a = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL)
-    b = _run(s, bt, tok, mk.MK_MODE_PEROP)
+    s, bt, tok, pages = big
+    a = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL, 8192, pages)
+    b = _run(s, bt, tok, mk.MK_MODE_PEROP, 8192, pages)
     assert np.array_equal(a["logits"], b["logits"])
     assert np.array_equal(a["xs"], b["xs"])
     assert np.array_equal(a["ids"], b["ids"])
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+
+
+@pytest.mark.parametrize("ctx", [32768, 262144])
+def test_a3b_long_context(weights, ctx):
+    """Long contexts: 32K end to end against the oracle; 256K (25.8 GB of
+    cache, attention split over many more chunks) with the sampled layers
+    teacher-forced, plus megakernel == per-op bit for bit."""
+    s, bt, tok, pages = _case(weights, ctx)
+    a = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL, ctx, pages)
+    assert np.all(np.isfinite(a["logits"]))
+    _check_against_oracle(s, bt, tok, a, ctx, end_to_end=ctx <= 32768)
+    b = _run(s, bt, tok, mk.MK_MODE_PEROP, ctx, pages)
+    assert np.array_equal(a["logits"], b["logits"])
+    assert np.array_equal(a["xs"], b["xs"])
+    del s, a, b
+    torch.cuda.empty_cache()
