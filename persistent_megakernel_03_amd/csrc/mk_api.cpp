@@ -99,7 +99,7 @@ std::string check_dims(const mk_dims& d) {
     if (d.n_experts > 256) return "n_experts must be <= 256";
     if (d.hidden % 8 || d.moe_inter % 8) return "hidden and moe_inter must be multiples of 8";
     if (d.max_batch > kMaxBatchValu) return "max_batch above what this build supports";
-    if (find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim) < 0)
+    if (find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts) < 0)
         return "no kernel build for this (hidden, attention width, expert width, head_dim)";
     return std::string();
 }
@@ -239,7 +239,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         h->o = o;
         h->device = device;
         h->n_cu = o.n_cu_override > 0 ? o.n_cu_override : prop.multiProcessorCount;
-        h->shape = find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim);
+        h->shape = find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts);
         for (int nb = 1; nb <= kMaxBatchValu; ++nb)
             if (!get_kernels(h->shape, nb, &h->kern[nb])) return fail(MK_ERR_UNSUPPORTED, "no kernels");
 
@@ -248,8 +248,10 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         // routing results, per-tile scalars.
         const int G = d.n_q_heads / d.n_kv_heads;
         const int max_chunks = max_chunks_for(d);
-        // attention: the new token's k and v (bf16), per-wave (m, l) and o^T
-        const size_t attn = (size_t)4 * d.head_dim + (size_t)2 * 4 * 16 * 4 + (size_t)4 * 16 * (d.head_dim + 1) * 4;
+        // attention: the new token's k and v (bf16), per-wave (m, l) and o^T,
+        // the merge factors and per-head (max, sum)
+        const size_t attn = (size_t)4 * d.head_dim + (size_t)2 * 4 * 16 * 4 + (size_t)4 * 16 * (d.head_dim + 1) * 4 +
+                            (size_t)(4 * 16 + 2 * 16) * 4;
         const size_t comb = (size_t)(16 + max_chunks + 4 + 1024) * 4;
         // down tile: its gate/up activations [B][k][I] fp32 at the start of
         // the general region, its output staging at the end

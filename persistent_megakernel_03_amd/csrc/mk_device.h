@@ -55,15 +55,52 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
     return u >> 16;
 }
 
-__device__ __forceinline__ float dot8(const uint4 w, const float* h, float acc) {
-    acc = fmaf(bflo(w.x), h[0], acc);
-    acc = fmaf(bfhi(w.x), h[1], acc);
-    acc = fmaf(bflo(w.y), h[2], acc);
-    acc = fmaf(bfhi(w.y), h[3], acc);
-    acc = fmaf(bflo(w.z), h[4], acc);
-    acc = fmaf(bfhi(w.z), h[5], acc);
-    acc = fmaf(bflo(w.w), h[6], acc);
-    acc = fmaf(bfhi(w.w), h[7], acc);
+// Activations enter the weight products as two BF16 parts, x = hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi), so |x - hi - lo| <= 2^-17 |x|: eight
+// values of one 16-byte weight chunk are held as four hi pairs then four lo
+// pairs. The products then run on the packed BF16 dot-product instruction
+// (two weight-activation products and an fp32 accumulate per instruction,
+// with no unpacking of the weights), half the vector instructions of
+// unpacking each weight to fp32 for a fused multiply-add.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const bf16x2_t h = {(__bf16)a, (__bf16)b};
+    const bf16x2_t l = {(__bf16)(a - (float)h[0]), (__bf16)(b - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Eight fp32 activations -> {hi pairs[4], lo pairs[4]}.
+__device__ __forceinline__ void split8(const float (&v)[8], uint32_t (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split_pair(v[2 * j], v[2 * j + 1], x[j], x[4 + j]);
+}
+
+// A lane's activation slices (NB tokens, NCH chunks) -> their BF16 parts.
+template <int NB, int NCH>
+__device__ __forceinline__ void split_x(const float (&h)[NB][NCH][8], uint32_t (&hx)[NB][NCH][8]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) split8(h[b][c], hx[b][c]);
+}
+
+__device__ __forceinline__ float dot2bf(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), acc,
+                                           false);
+}
+
+// acc + sum_j w_j x_j over one chunk of eight BF16 weights and split activations.
+__device__ __forceinline__ float dot8(const uint4 w, const uint32_t (&x)[8], float acc) {
+    acc = dot2bf(w.x, x[0], acc);
+    acc = dot2bf(w.y, x[1], acc);
+    acc = dot2bf(w.z, x[2], acc);
+    acc = dot2bf(w.w, x[3], acc);
+    acc = dot2bf(w.x, x[4], acc);
+    acc = dot2bf(w.y, x[5], acc);
+    acc = dot2bf(w.z, x[6], acc);
+    acc = dot2bf(w.w, x[7], acc);
     return acc;
 }
 
@@ -93,27 +130,6 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_mov<0x141>(v));
     v = fmaxf(v, dpp_mov<0x140>(v));
     return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
-}
-
-// Wave-wide maximum of 64-bit unsigned keys (DPP on both halves).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_mov64(uint64_t v) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
-    return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = max_u64(v, dpp_mov64<0xB1>(v));
-    v = max_u64(v, dpp_mov64<0x4E>(v));
-    v = max_u64(v, dpp_mov64<0x141>(v));
-    v = max_u64(v, dpp_mov64<0x140>(v));
-    return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 // Loads through global-address-space pointers. Weight pointers come from a
@@ -251,7 +267,14 @@ __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wai
         }
         if (tid_() == 0) *t_wait = wall_clock64();
     }
-    return __syncthreads_and(ok) != 0;
+    // wave 0's verdict to every thread through one LDS word; the second
+    // barrier keeps the next wait's write after every thread's read
+    __shared__ int s_ok;
+    if (tid_() == 0) s_ok = ok;
+    __syncthreads();
+    ok = s_ok;
+    __syncthreads();
+    return ok != 0;
 }
 
 // Complete this workgroup's device-scope stores and bump counter `ctr` (the
@@ -342,18 +365,18 @@ __device__ __forceinline__ void load_row(uint4 (&w)[NCH], const uint16_t* row, i
     }
 }
 
-// Wave-level streaming matrix-vector product over activation slices h that
-// the caller holds. The wave owns `nmine` row-vectors; rowptr(i) returns the
-// i-th. The first PF rows are loaded before ready() runs (ready holds the
-// dependency wait); then rows are consumed in order while the row PF places
-// ahead is in flight. reload(i, h) may refresh h before row i; emit(i, acc)
-// receives the wave-reduced dot products (every lane has them). Loads are
-// unconditional (slots past the last row re-read the last row, which is in
-// flight already), so the wait before each row covers that row only and the
-// stream stays PF rows deep.
-template <int NCH, int PF, int NB, class RowPtr, class Ready, class Reload, class Emit>
-__device__ __forceinline__ void gemv_rows(float (&h)[NB][NCH][8], int nmine, int K8, RowPtr rowptr, Ready ready,
-                                          Reload reload, Emit emit) {
+// Wave-level streaming matrix-vector product over split activation slices hx
+// (split_x) that the caller holds. The wave owns `nmine` row-vectors;
+// rowptr(i) returns the i-th. The first PF rows are loaded before ready()
+// runs (ready holds any dependency wait and may fill hx); then rows are
+// consumed in order while the row PF places ahead is in flight.
+// emit(i, acc) receives the wave-reduced dot products (every lane has them).
+// Loads are unconditional (slots past the last row re-read the last row,
+// which is in flight already), so the wait before each row covers that row
+// only and the stream stays PF rows deep.
+template <int NCH, int PF, int NB, class RowPtr, class Ready, class Emit>
+__device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine, int K8, RowPtr rowptr, Ready ready,
+                                          Emit emit) {
     if (nmine <= 0) {
         ready();
         return;
@@ -367,30 +390,34 @@ __device__ __forceinline__ void gemv_rows(float (&h)[NB][NCH][8], int nmine, int
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
             const int i = i0 + s;
-            const bool live = i < nmine;
-            if (live) reload(i, h);
             float acc[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float a = 0.f;
 #pragma unroll
-                for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], h[b][c], a);
+                for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], hx[b][c], a);
                 acc[b] = wave_sum(a);
             }
             const int nx = i + PF;
             if (i0 + PF < nmine) load_row<NCH>(buf[s], rowptr(nx < last ? nx : last), K8);
-            if (live) emit(i, acc);
+            if (i < nmine) emit(i, acc);
         }
     }
 }
 
 // The same with the activation slices owned here: ready(h) holds the
-// dependency wait and fills h.
-template <int NCH, int PF, int NB, class RowPtr, class Ready, class Reload, class Emit>
-__device__ __forceinline__ void gemv_stream(int nmine, int K8, RowPtr rowptr, Ready ready, Reload reload,
-                                            Emit emit) {
-    float h[NB][NCH][8];
-    gemv_rows<NCH, PF, NB>(h, nmine, K8, rowptr, [&]() { ready(h); }, reload, emit);
+// dependency wait and fills the fp32 slices h, which are then split.
+template <int NCH, int PF, int NB, class RowPtr, class Ready, class Emit>
+__device__ __forceinline__ void gemv_stream(int nmine, int K8, RowPtr rowptr, Ready ready, Emit emit) {
+    uint32_t hx[NB][NCH][8];
+    gemv_rows<NCH, PF, NB>(
+        hx, nmine, K8, rowptr,
+        [&]() {
+            float h[NB][NCH][8];
+            ready(h);
+            split_x<NB, NCH>(h, hx);
+        },
+        emit);
 }
 
 // ------------------------------------------------------------ routing
@@ -433,52 +460,72 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // keys; the lowest id holding the maximum is found with ballots. Then the
 // softmax over the selected logits (lane j holds the j-th), and the distinct
 // selected experts in ascending id as slots, with each token's rank of the
-// slot's expert. Ends with a block barrier.
+// slot's expert. NE = experts per lane (E <= 64 NE). All logits of a token are
+// requested at once (one memory round trip). Ends with a block barrier.
+template <int NE>
 __device__ __forceinline__ void compute_routing(const Params& p, const float* rl, RouteLds* r) {
     if (tid_() < 64) {
         const int lane = tid_();
         const int E = p.E, K = p.K;
-        uint32_t chosen[4] = {0u, 0u, 0u, 0u};  // bit b: token b chose expert lane + 64i
-        uint32_t rank[4] = {~0u, ~0u, ~0u, ~0u}; // byte b: its rank in token b's top-k
+        uint32_t chosen[NE], rank[NE];  // bit / byte b: token b chose expert lane + 64i, at that rank
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            chosen[i] = 0u;
+            rank[i] = ~0u;
+        }
         for (int b = 0; b < p.B; ++b) {
-            uint32_t u[4];
+            float lv[NE];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NE; ++i) {
                 const int e = lane + 64 * i;
-                u[i] = e < E ? fkey(ld_dev(rl + b * E + e)) : 0u;
+                lv[i] = ld_dev(rl + b * E + (e < E ? e : E - 1));
             }
-            float top = 0.f, sel = 0.f;
-#pragma unroll 1
-            for (int j = 0; j < K; ++j) {
-                const uint32_t m = wave_max_u32(max(max(u[0], u[1]), max(u[2], u[3])));
-                int best = -1;
+            uint32_t u[NE];  // 0: not a candidate (no float maps to 0)
 #pragma unroll
-                for (int i = 3; i >= 0; --i) {
-                    const uint64_t bal = __ballot(u[i] == m);
-                    if (bal != 0ull) best = 64 * i + (int)__builtin_ctzll(bal);
-                }
-                const float v = unkey(m);
-                if (j == 0) top = v;
-                if (lane == j) sel = v;
+            for (int i = 0; i < NE; ++i) u[i] = lane + 64 * i < E ? fkey(lv[i]) : 0u;
+            uint32_t top = 0u;
+            float sel = 0.f;  // lane j: the j-th selected logit
+            int myid = 0;     // lane j: the j-th selected expert
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (64 * i + lane == best) {
-                        u[i] = 0u;
-                        chosen[i] |= 1u << b;
-                        rank[i] = (rank[i] & ~(0xffu << (8 * b))) | ((uint32_t)j << (8 * b));
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (j < K) {
+                    uint32_t v = u[0];
+#pragma unroll
+                    for (int i = 1; i < NE; ++i) v = max(v, u[i]);
+                    const uint32_t m = wave_max_u32(v);
+                    int best = -1;
+#pragma unroll
+                    for (int i = NE - 1; i >= 0; --i) {
+                        const uint64_t bal = __ballot(u[i] == m);
+                        if (bal != 0ull) best = 64 * i + (int)__builtin_ctzll(bal);
+                    }
+                    if (j == 0) top = m;
+                    if (lane == j) {
+                        sel = unkey(m);
+                        myid = best;
+                    }
+#pragma unroll
+                    for (int i = 0; i < NE; ++i) {
+                        if (64 * i + lane == best) {
+                            u[i] = 0u;
+                            chosen[i] |= 1u << b;
+                            rank[i] = (rank[i] & ~(0xffu << (8 * b))) | ((uint32_t)j << (8 * b));
+                        }
                     }
                 }
-                if (lane == 0) r->ids[b][j] = best;
             }
             // softmax over the selected logits (the first is the largest)
-            const float ex = lane < K ? expf(sel - top) : 0.f;
+            const float ex = lane < K ? expf(sel - unkey(top)) : 0.f;
             const float sum = wave_sum(ex);
-            if (lane < K) r->w[b][lane] = ex / sum;
+            if (lane < K) {
+                r->ids[b][lane] = myid;
+                r->w[b][lane] = ex / sum;
+            }
         }
         // slots: selected experts in ascending id
         int base = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NE; ++i) {
             const uint64_t m = __ballot(chosen[i] != 0u);
             if (chosen[i] != 0u) {
                 const int slot = base + __popcll(m & ((1ull << lane) - 1ull));

@@ -11,9 +11,9 @@ constexpr int kThreads = 256;   // workgroup size of every kernel
 constexpr int kMaxBatchValu = 2; // largest batch the matrix-vector tiles take
 
 // Kernels are compiled per model shape: the number of 16-byte chunks per lane
-// per row for the hidden size, the attention width and the expert width, and
-// the head size. Returns -1 if no build matches.
-int find_shape(int hidden, int attn_width, int moe_inter, int head_dim);
+// per row for the hidden size, the attention width and the expert width, the
+// head size and the router logits per lane. Returns -1 if no build matches.
+int find_shape(int hidden, int attn_width, int moe_inter, int head_dim, int n_experts);
 
 struct KernelPair {
     const void* persistent;  // (Params, int general)

@@ -45,12 +45,13 @@ __global__ void k_fill_u32(uint32_t* dst, int64_t n, uint32_t v) {
         dst[i] = v;
 }
 
-// Supported shapes: {NCH_H, NCH_O, NCH_I, D, NCHP_I}.
-typedef Shape<1, 1, 1, 64, 1> ShapeSmall;    // e.g. hidden 256, 4x64 heads, expert width 128
-typedef Shape<4, 8, 2, 128, 3> ShapeA3B;     // hidden 2048, 32x128 heads, expert width 768
+// Supported shapes: {NCH_H, NCH_O, NCH_I, D, NCHP_I, NE}.
+typedef Shape<1, 1, 1, 64, 1, 1> ShapeSmall;  // e.g. hidden 256, 4x64 heads, expert width 128, 8 experts
+typedef Shape<4, 8, 2, 128, 3, 2> ShapeA3B;   // hidden 2048, 32x128 heads, expert width 768, 128 experts
 
 namespace {
-const int kShapes[][5] = {{1, 1, 1, 64, 1}, {4, 8, 2, 128, 3}};
+constexpr int kKey = 6;
+const int kShapes[][kKey] = {{1, 1, 1, 64, 1, 1}, {4, 8, 2, 128, 3, 2}};
 
 template <class S>
 void fill_pair(int nb, KernelPair* out) {
@@ -64,12 +65,12 @@ void fill_pair(int nb, KernelPair* out) {
 }
 }  // namespace
 
-int find_shape(int hidden, int attn_width, int moe_inter, int head_dim) {
-    const int key[5] = {(hidden + 511) / 512, (attn_width + 511) / 512, (moe_inter + 511) / 512, head_dim,
-                        (moe_inter + 255) / 256};
+int find_shape(int hidden, int attn_width, int moe_inter, int head_dim, int n_experts) {
+    const int key[kKey] = {(hidden + 511) / 512, (attn_width + 511) / 512, (moe_inter + 511) / 512, head_dim,
+                           (moe_inter + 255) / 256, (n_experts + 63) / 64};
     for (int i = 0; i < (int)(sizeof(kShapes) / sizeof(kShapes[0])); ++i) {
         bool same = true;
-        for (int j = 0; j < 5; ++j) same = same && key[j] == kShapes[i][j];
+        for (int j = 0; j < kKey; ++j) same = same && key[j] == kShapes[i][j];
         if (same) return i;
     }
     return -1;

@@ -126,7 +126,6 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
             load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, gn, p.eps);
             mark(cx, 0);
         },
-        [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
                 const int row = phys(v0 + wave + i * NWAVES);
@@ -180,6 +179,9 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     float* sM = reinterpret_cast<float*>(cx.lds + 4 * D);         // [NWAVES][16]
     float* sL = sM + NWAVES * 16;                                 // [NWAVES][16]
     float* sO = sL + NWAVES * 16;                                 // [NWAVES][16][D + 1]
+    float* sF = sO + NWAVES * 16 * (D + 1);                       // [NWAVES][16] merge factors
+    float* sMh = sF + NWAVES * 16;                                // [16] chunk maximum per head
+    float* sLh = sMh + 16;                                        // [16] chunk sum per head
 
     uint4 kf[NTBW][NDB];   // A operand of S^T: token col of the block, dims 32db + 8quad..+7
     uint2 vf[NTBW][NDV];   // A operand of O^T: dim 16dv + col, tokens 4quad..+3 of the block
@@ -208,30 +210,34 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
             }
         }
     };
-    // After the loads land: zero tokens past the cached range, insert the new token.
+    // After the loads land, in the (at most one per wave) block that reaches
+    // past the cached tokens: zero the values of slots at or past t_old (their
+    // probabilities are 0, but the slots may hold any bits) and insert the
+    // new token's k and v.
     auto fix_kv = [&](int st0) {
 #pragma unroll
         for (int i = 0; i < NTBW; ++i) {
             const int blk = st0 + (wave + NWAVES * i) * 16;
-            if (has_new && blk + col == pos) {
+            if (blk + 16 > t_old) {
+                if (has_new && blk + col == pos) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    kf[i][db] = *reinterpret_cast<const uint4*>(sKn + db * 32 + quad * 8);
-            }
-            const int tv = blk + 4 * quad;
+                    for (int db = 0; db < NDB; ++db)
+                        kf[i][db] = *reinterpret_cast<const uint4*>(sKn + db * 32 + quad * 8);
+                }
+                const int n = t_old - (blk + 4 * quad);   // cached tokens in this lane's group of four
+                const uint32_t mx = n >= 2 ? ~0u : (n == 1 ? 0xffffu : 0u);
+                const uint32_t my = n >= 4 ? ~0u : (n == 3 ? 0xffffu : 0u);
 #pragma unroll
-            for (int dv = 0; dv < NDV; ++dv) {
-                uint32_t w[2] = {vf[i][dv].x, vf[i][dv].y};
+                for (int dv = 0; dv < NDV; ++dv) vf[i][dv] = make_uint2(vf[i][dv].x & mx, vf[i][dv].y & my);
+                if (has_new && (pos >> 2) == (blk >> 2) + quad) {
+                    const int sh = 16 * (pos & 1);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int tok = tv + jj;
-                    if (tok >= t_old) {
-                        const uint32_t val = (has_new && tok == pos) ? (uint32_t)sVn[dv * 16 + col] : 0u;
-                        if (jj & 1) w[jj >> 1] = (w[jj >> 1] & 0x0000ffffu) | (val << 16);
-                        else w[jj >> 1] = (w[jj >> 1] & 0xffff0000u) | val;
+                    for (int dv = 0; dv < NDV; ++dv) {
+                        const uint32_t val = (uint32_t)sVn[dv * 16 + col] << sh;
+                        if (pos & 2) vf[i][dv].y |= val;
+                        else vf[i][dv].x |= val;
                     }
                 }
-                vf[i][dv] = make_uint2(w[0], w[1]);
             }
         }
     };
@@ -399,25 +405,34 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     }
     __syncthreads();
     mark(cx, 2);
+    // per head: the chunk maximum M, each wave's factor exp(m_w - M) and the sum
+    if (tid < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, sM[w * 16 + tid]);
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            const float mw = sM[w * 16 + tid];
+            const float e = mw == -INFINITY ? 0.f : expf(mw - M);
+            sF[w * 16 + tid] = e;
+            L += e * sL[w * 16 + tid];
+        }
+        sMh[tid] = M;
+        sLh[tid] = L;
+    }
+    __syncthreads();
     float* part = part_at(p, l) + ((int64_t)b * p.Hq + g * G) * p.max_chunks * D;
     float* ml = ml_at(p, l) + ((int64_t)b * p.Hq + g * G) * ml_row(p);
     for (int i = tid; i < G * D; i += NT) {
         const int h = i / D, d = i - h * D;
-        float M = -INFINITY;
+        float o = 0.f;
 #pragma unroll
-        for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, sM[w * 16 + h]);
-        float o = 0.f, L = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVES; ++w) {
-            const float mw = sM[w * 16 + h];
-            const float e = mw == -INFINITY ? 0.f : expf(mw - M);
-            o += e * sO[(w * 16 + h) * (D + 1) + d];
-            L += e * sL[w * 16 + h];
-        }
+        for (int w = 0; w < NWAVES; ++w) o += sF[w * 16 + h] * sO[(w * 16 + h) * (D + 1) + d];
         st_dev(part + ((int64_t)h * p.max_chunks + c) * D + d, o);
         if (d == 0) {
-            st_dev(ml + (int64_t)h * ml_row(p) + 2 * c, M);
-            st_dev(ml + (int64_t)h * ml_row(p) + 2 * c + 1, L);
+            st_dev(ml + (int64_t)h * ml_row(p) + 2 * c, sMh[h]);
+            st_dev(ml + (int64_t)h * ml_row(p) + 2 * c + 1, sLh[h]);
         }
     }
     mark(cx, 3);
@@ -525,7 +540,6 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, attout_at(p, l), K, p.B, K, nullptr, 0.f);
         },
-        [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if (lane == i) {
                 const int row = r0 + wave + i * NWAVES;
@@ -560,7 +574,6 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
         },
-        [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
                 const int row = r0 + wave + i * NWAVES;
@@ -585,22 +598,24 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
 // then waits for the logits (main counter) and computes the routing; only
 // then are the expert's rows known and streamed. Task a3 != 0: also store the
 // routing of this layer.
-template <int NCH, int PF, int NB>
+template <int NCH, int PF, int NB, int NE>
 __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1;
     const int wave = tid_() >> 6, lane = tid_() & 63;
     const int H = p.H;
     RouteLds* rt = route_lds(cx.lds, cx.general);
-    float h[NB][NCH][8];
+    uint32_t hx[NB][NCH][8];
     {
         uint4 gn[NCH];
         load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), H);
         if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+        float h[NB][NCH][8];
         load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
+        split_x<NB, NCH>(h, hx);
     }
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
-    compute_routing(p, rlogits_at(p, l), rt);
+    compute_routing<NE>(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
@@ -620,10 +635,9 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const int npair = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     float gate[NB];
     gemv_rows<NCH, PF, NB>(
-        h, 2 * npair, H >> 3,
+        hx, 2 * npair, H >> 3,
         [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
         [&]() { mark(cx, 1); },
-        [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if ((i & 1) == 0) {
 #pragma unroll
@@ -659,14 +673,14 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
 // cover (I = 768: three loads, where one row alone would need one full and
 // one half-empty load). Lane l's chunk c is chunk f = 64c + l of the pair:
 // row f / (I/8), column f % (I/8).
-template <int NCHP, int PF, int NB>
+template <int NCHP, int PF, int NB, int NE>
 __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0;
     const int tid = tid_(), wave = tid >> 6, lane = tid & 63;
     RouteLds* rt = route_lds(cx.lds, cx.general);
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
-    compute_routing(p, rlogits_at(p, l), rt);
+    compute_routing<NE>(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     const int I = p.I, K = p.K, B = p.B;
     const int K8 = I >> 3;
@@ -679,7 +693,8 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const int myslots = nslots > wave ? (nslots - wave + NWAVES - 1) / NWAVES : 0;
     const int nmine = myslots * npps;
     const uint16_t* Wd = wptr(p, l, W_DOWN);
-    float* sAct = reinterpret_cast<float*>(cx.lds);   // [B][K][I] gate/up outputs
+    // [B][K][I/8] chunks of the gate/up outputs, each as BF16 parts (hi pairs, lo pairs)
+    uint4* sAct = reinterpret_cast<uint4*>(cx.lds);
     float* sY = reinterpret_cast<float*>(cx.lds + cx.general) - kMaxBatch * kMaxTopK * kMaxDownRows;  // [B*K][nrows]
     const float* act = act_at(p, l);
     auto pairptr = [&](int q) {
@@ -695,26 +710,36 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     }
     bool ok = block_wait(p, t.ctr, t.target, cx.t_wait);
     if (ok) {
-        // all loads of a batch in flight before the LDS writes
-        const int n4 = (B * K * I) >> 2;
-        for (int i0 = 0; i0 < n4; i0 += 6 * NT) {
-            float4 v[6];
+        // all loads of a batch in flight before the LDS writes; each chunk
+        // of eight is split into BF16 parts once, here
+        const int n8 = (B * K * I) >> 3;
+        for (int i0 = 0; i0 < n8; i0 += 3 * NT) {
+            float4 v[3][2];
 #pragma unroll
-            for (int k = 0; k < 6; ++k) {
+            for (int k = 0; k < 3; ++k) {
                 const int i = i0 + k * NT + tid;
-                v[k] = ldf4(act + 4 * (i < n4 ? i : 0));
+                const float* a = act + 8 * (i < n8 ? i : 0);
+                v[k][0] = ldf4(a);
+                v[k][1] = ldf4(a + 4);
             }
 #pragma unroll
-            for (int k = 0; k < 6; ++k) {
+            for (int k = 0; k < 3; ++k) {
                 const int i = i0 + k * NT + tid;
-                if (i < n4) reinterpret_cast<float4*>(sAct)[i] = v[k];
+                if (i < n8) {
+                    const float f[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w,
+                                        v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+                    uint32_t x[8];
+                    split8(f, x);
+                    sAct[2 * i] = make_uint4(x[0], x[1], x[2], x[3]);
+                    sAct[2 * i + 1] = make_uint4(x[4], x[5], x[6], x[7]);
+                }
             }
         }
     }
     __syncthreads();
     mark(cx, 1);
     if (ok && nmine > 0) {
-        float hp[NB][NCHP][8];
+        uint32_t hp[NB][NCHP][8];
         for (int q0 = 0; q0 < nmine; q0 += PF) {
 #pragma unroll
             for (int s = 0; s < PF; ++s) {
@@ -730,14 +755,13 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
                             const int f = lane + 64 * c;
                             const int col = f < K8 ? f : f - K8;
                             if (rank >= 0 && f < 2 * K8) {
-                                const float* a = sAct + (b * K + rank) * I + col * 8;
-                                const float4 u = *reinterpret_cast<const float4*>(a);
-                                const float4 v = *reinterpret_cast<const float4*>(a + 4);
+                                const uint4* a = sAct + 2 * ((b * K + rank) * K8 + col);
+                                const uint4 u = a[0], v = a[1];
                                 hp[b][c][0] = u.x; hp[b][c][1] = u.y; hp[b][c][2] = u.z; hp[b][c][3] = u.w;
                                 hp[b][c][4] = v.x; hp[b][c][5] = v.y; hp[b][c][6] = v.z; hp[b][c][7] = v.w;
                             } else {
 #pragma unroll
-                                for (int jj = 0; jj < 8; ++jj) hp[b][c][jj] = 0.f;
+                                for (int jj = 0; jj < 8; ++jj) hp[b][c][jj] = 0u;
                             }
                         }
                     }
@@ -768,7 +792,8 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
             }
         }
     }
-    if (!__syncthreads_and(ok)) return false;
+    __syncthreads();
+    if (!ok) return false;  // block-uniform (block_wait)
     mark(cx, 2);
     float* xout = x_at(p, 2 * l + 2);
     if (tid < B * nrows) {
@@ -799,7 +824,6 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, gn, p.eps);
         },
-        [&](int, float(&)[NB][NCH][8]) {},
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
                 const int row = r0 + wave + i * NWAVES;
@@ -818,13 +842,15 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
 
 // Compile-time shape of a kernel build: 16-byte chunks per lane per row
 // (ceil(K / 512)) for the three reduction lengths in the model -- hidden
-// size H, attention width Hq*D and expert width I -- and the head size. Each
+// size H, attention width Hq*D and expert width I -- the head size, the
+// 16-byte chunks per lane of a pair of expert rows (ceil(I / 256)) and the
+// router logits per lane (ceil(E / 64)). Each
 // supported model gets its own kernels, so each tile is compiled only for
 // the reduction lengths it actually sees and register allocation is sized
 // per tile, not for every possible shape.
-template <int NCH_H_, int NCH_O_, int NCH_I_, int D_, int NCHP_I_>
+template <int NCH_H_, int NCH_O_, int NCH_I_, int D_, int NCHP_I_, int NE_>
 struct Shape {
-    static constexpr int NCH_H = NCH_H_, NCH_O = NCH_O_, NCH_I = NCH_I_, D = D_, NCHP_I = NCHP_I_;
+    static constexpr int NCH_H = NCH_H_, NCH_O = NCH_O_, NCH_I = NCH_I_, D = D_, NCHP_I = NCHP_I_, NE = NE_;
 };
 
 // Rows in flight per wave for a given chunk count and batch.
@@ -842,8 +868,8 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
         case OP_COMBINE: return tile_combine<S::D>(t, cx);
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
         case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
-        case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 8 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
-        case OP_DOWN: return tile_down<S::NCHP_I, (NB == 1 ? 8 : 4), NB>(t, cx);
+        case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 7 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
+        case OP_DOWN: return tile_down<S::NCHP_I, (NB == 1 ? 8 : 4), NB, S::NE>(t, cx);
         case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         default: return false;
     }
