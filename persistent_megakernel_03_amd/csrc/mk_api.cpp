@@ -320,6 +320,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         p.G = G;
         p.QKVD = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
         p.eps = d.rms_eps;
+        p.inv_h = 1.0f / (float)d.hidden;
         p.attn_scale = (float)(1.0 / std::sqrt((double)d.head_dim));
         p.max_batch = d.max_batch;
         p.max_pages = d.max_pages_per_seq;

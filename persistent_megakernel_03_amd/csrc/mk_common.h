@@ -96,7 +96,7 @@ MK_HD inline int64_t pad64(int64_t n) { return (n + 63) & ~(int64_t)63; }
 struct Params {
     // model shape
     int32_t L, H, Hq, Hkv, D, E, K, I, V, P, G, QKVD;
-    float eps, attn_scale;
+    float eps, attn_scale, inv_h;   // inv_h = 1 / H (RMSNorm mean)
     int32_t max_batch, max_pages, max_chunks;
     int64_t n_pages;
     // this step

@@ -309,10 +309,11 @@ __device__ __forceinline__ void load_gain(uint4 (&g)[NCH], const uint16_t* gain,
 
 // Each lane of each wave holds the activation values at the K positions its
 // weight chunks cover. With `g` non-null applies RMSNorm:
-// x / sqrt(mean(x^2) + eps) * gain.
+// x / sqrt(mean(x^2) + eps) * gain, the mean as sum(x^2) * inv_k (inv_k =
+// 1/K, a kernel argument, so no per-tile division is needed).
 template <int NCH, int NB>
 __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, int64_t stride, int nb,
-                                       int K, const uint4* g, float eps) {
+                                       int K, const uint4* g, float eps, float inv_k) {
     const int lane = tid_() & 63;
     const int K8 = K >> 3;
 #pragma unroll
@@ -334,7 +335,7 @@ __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, i
         }
         if (g != nullptr) {
             ss = wave_sum(ss);
-            const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+            const float inv = 1.0f / sqrtf(ss * inv_k + eps);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const uint4 gw = g[c];

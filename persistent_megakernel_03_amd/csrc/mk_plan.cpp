@@ -47,9 +47,12 @@ struct Tile {
 void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down) {
     *rows_gu = cfg.rows_gateup;
     *rows_down = cfg.rows_down;
-    // A down tile keeps all its weight rows (S experts x rows) in registers,
-    // at most 16 row-vectors per wave.
-    const int rd = std::min(64, 64 / std::max(1, S)) & ~1;   // even: the down tile takes rows in pairs
+    // A down tile keeps its weight rows (S experts x rows) in registers, 16
+    // row-vectors per wave (one matrix-core operand). Rows per tile are a
+    // power of two, so the 16 row-vectors of a wave hold whole experts or
+    // one part of one expert.
+    int rd = 64;
+    while (rd > 1 && rd * std::max(1, S) > 64) rd >>= 1;
     if (rd < cfg.rows_down) return;
     const int n_down = ceil_div(s.H, rd);
     const int per_slot = (n_wg - n_down) / std::max(1, S);
@@ -131,10 +134,16 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         const int lv = 1 + kLevelsPerLayer * l;
         const int in_ctr = l == 0 ? cl.embed() : cl.down(l - 1);
         const int in_target = l == 0 ? 1 : nd;
+        // the query/key/value weights and the cache pages of layer l start
+        // streaming once the previous layer's gate/up tiles are done, so that
+        // they do not compete with the expert weights, which cannot be
+        // fetched before the routing is known
+        const int defer_ctr = l == 0 ? -1 : cl.gateup(l - 1);
+        const int defer_target = l == 0 ? 0 : S * ngu;
         for (int g = 0; g < s.Hkv; ++g) {
             for (int i = 0; i < nq; ++i) {
                 const int v0 = i * cfg.rows_qkv, v1 = std::min(grows, v0 + cfg.rows_qkv);
-                add(make_task(OP_QKV, l, g, v0, v1, 0, -1, 0, in_ctr, in_target, cl.qkv(l, g), lv),
+                add(make_task(OP_QKV, l, g, v0, v1, 0, defer_ctr, defer_target, in_ctr, in_target, cl.qkv(l, g), lv),
                     2.0 * (v1 - v0) * s.H, kStatic);
             }
             P.targets[cl.qkv(l, g)] = nq;
@@ -144,7 +153,8 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
             for (int g = 0; g < s.Hkv; ++g)
                 for (int c = 0; c < n; ++c) {
                     const int toks = std::min(P.chunk, positions[b] + 1 - c * P.chunk);
-                    add(make_task(OP_ATTN, l, b, g, c, n, -1, 0, cl.qkv(l, g), nq, cl.attn(l, g), lv + 1),
+                    add(make_task(OP_ATTN, l, b, g, c, n, defer_ctr, defer_target, cl.qkv(l, g), nq, cl.attn(l, g),
+                                  lv + 1),
                         4.0 * toks * s.D, kStatic);
                 }
         }
@@ -177,7 +187,8 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         P.targets[cl.gateup(l)] = S * ngu;
         for (int i = 0; i < nd; ++i) {
             const int r0 = i * rows_down, r1 = std::min(s.H, r0 + rows_down);
-            add(make_task(OP_DOWN, l, r0, r1, 0, 0, cl.router(l), nr, cl.gateup(l), S * ngu, cl.down(l), lv + 6),
+            add(make_task(OP_DOWN, l, r0, r1, rows_down, 0, cl.router(l), nr, cl.gateup(l), S * ngu, cl.down(l),
+                          lv + 6),
                 2.0 * S * (r1 - r0) * s.I, kRouted);
         }
         P.targets[cl.down(l)] = nd;
@@ -206,11 +217,19 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     // one when another is free. Lists stay in level order (deadlock freedom).
     const double bw = cfg.model_bw_bytes_per_us / n_wg;   // bytes per microsecond per workgroup
     const double overhead = cfg.model_task_us, sync = cfg.model_sync_us;
+    //
+    // The expert tiles stream most of a layer's bytes once the routing is
+    // known, so they are spread evenly over compute units: with two
+    // workgroups per unit, workgroups w and w + n_wg/2 share one, so the
+    // gate/up tiles go to the upper half and the down tiles to the lower half
+    // (one of each per unit when both counts equal n_wg/2).
     std::vector<std::vector<Task>> lists(n_wg);
     P.wg_bytes.assign(n_wg, 0.0);
     typedef std::pair<double, int> Slot;
-    std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-    for (int w = 0; w < n_wg; ++w) heap.push({0.0, w});
+    typedef std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> Heap;
+    const int half = (n_wg % 2 == 0) ? n_wg / 2 : 0;
+    Heap heaps[2];   // [0]: workgroups below `half`, [1]: the rest
+    for (int w = 0; w < n_wg; ++w) heaps[w >= half ? 1 : 0].push({0.0, w});
     std::vector<double> level_end(P.n_levels, 0.0);
     auto producer_end = [&](int lv) { return lv > 0 ? level_end[lv - 1] + sync : 0.0; };
     for (int lv = 0; lv < P.n_levels; ++lv) {
@@ -224,6 +243,13 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         if (op == OP_DOWN) wready = producer_end(lv - 1);
         double end = 0.0;
         for (const Tile& t : tiles) {
+            int hsel;
+            if (half > 0 && op == OP_GATEUP) hsel = 1;
+            else if (half > 0 && op == OP_DOWN) hsel = 0;
+            else if (heaps[0].empty()) hsel = 1;
+            else if (heaps[1].empty()) hsel = 0;
+            else hsel = heaps[1].top() < heaps[0].top() ? 1 : 0;
+            Heap& heap = heaps[hsel];
             Slot s0 = heap.top();
             heap.pop();
             const double wr = t.kind == kDynamic ? ready : wready;

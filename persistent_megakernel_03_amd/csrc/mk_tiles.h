@@ -102,7 +102,8 @@ __device__ __forceinline__ bool tile_embed(const Task& t, TileCtx& cx) {
 // -------------------------------------------------------------------- QKV
 
 // Rows of one KV group g: the G*D query rows of its heads, then its D key
-// rows, then its D value rows ("virtual rows" a1..a2 of the group).
+// rows, then its D value rows ("virtual rows" a1..a2 of the group). The
+// weights start loading after the pre counter (if any) is reached.
 template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
@@ -116,6 +117,7 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
         if (v < GD + D) return p.Hq * D + g * D + (v - GD);
         return p.Hq * D + p.Hkv * D + g * D + (v - GD - D);
     };
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     bool ok = true;
     gemv_stream<NCH, PF, NB>(
         nmine, H >> 3, [&](int i) { return W + (int64_t)phys(v0 + wave + i * NWAVES) * H; },
@@ -123,7 +125,7 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
             uint4 gn[NCH];
             load_gain<NCH>(gn, wptr(p, l, W_ATTN_NORM), H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, gn, p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, gn, p.eps, p.inv_h);
             mark(cx, 0);
         },
         [&](int i, const float(&acc)[NB]) {
@@ -242,6 +244,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
         }
     };
 
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     load_kv(t0);
     // queries: lane (quad, col) holds head col's dims 32db + 8quad..+7 (zero
     // for col >= G); the rotary factors of those dims are a host input, so
@@ -538,7 +541,7 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
         nmine, K >> 3, [&](int i) { return W + (int64_t)(r0 + wave + i * NWAVES) * K; },
         [&](float(&h)[NB][NCH][8]) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, attout_at(p, l), K, p.B, K, nullptr, 0.f);
+            load_x<NCH, NB>(h, attout_at(p, l), K, p.B, K, nullptr, 0.f, 0.f);
         },
         [&](int i, const float(&acc)[NB]) {
             if (lane == i) {
@@ -572,7 +575,7 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
             uint4 gn[NCH];
             load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps, p.inv_h);
         },
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
@@ -611,7 +614,7 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
         load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), H);
         if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
         float h[NB][NCH][8];
-        load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps);
+        load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps, p.inv_h);
         split_x<NB, NCH>(h, hx);
     }
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
@@ -666,49 +669,53 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
 // the expert rows) is known once the router logits are (pre counter): the
 // tile computes it and starts its weights streaming into registers while the
 // gate/up tiles are still running, then waits for them (main counter) and
-// reads their activations once, into LDS.
+// reads their activations once, into LDS, split into BF16 parts.
 //
-// Rows are taken in pairs: two consecutive rows of an expert are contiguous,
-// so a pair of I-wide rows is 2I/8 16-byte chunks that NCHP full-wave loads
-// cover (I = 768: three loads, where one row alone would need one full and
-// one half-empty load). Lane l's chunk c is chunk f = 64c + l of the pair:
-// row f / (I/8), column f % (I/8).
-template <int NCHP, int PF, int NB, int NE>
+// The products run on the matrix cores (BF16 MFMA 16x16x32, fp32
+// accumulate). Wave w takes slots w, w+4, ...; its row-vectors are listed
+// slot-major with a2 (a power of two, >= the tile's rows) entries per slot,
+// and each group of 16 is one A operand: lane l holds row-vector l%16 at
+// k-chunk l/16 of every 32-wide k-step. The B operand's 16 columns are, per
+// slot of the group, per token, the hi and lo parts of that token's
+// activations for the slot's expert (zero where the token did not choose
+// it), so column pair (2m, 2m+1) of an A-row belonging to that slot is its
+// dot product in two parts.
+template <int KS, int NB, int NE>
 __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
-    const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0;
+    const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, rd = t.a2;
     const int tid = tid_(), wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, g4 = lane >> 4;
     RouteLds* rt = route_lds(cx.lds, cx.general);
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     compute_routing<NE>(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     const int I = p.I, K = p.K, B = p.B;
-    const int K8 = I >> 3;
+    const int K8 = I >> 3, nks = I >> 5;
     const int nslots = rt->nslots;
     // residual slice: ready since the output projection
     const float* xmid = x_at(p, 2 * l + 1);
     const float xres = tid < B * nrows ? ldg(xmid + (int64_t)(tid / nrows) * p.H + h0 + tid % nrows) : 0.f;
-    // wave w takes slots w, w+4, ...; pair-vector q -> slot index q / npps, rows 2(q % npps) + {0, 1}
-    const int npps = nrows >> 1;
     const int myslots = nslots > wave ? (nslots - wave + NWAVES - 1) / NWAVES : 0;
-    const int nmine = myslots * npps;
+    const int ngrp = (myslots * rd + 15) >> 4;
     const uint16_t* Wd = wptr(p, l, W_DOWN);
     // [B][K][I/8] chunks of the gate/up outputs, each as BF16 parts (hi pairs, lo pairs)
     uint4* sAct = reinterpret_cast<uint4*>(cx.lds);
     float* sY = reinterpret_cast<float*>(cx.lds + cx.general) - kMaxBatch * kMaxTopK * kMaxDownRows;  // [B*K][nrows]
     const float* act = act_at(p, l);
-    auto pairptr = [&](int q) {
-        const int s = wave + (q / npps) * NWAVES;
-        return Wd + ((int64_t)rt->slot_e[s] * p.H + h0 + 2 * (q % npps)) * I;
-    };
-    // every wave runs the same barriers; waves without slots only help copy
-    uint4 buf[PF][NCHP];
-    const int last = nmine > 0 ? nmine - 1 : 0;
-    if (nmine > 0) {
+    // the A-row of this lane in group grp (padding entries re-read a valid row)
+    uint4 wb[KS];
+    auto load_grp = [&](int grp) {
+        const int v = 16 * grp + col;
+        const int jl = v / rd, r = v - jl * rd;
+        const bool live = jl < myslots && r < nrows;
+        const int e = rt->slot_e[live ? wave + NWAVES * jl : 0];
+        const uint16_t* a = Wd + ((int64_t)e * p.H + h0 + (live ? r : 0)) * I + 8 * g4;
 #pragma unroll
-        for (int s = 0; s < PF; ++s) load_row<NCHP>(buf[s], pairptr(s < last ? s : last), 2 * K8);
-    }
-    bool ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+        for (int ks = 0; ks < KS; ++ks) wb[ks] = ld16(a + 32 * (ks < nks ? ks : nks - 1));
+    };
+    if (ngrp > 0) load_grp(0);
+    const bool ok = block_wait(p, t.ctr, t.target, cx.t_wait);
     if (ok) {
         // all loads of a batch in flight before the LDS writes; each chunk
         // of eight is split into BF16 parts once, here
@@ -738,56 +745,37 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     }
     __syncthreads();
     mark(cx, 1);
-    if (ok && nmine > 0) {
-        uint32_t hp[NB][NCHP][8];
-        for (int q0 = 0; q0 < nmine; q0 += PF) {
+    if (ok) {
+        for (int grp = 0; grp < ngrp; ++grp) {
+            if (grp > 0) load_grp(grp);
+            // this lane's B column: slot jc of the wave, token bc, part (hi / lo)
+            const int first = (16 * grp) / rd;
+            const int jc = first + col / (2 * NB), bc = (col >> 1) % NB, part = col & 1;
+            const int rank = (jc < myslots && bc < B) ? rt->slot_rank[wave + NWAVES * jc][bc] : -1;
+            const uint4* bsrc = sAct + 2 * ((bc * K + (rank >= 0 ? rank : 0)) * K8 + g4) + part;
+            // B operands eight k-steps at a time (their LDS reads in flight
+            // together), two accumulators (independent matrix-core chains)
+            f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int s = 0; s < PF; ++s) {
-                const int q = q0 + s;
-                const int sl = wave + (q / npps) * NWAVES;
-                if (q < nmine && q % npps == 0) {
-                    // this slot's activations at the columns of this lane's chunks
+            for (int k0 = 0; k0 < KS; k0 += 8) {
+                uint4 bv[8];
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const int rank = (b < B) ? rt->slot_rank[sl][b] : -1;
+                for (int j = 0; j < 8; ++j)
+                    bv[j] = (k0 + j < nks && rank >= 0) ? bsrc[8 * (k0 + j)] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-                        for (int c = 0; c < NCHP; ++c) {
-                            const int f = lane + 64 * c;
-                            const int col = f < K8 ? f : f - K8;
-                            if (rank >= 0 && f < 2 * K8) {
-                                const uint4* a = sAct + 2 * ((b * K + rank) * K8 + col);
-                                const uint4 u = a[0], v = a[1];
-                                hp[b][c][0] = u.x; hp[b][c][1] = u.y; hp[b][c][2] = u.z; hp[b][c][3] = u.w;
-                                hp[b][c][4] = v.x; hp[b][c][5] = v.y; hp[b][c][6] = v.z; hp[b][c][7] = v.w;
-                            } else {
+                for (int j = 0; j < 8; ++j)
+                    if (k0 + j < KS && k0 + j < nks) acc2[j & 1] = mfma16x16x32(wb[k0 + j], bv[j], acc2[j & 1]);
+            }
+            f32x4_t acc = acc2[0] + acc2[1];
+            // hi + lo (adjacent columns); lane (col, g4) holds A-rows 4 g4 + q
 #pragma unroll
-                                for (int jj = 0; jj < 8; ++jj) hp[b][c][jj] = 0u;
-                            }
-                        }
-                    }
-                }
-                float y0[NB], y1[NB];
+            for (int q = 0; q < 4; ++q) acc[q] += dpp_mov<0xB1>(acc[q]);
+            if ((col & 1) == 0 && rank >= 0) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-                    for (int c = 0; c < NCHP; ++c) {
-                        const float d = dot8(buf[s][c], hp[b][c], 0.f);
-                        if (lane + 64 * c < K8) a0 += d;
-                        else a1 += d;
-                    }
-                    y0[b] = wave_sum(a0);
-                    y1[b] = wave_sum(a1);
-                }
-                const int nx = q + PF;
-                if (q0 + PF < nmine) load_row<NCHP>(buf[s], pairptr(nx < last ? nx : last), 2 * K8);
-                if (q < nmine && lane < 2) {
-                    const int r = 2 * (q % npps) + lane;
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const int rank = (b < B) ? rt->slot_rank[sl][b] : -1;
-                        if (rank >= 0) sY[(b * K + rank) * nrows + r] = lane == 0 ? y0[b] : y1[b];
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int v = 16 * grp + 4 * g4 + q;
+                    const int jl = v / rd, r = v - jl * rd;
+                    if (jl == jc && r < nrows) sY[(bc * K + rank) * nrows + r] = acc[q];
                 }
             }
         }
@@ -822,7 +810,7 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
             uint4 gn[NCH];
             load_gain<NCH>(gn, p.final_norm, H);
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, gn, p.eps);
+            load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, gn, p.eps, p.inv_h);
         },
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
@@ -842,9 +830,9 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
 
 // Compile-time shape of a kernel build: 16-byte chunks per lane per row
 // (ceil(K / 512)) for the three reduction lengths in the model -- hidden
-// size H, attention width Hq*D and expert width I -- the head size, the
-// 16-byte chunks per lane of a pair of expert rows (ceil(I / 256)) and the
-// router logits per lane (ceil(E / 64)). Each
+// size H, attention width Hq*D and expert width I -- the head size,
+// ceil(I / 256) (the down tile runs at most 8 times that many 32-wide
+// k-steps) and the router logits per lane (ceil(E / 64)). Each
 // supported model gets its own kernels, so each tile is compiled only for
 // the reduction lengths it actually sees and register allocation is sized
 // per tile, not for every possible shape.
@@ -869,7 +857,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
         case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
         case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 7 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
-        case OP_DOWN: return tile_down<S::NCHP_I, (NB == 1 ? 8 : 4), NB, S::NE>(t, cx);
+        case OP_DOWN: return tile_down<8 * S::NCHP_I, NB, S::NE>(t, cx);
         case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
         default: return false;
     }
