@@ -198,7 +198,10 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
 // ------------------------------------------------------ counter protocol
 
 __device__ __forceinline__ void raise_error(const Params& p, int32_t code, int32_t detail, bool abort) {
+    // operands made opaque here, on the rare error path: as constants they
+    // would be hoisted into registers held across the whole task loop
     int32_t expected = 0;
+    asm volatile("" : "+v"(code), "+v"(expected));
     if (__hip_atomic_compare_exchange_strong(p.err, &expected, code, __ATOMIC_RELAXED,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
         __hip_atomic_store(p.err + 1, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -233,10 +236,12 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 // device-scope loads; the barrier then orders every thread's later loads
 // after the observation. Returns false if the step was aborted (watchdog
 // here or elsewhere). Records when the wait ended in *t_wait (thread 0).
-__device__ __forceinline__ uint32_t counter_sum(const Params& p, int ctr) {
+__device__ __forceinline__ uint32_t counter_line(const Params& p, int ctr) {
     const int lane = tid_() & 63;
     const uint32_t* c = p.ctr + ((int64_t)ctr * kCtrSub + (lane & (kCtrSub - 1))) * kCtrStride;
-    const uint32_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t line_sum(uint32_t v) {
     uint32_t s = 0;
 #pragma unroll
     for (int j = 0; j < kCtrSub; ++j) s += (uint32_t)__builtin_amdgcn_readlane((int)v, j);
@@ -247,10 +252,10 @@ __device__ bool block_wait(const Params& p, int ctr, int target, uint64_t* t_wai
     if (p.perop || ctr < 0) return true;
     int ok = 1;
     if (tid_() < 64) {
-        if (counter_sum(p, ctr) < (uint32_t)target) {
+        if (line_sum(counter_line(p, ctr)) < (uint32_t)target) {
             const uint64_t t0 = wall_clock64();
             uint32_t it = 0;
-            while (counter_sum(p, ctr) < (uint32_t)target) {
+            while (line_sum(counter_line(p, ctr)) < (uint32_t)target) {
                 __builtin_amdgcn_s_sleep(1);
                 if ((++it & 31u) == 0) {
                     if (__hip_atomic_load(p.err + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
@@ -402,6 +407,50 @@ __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine,
             const int nx = i + PF;
             if (i0 + PF < nmine) load_row<NCH>(buf[s], rowptr(nx < last ? nx : last), K8);
             if (i < nmine) emit(i, acc);
+        }
+    }
+}
+
+// Instruction-cache warm-up. A tile's code after its dependency wait has
+// usually been evicted since the tile type last ran on this compute unit, so
+// it would run on cold instruction fetches exactly when it is on the
+// critical path. gemv_rows_warm runs the same instructions twice: pass 0
+// before the wait on dummy activations (results dropped), pass 1 for real.
+// ready(pass) fills hx: in pass 0 from a source that is not an exchange
+// buffer (no early read may cache a line before its producer writes it), in
+// pass 1 after the dependency wait. The pass loop is kept rolled so both
+// passes execute one copy of the code.
+template <int NCH, int PF, int NB, class RowPtr, class Ready, class Emit>
+__device__ __forceinline__ void gemv_rows_warm(uint32_t (&hx)[NB][NCH][8], int nmine, int K8, RowPtr rowptr,
+                                               Ready ready, Emit emit) {
+    if (nmine <= 0) {
+        ready(1);
+        return;
+    }
+    uint4 buf[PF][NCH];
+    const int last = nmine - 1;
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], rowptr(s < last ? s : last), K8);
+#pragma clang loop unroll(disable)
+    for (int pass = 0; pass < 2; ++pass) {
+        ready(pass);
+        for (int i0 = 0; i0 < nmine; i0 += PF) {
+#pragma unroll
+            for (int s = 0; s < PF; ++s) {
+                const int i = i0 + s;
+                float acc[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], hx[b][c], a);
+                    acc[b] = wave_sum(a);
+                }
+                const int nx = i + PF;
+                if (pass == 1 && i0 + PF < nmine) load_row<NCH>(buf[s], rowptr(nx < last ? nx : last), K8);
+                if (pass == 1 && i < nmine) emit(i, acc);
+            }
+            if (pass == 0) break;   // the first PF rows are enough to warm the loop body
         }
     }
 }

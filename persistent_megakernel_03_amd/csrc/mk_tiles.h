@@ -119,14 +119,19 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
     };
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     bool ok = true;
-    gemv_stream<NCH, PF, NB>(
-        nmine, H >> 3, [&](int i) { return W + (int64_t)phys(v0 + wave + i * NWAVES) * H; },
-        [&](float(&h)[NB][NCH][8]) {
-            uint4 gn[NCH];
-            load_gain<NCH>(gn, wptr(p, l, W_ATTN_NORM), H);
-            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-            load_x<NCH, NB>(h, x_at(p, 2 * l), H, p.B, H, gn, p.eps, p.inv_h);
-            mark(cx, 0);
+    uint4 gn[NCH];
+    load_gain<NCH>(gn, wptr(p, l, W_ATTN_NORM), H);
+    uint32_t hx[NB][NCH][8];
+    gemv_rows_warm<NCH, PF, NB>(
+        hx, nmine, H >> 3, [&](int i) { return W + (int64_t)phys(v0 + wave + i * NWAVES) * H; },
+        [&](int pass) {
+            // pass 0 reads the layer's weight matrix as dummy activations
+            if (pass) ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            const float* src = pass ? x_at(p, 2 * l) : reinterpret_cast<const float*>(W);
+            float h[NB][NCH][8];
+            load_x<NCH, NB>(h, src, H, p.B, H, gn, p.eps, p.inv_h);
+            split_x<NB, NCH>(h, hx);
+            if (pass) mark(cx, 0);
         },
         [&](int i, const float(&acc)[NB]) {
             if (lane == 0) {
@@ -447,7 +452,9 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
 // o = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c with M = max_c m_c
 // (the softmax over all cached tokens, split by chunks). Each thread sums a
 // fixed set of chunks for four dimensions, then the sets are added in a fixed
-// order, so the result does not depend on timing.
+// order, so the result does not depend on timing. The thread's first kPre
+// chunk partials are requested together with the (m, l) pairs, so the merge
+// costs one memory round trip.
 template <int D>
 __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
@@ -455,6 +462,7 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     const int tid = tid_(), lane = tid & 63, wave = tid >> 6;
     constexpr int NQ = D / 4;          // float4 columns
     constexpr int NPH = NT / NQ;       // chunk phases
+    constexpr int kPre = 12;           // chunks per thread fetched up front
     float* sred = reinterpret_cast<float*>(cx.lds);           // [NWAVES][2] reductions
     float* coef = sred + 16;                                  // [nch]
     float* sacc = coef + ((p.max_chunks + 3) & ~3);           // [NPH][D]
@@ -462,16 +470,40 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     const int64_t row = (int64_t)b * p.Hq + h;
     const float* ml = ml_at(p, l) + row * ml_row(p);
     const float* po = part_at(p, l) + row * p.max_chunks * D;
+    const int q = tid % NQ, ph = tid / NQ;
+    float4 pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int c = ph + k * NPH;
+        pre[k] = c < nch ? ldf4(po + (int64_t)c * D + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // (m, l) of this thread's chunks
+    float mv[2], lv[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int c = tid + k * NT;
+        mv[k] = c < nch ? ld_dev(ml + 2 * c) : -INFINITY;
+        lv[k] = c < nch ? ld_dev(ml + 2 * c + 1) : 0.f;
+    }
     // M = max_c m_c
-    float mx = -INFINITY;
-    for (int c = tid; c < nch; c += NT) mx = fmaxf(mx, ld_dev(ml + 2 * c));
+    float mx = fmaxf(mv[0], mv[1]);
+    for (int c = tid + 2 * NT; c < nch; c += NT) mx = fmaxf(mx, ld_dev(ml + 2 * c));
     mx = wave_max(mx);
     if (lane == 0) sred[wave] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
     // L = sum_c exp(m_c - M) l_c
     float ls = 0.f;
-    for (int c = tid; c < nch; c += NT) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int c = tid + k * NT;
+        if (c < nch) {
+            const float e = expf(mv[k] - mx);
+            coef[c] = e;
+            ls += e * lv[k];
+        }
+    }
+    for (int c = tid + 2 * NT; c < nch; c += NT) {
         const float e = expf(ld_dev(ml + 2 * c) - mx);
         coef[c] = e;
         ls += e * ld_dev(ml + 2 * c + 1);
@@ -481,22 +513,18 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     __syncthreads();
     const float inv = 1.0f / (((sred[NWAVES] + sred[NWAVES + 1]) + sred[NWAVES + 2]) + sred[NWAVES + 3]);
     mark(cx, 0);
-    // o[d] = sum_c coef_c o_c[d] * inv
-    const int q = tid % NQ, ph = tid / NQ;
+    // o[d] = sum_c coef_c o_c[d] * inv, chunks ph, ph + NPH, ... in order
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int c = ph;
-    for (; c + 3 * NPH < nch; c += 4 * NPH) {
-        const float4 v0 = ldf4(po + (int64_t)c * D + 4 * q);
-        const float4 v1 = ldf4(po + (int64_t)(c + NPH) * D + 4 * q);
-        const float4 v2 = ldf4(po + (int64_t)(c + 2 * NPH) * D + 4 * q);
-        const float4 v3 = ldf4(po + (int64_t)(c + 3 * NPH) * D + 4 * q);
-        const float w0 = coef[c], w1 = coef[c + NPH], w2 = coef[c + 2 * NPH], w3 = coef[c + 3 * NPH];
-        acc.x = fmaf(w0, v0.x, acc.x); acc.y = fmaf(w0, v0.y, acc.y); acc.z = fmaf(w0, v0.z, acc.z); acc.w = fmaf(w0, v0.w, acc.w);
-        acc.x = fmaf(w1, v1.x, acc.x); acc.y = fmaf(w1, v1.y, acc.y); acc.z = fmaf(w1, v1.z, acc.z); acc.w = fmaf(w1, v1.w, acc.w);
-        acc.x = fmaf(w2, v2.x, acc.x); acc.y = fmaf(w2, v2.y, acc.y); acc.z = fmaf(w2, v2.z, acc.z); acc.w = fmaf(w2, v2.w, acc.w);
-        acc.x = fmaf(w3, v3.x, acc.x); acc.y = fmaf(w3, v3.y, acc.y); acc.z = fmaf(w3, v3.z, acc.z); acc.w = fmaf(w3, v3.w, acc.w);
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int c = ph + k * NPH;
+        if (c < nch) {
+            const float w = coef[c];
+            acc.x = fmaf(w, pre[k].x, acc.x); acc.y = fmaf(w, pre[k].y, acc.y);
+            acc.z = fmaf(w, pre[k].z, acc.z); acc.w = fmaf(w, pre[k].w, acc.w);
+        }
     }
-    for (; c < nch; c += NPH) {
+    for (int c = ph + kPre * NPH; c < nch; c += NPH) {
         const float4 v = ldf4(po + (int64_t)c * D + 4 * q);
         const float w = coef[c];
         acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y); acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
