@@ -148,6 +148,18 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
     const u32x4_t v = *(const MK_GLOBAL u32x4_t*)p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Streamed data read once per step (weights, cache pages): non-temporal
+// loads, so they do not displace the activations and counters that many
+// workgroups share in the L2 and the last-level cache.
+__device__ __forceinline__ uint4 ld16s(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load((const MK_GLOBAL u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8s(const void* p) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_nontemporal_load((const MK_GLOBAL u32x2_t*)p);
+    return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ uint2 ld8(const void* p) {
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     const u32x2_t v = *(const MK_GLOBAL u32x2_t*)p;
@@ -367,7 +379,7 @@ __device__ __forceinline__ void load_row(uint4 (&w)[NCH], const uint16_t* row, i
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int ch = lane + 64 * c;
-        w[c] = ld16(row + (ch < K8 ? ch : K8 - 1) * 8);
+        w[c] = ld16s(row + (ch < K8 ? ch : K8 - 1) * 8);
     }
 }
 

@@ -201,7 +201,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
             if (tk < t_old) {
                 const uint16_t* kb = p.k_pool + page * hstride + (tk & 15) * D + quad * 8;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) kf[i][db] = ld16(kb + db * 32);
+                for (int db = 0; db < NDB; ++db) kf[i][db] = ld16s(kb + db * 32);
             } else {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) kf[i][db] = make_uint4(0u, 0u, 0u, 0u);
@@ -210,7 +210,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
             if (tv < t_old) {
                 const uint16_t* vb = p.v_pool + page * hstride + (tv & 15);
 #pragma unroll
-                for (int dv = 0; dv < NDV; ++dv) vf[i][dv] = ld8(vb + (int64_t)(dv * 16 + col) * 16);
+                for (int dv = 0; dv < NDV; ++dv) vf[i][dv] = ld8s(vb + (int64_t)(dv * 16 + col) * 16);
             } else {
 #pragma unroll
                 for (int dv = 0; dv < NDV; ++dv) vf[i][dv] = make_uint2(0u, 0u);
@@ -740,7 +740,7 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
         const int e = rt->slot_e[live ? wave + NWAVES * jl : 0];
         const uint16_t* a = Wd + ((int64_t)e * p.H + h0 + (live ? r : 0)) * I + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) wb[ks] = ld16(a + 32 * (ks < nks ? ks : nks - 1));
+        for (int ks = 0; ks < KS; ++ks) wb[ks] = ld16s(a + 32 * (ks < nks ? ks : nks - 1));
     };
     if (ngrp > 0) load_grp(0);
     const bool ok = block_wait(p, t.ctr, t.target, cx.t_wait);
