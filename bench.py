@@ -193,7 +193,7 @@ def main():
         "config": {"workload": f"30B-A3B synthetic MoE decode, batch {B}, {ctx} cached tokens, greedy",
                    "batch": B, "context": ctx, "layers": cfg["n_layers"], "experts": cfg["n_experts"],
                    "top_k": cfg["top_k"], "parallelism": "single GPU",
-                   "precision": "BF16 weights and KV, fp32 activations and accumulation"},
+                   "precision": "BF16 weights and KV; fp32 activations, entering weight products as two BF16 parts; fp32 accumulation"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(B, ctx),
                      "kernel": "k_persistent (one launch per step)", "bytes_per_launch": bytes_step,
