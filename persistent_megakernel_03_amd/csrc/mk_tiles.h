@@ -432,13 +432,25 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     __syncthreads();
     float* part = part_at(p, l) + ((int64_t)b * p.Hq + g * G) * p.max_chunks * D;
     float* ml = ml_at(p, l) + ((int64_t)b * p.Hq + g * G) * ml_row(p);
-    for (int i = tid; i < G * D; i += NT) {
-        const int h = i / D, d = i - h * D;
-        float o = 0.f;
+    // each thread: four consecutive dimensions of one head, all LDS reads
+    // issued before the sums (the same per-output order as one at a time)
+    for (int i4 = tid; i4 < G * (D / 4); i4 += NT) {
+        const int h = i4 / (D / 4), d0 = (i4 - h * (D / 4)) * 4;
+        float f[NWAVES], ov[NWAVES][4];
 #pragma unroll
-        for (int w = 0; w < NWAVES; ++w) o += sF[w * 16 + h] * sO[(w * 16 + h) * (D + 1) + d];
-        st_dev(part + ((int64_t)h * p.max_chunks + c) * D + d, o);
-        if (d == 0) {
+        for (int w = 0; w < NWAVES; ++w) {
+            f[w] = sF[w * 16 + h];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ov[w][j] = sO[(w * 16 + h) * (D + 1) + d0 + j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float o = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) o += f[w] * ov[w][j];
+            st_dev(part + ((int64_t)h * p.max_chunks + c) * D + d0 + j, o);
+        }
+        if (d0 == 0) {
             st_dev(ml + (int64_t)h * ml_row(p) + 2 * c, sMh[h]);
             st_dev(ml + (int64_t)h * ml_row(p) + 2 * c + 1, sLh[h]);
         }
@@ -534,8 +546,12 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     mark(cx, 1);
     float* out = attout_at(p, l) + row * D;
     for (int d = tid; d < D; d += NT) {
+        float v[NPH];
+#pragma unroll
+        for (int k = 0; k < NPH; ++k) v[k] = sacc[k * D + d];
         float s = 0.f;
-        for (int k = 0; k < NPH; ++k) s += sacc[k * D + d];
+#pragma unroll
+        for (int k = 0; k < NPH; ++k) s += v[k];
         st_dev(out + d, s * inv);
     }
     block_signal(p, t.signal);
@@ -814,8 +830,16 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     float* xout = x_at(p, 2 * l + 2);
     if (tid < B * nrows) {
         const int b = tid / nrows, r = tid - b * nrows;
+        float wv[kMaxTopK], yv[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            wv[j] = j < K ? rt->w[b][j] : 0.f;
+            yv[j] = j < K ? sY[(b * K + j) * nrows + r] : 0.f;
+        }
         float acc = 0.f;
-        for (int j = 0; j < K; ++j) acc += rt->w[b][j] * sY[(b * K + j) * nrows + r];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < K) acc += wv[j] * yv[j];
         st_dev(xout + (int64_t)b * p.H + h0 + r, xres + acc);
     }
     block_signal(p, t.signal);
