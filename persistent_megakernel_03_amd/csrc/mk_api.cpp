@@ -53,8 +53,8 @@ constexpr int kMaxChunksCap = 512;
 constexpr int kStageSlots = 4;
 
 struct Layout {
-    size_t err, banks, x, qkv, att_part, att_ml, att_out, rlogits, route_ids, route_w, act, wtab, step, tasks, wg_off,
-        level_tasks, trace, total;
+    size_t err, banks, x, qkv, att_part, att_ml, att_out, rlogits, route_ids, route_w, act, rtab, ybuf, wtab, step,
+        tasks, wg_off, level_tasks, trace, total;
     int64_t bank_words;
     int max_chunks;
     int64_t cap_tasks;
@@ -98,7 +98,10 @@ std::string check_dims(const mk_dims& d) {
     if (d.top_k > 8 || d.top_k > d.n_experts) return "top_k must be <= 8 and <= n_experts";
     if (d.n_experts > 256) return "n_experts must be <= 256";
     if (d.hidden % 8 || d.moe_inter % 8) return "hidden and moe_inter must be multiples of 8";
-    if (d.max_batch > kMaxBatchValu) return "max_batch above what this build supports";
+    if (d.max_batch > kMaxBatchMM) return "max_batch above 64";
+    if (d.max_batch > kMaxBatchValu &&
+        (d.hidden % 128 || (d.n_q_heads * d.head_dim) % 128 || d.moe_inter % 32))
+        return "batches above 2 need hidden and n_q_heads*head_dim multiples of 128, moe_inter of 32";
     if (find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts) < 0)
         return "no kernel build for this (hidden, attention width, expert width, head_dim)";
     return std::string();
@@ -141,6 +144,10 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
     L.route_ids = take((size_t)d.n_layers * B * d.top_k * 4);
     L.route_w = take((size_t)d.n_layers * B * d.top_k * 4);
     L.act = take(Ln * pad64(B * d.top_k * d.moe_inter) * 4);
+    // batches of 3+: routing tables and per-(token, rank) expert outputs
+    const bool mm = d.max_batch > kMaxBatchValu;
+    L.rtab = take(mm ? Ln * rtab_words(d.n_experts, d.top_k, d.max_batch) * 4 : 0);
+    L.ybuf = take(mm ? Ln * pad64(B * d.top_k * H) * 4 : 0);
     L.wtab = take((size_t)d.n_layers * W_NKINDS * 8);
     // per-step arrays: positions, chunk counts, rotary table, block tables
     L.step_bytes = align256((size_t)B * 4) * 2 + align256((size_t)B * d.head_dim * 4) +
@@ -164,9 +171,10 @@ struct mk_handle {
     int wg_per_cu = 0;
     int n_wg = 0;
     int shape = -1;
+    // [1], [2]: the one- and two-token kernels; [0]: batches of 3+ (if max_batch > 2)
     KernelPair kern[kMaxBatchValu + 1];
-    size_t lds_bytes = 0;
-    int general = 0;
+    size_t lds_bytes[kMaxBatchValu + 1] = {0, 0, 0};
+    int general[kMaxBatchValu + 1] = {0, 0, 0};
     Layout lay;
     char* ws = nullptr;
     int bank = 0;
@@ -240,7 +248,8 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         h->device = device;
         h->n_cu = o.n_cu_override > 0 ? o.n_cu_override : prop.multiProcessorCount;
         h->shape = find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts);
-        for (int nb = 1; nb <= kMaxBatchValu; ++nb)
+        const bool mm = d.max_batch > kMaxBatchValu;
+        for (int nb = mm ? 0 : 1; nb <= kMaxBatchValu; ++nb)
             if (!get_kernels(h->shape, nb, &h->kern[nb])) return fail(MK_ERR_UNSUPPORTED, "no kernels");
 
         // LDS: general region (attention tiles + query fragments, combine
@@ -256,18 +265,21 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         // down tile: its gate/up activations [B][k][I] fp32 at the start of
         // the general region, its output staging at the end
         const size_t ystage = (size_t)2 * 8 * 64 * 4;
-        const size_t act = (size_t)d.max_batch * d.top_k * d.moe_inter * 4;
-        const size_t general = align256(std::max(std::max(attn, comb), act) + ystage);
-        h->general = (int)general;
-        h->lds_bytes = general + 1024 + 1024;
-        if (h->lds_bytes > (size_t)prop.sharedMemPerBlock && h->lds_bytes > 160 * 1024)
-            return fail(MK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", h->lds_bytes);
-        for (int nb = 1; nb <= kMaxBatchValu; ++nb) MK_HIP(set_kernel_attributes(h->kern[nb], h->lds_bytes));
-        int occ = 0;
-        for (int nb = 1; nb <= d.max_batch; ++nb) {
+        const size_t act = (size_t)std::min(d.max_batch, kMaxBatchValu) * d.top_k * d.moe_inter * 4;
+        const size_t gen_v = align256(std::max(std::max(attn, comb), act) + ystage);
+        // matrix-core tiles: block-product partials or the routing tile's tables
+        const size_t gen_m = align256(std::max(std::max(attn, comb), (size_t)std::max(kMmLdsBytes, kRouteLdsBytes)));
+        int occ = 1 << 30;
+        for (int nb = mm ? 0 : 1; nb <= kMaxBatchValu; ++nb) {
+            h->general[nb] = (int)(nb == 0 ? gen_m : gen_v);
+            h->lds_bytes[nb] = h->general[nb] + 1024 + 1024;
+            if (h->lds_bytes[nb] > (size_t)prop.sharedMemPerBlock && h->lds_bytes[nb] > 160 * 1024)
+                return fail(MK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", h->lds_bytes[nb]);
+            MK_HIP(set_kernel_attributes(h->kern[nb], h->lds_bytes[nb]));
+            if (nb > d.max_batch) continue;
             int o2 = 0;
-            MK_HIP(persistent_occupancy(h->kern[nb], h->lds_bytes, &o2));
-            occ = nb == 1 ? o2 : std::min(occ, o2);
+            MK_HIP(persistent_occupancy(h->kern[nb], h->lds_bytes[nb], &o2));
+            occ = std::min(occ, o2);
         }
         if (occ < 1) return fail(MK_ERR_UNSUPPORTED, "persistent kernel does not fit on a compute unit");
         h->wg_per_cu = o.wg_per_cu > 0 ? std::min(o.wg_per_cu, occ) : std::min(occ, 2);
@@ -350,6 +362,8 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         p.route_ids = reinterpret_cast<int32_t*>(h->ws + h->lay.route_ids);
         p.route_w = reinterpret_cast<float*>(h->ws + h->lay.route_w);
         p.act = reinterpret_cast<float*>(h->ws + h->lay.act);
+        p.rtab = reinterpret_cast<int32_t*>(h->ws + h->lay.rtab);
+        p.ybuf = reinterpret_cast<float*>(h->ws + h->lay.ybuf);
         p.bank_words = h->lay.bank_words;
         p.cl = CounterLayout{d.n_layers, d.n_kv_heads, d.max_batch};
         p.err = reinterpret_cast<int32_t*>(h->ws + h->lay.err);
@@ -486,14 +500,16 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
         uint32_t* banks = reinterpret_cast<uint32_t*>(h->ws + h->lay.banks);
         p.ctr = banks + (int64_t)h->bank * h->lay.bank_words;
         p.ctr_other = banks + (int64_t)(1 - h->bank) * h->lay.bank_words;
-        const int nb = batch <= 1 ? 1 : 2;
+        const int nb = batch <= kMaxBatchValu ? batch : 0;
         const KernelPair& k = h->kern[nb];
+        const int general = h->general[nb];
+        const size_t lds_bytes = h->lds_bytes[nb];
         if (h->o.time_kernels) MK_HIP(hipEventRecord(h->t_begin, stream));
         if (h->o.mode == MK_MODE_MEGAKERNEL) {
             p.perop = 0;
             p.tasks = reinterpret_cast<const Task*>(h->ws + h->lay.tasks);
             p.wg_off = reinterpret_cast<const int32_t*>(h->ws + h->lay.wg_off);
-            MK_HIP(launch_persistent(k, p, h->general, h->lds_bytes, h->n_wg, stream));
+            MK_HIP(launch_persistent(k, p, general, lds_bytes, h->n_wg, stream));
         } else {
             p.perop = 1;
             p.tasks = reinterpret_cast<const Task*>(h->ws + h->lay.level_tasks);
@@ -502,7 +518,7 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
             const Plan& P2 = h->plan;
             for (int lv = 0; lv < P2.n_levels; ++lv) {
                 const int first = P2.level_off[lv], count = P2.level_off[lv + 1] - first;
-                if (count > 0) MK_HIP(launch_perop_level(k, p, h->general, h->lds_bytes, first, count, stream));
+                if (count > 0) MK_HIP(launch_perop_level(k, p, general, lds_bytes, first, count, stream));
             }
         }
         if (h->o.time_kernels) {

@@ -28,13 +28,29 @@ enum Op : int32_t {
     OP_COMBINE = 3, // merge one query head's chunk partials (log-sum-exp)
     OP_OPROJ = 4,   // output projection + residual
     OP_ROUTER = 5,  // fused RMSNorm + router logits
-    OP_GATEUP = 6,  // top-k + expert gate/up rows + SwiGLU
-    OP_DOWN = 7,    // top-k + expert down rows + weighted combine + residual
-    OP_LMHEAD = 8,  // fused final RMSNorm + LM-head rows
-    OP_COUNT = 9
+    OP_ROUTE = 6,   // batches of 3+: top-k of every token + per-expert token lists
+    OP_GATEUP = 7,  // expert gate/up rows + SwiGLU (batches of 1-2: also the top-k)
+    OP_DOWN = 8,    // expert down rows (batches of 1-2: + weighted combine + residual)
+    OP_MOESUM = 9,  // batches of 3+: weighted sum of the experts' outputs + residual
+    OP_LMHEAD = 10, // fused final RMSNorm + LM-head rows
+    OP_COUNT = 11
 };
 
-constexpr int kLevelsPerLayer = 7;  // QKV, ATTN, COMBINE, OPROJ, ROUTER, GATEUP, DOWN
+// QKV, ATTN, COMBINE, OPROJ, ROUTER, ROUTE, GATEUP, DOWN, MOESUM; ROUTE and
+// MOESUM have no tiles in the one- and two-token schedule.
+constexpr int kLevelsPerLayer = 9;
+
+// Largest batch of the matrix-vector (dot-product) tiles; larger batches run
+// every weight product on the matrix cores, up to kMaxBatchMM tokens.
+constexpr int kMaxBatchValu = 2;
+constexpr int kMaxBatchMM = 64;
+
+// LDS of the matrix-core tiles (general region): a block product's per-wave
+// partials [4][16][64] and sums of squares [4][64] fp32 plus 64 token-list
+// entries; the routing tile's token masks [256][2], ranks [64][256] (bytes)
+// and per-wave counts.
+constexpr int kMmLdsBytes = (4 * 16 * 64 + 4 * 64 + 64) * 4;
+constexpr int kRouteLdsBytes = 2 * 256 * 4 + kMaxBatchMM * 256 + 16;
 
 // Dependency level of an op in layer l (0 = embedding, last = LM head).
 inline int op_level(int op, int layer, int n_layers) {
@@ -64,7 +80,7 @@ enum WKind : int32_t {
 
 // Counter bank layout: one counter per 128-byte line. Per layer: one QKV
 // counter and one attention counter per KV group, then the combine, output
-// projection, router, gate/up and down counters.
+// projection, router, routing, gate/up, down and expert-sum counters.
 constexpr int kCtrStride = 32;  // uint32 words per counter line
 // Each counter is split over kCtrSub lines: a producer bumps the line of its
 // workgroup index modulo kCtrSub and a consumer sums them, so the hundreds of
@@ -73,15 +89,17 @@ constexpr int kCtrSub = 8;
 
 struct CounterLayout {
     int n_layers, n_kv_heads, max_batch;
-    MK_HD int per_layer() const { return 2 * n_kv_heads + 5; }
+    MK_HD int per_layer() const { return 2 * n_kv_heads + 7; }
     MK_HD int embed() const { return 0; }
     MK_HD int qkv(int l, int g) const { return 1 + l * per_layer() + g; }
     MK_HD int attn(int l, int g) const { return 1 + l * per_layer() + n_kv_heads + g; }
     MK_HD int combine(int l) const { return 1 + l * per_layer() + 2 * n_kv_heads; }
     MK_HD int oproj(int l) const { return combine(l) + 1; }
     MK_HD int router(int l) const { return combine(l) + 2; }
-    MK_HD int gateup(int l) const { return combine(l) + 3; }
-    MK_HD int down(int l) const { return combine(l) + 4; }
+    MK_HD int route(int l) const { return combine(l) + 3; }
+    MK_HD int gateup(int l) const { return combine(l) + 4; }
+    MK_HD int down(int l) const { return combine(l) + 5; }
+    MK_HD int moesum(int l) const { return combine(l) + 6; }
     MK_HD int n_main() const { return 1 + n_layers * per_layer(); }
     MK_HD int64_t bank_words() const { return ((int64_t)n_main() * kCtrSub * kCtrStride + 63) & ~(int64_t)63; }
 };
@@ -129,6 +147,8 @@ struct Params {
     int32_t* route_ids;  // [L][max_batch][K]
     float* route_w;      // [L][max_batch][K]
     float* act;          // [L][max_batch*K][I]
+    int32_t* rtab;       // [L][rtab_words]: batches of 3+, routing table (see rtab_words)
+    float* ybuf;         // [L][max_batch*K][H]: batches of 3+, each expert's output per (token, rank)
     uint32_t* ctr;       // this step's counter bank
     uint32_t* ctr_other; // the bank the next step uses (cleared by this step)
     int64_t bank_words;
@@ -138,6 +158,15 @@ struct Params {
     const int32_t* wg_off;
     uint64_t* trace;     // [n_tasks][4]
 };
+
+// Routing table of one layer for batches of 3+ (int32 words): [0] number of
+// distinct selected experts ("slots", ascending expert id); [64 + s] expert
+// of slot s; [64 + E + s] tokens routed to it; [64 + 2E + s*max_batch + c]
+// its c-th token as (token | rank << 16), rank = the expert's place in that
+// token's top-k; then the routing weights [max_batch][K] as fp32.
+MK_HD inline int64_t rtab_words(int E, int K, int max_batch) {
+    return pad64(64 + 2 * (int64_t)E + (int64_t)E * max_batch + (int64_t)max_batch * K);
+}
 
 // Device error codes (mirror mk_status values).
 constexpr int32_t kErrTimeout = -6;

@@ -8,7 +8,6 @@
 namespace mk {
 
 constexpr int kThreads = 256;   // workgroup size of every kernel
-constexpr int kMaxBatchValu = 2; // largest batch the matrix-vector tiles take
 
 // Kernels are compiled per model shape: the number of 16-byte chunks per lane
 // per row for the hidden size, the attention width and the expert width, the
@@ -19,6 +18,8 @@ struct KernelPair {
     const void* persistent;  // (Params, int general)
     const void* perop;       // (Params, int general, int first)
 };
+// nb = 1, 2: the one- and two-token builds; nb = 0: the build for batches of
+// 3 to kMaxBatchMM tokens.
 bool get_kernels(int shape, int nb, KernelPair* out);
 
 hipError_t set_kernel_attributes(const KernelPair& k, size_t lds_bytes);

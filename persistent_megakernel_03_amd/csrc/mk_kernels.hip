@@ -55,7 +55,10 @@ const int kShapes[][kKey] = {{1, 1, 1, 64, 1, 1}, {4, 8, 2, 128, 3, 2}};
 
 template <class S>
 void fill_pair(int nb, KernelPair* out) {
-    if (nb == 1) {
+    if (nb == 0) {
+        out->persistent = reinterpret_cast<const void*>(&k_persistent<S, 0>);
+        out->perop = reinterpret_cast<const void*>(&k_perop<S, 0>);
+    } else if (nb == 1) {
         out->persistent = reinterpret_cast<const void*>(&k_persistent<S, 1>);
         out->perop = reinterpret_cast<const void*>(&k_perop<S, 1>);
     } else {
@@ -77,7 +80,7 @@ int find_shape(int hidden, int attn_width, int moe_inter, int head_dim, int n_ex
 }
 
 bool get_kernels(int shape, int nb, KernelPair* out) {
-    if (nb < 1 || nb > kMaxBatchValu) return false;
+    if (nb < 0 || nb > kMaxBatchValu) return false;
     switch (shape) {
         case 0: fill_pair<ShapeSmall>(nb, out); return true;
         case 1: fill_pair<ShapeA3B>(nb, out); return true;
@@ -118,6 +121,10 @@ hipError_t launch_fill(uint32_t* dst, int64_t n, uint32_t v, hipStream_t stream)
     return hipGetLastError();
 }
 
+template __global__ void k_persistent<ShapeSmall, 0>(Params, int);
+template __global__ void k_persistent<ShapeA3B, 0>(Params, int);
+template __global__ void k_perop<ShapeSmall, 0>(Params, int, int);
+template __global__ void k_perop<ShapeA3B, 0>(Params, int, int);
 template __global__ void k_persistent<ShapeSmall, 1>(Params, int);
 template __global__ void k_persistent<ShapeSmall, 2>(Params, int);
 template __global__ void k_persistent<ShapeA3B, 1>(Params, int);

@@ -44,6 +44,12 @@ struct Tile {
 
 }  // namespace
 
+static void build_levels_valu(const ModelShape& s, const TileConfig& cfg, int n_wg, int B, const int32_t* positions,
+                              Plan& P, std::vector<std::vector<Tile>>& levels);
+static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg, int B, const int32_t* positions,
+                            Plan& P, std::vector<std::vector<Tile>>& levels);
+static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector<Tile>>& levels, Plan& P);
+
 void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down) {
     *rows_gu = cfg.rows_gateup;
     *rows_down = cfg.rows_down;
@@ -61,6 +67,15 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
     rg = ceil_div(rg, 4) * 4;
     *rows_gu = rg;
     *rows_down = rd;
+}
+
+void expert_rows_mm(const ModelShape& s, int n_wg, int S, int* rows_gu, int* down_groups) {
+    // gate/up: 16 rows per tile unless that makes more than four tiles per
+    // workgroup; down: 16-row blocks of the hidden size, the slots split into
+    // groups so that the down tiles cover about half the workgroups
+    *rows_gu = (int64_t)S * ceil_div(s.I, 16) <= 4 * (int64_t)n_wg ? 16 : 32;
+    const int nblk = ceil_div(s.H, 16);
+    *down_groups = std::max(1, std::min(S, n_wg / 2 / std::max(1, nblk)));
 }
 
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested) {
@@ -82,13 +97,27 @@ int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions,
 
 int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
     const int G = s.Hq / s.Hkv;
-    const int64_t per_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.rows_qkv) +
-                              (int64_t)s.max_batch * s.Hkv * s.max_chunks + (int64_t)s.max_batch * s.Hq +
+    const int bv = std::min(s.max_batch, kMaxBatchValu);
+    const int64_t attn = (int64_t)s.Hkv * s.max_chunks, comb = s.Hq;
+    const int64_t per_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.rows_qkv) + bv * (attn + comb) +
                               ceil_div(s.H, cfg.rows_o) +
                               ceil_div(s.E, cfg.rows_router) +
-                              (int64_t)std::min(s.E, s.max_batch * s.K) * ceil_div(s.I, cfg.rows_gateup) +
+                              (int64_t)std::min(s.E, bv * s.K) * ceil_div(s.I, cfg.rows_gateup) +
                               ceil_div(s.H, cfg.rows_down);
-    return 1 + (int64_t)s.L * per_layer + ceil_div(s.V, cfg.rows_lm);
+    int64_t n = 1 + (int64_t)s.L * per_layer + ceil_div(s.V, cfg.rows_lm);
+    if (s.max_batch > kMaxBatchValu) {
+        // matrix-core schedule: at most 2048 workgroups (down slot groups),
+        // gate/up tiles of at least 16 rows
+        const int S = std::min(s.E, s.max_batch * s.K);
+        const int64_t mm_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.mm_rows_qkv) +
+                                 s.max_batch * (attn + comb) + ceil_div(s.H, cfg.mm_rows_o) +
+                                 ceil_div(s.E, cfg.mm_rows_router) + 1 + (int64_t)S * ceil_div(s.I, 16) +
+                                 (int64_t)ceil_div(s.H, 16) * std::min(S, 1024) + ceil_div(s.H, cfg.mm_rows_sum);
+        const int64_t m = ceil_div(s.max_batch, cfg.mm_embed_tokens) + (int64_t)s.L * mm_layer +
+                          ceil_div(s.V, cfg.mm_rows_lm);
+        n = std::max(n, m);
+    }
+    return n;
 }
 
 std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int B, const int32_t* positions,
@@ -96,7 +125,6 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     if (n_wg <= 0) return "n_wg must be positive";
     if (B <= 0 || B > s.max_batch) return "batch out of range";
     const CounterLayout cl{s.L, s.Hkv, s.max_batch};
-    const int G = s.Hq / s.Hkv;
     Plan& P = *out;
     P = Plan();
     P.n_wg = n_wg;
@@ -112,6 +140,22 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     }
 
     std::vector<std::vector<Tile>> levels(P.n_levels);
+    if (B > kMaxBatchValu) {
+        build_levels_mm(s, cfg, n_wg, B, positions, P, levels);
+    } else {
+        build_levels_valu(s, cfg, n_wg, B, positions, P, levels);
+    }
+    place_tiles(cfg, n_wg, levels, P);
+    return std::string();
+}
+
+// The one- and two-token schedule: per layer QKV, attention, merge, output
+// projection, router, gate/up (each tile also computes the routing) and down
+// (which also sums the experts onto the residual).
+static void build_levels_valu(const ModelShape& s, const TileConfig& cfg, int n_wg, int B, const int32_t* positions,
+                       Plan& P, std::vector<std::vector<Tile>>& levels) {
+    const CounterLayout cl{s.L, s.Hkv, s.max_batch};
+    const int G = s.Hq / s.Hkv;
     auto add = [&](const Task& t, double bytes, int kind) { levels[t.level].push_back({t, bytes, kind}); };
 
     add(make_task(OP_EMBED, 0, 0, B, 0, 0, -1, 0, -1, 0, cl.embed(), 0), 2.0 * B * s.H, kStatic);
@@ -198,7 +242,116 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         add(make_task(OP_LMHEAD, 0, r0, r1, 0, 0, -1, 0, cl.down(s.L - 1), nd, -1, P.n_levels - 1),
             2.0 * (r1 - r0) * s.H, kStatic);
     }
+}
 
+// Batches of 3+: every weight product on the matrix cores. Per layer QKV,
+// attention, merge, output projection, router, routing (one tile), gate/up
+// over the routing table's slots, down per (16 hidden rows, slot group), and
+// the per-token expert sum.
+static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg, int B, const int32_t* positions,
+                     Plan& P, std::vector<std::vector<Tile>>& levels) {
+    const CounterLayout cl{s.L, s.Hkv, s.max_batch};
+    const int G = s.Hq / s.Hkv;
+    auto add = [&](const Task& t, double bytes, int kind) { levels[t.level].push_back({t, bytes, kind}); };
+
+    const int ne = ceil_div(B, cfg.mm_embed_tokens);
+    for (int i = 0; i < ne; ++i) {
+        const int b0 = i * cfg.mm_embed_tokens, b1 = std::min(B, b0 + cfg.mm_embed_tokens);
+        add(make_task(OP_EMBED, 0, b0, b1, 0, 0, -1, 0, -1, 0, cl.embed(), 0), 2.0 * (b1 - b0) * s.H, kStatic);
+    }
+    P.targets[cl.embed()] = ne;
+
+    const int grows = (G + 2) * s.D;
+    const int nq = ceil_div(grows, cfg.mm_rows_qkv);
+    const int no = ceil_div(s.H, cfg.mm_rows_o);
+    const int nr = ceil_div(s.E, cfg.mm_rows_router);
+    const int S = std::min(s.E, B * s.K);
+    int rows_gu = 16, Q = 1;
+    expert_rows_mm(s, n_wg, S, &rows_gu, &Q);
+    const int ngu = ceil_div(s.I, rows_gu);
+    const int nblk = ceil_div(s.H, 16);
+    const int nd = nblk * Q;
+    const int ns = ceil_div(s.H, cfg.mm_rows_sum);
+    const int nl = ceil_div(s.V, cfg.mm_rows_lm);
+    int total_chunks = 0;
+    for (int b = 0; b < B; ++b) total_chunks += P.n_chunks[b];
+
+    for (int l = 0; l < s.L; ++l) {
+        const int lv = 1 + kLevelsPerLayer * l;
+        const int in_ctr = l == 0 ? cl.embed() : cl.moesum(l - 1);
+        const int in_target = l == 0 ? ne : ns;
+        const int defer_ctr = l == 0 ? -1 : cl.gateup(l - 1);
+        const int defer_target = l == 0 ? 0 : S * ngu;
+        for (int g = 0; g < s.Hkv; ++g) {
+            for (int i = 0; i < nq; ++i) {
+                const int v0 = i * cfg.mm_rows_qkv, v1 = std::min(grows, v0 + cfg.mm_rows_qkv);
+                add(make_task(OP_QKV, l, g, v0, v1, 0, defer_ctr, defer_target, in_ctr, in_target, cl.qkv(l, g), lv),
+                    2.0 * (v1 - v0) * s.H, kStatic);
+            }
+            P.targets[cl.qkv(l, g)] = nq;
+        }
+        for (int b = 0; b < B; ++b) {
+            const int n = P.n_chunks[b];
+            for (int g = 0; g < s.Hkv; ++g)
+                for (int c = 0; c < n; ++c) {
+                    const int toks = std::min(P.chunk, positions[b] + 1 - c * P.chunk);
+                    add(make_task(OP_ATTN, l, b, g, c, n, defer_ctr, defer_target, cl.qkv(l, g), nq, cl.attn(l, g),
+                                  lv + 1),
+                        4.0 * toks * s.D, kStatic);
+                }
+        }
+        for (int g = 0; g < s.Hkv; ++g) P.targets[cl.attn(l, g)] = total_chunks;
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < s.Hq; ++h)
+                add(make_task(OP_COMBINE, l, b, h, P.n_chunks[b], 0, -1, 0, cl.attn(l, h / G), total_chunks,
+                              cl.combine(l), lv + 2),
+                    4.0 * P.n_chunks[b] * (s.D + 2), kDynamic);
+        P.targets[cl.combine(l)] = B * s.Hq;
+        for (int i = 0; i < no; ++i) {
+            const int r0 = i * cfg.mm_rows_o, r1 = std::min(s.H, r0 + cfg.mm_rows_o);
+            add(make_task(OP_OPROJ, l, r0, r1, 0, 0, -1, 0, cl.combine(l), B * s.Hq, cl.oproj(l), lv + 3),
+                2.0 * (r1 - r0) * s.Hq * s.D, kStatic);
+        }
+        P.targets[cl.oproj(l)] = no;
+        for (int i = 0; i < nr; ++i) {
+            const int r0 = i * cfg.mm_rows_router, r1 = std::min(s.E, r0 + cfg.mm_rows_router);
+            add(make_task(OP_ROUTER, l, r0, r1, 0, 0, -1, 0, cl.oproj(l), no, cl.router(l), lv + 4),
+                2.0 * (r1 - r0) * s.H, kStatic);
+        }
+        P.targets[cl.router(l)] = nr;
+        add(make_task(OP_ROUTE, l, 0, 1, 0, 0, -1, 0, cl.router(l), nr, cl.route(l), lv + 5), 4.0 * B * s.E,
+            kDynamic);
+        P.targets[cl.route(l)] = 1;
+        for (int sl = 0; sl < S; ++sl)
+            for (int i = 0; i < ngu; ++i) {
+                const int r0 = i * rows_gu, r1 = std::min(s.I, r0 + rows_gu);
+                add(make_task(OP_GATEUP, l, sl, r0, r1, 0, -1, 0, cl.route(l), 1, cl.gateup(l), lv + 6),
+                    4.0 * (r1 - r0) * s.H, kRouted);
+            }
+        P.targets[cl.gateup(l)] = S * ngu;
+        for (int q = 0; q < Q; ++q)
+            for (int i = 0; i < nblk; ++i) {
+                const int r0 = i * 16, r1 = std::min(s.H, r0 + 16);
+                add(make_task(OP_DOWN, l, r0, r1, q, Q, -1, 0, cl.gateup(l), S * ngu, cl.down(l), lv + 7),
+                    2.0 * ceil_div(S - q, Q) * (r1 - r0) * s.I, kRouted);
+            }
+        P.targets[cl.down(l)] = nd;
+        for (int i = 0; i < ns; ++i) {
+            const int r0 = i * cfg.mm_rows_sum, r1 = std::min(s.H, r0 + cfg.mm_rows_sum);
+            add(make_task(OP_MOESUM, l, r0, r1, 0, 0, -1, 0, cl.down(l), nd, cl.moesum(l), lv + 8),
+                4.0 * B * (s.K + 1) * (r1 - r0), kDynamic);
+        }
+        P.targets[cl.moesum(l)] = ns;
+    }
+    for (int i = 0; i < nl; ++i) {
+        const int r0 = i * cfg.mm_rows_lm, r1 = std::min(s.V, r0 + cfg.mm_rows_lm);
+        add(make_task(OP_LMHEAD, 0, r0, r1, 0, 0, -1, 0, cl.moesum(s.L - 1), ns, -1, P.n_levels - 1),
+            2.0 * (r1 - r0) * s.H, kStatic);
+    }
+}
+
+// Workgroup lists from the levels (see the comment inside).
+static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector<Tile>>& levels, Plan& P) {
     // Per-op order: level by level.
     P.level_off.assign(P.n_levels + 1, 0);
     for (int lv = 0; lv < P.n_levels; ++lv) {
@@ -260,7 +413,8 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
             end = std::max(end, fin);
             heap.push(s0);
         }
-        level_end[lv] = end;
+        // a level with no tiles ends with the one before it
+        level_end[lv] = tiles.empty() ? (lv > 0 ? level_end[lv - 1] : 0.0) : end;
     }
     P.model_us = level_end.back();
     P.wg_off.assign(n_wg + 1, 0);
@@ -268,7 +422,6 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
         P.wg_off[w + 1] = P.wg_off[w] + (int)lists[w].size();
         P.tasks.insert(P.tasks.end(), lists[w].begin(), lists[w].end());
     }
-    return std::string();
 }
 
 std::string validate_plan(const ModelShape& s, const Plan& P) {
@@ -315,10 +468,15 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         switch (t.op) {
             case OP_QKV: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
             case OP_ATTN: ranges[std::make_tuple(t.op, t.layer, t.a0, t.a1)].push_back({t.a2, t.a2 + 1}); break;
+            case OP_EMBED:
             case OP_OPROJ:
             case OP_ROUTER:
-            case OP_DOWN:
+            case OP_ROUTE:
+            case OP_MOESUM:
             case OP_LMHEAD: ranges[std::make_tuple(t.op, t.layer, 0, 0)].push_back({t.a0, t.a1}); break;
+            // one-/two-token down tiles carry their row count in a2 (the same for
+            // every tile); matrix-core down tiles their slot group
+            case OP_DOWN: ranges[std::make_tuple(t.op, t.layer, t.a2, 0)].push_back({t.a0, t.a1}); break;
             case OP_GATEUP: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
             case OP_COMBINE: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a1 + 1}); break;
             default: break;
@@ -336,10 +494,12 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         const int op = std::get<0>(kv.first);
         int want = 0;
         switch (op) {
+            case OP_EMBED: want = P.B; break;
+            case OP_ROUTE: want = 1; break;
             case OP_QKV: want = (G + 2) * s.D; break;
             case OP_ATTN: want = P.n_chunks[std::get<2>(kv.first)]; break;
             case OP_COMBINE: want = s.Hq; break;
-            case OP_OPROJ: case OP_DOWN: want = s.H; break;
+            case OP_OPROJ: case OP_DOWN: case OP_MOESUM: want = s.H; break;
             case OP_ROUTER: want = s.E; break;
             case OP_GATEUP: want = s.I; break;
             case OP_LMHEAD: want = s.V; break;

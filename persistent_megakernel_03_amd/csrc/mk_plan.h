@@ -32,6 +32,13 @@ struct TileConfig {
     int rows_gateup = 16;
     int rows_down = 4;
     int rows_lm = 64;
+    // batches of 3+ (matrix-core tiles): rows per tile
+    int mm_rows_qkv = 16;
+    int mm_rows_o = 8;
+    int mm_rows_router = 8;
+    int mm_rows_sum = 16;
+    int mm_rows_lm = 32;
+    int mm_embed_tokens = 4;
     int chunk = 0;  // attention chunk in tokens (multiple of 64); 0 = choose
     // timing model used to place tiles on workgroups
     double model_bw_bytes_per_us = 5.6e6;  // whole-device HBM bandwidth
@@ -60,6 +67,9 @@ struct Plan {
 // once: the down weights then stream alongside the gate/up weights instead of
 // after them. Otherwise the configured sizes.
 void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down);
+
+// Batches of 3+: rows per gate/up tile (16 or 32), down tiles' slot groups.
+void expert_rows_mm(const ModelShape& s, int n_wg, int S, int* rows_gu, int* down_groups);
 
 // Attention chunk length for these contexts (tokens, multiple of 64).
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested);

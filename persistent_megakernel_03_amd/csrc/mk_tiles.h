@@ -10,69 +10,10 @@
 // delay is between operations").
 #pragma once
 
-#include "mk_device.h"
+#include "mk_tile_ctx.h"
+#include "mk_tiles_mm.h"
 
 namespace mk {
-
-// LDS layout (dynamic shared memory), byte offsets.
-//   [0, kLdsRoute)            general region: attention scores/probabilities
-//                             and combine coefficients, or the down tile's
-//                             staged expert activations and outputs
-//   [kLdsRoute, +kLdsRouteSz) routing results
-//   then 512 bytes of per-tile scalars
-constexpr int kLdsRouteSz = 1024;
-constexpr int kMaxDownRows = 64;
-
-struct LdsMap {
-    int route;  // offset of RouteLds
-    int misc;   // offset of scalars
-};
-
-__device__ __forceinline__ RouteLds* route_lds(char* lds, int general_bytes) {
-    return reinterpret_cast<RouteLds*>(lds + general_bytes);
-}
-__device__ __forceinline__ int* misc_lds(char* lds, int general_bytes) {
-    return reinterpret_cast<int*>(lds + general_bytes + kLdsRouteSz);
-}
-
-struct TileCtx {
-    const Params& p;
-    char* lds;
-    int general;      // bytes of the general LDS region
-    uint64_t* t_wait; // trace: when the compute wait ended
-    uint64_t* marks;  // trace: four phase stamps inside the tile
-    const Task* next; // the workgroup's next task (persistent mode), else null
-};
-
-// Trace stamp k (0..3) of the current tile (thread 0, tracing on).
-__device__ __forceinline__ void mark(TileCtx& cx, int k) {
-    if (cx.p.trace_on && tid_() == 0) cx.marks[k] = wall_clock64();
-}
-
-// Per-layer slices of the exchange buffers, each padded to 256 bytes.
-__device__ __forceinline__ float* x_at(const Params& p, int idx) {
-    return p.x + (int64_t)idx * pad64((int64_t)p.max_batch * p.H);
-}
-__device__ __forceinline__ float* qkv_at(const Params& p, int l) {
-    return p.qkv + (int64_t)l * pad64((int64_t)p.max_batch * p.QKVD);
-}
-__device__ __forceinline__ float* part_at(const Params& p, int l) {
-    return p.att_part + (int64_t)l * pad64((int64_t)p.max_batch * p.Hq * p.max_chunks * p.D);
-}
-// (max, sum) pairs: one padded row of max_chunks pairs per (sequence, head)
-__device__ __forceinline__ int64_t ml_row(const Params& p) { return pad64(2 * (int64_t)p.max_chunks); }
-__device__ __forceinline__ float* ml_at(const Params& p, int l) {
-    return p.att_ml + (int64_t)l * p.max_batch * p.Hq * ml_row(p);
-}
-__device__ __forceinline__ float* attout_at(const Params& p, int l) {
-    return p.att_out + (int64_t)l * pad64((int64_t)p.max_batch * p.Hq * p.D);
-}
-__device__ __forceinline__ float* rlogits_at(const Params& p, int l) {
-    return p.rlogits + (int64_t)l * pad64((int64_t)p.max_batch * p.E);
-}
-__device__ __forceinline__ float* act_at(const Params& p, int l) {
-    return p.act + (int64_t)l * pad64((int64_t)p.max_batch * p.K * p.I);
-}
 
 // ------------------------------------------------------------------ embed
 
@@ -899,19 +840,38 @@ struct Pf {
     static constexpr int v = NB == 1 ? (NCH <= 2 ? 8 : (NCH <= 4 ? 4 : 2)) : (NCH <= 1 ? 8 : (NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1)));
 };
 
+// NB = 1, 2: the one- and two-token tiles; NB = 0: the matrix-core tiles of
+// batches of 3 or more (attention, its merge and the embedding are shared).
 template <class S, int NB>
 __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
-    switch (t.op) {
-        case OP_EMBED: return tile_embed(t, cx);
-        case OP_QKV: return tile_qkv<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 6 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
-        case OP_ATTN: return tile_attn<S::D>(t, cx);
-        case OP_COMBINE: return tile_combine<S::D>(t, cx);
-        case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
-        case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
-        case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 7 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
-        case OP_DOWN: return tile_down<8 * S::NCHP_I, NB, S::NE>(t, cx);
-        case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
-        default: return false;
+    if constexpr (NB == 0) {
+        switch (t.op) {
+            case OP_EMBED: return tile_embed(t, cx);
+            case OP_QKV: return tile_qkv_mm(t, cx);
+            case OP_ATTN: return tile_attn<S::D>(t, cx);
+            case OP_COMBINE: return tile_combine<S::D>(t, cx);
+            case OP_OPROJ: return tile_oproj_mm(t, cx);
+            case OP_ROUTER: return tile_router_mm(t, cx);
+            case OP_ROUTE: return tile_route<S::NE>(t, cx);
+            case OP_GATEUP: return tile_gateup_mm(t, cx);
+            case OP_DOWN: return tile_down_mm(t, cx);
+            case OP_MOESUM: return tile_moesum(t, cx);
+            case OP_LMHEAD: return tile_lmhead_mm(t, cx);
+            default: return false;
+        }
+    } else {
+        switch (t.op) {
+            case OP_EMBED: return tile_embed(t, cx);
+            case OP_QKV: return tile_qkv<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 6 : Pf<S::NCH_H, NB>::v), NB>(t, cx);
+            case OP_ATTN: return tile_attn<S::D>(t, cx);
+            case OP_COMBINE: return tile_combine<S::D>(t, cx);
+            case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
+            case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+            case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 7 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
+            case OP_DOWN: return tile_down<8 * S::NCHP_I, NB, S::NE>(t, cx);
+            case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
+            default: return false;
+        }
     }
 }
 

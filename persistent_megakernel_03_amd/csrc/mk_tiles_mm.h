@@ -1,0 +1,601 @@
+// mk_tiles_mm.h -- the tiles of a decode step for batches of 3 to 64 tokens.
+//
+// At these batches every weight product runs on the matrix cores (BF16 MFMA
+// 16x16x32, fp32 accumulate), still bounded by the weight stream: weights are
+// the A operand (16 rows per block), the batch's activations the B operand
+// (16 tokens per column block). As in the one- and two-token tiles, fp32
+// activations enter as two BF16 parts (hi = bf16(x), lo = bf16(x - hi)), each
+// its own MFMA into the same accumulator, so the products keep ~2^-17
+// relative activation precision and the routing decisions the oracle's fp32
+// products make. The pages build the step from ordinary tiled matrix
+// multiplications ("Cohere Publishes One-Kernel Server for North Mini Code,
+// Claims 1.58x vLLM Speedup", section "A hand-built approach to a specialized
+// server"), and continuous batching is part of the serving model they
+// describe (same page, opening section).
+//
+// Routing gets a level of its own here: one tile computes every token's top-k
+// and publishes, per selected expert ("slot", ascending expert id), the tokens
+// routed to it. Expert tiles then stream only the selected experts' rows. The
+// down tiles write each expert's output per (token, rank); a last level sums
+// them per token in top-k rank order onto the residual, so the result does
+// not depend on how tiles were placed.
+#pragma once
+
+#include "mk_tile_ctx.h"
+
+namespace mk {
+
+// ------------------------------------------------------------ exchange slices
+
+__device__ __forceinline__ int32_t* rtab_at(const Params& p, int l) {
+    return p.rtab + (int64_t)l * rtab_words(p.E, p.K, p.max_batch);
+}
+// routing weights of a layer inside its routing table: [max_batch][K] floats
+__device__ __forceinline__ float* rtab_w(const Params& p, int32_t* rt) {
+    return reinterpret_cast<float*>(rt + 64 + 2 * p.E + (int64_t)p.E * p.max_batch);
+}
+__device__ __forceinline__ float* ybuf_at(const Params& p, int l) {
+    return p.ybuf + (int64_t)l * pad64((int64_t)p.max_batch * p.K * p.H);
+}
+
+__device__ __forceinline__ void st_dev_i(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------- MFMA engine
+
+// Column blocks of 16 tokens: compile-time 1, 2 or 4, chosen per call.
+template <int N>
+struct Ncb {
+    static constexpr int v = N;
+};
+template <class F>
+__device__ __forceinline__ void with_ncb(int ncb, F&& f) {
+    if (ncb <= 1) f(Ncb<1>());
+    else if (ncb <= 2) f(Ncb<2>());
+    else f(Ncb<4>());
+}
+__device__ __forceinline__ int ncb_cols(int ncb) { return 16 * (ncb <= 1 ? 1 : (ncb <= 2 ? 2 : 4)); }
+
+// k-steps of 32 per load batch (two batches in flight).
+template <int NCB>
+struct MmPf {
+    static constexpr int v = NCB == 1 ? 4 : 2;
+};
+
+// One wave's product over `nsteps` k-steps of 32:
+//   acc[cb] += A(16 rows) * (g o X)(16 columns of block cb), ss[cb] += X^2,
+// X entering as two BF16 parts. Lane layout of the 16x16x32 MFMA: lane l
+// holds A[l%16][8(l/16) .. +7], B[8(l/16) .. +7][l%16], D[4(l/16) .. +3][l%16],
+// so `arow`, `xc` and `gain` are already offset to this lane's row or column
+// and its 8-element k slice; a null column is zero. The A rows of the first
+// two batches (and the gains) are issued before `ready()` is called, the
+// activations after it. Two load batches alternate, so one batch is always
+// in flight while the other is consumed.
+template <int NCB, bool GAIN, class Ready>
+__device__ __forceinline__ void mm_wave(const uint16_t* arow, const float* const (&xc)[NCB], const uint16_t* gain,
+                                        int nsteps, Ready&& ready, f32x4_t (&acc)[NCB], float (&ss)[NCB]) {
+    constexpr int PF = MmPf<NCB>::v;
+    uint4 a0[PF], a1[PF], g0[PF], g1[PF];
+    float4 x0[PF][NCB][2], x1[PF][NCB][2];
+    auto loadA = [&](uint4(&a)[PF], uint4(&g)[PF], int bt) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int s = bt * PF + j;
+            if (s < nsteps) {
+                a[j] = ld16s(arow + 32 * s);
+                if (GAIN) g[j] = ld16(gain + 32 * s);
+            }
+        }
+    };
+    auto loadX = [&](float4(&x)[PF][NCB][2], int bt) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int s = bt * PF + j;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (s < nsteps && xc[cb] != nullptr) {
+                    x[j][cb][0] = ldf4(xc[cb] + 32 * s);
+                    x[j][cb][1] = ldf4(xc[cb] + 32 * s + 4);
+                } else {
+                    x[j][cb][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    x[j][cb][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+        }
+    };
+    auto compute = [&](const uint4(&a)[PF], const uint4(&g)[PF], const float4(&x)[PF][NCB][2], int bt) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            if (bt * PF + j < nsteps) {
+                float gv[8];
+                if (GAIN) {
+                    const uint4 w = g[j];
+                    gv[0] = bflo(w.x); gv[1] = bfhi(w.x); gv[2] = bflo(w.y); gv[3] = bfhi(w.y);
+                    gv[4] = bflo(w.z); gv[5] = bfhi(w.z); gv[6] = bflo(w.w); gv[7] = bfhi(w.w);
+                }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float v[8] = {x[j][cb][0].x, x[j][cb][0].y, x[j][cb][0].z, x[j][cb][0].w,
+                                  x[j][cb][1].x, x[j][cb][1].y, x[j][cb][1].z, x[j][cb][1].w};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        ss[cb] = fmaf(v[q], v[q], ss[cb]);
+                        if (GAIN) v[q] *= gv[q];
+                    }
+                    uint32_t h[8];
+                    split8(v, h);
+                    acc[cb] = mfma16x16x32(a[j], make_uint4(h[0], h[1], h[2], h[3]), acc[cb]);
+                    acc[cb] = mfma16x16x32(a[j], make_uint4(h[4], h[5], h[6], h[7]), acc[cb]);
+                }
+            }
+        }
+    };
+    const int nb = (nsteps + PF - 1) / PF;
+    loadA(a0, g0, 0);
+    if (nb > 1) loadA(a1, g1, 1);
+    ready();
+    loadX(x0, 0);
+    for (int bt = 0; bt < nb; bt += 2) {
+        if (bt + 1 < nb) loadX(x1, bt + 1);
+        compute(a0, g0, x0, bt);
+        if (bt + 2 < nb) {
+            loadA(a0, g0, bt + 2);
+            loadX(x0, bt + 2);
+        }
+        if (bt + 1 < nb) {
+            compute(a1, g1, x1, bt + 1);
+            if (bt + 3 < nb) loadA(a1, g1, bt + 3);
+        }
+    }
+}
+
+// LDS of a block product, at the start of the general region: per-wave
+// partial products [4][16][16 NCB] and sums of squares [4][16 NCB].
+constexpr int kMmPartFloats = NWAVES * 16 * 64;
+constexpr int kMmSsFloats = NWAVES * 64;
+static_assert(kMmLdsBytes == (kMmPartFloats + kMmSsFloats + 64) * 4, "matrix-core LDS size");
+
+// A product of `na` (1, 2 or 4) blocks of 16 weight rows with 16 NCB
+// activation columns over length K, by the whole workgroup: wave w takes row
+// block w % na and K part w / na (4 / na parts). arow(blk, r) is the start of
+// A row r of block blk, xcol(c) that of activation column c (null: absent),
+// gain the RMSNorm gain (GAIN) applied to the activations. The partial sums
+// land in LDS; mm_c / mm_ss read the totals, summed over K parts in order.
+template <int NCB, bool GAIN, class ARow, class XCol, class Ready>
+__device__ __forceinline__ void mm_block(int na, int K, ARow&& arow, XCol&& xcol, const uint16_t* gain, Ready&& ready,
+                                         float* sPart, float* sSS) {
+    const int tid = tid_(), wave = tid >> 6, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
+    const int blk = wave % na, kp = wave / na, KP = NWAVES / na;
+    const int kl = K / KP, k0 = kp * kl + 8 * g4;
+    const uint16_t* ar = arow(blk, col) + k0;
+    const float* xc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const float* q = xcol(16 * cb + col);
+        xc[cb] = q != nullptr ? q + k0 : nullptr;
+    }
+    f32x4_t acc[NCB];
+    float ss[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ss[cb] = 0.f;
+    }
+    mm_wave<NCB, GAIN>(ar, xc, GAIN ? gain + k0 : nullptr, kl >> 5, ready, acc, ss);
+    constexpr int NC = 16 * NCB;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sPart[(wave * 16 + 4 * g4 + q) * NC + 16 * cb + col] = acc[cb][q];
+        float s = ss[cb];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (g4 == 0) sSS[wave * NC + 16 * cb + col] = s;
+    }
+    __syncthreads();
+}
+
+// Total of row r of block blk, column c (nc = 16 NCB columns).
+__device__ __forceinline__ float mm_c(const float* sPart, int nc, int na, int blk, int r, int c) {
+    float v = 0.f;
+    for (int kp = 0; kp < NWAVES / na; ++kp) v += sPart[((kp * na + blk) * 16 + r) * nc + c];
+    return v;
+}
+// Sum of squares of activation column c over the whole K.
+__device__ __forceinline__ float mm_ss(const float* sSS, int nc, int na, int c) {
+    float v = 0.f;
+    for (int kp = 0; kp < NWAVES / na; ++kp) v += sSS[kp * na * nc + c];
+    return v;
+}
+// RMSNorm scale 1 / sqrt(mean(x^2) + eps) from a sum of squares.
+__device__ __forceinline__ float rms_scale(const Params& p, float ss) { return 1.0f / sqrtf(ss * p.inv_h + p.eps); }
+
+// Row blocks for a tile of n rows (n <= 64).
+__device__ __forceinline__ int row_blocks(int n) { return n <= 16 ? 1 : (n <= 32 ? 2 : 4); }
+
+// -------------------------------------------------------------------- QKV
+
+// Virtual rows a1..a2 (<= 16) of KV group a0 (query rows of its heads, then
+// its key rows, then its value rows) for every token: q, k, v =
+// W_qkv (g o x) / rms(x). The RMSNorm scale is applied to the product, so the
+// activations are read once, for both the product and their sum of squares.
+__device__ __forceinline__ bool tile_qkv_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, g = t.a0, v0 = t.a1, nrows = t.a2 - t.a1;
+    const int H = p.H, D = p.D, GD = p.G * p.D, B = p.B;
+    auto phys = [&](int v) -> int {
+        if (v < GD) return g * GD + v;
+        if (v < GD + D) return p.Hq * D + g * D + (v - GD);
+        return p.Hq * D + p.Hkv * D + g * D + (v - GD - D);
+    };
+    const uint16_t* W = wptr(p, l, W_QKV);
+    float* sPart = reinterpret_cast<float*>(cx.lds);
+    float* sSS = sPart + kMmPartFloats;
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+    bool ok = true;
+    const float* xin = x_at(p, 2 * l);
+    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
+    with_ncb(ncb, [&](auto n) {
+        mm_block<decltype(n)::v, true>(
+            1, H, [&](int, int r) { return W + (int64_t)phys(v0 + (r < nrows ? r : nrows - 1)) * H; },
+            [&](int c) -> const float* { return c < B ? xin + (int64_t)c * H : nullptr; }, wptr(p, l, W_ATTN_NORM),
+            [&]() {
+                ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+                mark(cx, 0);
+            },
+            sPart, sSS);
+    });
+    if (!ok) return false;
+    float* out = qkv_at(p, l);
+    for (int i = tid_(); i < nrows * B; i += NT) {
+        const int r = i / B, b = i - r * B;
+        const float v = mm_c(sPart, nc, 1, 0, r, b) * rms_scale(p, mm_ss(sSS, nc, 1, b));
+        st_dev(out + (int64_t)b * p.QKVD + phys(v0 + r), v);
+    }
+    mark(cx, 1);
+    block_signal(p, t.signal);
+    return true;
+}
+
+// --------------------------------------------------------- output projection
+
+// Rows a0..a1 (<= 16) of the hidden size: x_mid = x_in + W_o attn.
+__device__ __forceinline__ bool tile_oproj_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0, B = p.B;
+    const int K = p.Hq * p.D;
+    const uint16_t* W = wptr(p, l, W_O);
+    float* sPart = reinterpret_cast<float*>(cx.lds);
+    float* sSS = sPart + kMmPartFloats;
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+    bool ok = true;
+    const float* att = attout_at(p, l);
+    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
+    with_ncb(ncb, [&](auto n) {
+        mm_block<decltype(n)::v, false>(
+            1, K, [&](int, int r) { return W + (int64_t)(r0 + (r < nrows ? r : nrows - 1)) * K; },
+            [&](int c) -> const float* { return c < B ? att + (int64_t)c * K : nullptr; }, nullptr,
+            [&]() {
+                ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+                mark(cx, 0);
+            },
+            sPart, sSS);
+    });
+    if (!ok) return false;
+    const float* xin = x_at(p, 2 * l);
+    float* xout = x_at(p, 2 * l + 1);
+    for (int i = tid_(); i < nrows * B; i += NT) {
+        const int r = i / B, b = i - r * B;
+        const int64_t o = (int64_t)b * p.H + r0 + r;
+        st_dev(xout + o, ldg(xin + o) + mm_c(sPart, nc, 1, 0, r, b));
+    }
+    mark(cx, 1);
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ------------------------------------------------------------------ router
+
+// Rows a0..a1 (<= 16) of the router: logits = W_r (g o x_mid) / rms(x_mid) (+ bias).
+__device__ __forceinline__ bool tile_router_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0, B = p.B, H = p.H;
+    const uint16_t* W = wptr(p, l, W_ROUTER);
+    const float* bias = reinterpret_cast<const float*>(p.wtab[l * W_NKINDS + W_RBIAS]);
+    float* sPart = reinterpret_cast<float*>(cx.lds);
+    float* sSS = sPart + kMmPartFloats;
+    bool ok = true;
+    const float* xm = x_at(p, 2 * l + 1);
+    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
+    with_ncb(ncb, [&](auto n) {
+        mm_block<decltype(n)::v, true>(
+            1, H, [&](int, int r) { return W + (int64_t)(r0 + (r < nrows ? r : nrows - 1)) * H; },
+            [&](int c) -> const float* { return c < B ? xm + (int64_t)c * H : nullptr; }, wptr(p, l, W_FFN_NORM),
+            [&]() {
+                ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+                mark(cx, 0);
+            },
+            sPart, sSS);
+    });
+    if (!ok) return false;
+    float* out = rlogits_at(p, l);
+    for (int i = tid_(); i < nrows * B; i += NT) {
+        const int r = i / B, b = i - r * B;
+        const float v = mm_c(sPart, nc, 1, 0, r, b) * rms_scale(p, mm_ss(sSS, nc, 1, b));
+        st_dev(out + (int64_t)b * p.E + r0 + r, bias != nullptr ? v + ldg(bias + r0 + r) : v);
+    }
+    mark(cx, 1);
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ----------------------------------------------------------------- routing
+
+// Every token's top-k (ties to the lower expert index, the largest first)
+// and its routing weights (softmax over the selected logits); then the
+// routing table: selected experts in ascending id, each with its tokens in
+// ascending token order and their ranks. Wave w takes tokens w, w+4, ...;
+// thread e owns expert e (E <= 256).
+template <int NE>
+__device__ __forceinline__ bool tile_route(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, E = p.E, K = p.K, B = p.B;
+    const int tid = tid_(), wave = tid >> 6, lane = tid & 63;
+    uint32_t* sMask = reinterpret_cast<uint32_t*>(cx.lds);            // [256][2] tokens per expert
+    int8_t* sRank = reinterpret_cast<int8_t*>(sMask + 2 * 256);      // [64][256] rank of expert e for token b
+    int* sWave = reinterpret_cast<int*>(sRank + kMaxBatchMM * 256);  // [NWAVES] selected experts per wave
+    for (int i = tid; i < 2 * 256; i += NT) sMask[i] = 0u;
+    __syncthreads();
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    mark(cx, 0);
+    const float* rl = rlogits_at(p, l);
+    int32_t* rt = rtab_at(p, l);
+    float* rw = rtab_w(p, rt);
+    for (int b = wave; b < B; b += NWAVES) {
+        uint32_t u[NE];  // 0: not a candidate (no float maps to 0)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = lane + 64 * i;
+            const float v = ld_dev(rl + (int64_t)b * E + (e < E ? e : E - 1));
+            u[i] = e < E ? fkey(v) : 0u;
+        }
+        uint32_t top = 0u;
+        float sel = 0.f;
+        int myid = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < K) {
+                uint32_t v = u[0];
+#pragma unroll
+                for (int i = 1; i < NE; ++i) v = max(v, u[i]);
+                const uint32_t m = wave_max_u32(v);
+                int best = -1;
+#pragma unroll
+                for (int i = NE - 1; i >= 0; --i) {
+                    const uint64_t bal = __ballot(u[i] == m);
+                    if (bal != 0ull) best = 64 * i + (int)__builtin_ctzll(bal);
+                }
+                if (j == 0) top = m;
+                if (lane == j) {
+                    sel = unkey(m);
+                    myid = best;
+                }
+#pragma unroll
+                for (int i = 0; i < NE; ++i)
+                    if (64 * i + lane == best) u[i] = 0u;
+            }
+        }
+        const float ex = lane < K ? expf(sel - unkey(top)) : 0.f;
+        const float sum = wave_sum(ex);
+        if (lane < K) {
+            const float w = ex / sum;
+            sRank[b * 256 + myid] = (int8_t)lane;
+            atomicOr(&sMask[2 * myid + (b >> 5)], 1u << (b & 31));
+            st_dev(rw + b * K + lane, w);
+            p.route_ids[((int64_t)l * p.max_batch + b) * K + lane] = myid;
+            p.route_w[((int64_t)l * p.max_batch + b) * K + lane] = w;
+        }
+    }
+    __syncthreads();
+    const int e = tid;
+    const uint32_t m0 = e < E ? sMask[2 * e] : 0u, m1 = e < E ? sMask[2 * e + 1] : 0u;
+    const int n = __popc(m0) + __popc(m1);
+    const uint64_t bal = __ballot(n > 0);
+    if (lane == 0) sWave[wave] = __popcll(bal);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += sWave[w];
+    if (n > 0) {
+        const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
+        st_dev_i(rt + 64 + slot, e);
+        st_dev_i(rt + 64 + E + slot, n);
+        int32_t* lst = rt + 64 + 2 * E + (int64_t)slot * p.max_batch;
+        int c = 0;
+        for (int h = 0; h < 2; ++h) {
+            uint32_t m = h ? m1 : m0;
+            while (m != 0u) {
+                const int b = 32 * h + __builtin_ctz(m);
+                m &= m - 1u;
+                st_dev_i(lst + c++, b | ((int)sRank[b * 256 + e] << 16));
+            }
+        }
+    }
+    if (tid == 0) st_dev_i(rt, sWave[0] + sWave[1] + sWave[2] + sWave[3]);
+    mark(cx, 1);
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ---------------------------------------------------------- expert gate/up
+
+// Slot a0 of the routing table, rows a1..a2 (<= 32) of its expert's gate and
+// up matrices, for the tokens routed to it: a = SiLU(W_gate h2) * (W_up h2),
+// h2 = RMSNorm(x_mid), written to the (token, rank) row of the activations.
+// Row blocks: the gate rows first, then the up rows.
+__device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1, H = p.H, K = p.K, I = p.I;
+    float* sPart = reinterpret_cast<float*>(cx.lds);
+    float* sSS = sPart + kMmPartFloats;
+    int* sList = reinterpret_cast<int*>(sSS + kMmSsFloats);
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    mark(cx, 0);
+    const int32_t* rt = rtab_at(p, l);
+    if (slot >= ldg(rt)) {
+        block_signal(p, t.signal);
+        return true;
+    }
+    const int e = ldg(rt + 64 + slot), n = ldg(rt + 64 + p.E + slot);
+    for (int i = tid_(); i < n; i += NT) sList[i] = ldg(rt + 64 + 2 * p.E + (int64_t)slot * p.max_batch + i);
+    __syncthreads();
+    const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * I * H;
+    const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * I * H;
+    const int nrb = row_blocks(nrows), na = 2 * nrb;
+    const float* xm = x_at(p, 2 * l + 1);
+    const int ncb = (n + 15) >> 4, nc = ncb_cols(ncb);
+    with_ncb(ncb, [&](auto nn) {
+        mm_block<decltype(nn)::v, true>(
+            na, H,
+            [&](int blk, int r) {
+                const int up = blk >= nrb, rr = 16 * (up ? blk - nrb : blk) + r;
+                return (up ? Wu : Wg) + (int64_t)(r0 + (rr < nrows ? rr : nrows - 1)) * H;
+            },
+            [&](int c) -> const float* { return c < n ? xm + (int64_t)(sList[c] & 0xffff) * H : nullptr; },
+            wptr(p, l, W_FFN_NORM), [] {}, sPart, sSS);
+    });
+    mark(cx, 1);
+    float* act = act_at(p, l);
+    for (int i = tid_(); i < nrows * n; i += NT) {
+        const int r = i / n, c = i - r * n;
+        const float rs = rms_scale(p, mm_ss(sSS, nc, na, c));
+        const float gv = mm_c(sPart, nc, na, r >> 4, r & 15, c) * rs;
+        const float uv = mm_c(sPart, nc, na, nrb + (r >> 4), r & 15, c) * rs;
+        const int ent = sList[c];
+        st_dev(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I + r0 + r, (gv / (1.0f + expf(-gv))) * uv);
+    }
+    mark(cx, 2);
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ------------------------------------------------------------ expert down
+
+// Rows a0..a1 (<= 16) of the hidden size, for slots a2, a2 + a3, a2 + 2 a3, ...
+// of the routing table: y = W_down a for each token routed to the slot's
+// expert, written to that token's (token, rank) row of the expert outputs.
+// Waves take the tile's slots in turn, each slot a whole product of its own.
+__device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, q0 = t.a2, Q = t.a3;
+    const int H = p.H, K = p.K, I = p.I;
+    const int tid = tid_(), wave = tid >> 6, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    mark(cx, 0);
+    const int32_t* rt = rtab_at(p, l);
+    const int nact = ldg(rt);
+    const uint16_t* Wd = wptr(p, l, W_DOWN);
+    const float* act = act_at(p, l);
+    float* y = ybuf_at(p, l);
+    for (int s = q0 + Q * wave; s < nact; s += Q * NWAVES) {
+        const int e = ldg(rt + 64 + s), n = ldg(rt + 64 + p.E + s);
+        const int32_t* lst = rt + 64 + 2 * p.E + (int64_t)s * p.max_batch;
+        with_ncb((n + 15) >> 4, [&](auto nn) {
+            constexpr int NCB = decltype(nn)::v;
+            int ent[NCB];
+            const float* xc[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int c = 16 * cb + col;
+                ent[cb] = c < n ? ldg(lst + c) : -1;
+                xc[cb] = ent[cb] >= 0 ? act + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * I + 8 * g4 : nullptr;
+            }
+            const uint16_t* ar = Wd + ((int64_t)e * H + h0 + (col < nrows ? col : nrows - 1)) * I + 8 * g4;
+            f32x4_t acc[NCB];
+            float ss[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                ss[cb] = 0.f;
+            }
+            mm_wave<NCB, false>(ar, xc, nullptr, I >> 5, [] {}, acc, ss);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (ent[cb] < 0) continue;
+                float* yr = y + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * H + h0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
+            }
+        });
+    }
+    mark(cx, 1);
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ------------------------------------------------------------- expert sum
+
+// Rows a0..a1 of the hidden size: x_out = x_mid + sum_j w_j y_j over each
+// token's top-k in rank order.
+__device__ __forceinline__ bool tile_moesum(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, H = p.H, K = p.K;
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    const float* w = rtab_w(p, rtab_at(p, l));
+    const float* y = ybuf_at(p, l);
+    const float* xm = x_at(p, 2 * l + 1);
+    float* xo = x_at(p, 2 * l + 2);
+    for (int i = tid_(); i < p.B * nrows; i += NT) {
+        const int b = i / nrows, r = i - b * nrows;
+        float wv[kMaxTopK], yv[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            wv[j] = j < K ? ldg(w + b * K + j) : 0.f;
+            yv[j] = j < K ? ldg(y + ((int64_t)b * K + j) * H + h0 + r) : 0.f;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < K) acc += wv[j] * yv[j];
+        const int64_t o = (int64_t)b * H + h0 + r;
+        st_dev(xo + o, ldg(xm + o) + acc);
+    }
+    block_signal(p, t.signal);
+    return true;
+}
+
+// ---------------------------------------------------------------- LM head
+
+// Rows a0..a1 (<= 64) of the LM head: logits = W_lm (g o x) / rms(x).
+__device__ __forceinline__ bool tile_lmhead_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int r0 = t.a0, nrows = t.a1 - t.a0, B = p.B, H = p.H;
+    float* sPart = reinterpret_cast<float*>(cx.lds);
+    float* sSS = sPart + kMmPartFloats;
+    bool ok = true;
+    const float* xf = x_at(p, 2 * p.L);
+    const int na = row_blocks(nrows);
+    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
+    with_ncb(ncb, [&](auto n) {
+        mm_block<decltype(n)::v, true>(
+            na, H,
+            [&](int blk, int r) {
+                const int rr = 16 * blk + r;
+                return p.lm_head + (int64_t)(r0 + (rr < nrows ? rr : nrows - 1)) * H;
+            },
+            [&](int c) -> const float* { return c < B ? xf + (int64_t)c * H : nullptr; }, p.final_norm,
+            [&]() { ok = block_wait(p, t.ctr, t.target, cx.t_wait); }, sPart, sSS);
+    });
+    if (!ok) return false;
+    for (int i = tid_(); i < nrows * B; i += NT) {
+        const int r = i / B, b = i - r * B;
+        p.logits[(int64_t)b * p.V + r0 + r] =
+            mm_c(sPart, nc, na, r >> 4, r & 15, b) * rms_scale(p, mm_ss(sSS, nc, na, b));
+    }
+    mark(cx, 1);
+    block_signal(p, t.signal);
+    return true;
+}
+
+}  // namespace mk

@@ -13,7 +13,9 @@ import pytest
 from persistent_megakernel_03_amd import configs, mk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_ROUTER, OP_GATEUP, OP_DOWN, OP_LMHEAD = range(9)
+(OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_ROUTER, OP_ROUTE, OP_GATEUP, OP_DOWN, OP_MOESUM,
+ OP_LMHEAD) = range(11)
+LEVELS_PER_LAYER = 9
 
 
 def header_functions():
@@ -81,10 +83,13 @@ def simulate(tasks, offs, targets, rng):
     ("TINY", 1, [0], 512),
     ("A3B", 1, [8192], 512),
     ("A3B", 2, [100, 3000], 256),
+    ("TINY", 3, [64, 0, 17], 16),
+    ("TINY", 8, [5, 70, 64, 63, 1, 0, 127, 300], 512),
+    ("A3B", 4, [8192, 100, 3000, 5], 512),
 ])
 def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
     cfg = configs.dims_of(cfg_name)
-    d = mk.make_dims(cfg, 2, 600, 1200)
+    d = mk.make_dims(cfg, max(2, batch), 600, 1200)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), n_wg, positions)
     assert info.n_tasks == len(tasks) and offs[-1] == len(tasks)
     # each workgroup list is in non-decreasing dependency level
@@ -92,7 +97,7 @@ def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
         lv = tasks[offs[w]:offs[w + 1], 11]
         assert np.all(np.diff(lv) >= 0)
     # the counters reach exactly their targets, whatever the interleaving
-    for seed in range(2 if cfg_name == "A3B" else 5):
+    for seed in range(1 if batch > 2 and cfg_name == "A3B" else (2 if cfg_name == "A3B" else 5)):
         ctr, steps = simulate(tasks, offs, targets, random.Random(seed))
         assert steps == len(tasks)
         for c, t in enumerate(targets):
@@ -109,7 +114,7 @@ def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
 def test_plan_counts_for_the_30b_shape():
     d = mk.make_dims(configs.A3B, 1, 520, 520)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192])
-    ops = np.bincount(tasks[:, 0], minlength=9)
+    ops = np.bincount(tasks[:, 0], minlength=11)
     assert ops[OP_EMBED] == 1
     assert ops[OP_QKV] == 48 * 4 * 54          # 1280 rows per KV group, 24 per tile
     assert ops[OP_ATTN] == 48 * 4 * 65         # 8193 tokens in 128-token chunks
@@ -119,7 +124,33 @@ def test_plan_counts_for_the_30b_shape():
     assert ops[OP_GATEUP] == 48 * 8 * 32       # 8 slots x 768 rows / 24 (gate/up and down fit 512 workgroups)
     assert ops[OP_DOWN] == 48 * 256            # 2048 rows / 8: 8 experts x 8 rows per tile held in registers
     assert ops[OP_LMHEAD] == -(-151936 // 64)
-    assert info.n_levels == 2 + 7 * 48
+    assert ops[OP_ROUTE] == 0 and ops[OP_MOESUM] == 0
+    assert info.n_levels == 2 + LEVELS_PER_LAYER * 48
+
+
+@pytest.mark.parametrize("batch,rows_gu", [(4, 16), (16, 32), (64, 32)])
+def test_plan_counts_for_30b_batches(batch, rows_gu):
+    # batches of 3+: every weight product in 16-row matrix-core blocks, one
+    # routing tile, gate/up tiles over all min(E, B*k) possible slots
+    d = mk.make_dims(configs.A3B, batch, 520, 520 * batch)
+    info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192] * batch)
+    ops = np.bincount(tasks[:, 0], minlength=11)
+    slots = min(128, 8 * batch)
+    assert ops[OP_EMBED] == -(-batch // 4)
+    assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
+    assert ops[OP_COMBINE] == 48 * 32 * batch
+    assert ops[OP_OPROJ] == 48 * 256           # 8 rows per tile
+    assert ops[OP_ROUTER] == 48 * 16
+    assert ops[OP_ROUTE] == 48
+    assert ops[OP_GATEUP] == 48 * slots * (768 // rows_gu)
+    assert ops[OP_DOWN] == 48 * 128 * 2        # 16-row blocks x 2 slot groups
+    assert ops[OP_MOESUM] == 48 * 128
+    assert ops[OP_LMHEAD] == -(-151936 // 32)
+    att = tasks[tasks[:, 0] == OP_ATTN]
+    assert len(att) == 48 * batch * 4 * att[0, 5]
+    # down slot groups: every slot in exactly one group
+    dn = tasks[(tasks[:, 0] == OP_DOWN) & (tasks[:, 1] == 0)]
+    assert set(dn[:, 5]) == {2} and set(dn[:, 4]) == {0, 1}
 
 
 def test_plan_rejects_bad_input():

@@ -76,10 +76,12 @@ def _margin(r, a, b):
     return abs(r[a] - r[b])
 
 
-def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True):
+def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True, written=None):
     """end_to_end: the whole step with the device's routing adopted, then the
     sampled layers teacher-forced. Otherwise (very long caches, to bound host
-    memory) layer 0 teacher-forced only."""
+    memory) layer 0 teacher-forced only. written: the (page, slot) pairs the
+    whole batch wrote (default: this sequence's new slot); None of the
+    checks below look at other rows' slots otherwise."""
     L = CFG["n_layers"]
     model = s.oracle_model(lazy_experts=True)
     cos, sin = rope_cos_sin(CTX, CFG["head_dim"], CFG["rope_theta"])
@@ -144,7 +146,7 @@ def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True):
     # the cache changed exactly at the new slot of every layer (compared on the device)
     ck = {tuple(int(t) for t in x) for x in torch.nonzero(torch.any(g["k"] != s.k0, dim=4).any(dim=2)).tolist()}
     cv = {tuple(int(t) for t in x) for x in torch.nonzero(torch.any(g["v"] != s.v0, dim=3).any(dim=2)).tolist()}
-    want = {(l, page, slot) for l in range(L)}
+    want = {(l, pg, sl) for l in range(L) for pg, sl in (written or {(page, slot)})}
     assert ck == want and cv == want
 
 
@@ -177,4 +179,44 @@ def test_a3b_long_context(weights, ctx):
     assert np.array_equal(a["logits"], b["logits"])
     assert np.array_equal(a["xs"], b["xs"])
     del s, a, b
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_a3b_batch_matches_oracle(weights, B):
+    """The batch sweep's shape: B sequences at 8192 cached tokens each, pages
+    from a shuffled pool, per-sequence seeded first tokens. Rows 0 and B-1
+    are checked end to end against the oracle as above; B = 4 also
+    megakernel == per-op bit for bit."""
+    ctx = 8192
+    pages = ctx // P + 2
+    n_pages = B * pages + 7
+    print(f"a3b batch {B}: cache for {B} x {ctx} tokens ({n_pages} pages)", flush=True)
+    s = Setup(CFG, n_pages=n_pages, seed=0, device_gen=True, weights=weights)
+    bts = [[int(x) for x in r] for r in synth.make_block_tables(B, pages, n_pages, seed=B, shuffle=True)]
+    toks = [int(t) for t in synth.make_tokens(B, CFG["vocab"], seed=100 + B)]
+    outs = []
+    for mode in ([mk.MK_MODE_MEGAKERNEL, mk.MK_MODE_PEROP] if B == 4 else [mk.MK_MODE_MEGAKERNEL]):
+        k, v = s.fresh_pools()
+        dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=B, max_pages_per_seq=pages, mode=mode)
+        tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
+        logits = torch.empty(B, CFG["vocab"], dtype=torch.float32, device="cuda")
+        print(f"a3b batch {B}: one step, mode {mode}", flush=True)
+        dec.step([ctx] * B, bts, tokens, logits)
+        assert dec.sync_check() == mk.MK_OK
+        outs.append(dict(logits=logits.cpu().numpy(), xs=x_layers(dec).cpu().numpy(),
+                         ids=route_ids(dec).cpu().numpy(), k=k, v=v))
+        dec.close()
+    if len(outs) == 2:
+        a, b = outs
+        assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["xs"], b["xs"])
+        assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+        del outs[1]
+    g = outs[0]
+    written = {(bts[b][ctx // P], ctx % P) for b in range(B)}
+    for b in (0, B - 1):
+        row = dict(logits=g["logits"][b], xs=g["xs"][:, b], ids=g["ids"][:, b], k=g["k"], v=g["v"])
+        print(f"a3b batch {B}: oracle on row {b}", flush=True)
+        _check_against_oracle(s, bts[b], toks[b], row, ctx, written=written)
+    del s, g, outs
     torch.cuda.empty_cache()
