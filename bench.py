@@ -13,6 +13,12 @@ build of the same tiles in the same harness, the roofline of the megakernel
 the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--sweep 4,16,64 [--sweep-steps K]]
+
+--sweep adds, under "batch_sweep", the same measurement at other batch sizes
+(each sequence at the same context, pages from a shuffled pool, per-sequence
+seeded first tokens): megakernel and per-op tok/s, kernel time, algorithmic
+bytes per step with the counted distinct experts, and % of 8 TB/s.
 """
 
 from __future__ import annotations
@@ -80,6 +86,8 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-perop", action="store_true")
     ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--sweep", type=str, default="", help="comma-separated batch sizes to measure as well")
+    ap.add_argument("--sweep-steps", type=int, default=32)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -95,23 +103,28 @@ def main():
     cfg = configs.A3B
     B, ctx = args.batch, args.context
     P = cfg["page_size"]
-    total_tokens = ctx + args.warmup + args.steps + 16 + 1  # + the per-step kernel timing pass
-    pages_per_seq = -(-total_tokens // P)
-    n_pages = pages_per_seq * B + 1
     t0 = time.time()
-    log(f"generating weights ({cfg['n_layers']} layers) and KV ({n_pages} pages) on device")
+    log(f"generating weights ({cfg['n_layers']} layers) on device")
     weights = synth.make_model(cfg, 0, "cuda")
-    k_pool, v_oracle_layout = synth.make_kv_pool(cfg, n_pages, 1, "cuda")
-    v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
-    del v_oracle_layout
-    torch.cuda.synchronize()
+
+    def make_inputs(B, steps, warmup):
+        total_tokens = ctx + warmup + steps + 16 + 1  # + the per-step kernel timing pass
+        pages_per_seq = -(-total_tokens // P)
+        n_pages = pages_per_seq * B + 1
+        log(f"batch {B}: KV for {B} x {ctx} tokens ({n_pages} pages) on device")
+        k_pool, v_oracle_layout = synth.make_kv_pool(cfg, n_pages, 1, "cuda")
+        v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
+        del v_oracle_layout
+        torch.cuda.synchronize()
+        block_tables = synth.make_block_tables(B, pages_per_seq, n_pages, shuffle=B > 1)
+        tok0 = synth.make_tokens(B, cfg["vocab"], seed=3)
+        return pages_per_seq, k_pool, v_pool, block_tables, tok0
+
+    pages_per_seq, k_pool, v_pool, block_tables, tok0 = make_inputs(B, args.steps, args.warmup)
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
-    block_tables = synth.make_block_tables(B, pages_per_seq, n_pages, shuffle=B > 1)
-    tok0 = synth.make_tokens(B, cfg["vocab"], seed=3)
-    results = {}
-
-    def run(mode: int, steps: int, warmup: int, k, v):
+    def run(mode: int, steps: int, warmup: int, k, v, B=B, pages_per_seq=pages_per_seq, block_tables=block_tables,
+            tok0=tok0):
         dec = mk.Decoder(cfg, weights, k, v, max_batch=B, max_pages_per_seq=pages_per_seq, mode=mode,
                          wg_per_cu=args.wg_per_cu, time_kernels=True)
         tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
@@ -177,6 +190,35 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, args.cpu_steps)
 
+    sweep = []
+    if args.sweep:
+        del k_pool, v_pool
+        torch.cuda.empty_cache()
+        for Bs in [int(x) for x in args.sweep.split(",") if x]:
+            steps_s, warm_s = args.sweep_steps, 5
+            pps, kp, vp, bts, tk = make_inputs(Bs, steps_s, warm_s)
+            k1, v1 = kp.clone(), vp.clone()
+            el_s, kms_s, rid_s, pe_s = run(mk.MK_MODE_MEGAKERNEL, steps_s, warm_s, k1, v1, Bs, pps, bts, tk)
+            del k1, v1
+            k2, v2 = kp.clone(), vp.clone()
+            el_p, kms_p, _, _ = run(mk.MK_MODE_PEROP, max(8, steps_s // 2), 3, k2, v2, Bs, pps, bts, tk)
+            del k2, v2, kp, vp
+            torch.cuda.empty_cache()
+            nexp = distinct_experts(rid_s, Bs)
+            by = sol.step_bytes(cfg, [p - 1 for p in pe_s], nexp, distinct_tokens=Bs)
+            ach = by / (kms_s * 1e-3) / 1e9
+            rec = {"batch": Bs, "value": round(Bs * steps_s / el_s, 2), "unit": "tok/s",
+                   "ms_per_step": round(1e3 * el_s / steps_s, 4), "kernel_ms": round(kms_s, 4),
+                   "bytes_per_step": by, "distinct_experts_mean": round(float(np.mean(nexp)), 2),
+                   "achieved_gbs": round(ach, 1), "frac": round(ach / PEAK_GBS, 4),
+                   "sol_tok_s": round(sol.sol_tokens_per_s(by, Bs), 1),
+                   "perop_value": round(Bs * max(8, steps_s // 2) / el_p, 2), "perop_kernel_ms": round(kms_p, 4),
+                   "steps": steps_s}
+            log(f"batch {Bs}: {rec['value']:.1f} tok/s (kernel {kms_s:.3f} ms, {100 * rec['frac']:.1f}% of 8 TB/s, "
+                f"{rec['distinct_experts_mean']} experts/layer); per-op {rec['perop_value']:.1f} tok/s "
+                f"(kernels {kms_p:.3f} ms)")
+            sweep.append(rec)
+
     out = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -203,6 +245,8 @@ def main():
         "perop_baseline": perop,
         "cpu_baseline": cpu,
     }
+    if sweep:
+        out["batch_sweep"] = sweep
     print(json.dumps(out), flush=True)
 
     if args.calib_copy:

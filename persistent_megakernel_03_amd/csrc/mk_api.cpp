@@ -53,7 +53,7 @@ constexpr int kMaxChunksCap = 512;
 constexpr int kStageSlots = 4;
 
 struct Layout {
-    size_t err, banks, x, qkv, att_part, att_ml, att_out, rlogits, route_ids, route_w, act, rtab, ybuf, wtab, step,
+    size_t err, banks, x, qkv, att_part, att_ml, att_out, rlogits, route_ids, route_w, act, rtab, ybuf, h2s, wtab, step,
         tasks, wg_off, level_tasks, trace, total;
     int64_t bank_words;
     int max_chunks;
@@ -148,6 +148,7 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
     const bool mm = d.max_batch > kMaxBatchValu;
     L.rtab = take(mm ? Ln * rtab_words(d.n_experts, d.top_k, d.max_batch) * 4 : 0);
     L.ybuf = take(mm ? Ln * pad64(B * d.top_k * H) * 4 : 0);
+    L.h2s = take(mm ? Ln * pad64(B * H) * 4 : 0);
     L.wtab = take((size_t)d.n_layers * W_NKINDS * 8);
     // per-step arrays: positions, chunk counts, rotary table, block tables
     L.step_bytes = align256((size_t)B * 4) * 2 + align256((size_t)B * d.head_dim * 4) +
@@ -364,6 +365,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         p.act = reinterpret_cast<float*>(h->ws + h->lay.act);
         p.rtab = reinterpret_cast<int32_t*>(h->ws + h->lay.rtab);
         p.ybuf = reinterpret_cast<float*>(h->ws + h->lay.ybuf);
+        p.h2s = reinterpret_cast<float*>(h->ws + h->lay.h2s);
         p.bank_words = h->lay.bank_words;
         p.cl = CounterLayout{d.n_layers, d.n_kv_heads, d.max_batch};
         p.err = reinterpret_cast<int32_t*>(h->ws + h->lay.err);

@@ -142,13 +142,14 @@ struct Params {
     float* qkv;       // [L][max_batch][QKVD]
     float* att_part;  // [L][max_batch][Hq][max_chunks][D] unnormalised outputs
     float* att_ml;    // [L][max_batch][Hq][pad64(2 max_chunks)] running max and sum
-    float* att_out;   // [L][max_batch][Hq*D]
+    float* att_out;   // [L][max_batch][Hq*D] (split form for batches of 3+)
     float* rlogits;   // [L][max_batch][E]
     int32_t* route_ids;  // [L][max_batch][K]
     float* route_w;      // [L][max_batch][K]
-    float* act;          // [L][max_batch*K][I]
+    float* act;          // [L][max_batch*K][I] (split form for batches of 3+)
     int32_t* rtab;       // [L][rtab_words]: batches of 3+, routing table (see rtab_words)
     float* ybuf;         // [L][max_batch*K][H]: batches of 3+, each expert's output per (token, rank)
+    float* h2s;          // [L][max_batch][H]: batches of 3+, the experts' normalised input, split
     uint32_t* ctr;       // this step's counter bank
     uint32_t* ctr_other; // the bank the next step uses (cleared by this step)
     int64_t bank_words;

@@ -72,10 +72,10 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
 void expert_rows_mm(const ModelShape& s, int n_wg, int S, int* rows_gu, int* down_groups) {
     // gate/up: 16 rows per tile unless that makes more than four tiles per
     // workgroup; down: 16-row blocks of the hidden size, the slots split into
-    // groups so that the down tiles cover about half the workgroups
+    // groups so that there are about as many down tiles as workgroups
     *rows_gu = (int64_t)S * ceil_div(s.I, 16) <= 4 * (int64_t)n_wg ? 16 : 32;
     const int nblk = ceil_div(s.H, 16);
-    *down_groups = std::max(1, std::min(S, n_wg / 2 / std::max(1, nblk)));
+    *down_groups = std::max(1, std::min(S, n_wg / std::max(1, nblk)));
 }
 
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested) {
@@ -313,9 +313,13 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
                 2.0 * (r1 - r0) * s.Hq * s.D, kStatic);
         }
         P.targets[cl.oproj(l)] = no;
+        // router tile i also writes 8-element groups [g0, g1) of the experts'
+        // normalised input
+        const int ng = s.H / 8, gs = ceil_div(ng, nr);
         for (int i = 0; i < nr; ++i) {
             const int r0 = i * cfg.mm_rows_router, r1 = std::min(s.E, r0 + cfg.mm_rows_router);
-            add(make_task(OP_ROUTER, l, r0, r1, 0, 0, -1, 0, cl.oproj(l), no, cl.router(l), lv + 4),
+            const int g0 = std::min(ng, i * gs), g1 = std::min(ng, g0 + gs);
+            add(make_task(OP_ROUTER, l, r0, r1, g0, g1, -1, 0, cl.oproj(l), no, cl.router(l), lv + 4),
                 2.0 * (r1 - r0) * s.H, kStatic);
         }
         P.targets[cl.router(l)] = nr;
@@ -380,7 +384,9 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     P.wg_bytes.assign(n_wg, 0.0);
     typedef std::pair<double, int> Slot;
     typedef std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> Heap;
-    const int half = (n_wg % 2 == 0) ? n_wg / 2 : 0;
+    // (one- and two-token schedule only; the matrix-core expert tiles are many
+    // more than the workgroups and go wherever a workgroup is free first)
+    const int half = (n_wg % 2 == 0 && P.B <= kMaxBatchValu) ? n_wg / 2 : 0;
     Heap heaps[2];   // [0]: workgroups below `half`, [1]: the rest
     for (int w = 0; w < n_wg; ++w) heaps[w >= half ? 1 : 0].push({0.0, w});
     std::vector<double> level_end(P.n_levels, 0.0);

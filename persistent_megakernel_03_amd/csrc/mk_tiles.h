@@ -486,14 +486,32 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     __syncthreads();
     mark(cx, 1);
     float* out = attout_at(p, l) + row * D;
-    for (int d = tid; d < D; d += NT) {
-        float v[NPH];
+    if (p.B > kMaxBatchValu) {
+        // batches of 3+: the output projection takes it split (see st_split8)
+        if (tid < D / 8) {
+            float o8[8];
 #pragma unroll
-        for (int k = 0; k < NPH; ++k) v[k] = sacc[k * D + d];
-        float s = 0.f;
+            for (int j = 0; j < 8; ++j) {
+                float v[NPH];
 #pragma unroll
-        for (int k = 0; k < NPH; ++k) s += v[k];
-        st_dev(out + d, s * inv);
+                for (int k = 0; k < NPH; ++k) v[k] = sacc[k * D + 8 * tid + j];
+                float s = 0.f;
+#pragma unroll
+                for (int k = 0; k < NPH; ++k) s += v[k];
+                o8[j] = s * inv;
+            }
+            st_split8(out + 8 * tid, o8);
+        }
+    } else {
+        for (int d = tid; d < D; d += NT) {
+            float v[NPH];
+#pragma unroll
+            for (int k = 0; k < NPH; ++k) v[k] = sacc[k * D + d];
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < NPH; ++k) s += v[k];
+            st_dev(out + d, s * inv);
+        }
     }
     block_signal(p, t.signal);
     return true;

@@ -41,6 +41,28 @@ __device__ __forceinline__ float* ybuf_at(const Params& p, int l) {
 __device__ __forceinline__ void st_dev_i(int32_t* p, int32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ float* h2s_at(const Params& p, int l) {
+    return p.h2s + (int64_t)l * pad64((int64_t)p.max_batch * p.H);
+}
+
+// Split activations. Vectors that feed a weight product and need no
+// normalisation there (the attention output, the FFN input after its
+// RMSNorm, the SwiGLU output) are stored by their producers already split:
+// each group of 8 elements becomes its BF16 hi pairs then its lo pairs (the
+// two halves of split8), in the 32 bytes the 8 fp32 values would take.
+__device__ __forceinline__ void st_dev_u4(uint4* q, uint4 v) {
+    uint64_t* d = reinterpret_cast<uint64_t*>(q);
+    __hip_atomic_store(d, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(d + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Store 8 values (element offset a multiple of 8) in split form.
+__device__ __forceinline__ void st_split8(float* dst, const float (&v)[8]) {
+    uint32_t h[8];
+    split8(v, h);
+    uint4* q = reinterpret_cast<uint4*>(dst);
+    st_dev_u4(q, make_uint4(h[0], h[1], h[2], h[3]));
+    st_dev_u4(q + 1, make_uint4(h[4], h[5], h[6], h[7]));
+}
 
 // ------------------------------------------------------------- MFMA engine
 
@@ -211,6 +233,114 @@ __device__ __forceinline__ float mm_ss(const float* sSS, int nc, int na, int c) 
 // RMSNorm scale 1 / sqrt(mean(x^2) + eps) from a sum of squares.
 __device__ __forceinline__ float rms_scale(const Params& p, float ss) { return 1.0f / sqrtf(ss * p.inv_h + p.eps); }
 
+// ------------------------------------------- MFMA engine, split activations
+
+// Column blocks of 8 tokens (each token's hi and lo part in adjacent
+// columns): compile-time 1, 2, 4 or 8, chosen per call.
+template <class F>
+__device__ __forceinline__ void with_nc8(int n, F&& f) {
+    if (n <= 8) f(Ncb<1>());
+    else if (n <= 16) f(Ncb<2>());
+    else if (n <= 32) f(Ncb<4>());
+    else f(Ncb<8>());
+}
+__device__ __forceinline__ int nc8_tokens(int n) { return n <= 8 ? 8 : (n <= 16 ? 16 : (n <= 32 ? 32 : 64)); }
+
+template <int NC8>
+struct MmPfS {
+    static constexpr int v = NC8 == 1 ? 8 : (NC8 == 2 ? 6 : (NC8 == 4 ? 4 : 2));
+};
+
+// One wave's product over `nsteps` k-steps of 32 with split activations:
+// column 2j + part of block cb is part (hi / lo) of token 8 cb + j, so a
+// lane's B operand is one 16-byte load of its part (xc: this lane's token,
+// part and k slice, in 16-byte units; null = zero). Twice the k-steps in
+// flight of the fp32-input engine for the same registers. On return, lanes
+// with an even column hold the token's full product (hi + lo) in acc.
+template <int NC8, class Ready>
+__device__ __forceinline__ void mm_wave_s(const uint16_t* arow, const uint4* const (&xc)[NC8], int nsteps,
+                                          Ready&& ready, f32x4_t (&acc)[NC8]) {
+    constexpr int PF = MmPfS<NC8>::v;
+    uint4 a0[PF], a1[PF], x0[PF][NC8], x1[PF][NC8];
+    auto loadA = [&](uint4(&a)[PF], int bt) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int s = bt * PF + j;
+            if (s < nsteps) a[j] = ld16s(arow + 32 * s);
+        }
+    };
+    auto loadX = [&](uint4(&x)[PF][NC8], int bt) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int s = bt * PF + j;
+#pragma unroll
+            for (int cb = 0; cb < NC8; ++cb)
+                x[j][cb] = (s < nsteps && xc[cb] != nullptr) ? ld16(xc[cb] + 8 * s) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto compute = [&](const uint4(&a)[PF], const uint4(&x)[PF][NC8], int bt) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j)
+            if (bt * PF + j < nsteps) {
+#pragma unroll
+                for (int cb = 0; cb < NC8; ++cb) acc[cb] = mfma16x16x32(a[j], x[j][cb], acc[cb]);
+            }
+    };
+    const int nb = (nsteps + PF - 1) / PF;
+    loadA(a0, 0);
+    if (nb > 1) loadA(a1, 1);
+    ready();
+    loadX(x0, 0);
+    for (int bt = 0; bt < nb; bt += 2) {
+        if (bt + 1 < nb) loadX(x1, bt + 1);
+        compute(a0, x0, bt);
+        if (bt + 2 < nb) {
+            loadA(a0, bt + 2);
+            loadX(x0, bt + 2);
+        }
+        if (bt + 1 < nb) {
+            compute(a1, x1, bt + 1);
+            if (bt + 3 < nb) loadA(a1, bt + 3);
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NC8; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[cb][q] += dpp_mov<0xB1>(acc[cb][q]);
+}
+
+// This lane's B-operand pointer into a split vector: token row `row` (null:
+// absent), element offset k (a multiple of 8), part = lane column & 1.
+__device__ __forceinline__ const uint4* split_ptr(const float* row, int k, int part) {
+    return row != nullptr ? reinterpret_cast<const uint4*>(row + k) + part : nullptr;
+}
+
+// Block product as mm_block, over split activations: xrow(j) is the split
+// vector of token column j (null: absent). Totals per (block, row, token)
+// via mm_c with nc = 8 NC8.
+template <int NC8, class ARow, class XRow, class Ready>
+__device__ __forceinline__ void mm_block_s(int na, int K, ARow&& arow, XRow&& xrow, Ready&& ready, float* sPart) {
+    const int tid = tid_(), wave = tid >> 6, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
+    const int blk = wave % na, kp = wave / na, KP = NWAVES / na;
+    const int kl = K / KP, k0 = kp * kl + 8 * g4;
+    const uint16_t* ar = arow(blk, col) + k0;
+    const uint4* xc[NC8];
+#pragma unroll
+    for (int cb = 0; cb < NC8; ++cb) xc[cb] = split_ptr(xrow(8 * cb + (col >> 1)), k0, col & 1);
+    f32x4_t acc[NC8];
+#pragma unroll
+    for (int cb = 0; cb < NC8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mm_wave_s<NC8>(ar, xc, kl >> 5, ready, acc);
+    constexpr int NC = 8 * NC8;
+    if ((col & 1) == 0) {
+#pragma unroll
+        for (int cb = 0; cb < NC8; ++cb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sPart[(wave * 16 + 4 * g4 + q) * NC + 8 * cb + (col >> 1)] = acc[cb][q];
+    }
+    __syncthreads();
+}
+
 // Row blocks for a tile of n rows (n <= 64).
 __device__ __forceinline__ int row_blocks(int n) { return n <= 16 ? 1 : (n <= 32 ? 2 : 4); }
 
@@ -260,27 +390,27 @@ __device__ __forceinline__ bool tile_qkv_mm(const Task& t, TileCtx& cx) {
 
 // --------------------------------------------------------- output projection
 
-// Rows a0..a1 (<= 16) of the hidden size: x_mid = x_in + W_o attn.
+// Rows a0..a1 (<= 16) of the hidden size: x_mid = x_in + W_o attn (the
+// attention output arrives split).
 __device__ __forceinline__ bool tile_oproj_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0, B = p.B;
     const int K = p.Hq * p.D;
     const uint16_t* W = wptr(p, l, W_O);
     float* sPart = reinterpret_cast<float*>(cx.lds);
-    float* sSS = sPart + kMmPartFloats;
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     bool ok = true;
-    const float* att = attout_at(p, l);
-    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
-    with_ncb(ncb, [&](auto n) {
-        mm_block<decltype(n)::v, false>(
+    const float* att = attout_at(p, l);   // split form (see st_split8)
+    const int nc = nc8_tokens(B);
+    with_nc8(B, [&](auto n) {
+        mm_block_s<decltype(n)::v>(
             1, K, [&](int, int r) { return W + (int64_t)(r0 + (r < nrows ? r : nrows - 1)) * K; },
-            [&](int c) -> const float* { return c < B ? att + (int64_t)c * K : nullptr; }, nullptr,
+            [&](int c) -> const float* { return c < B ? att + (int64_t)c * K : nullptr; },
             [&]() {
                 ok = block_wait(p, t.ctr, t.target, cx.t_wait);
                 mark(cx, 0);
             },
-            sPart, sSS);
+            sPart);
     });
     if (!ok) return false;
     const float* xin = x_at(p, 2 * l);
@@ -297,7 +427,10 @@ __device__ __forceinline__ bool tile_oproj_mm(const Task& t, TileCtx& cx) {
 
 // ------------------------------------------------------------------ router
 
-// Rows a0..a1 (<= 16) of the router: logits = W_r (g o x_mid) / rms(x_mid) (+ bias).
+// Rows a0..a1 (<= 16) of the router: logits = W_r (g o x_mid) / rms(x_mid)
+// (+ bias). Also writes its share (8-element groups a2..a3) of the experts'
+// input h2 = RMSNorm(x_mid) * g in split form, as the one- and two-token
+// tiles normalise it: (x * rs) * g.
 __device__ __forceinline__ bool tile_router_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0, B = p.B, H = p.H;
@@ -324,6 +457,23 @@ __device__ __forceinline__ bool tile_router_mm(const Task& t, TileCtx& cx) {
         const int r = i / B, b = i - r * B;
         const float v = mm_c(sPart, nc, 1, 0, r, b) * rms_scale(p, mm_ss(sSS, nc, 1, b));
         st_dev(out + (int64_t)b * p.E + r0 + r, bias != nullptr ? v + ldg(bias + r0 + r) : v);
+    }
+    // this tile's share of the expert input h2 = RMSNorm(x_mid) * g, split:
+    // groups of 8 elements [t.a2, t.a3)
+    const uint16_t* gn = wptr(p, l, W_FFN_NORM);
+    float* h2 = h2s_at(p, l);
+    const int g0 = t.a2, ng = t.a3 - t.a2;
+    for (int i = tid_(); i < ng * B; i += NT) {
+        const int b = i / ng, k = 8 * (g0 + i - b * ng);
+        const float rs = rms_scale(p, mm_ss(sSS, nc, 1, b));
+        const float4 u = ldf4(xm + (int64_t)b * H + k), v = ldf4(xm + (int64_t)b * H + k + 4);
+        const uint4 gw = ld16(gn + k);
+        const float x8[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+        const float g8[8] = {bflo(gw.x), bfhi(gw.x), bflo(gw.y), bfhi(gw.y), bflo(gw.z), bfhi(gw.z), bflo(gw.w), bfhi(gw.w)};
+        float h8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h8[j] = (x8[j] * rs) * g8[j];
+        st_split8(h2 + (int64_t)b * H + k, h8);
     }
     mark(cx, 1);
     block_signal(p, t.signal);
@@ -429,9 +579,10 @@ __device__ __forceinline__ bool tile_route(const Task& t, TileCtx& cx) {
 
 // ---------------------------------------------------------- expert gate/up
 
-// Slot a0 of the routing table, rows a1..a2 (<= 32) of its expert's gate and
-// up matrices, for the tokens routed to it: a = SiLU(W_gate h2) * (W_up h2),
-// h2 = RMSNorm(x_mid), written to the (token, rank) row of the activations.
+// Slot a0 of the routing table, rows a1..a2 (<= 32, a multiple of 8) of its
+// expert's gate and up matrices, for the tokens routed to it:
+// a = SiLU(W_gate h2) * (W_up h2), h2 = RMSNorm(x_mid) * g (split, from the
+// router tiles), written split to the (token, rank) row of the activations.
 // Row blocks: the gate rows first, then the up rows.
 __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
@@ -452,27 +603,34 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
     const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * I * H;
     const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * I * H;
     const int nrb = row_blocks(nrows), na = 2 * nrb;
-    const float* xm = x_at(p, 2 * l + 1);
-    const int ncb = (n + 15) >> 4, nc = ncb_cols(ncb);
-    with_ncb(ncb, [&](auto nn) {
-        mm_block<decltype(nn)::v, true>(
+    const float* h2 = h2s_at(p, l);   // split form
+    const int nc = nc8_tokens(n);
+    with_nc8(n, [&](auto nn) {
+        mm_block_s<decltype(nn)::v>(
             na, H,
             [&](int blk, int r) {
                 const int up = blk >= nrb, rr = 16 * (up ? blk - nrb : blk) + r;
                 return (up ? Wu : Wg) + (int64_t)(r0 + (rr < nrows ? rr : nrows - 1)) * H;
             },
-            [&](int c) -> const float* { return c < n ? xm + (int64_t)(sList[c] & 0xffff) * H : nullptr; },
-            wptr(p, l, W_FFN_NORM), [] {}, sPart, sSS);
+            [&](int c) -> const float* { return c < n ? h2 + (int64_t)(sList[c] & 0xffff) * H : nullptr; }, [] {},
+            sPart);
     });
     mark(cx, 1);
+    // outputs in split form, 8 rows per thread
     float* act = act_at(p, l);
-    for (int i = tid_(); i < nrows * n; i += NT) {
-        const int r = i / n, c = i - r * n;
-        const float rs = rms_scale(p, mm_ss(sSS, nc, na, c));
-        const float gv = mm_c(sPart, nc, na, r >> 4, r & 15, c) * rs;
-        const float uv = mm_c(sPart, nc, na, nrb + (r >> 4), r & 15, c) * rs;
+    const int n8 = nrows >> 3;
+    for (int i = tid_(); i < n8 * n; i += NT) {
+        const int c = i / n8, r = 8 * (i - c * n8);
+        float a8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int rr = r + j;
+            const float gv = mm_c(sPart, nc, na, rr >> 4, rr & 15, c);
+            const float uv = mm_c(sPart, nc, na, nrb + (rr >> 4), rr & 15, c);
+            a8[j] = (gv / (1.0f + expf(-gv))) * uv;
+        }
         const int ent = sList[c];
-        st_dev(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I + r0 + r, (gv / (1.0f + expf(-gv))) * uv);
+        st_split8(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I + r0 + r, a8);
     }
     mark(cx, 2);
     block_signal(p, t.signal);
@@ -482,8 +640,9 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
 // ------------------------------------------------------------ expert down
 
 // Rows a0..a1 (<= 16) of the hidden size, for slots a2, a2 + a3, a2 + 2 a3, ...
-// of the routing table: y = W_down a for each token routed to the slot's
-// expert, written to that token's (token, rank) row of the expert outputs.
+// of the routing table: y = W_down a (a split, from the gate/up tiles) for
+// each token routed to the slot's expert, written to that token's
+// (token, rank) row of the expert outputs.
 // Waves take the tile's slots in turn, each slot a whole product of its own.
 __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
@@ -500,32 +659,31 @@ __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     for (int s = q0 + Q * wave; s < nact; s += Q * NWAVES) {
         const int e = ldg(rt + 64 + s), n = ldg(rt + 64 + p.E + s);
         const int32_t* lst = rt + 64 + 2 * p.E + (int64_t)s * p.max_batch;
-        with_ncb((n + 15) >> 4, [&](auto nn) {
-            constexpr int NCB = decltype(nn)::v;
-            int ent[NCB];
-            const float* xc[NCB];
+        with_nc8(n, [&](auto nn) {
+            constexpr int NC8 = decltype(nn)::v;
+            int ent[NC8];
+            const uint4* xc[NC8];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const int c = 16 * cb + col;
+            for (int cb = 0; cb < NC8; ++cb) {
+                const int c = 8 * cb + (col >> 1);
                 ent[cb] = c < n ? ldg(lst + c) : -1;
-                xc[cb] = ent[cb] >= 0 ? act + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * I + 8 * g4 : nullptr;
+                xc[cb] = split_ptr(ent[cb] >= 0 ? act + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * I : nullptr,
+                                   8 * g4, col & 1);
             }
             const uint16_t* ar = Wd + ((int64_t)e * H + h0 + (col < nrows ? col : nrows - 1)) * I + 8 * g4;
-            f32x4_t acc[NCB];
-            float ss[NCB];
+            f32x4_t acc[NC8];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                ss[cb] = 0.f;
-            }
-            mm_wave<NCB, false>(ar, xc, nullptr, I >> 5, [] {}, acc, ss);
+            for (int cb = 0; cb < NC8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            mm_wave_s<NC8>(ar, xc, I >> 5, [] {}, acc);
+            if ((col & 1) == 0) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                if (ent[cb] < 0) continue;
-                float* yr = y + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * H + h0;
+                for (int cb = 0; cb < NC8; ++cb) {
+                    if (ent[cb] < 0) continue;
+                    float* yr = y + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * H + h0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
+                    for (int q = 0; q < 4; ++q)
+                        if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
+                }
             }
         });
     }

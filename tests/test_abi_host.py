@@ -143,14 +143,14 @@ def test_plan_counts_for_30b_batches(batch, rows_gu):
     assert ops[OP_ROUTER] == 48 * 16
     assert ops[OP_ROUTE] == 48
     assert ops[OP_GATEUP] == 48 * slots * (768 // rows_gu)
-    assert ops[OP_DOWN] == 48 * 128 * 2        # 16-row blocks x 2 slot groups
+    assert ops[OP_DOWN] == 48 * 128 * 4        # 16-row blocks x 4 slot groups
     assert ops[OP_MOESUM] == 48 * 128
     assert ops[OP_LMHEAD] == -(-151936 // 32)
     att = tasks[tasks[:, 0] == OP_ATTN]
     assert len(att) == 48 * batch * 4 * att[0, 5]
     # down slot groups: every slot in exactly one group
     dn = tasks[(tasks[:, 0] == OP_DOWN) & (tasks[:, 1] == 0)]
-    assert set(dn[:, 5]) == {2} and set(dn[:, 4]) == {0, 1}
+    assert set(dn[:, 5]) == {4} and set(dn[:, 4]) == {0, 1, 2, 3}
 
 
 def test_plan_rejects_bad_input():
