@@ -46,10 +46,10 @@ constexpr int kMaxBatchValu = 2;
 constexpr int kMaxBatchMM = 64;
 
 // LDS of the matrix-core tiles (general region): a block product's per-wave
-// partials [4][16][64] and sums of squares [4][64] fp32 plus 64 token-list
-// entries; the routing tile's token masks [256][2], ranks [64][256] (bytes)
+// partials [4][16][64] and sums of squares [4][64] fp32 plus 128 words of
+// token list and routing-table entries; the routing tile's token masks [256][2], ranks [64][256] (bytes)
 // and per-wave counts.
-constexpr int kMmLdsBytes = (4 * 16 * 64 + 4 * 64 + 64) * 4;
+constexpr int kMmLdsBytes = (4 * 16 * 64 + 4 * 64 + 128) * 4;
 constexpr int kRouteLdsBytes = 2 * 256 * 4 + kMaxBatchMM * 256 + 16;
 
 // Dependency level of an op in layer l (0 = embedding, last = LM head).

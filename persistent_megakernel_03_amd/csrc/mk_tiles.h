@@ -870,7 +870,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
             case OP_COMBINE: return tile_combine<S::D>(t, cx);
             case OP_OPROJ: return tile_oproj_mm(t, cx);
             case OP_ROUTER: return tile_router_mm(t, cx);
-            case OP_ROUTE: return tile_route<S::NE>(t, cx);
+            case OP_ROUTE: return tile_route<4 * S::NE>(t, cx);
             case OP_GATEUP: return tile_gateup_mm(t, cx);
             case OP_DOWN: return tile_down_mm(t, cx);
             case OP_MOESUM: return tile_moesum(t, cx);

@@ -176,7 +176,7 @@ __device__ __forceinline__ void mm_wave(const uint16_t* arow, const float* const
 // partial products [4][16][16 NCB] and sums of squares [4][16 NCB].
 constexpr int kMmPartFloats = NWAVES * 16 * 64;
 constexpr int kMmSsFloats = NWAVES * 64;
-static_assert(kMmLdsBytes == (kMmPartFloats + kMmSsFloats + 64) * 4, "matrix-core LDS size");
+static_assert(kMmLdsBytes == (kMmPartFloats + kMmSsFloats + 128) * 4, "matrix-core LDS size");
 
 // A product of `na` (1, 2 or 4) blocks of 16 weight rows with 16 NCB
 // activation columns over length K, by the whole workgroup: wave w takes row
@@ -482,12 +482,33 @@ __device__ __forceinline__ bool tile_router_mm(const Task& t, TileCtx& cx) {
 
 // ----------------------------------------------------------------- routing
 
+// Reductions over each row of 16 lanes (every lane of the row gets the result).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    return max(v, dpp_u32<0x140>(v));
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t v) {
+    v = min(v, dpp_u32<0xB1>(v));
+    v = min(v, dpp_u32<0x4E>(v));
+    v = min(v, dpp_u32<0x141>(v));
+    return min(v, dpp_u32<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    return v + dpp_mov<0x140>(v);
+}
+
 // Every token's top-k (ties to the lower expert index, the largest first)
 // and its routing weights (softmax over the selected logits); then the
 // routing table: selected experts in ascending id, each with its tokens in
-// ascending token order and their ranks. Wave w takes tokens w, w+4, ...;
-// thread e owns expert e (E <= 256).
-template <int NE>
+// ascending token order and their ranks. Each row of 16 lanes takes one
+// token (NE16 logits per lane, E <= 16 NE16), so a wave ranks four tokens at
+// once; thread e owns expert e for the table (E <= 256).
+template <int NE16>
 __device__ __forceinline__ bool tile_route(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, E = p.E, K = p.K, B = p.B;
@@ -502,13 +523,15 @@ __device__ __forceinline__ bool tile_route(const Task& t, TileCtx& cx) {
     const float* rl = rlogits_at(p, l);
     int32_t* rt = rtab_at(p, l);
     float* rw = rtab_w(p, rt);
-    for (int b = wave; b < B; b += NWAVES) {
-        uint32_t u[NE];  // 0: not a candidate (no float maps to 0)
+    const int gq = lane >> 4, li = lane & 15;
+    for (int b0 = 4 * wave; b0 < B; b0 += 4 * NWAVES) {
+        const int b = b0 + gq;
+        const bool valid = b < B;
+        uint32_t u[NE16];  // 0: not a candidate (no float maps to 0)
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int e = lane + 64 * i;
-            const float v = ld_dev(rl + (int64_t)b * E + (e < E ? e : E - 1));
-            u[i] = e < E ? fkey(v) : 0u;
+        for (int i = 0; i < NE16; ++i) {
+            const int e = li + 16 * i;
+            u[i] = (valid && e < E) ? fkey(ld_dev(rl + (int64_t)b * E + e)) : 0u;
         }
         uint32_t top = 0u;
         float sel = 0.f;
@@ -518,33 +541,32 @@ __device__ __forceinline__ bool tile_route(const Task& t, TileCtx& cx) {
             if (j < K) {
                 uint32_t v = u[0];
 #pragma unroll
-                for (int i = 1; i < NE; ++i) v = max(v, u[i]);
-                const uint32_t m = wave_max_u32(v);
-                int best = -1;
+                for (int i = 1; i < NE16; ++i) v = max(v, u[i]);
+                const uint32_t m = row16_max_u32(v);
+                uint32_t cand = 0xffffu;
 #pragma unroll
-                for (int i = NE - 1; i >= 0; --i) {
-                    const uint64_t bal = __ballot(u[i] == m);
-                    if (bal != 0ull) best = 64 * i + (int)__builtin_ctzll(bal);
-                }
+                for (int i = 0; i < NE16; ++i)
+                    if (u[i] == m) cand = min(cand, (uint32_t)(li + 16 * i));
+                const int best = (int)row16_min_u32(cand);
                 if (j == 0) top = m;
-                if (lane == j) {
+                if (li == j) {
                     sel = unkey(m);
                     myid = best;
                 }
 #pragma unroll
-                for (int i = 0; i < NE; ++i)
-                    if (64 * i + lane == best) u[i] = 0u;
+                for (int i = 0; i < NE16; ++i)
+                    if (li + 16 * i == best) u[i] = 0u;
             }
         }
-        const float ex = lane < K ? expf(sel - unkey(top)) : 0.f;
-        const float sum = wave_sum(ex);
-        if (lane < K) {
+        const float ex = li < K ? expf(sel - unkey(top)) : 0.f;
+        const float sum = row16_sum(ex);
+        if (valid && li < K) {
             const float w = ex / sum;
-            sRank[b * 256 + myid] = (int8_t)lane;
+            sRank[b * 256 + myid] = (int8_t)li;
             atomicOr(&sMask[2 * myid + (b >> 5)], 1u << (b & 31));
-            st_dev(rw + b * K + lane, w);
-            p.route_ids[((int64_t)l * p.max_batch + b) * K + lane] = myid;
-            p.route_w[((int64_t)l * p.max_batch + b) * K + lane] = w;
+            st_dev(rw + b * K + li, w);
+            p.route_ids[((int64_t)l * p.max_batch + b) * K + li] = myid;
+            p.route_w[((int64_t)l * p.max_batch + b) * K + li] = w;
         }
     }
     __syncthreads();
@@ -592,14 +614,22 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
     int* sList = reinterpret_cast<int*>(sSS + kMmSsFloats);
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
     mark(cx, 0);
+    // slot count, the slot's expert and token count, and its token list in
+    // one round trip (sList[64..66] = count, expert, tokens)
     const int32_t* rt = rtab_at(p, l);
-    if (slot >= ldg(rt)) {
+    {
+        const int tid = tid_();
+        int32_t v = 0;
+        if (tid < p.max_batch) v = ldg(rt + 64 + 2 * p.E + (int64_t)slot * p.max_batch + tid);
+        else if (tid >= 64 && tid < 67) v = ldg(rt + (tid == 64 ? 0 : 64 + (tid - 65) * p.E + slot));
+        if (tid < p.max_batch || (tid >= 64 && tid < 67)) sList[tid] = v;
+    }
+    __syncthreads();
+    if (slot >= sList[64]) {
         block_signal(p, t.signal);
         return true;
     }
-    const int e = ldg(rt + 64 + slot), n = ldg(rt + 64 + p.E + slot);
-    for (int i = tid_(); i < n; i += NT) sList[i] = ldg(rt + 64 + 2 * p.E + (int64_t)slot * p.max_batch + i);
-    __syncthreads();
+    const int e = sList[65], n = sList[66];
     const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * I * H;
     const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * I * H;
     const int nrb = row_blocks(nrows), na = 2 * nrb;
@@ -642,12 +672,14 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
 // Rows a0..a1 (<= 16) of the hidden size, for slots a2, a2 + a3, a2 + 2 a3, ...
 // of the routing table: y = W_down a (a split, from the gate/up tiles) for
 // each token routed to the slot's expert, written to that token's
-// (token, rank) row of the expert outputs.
-// Waves take the tile's slots in turn, each slot a whole product of its own.
+// (token, rank) row of the expert outputs. The slots' tables are read into
+// LDS once; waves take the slots in turn.
+constexpr int kDownLdsInts = 4096;
+static_assert(kDownLdsInts * 4 <= kRouteLdsBytes, "down tile tables fit the general LDS region");
 __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, q0 = t.a2, Q = t.a3;
-    const int H = p.H, K = p.K, I = p.I;
+    const int H = p.H, K = p.K, I = p.I, maxB = p.max_batch;
     const int tid = tid_(), wave = tid >> 6, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
     mark(cx, 0);
@@ -656,36 +688,114 @@ __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const uint16_t* Wd = wptr(p, l, W_DOWN);
     const float* act = act_at(p, l);
     float* y = ybuf_at(p, l);
-    for (int s = q0 + Q * wave; s < nact; s += Q * NWAVES) {
-        const int e = ldg(rt + 64 + s), n = ldg(rt + 64 + p.E + s);
-        const int32_t* lst = rt + 64 + 2 * p.E + (int64_t)s * p.max_batch;
-        with_nc8(n, [&](auto nn) {
-            constexpr int NC8 = decltype(nn)::v;
-            int ent[NC8];
-            const uint4* xc[NC8];
-#pragma unroll
-            for (int cb = 0; cb < NC8; ++cb) {
+    // this tile's slots q0 + Q i, i < mt, in chunks whose tables fit the LDS
+    const int mt = nact > q0 ? (nact - q0 + Q - 1) / Q : 0;
+    const int chunk = (kDownLdsInts - 64) / (maxB + 2);
+    int* sE = reinterpret_cast<int*>(cx.lds);
+    int* sN = sE + chunk;
+    int* sEnt = sN + chunk;
+    const int nsteps = I >> 5;
+    const int rsel = col < nrows ? col : nrows - 1;
+    for (int c0 = 0; c0 < mt; c0 += chunk) {
+        const int mc = min(chunk, mt - c0);
+        // the chunk's experts, token counts and token lists: one round trip
+        for (int i = tid; i < mc; i += NT) {
+            const int s = q0 + Q * (c0 + i);
+            sE[i] = ldg(rt + 64 + s);
+            sN[i] = ldg(rt + 64 + p.E + s);
+        }
+        for (int i = tid; i < mc * maxB; i += NT) {
+            const int j = i / maxB, c = i - j * maxB;
+            sEnt[i] = ldg(rt + 64 + 2 * p.E + (int64_t)(q0 + Q * (c0 + j)) * maxB + c);
+        }
+        __syncthreads();
+        uint32_t mx = 0u;
+        for (int i = lane; i < mc; i += 64) mx = max(mx, (uint32_t)sN[i]);
+        mx = wave_max_u32(mx);
+        // wave w takes the chunk's slots w, w + 4, ...: all its slots form one
+        // pipeline of load batches, so the next slot's rows are in flight
+        // while the current one finishes
+        const int mw = mc > wave ? (mc - wave + NWAVES - 1) / NWAVES : 0;
+        with_nc8((int)mx, [&](auto nn) {
+            constexpr int NC8 = decltype(nn)::v, PF = MmPfS<NC8>::v;
+            int spb = PF;   // k-steps per batch: the largest divisor of nsteps <= PF
+            while (nsteps % spb) --spb;
+            const int nbps = nsteps / spb, nbt = mw * nbps;
+            auto a_ptr = [&](int b) {
+                const int j = b / nbps, kb = b - j * nbps;
+                return Wd + ((int64_t)sE[wave + NWAVES * j] * H + h0 + rsel) * I + 8 * g4 + 32 * spb * kb;
+            };
+            auto x_ptr = [&](int b, int cb) -> const uint4* {
+                const int j = b / nbps, kb = b - j * nbps, i = wave + NWAVES * j;
                 const int c = 8 * cb + (col >> 1);
-                ent[cb] = c < n ? ldg(lst + c) : -1;
-                xc[cb] = split_ptr(ent[cb] >= 0 ? act + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * I : nullptr,
-                                   8 * g4, col & 1);
-            }
-            const uint16_t* ar = Wd + ((int64_t)e * H + h0 + (col < nrows ? col : nrows - 1)) * I + 8 * g4;
+                if (c >= sN[i]) return nullptr;
+                const int ent = sEnt[i * maxB + c];
+                return split_ptr(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I, 8 * g4 + 32 * spb * kb, col & 1);
+            };
+            uint4 a0[PF], a1[PF], x0[PF][NC8], x1[PF][NC8];
+            auto loadA = [&](uint4(&a)[PF], int b) {
+                const uint16_t* ap = a_ptr(b);
+#pragma unroll
+                for (int j = 0; j < PF; ++j)
+                    if (j < spb) a[j] = ld16s(ap + 32 * j);
+            };
+            auto loadX = [&](uint4(&x)[PF][NC8], int b) {
+#pragma unroll
+                for (int cb = 0; cb < NC8; ++cb) {
+                    const uint4* xp = x_ptr(b, cb);
+#pragma unroll
+                    for (int j = 0; j < PF; ++j)
+                        x[j][cb] = (j < spb && xp != nullptr) ? ld16(xp + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+                }
+            };
             f32x4_t acc[NC8];
 #pragma unroll
             for (int cb = 0; cb < NC8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            mm_wave_s<NC8>(ar, xc, I >> 5, [] {}, acc);
-            if ((col & 1) == 0) {
+            auto compute = [&](const uint4(&a)[PF], const uint4(&x)[PF][NC8], int b) {
 #pragma unroll
-                for (int cb = 0; cb < NC8; ++cb) {
-                    if (ent[cb] < 0) continue;
-                    float* yr = y + ((int64_t)(ent[cb] & 0xffff) * K + (ent[cb] >> 16)) * H + h0;
+                for (int j = 0; j < PF; ++j)
+                    if (j < spb) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
+                        for (int cb = 0; cb < NC8; ++cb) acc[cb] = mfma16x16x32(a[j], x[j][cb], acc[cb]);
+                    }
+                if ((b + 1) % nbps == 0) {
+                    // the slot's last batch: hi + lo, store, restart
+                    const int i = wave + NWAVES * (b / nbps);
+#pragma unroll
+                    for (int cb = 0; cb < NC8; ++cb) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[cb][q] += dpp_mov<0xB1>(acc[cb][q]);
+                        const int c = 8 * cb + (col >> 1);
+                        if ((col & 1) == 0 && c < sN[i]) {
+                            const int ent = sEnt[i * maxB + c];
+                            float* yr = y + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * H + h0;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
+                        }
+                        acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+            };
+            if (nbt > 0) {
+                loadA(a0, 0);
+                if (nbt > 1) loadA(a1, 1);
+                loadX(x0, 0);
+                for (int bt = 0; bt < nbt; bt += 2) {
+                    if (bt + 1 < nbt) loadX(x1, bt + 1);
+                    compute(a0, x0, bt);
+                    if (bt + 2 < nbt) {
+                        loadA(a0, bt + 2);
+                        loadX(x0, bt + 2);
+                    }
+                    if (bt + 1 < nbt) {
+                        compute(a1, x1, bt + 1);
+                        if (bt + 3 < nbt) loadA(a1, bt + 3);
+                    }
                 }
             }
         });
+        __syncthreads();
     }
     mark(cx, 1);
     block_signal(p, t.signal);
