@@ -15,6 +15,11 @@ the CPU oracle on a bounded sample.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                        [--sweep 4,16,64 [--sweep-steps K]]
 
+--ragged adds, under "ragged", the churning batch: 32 sequences with contexts
+log-uniform on [128, 32768], 4 of them replaced every 8 steps by new ones
+(contexts uniform on [128, 2048]), a Zipf(1.1) router bias, 256 timed steps;
+the megakernel and the per-op build.
+
 --sweep adds, under "batch_sweep", the same measurement at other batch sizes
 (each sequence at the same context, pages from a shuffled pool, per-sequence
 seeded first tokens): megakernel and per-op tok/s, kernel time, algorithmic
@@ -88,6 +93,8 @@ def main():
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--sweep", type=str, default="", help="comma-separated batch sizes to measure as well")
     ap.add_argument("--sweep-steps", type=int, default=32)
+    ap.add_argument("--ragged", action="store_true", help="also measure the churning 32-sequence batch")
+    ap.add_argument("--ragged-steps", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -247,6 +254,11 @@ def main():
     }
     if sweep:
         out["batch_sweep"] = sweep
+    if args.ragged:
+        if not args.sweep:
+            del k_pool, v_pool
+            torch.cuda.empty_cache()
+        out["ragged"] = run_ragged(cfg, weights, args.ragged_steps)
     print(json.dumps(out), flush=True)
 
     if args.calib_copy:
@@ -256,6 +268,78 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("calibration copy of 1 GiB done (3 launches)")
+
+
+def run_ragged(cfg, weights, steps, warmup=8, B=32):
+    """The churning batch (see the module docstring), megakernel then per-op,
+    each from the same initial state. Throughput is tokens over wall time of
+    the timed steps (host scheduling, plan rebuilds and joins included)."""
+    import torch
+
+    from persistent_megakernel_03_amd import mk, sol, synth
+
+    biases, alpha, slope = synth.zipf_router_bias(cfg)
+    w2 = dict(weights)
+    for l, b in enumerate(biases):
+        w2[f"layers.{l}.router_bias"] = torch.as_tensor(b).cuda()
+    P = cfg["page_size"]
+    max_pages = 32768 // P + (steps + warmup) // P + 2
+    probe = synth.RaggedBatch(B, 1 << 20, P, max_pages, cfg["vocab"])
+    for _ in range(steps + warmup + 16):
+        probe.advance()
+    n_pages = probe.peak_pages + 64
+    log(f"ragged: Zipf bias alpha {alpha:.4f} (fitted slope {slope:.3f}); pool of {n_pages} pages")
+    k_pool, v_oracle_layout = synth.make_kv_pool(cfg, n_pages, 1, "cuda")
+    v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
+    del v_oracle_layout
+    res = {}
+    for mode, nsteps in ((mk.MK_MODE_MEGAKERNEL, steps), (mk.MK_MODE_PEROP, max(16, steps // 4))):
+        k, v = k_pool.clone(), v_pool.clone()
+        rb = synth.RaggedBatch(B, n_pages, P, max_pages, cfg["vocab"])
+        dec = mk.Decoder(cfg, w2, k, v, max_batch=B, max_pages_per_seq=max_pages, mode=mode, time_kernels=True)
+        tokens = torch.tensor(rb.tokens, dtype=torch.int32, device="cuda")
+        logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
+
+        def one():
+            dec.step(rb.pos, rb.tables(), tokens, logits, seq_ids=rb.ids)
+            tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+            for b, tok in rb.advance().items():
+                tokens[b] = tok
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        assert dec.sync_check() == mk.MK_OK
+        t0 = time.perf_counter()
+        for _ in range(nsteps):
+            one()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if dec.sync_check() != mk.MK_OK:
+            raise RuntimeError("device status after the ragged run")
+        ctx = list(rb.pos)
+        dec.step(rb.pos, rb.tables(), tokens, logits, seq_ids=rb.ids)
+        kms = dec.kernel_ms()
+        dbg = dec.debug()
+        off = dbg.route_ids - dec.workspace.data_ptr()
+        n = cfg["n_layers"] * B * cfg["top_k"]
+        rid = dec.workspace[off:off + 4 * n].view(torch.int32).view(cfg["n_layers"], B, cfg["top_k"]).cpu().numpy()
+        dec.close()
+        del k, v
+        nexp = distinct_experts(rid, B)
+        by = sol.step_bytes(cfg, ctx, nexp, distinct_tokens=B)
+        name = "megakernel" if mode == mk.MK_MODE_MEGAKERNEL else "perop"
+        res[name] = {"value": round(B * nsteps / el, 2), "unit": "tok/s", "steps": nsteps,
+                     "ms_per_step": round(1e3 * el / nsteps, 4), "kernel_ms_sample": round(kms, 4),
+                     "bytes_per_step_sample": by, "distinct_experts_mean": round(float(np.mean(nexp)), 2),
+                     "frac_sample": round(by / (kms * 1e-3) / 1e9 / PEAK_GBS, 4),
+                     "mean_context": round(float(np.mean(ctx)), 1)}
+        log(f"ragged {name}: {res[name]['value']:.1f} tok/s over {nsteps} steps ({res[name]['ms_per_step']:.2f} ms/step); "
+            f"sample step kernel {kms:.3f} ms, {res[name]['distinct_experts_mean']} experts/layer, "
+            f"{100 * res[name]['frac_sample']:.1f}% of 8 TB/s")
+    res["zipf"] = {"s": 1.1, "alpha": round(alpha, 5), "fitted_slope": round(slope, 4)}
+    res["workload"] = "32 sequences, contexts log-uniform [128, 32768], 4 replaced every 8 steps (contexts [128, 2048])"
+    return res
 
 
 def cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, n_steps):

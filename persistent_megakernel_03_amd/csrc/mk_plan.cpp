@@ -69,13 +69,13 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
     *rows_down = rd;
 }
 
-void expert_rows_mm(const ModelShape& s, int n_wg, int S, int* rows_gu, int* down_groups) {
-    // gate/up: 16 rows per tile unless that makes more than four tiles per
-    // workgroup; down: 16-row blocks of the hidden size, the slots split into
-    // groups so that there are about as many down tiles as workgroups
-    *rows_gu = (int64_t)S * ceil_div(s.I, 16) <= 4 * (int64_t)n_wg ? 16 : 32;
-    const int nblk = ceil_div(s.H, 16);
-    *down_groups = std::max(1, std::min(S, n_wg / std::max(1, nblk)));
+void expert_groups_mm(const ModelShape& s, int n_wg, int S, int* gu_groups, int* down_groups) {
+    // gate/up: 8-row blocks of the expert width, the slots in groups so that
+    // there are about 1.5 tiles per workgroup; down: 16-row blocks of the
+    // hidden size, about one tile per workgroup
+    const int gblk = ceil_div(s.I, 8), dblk = ceil_div(s.H, 16);
+    *gu_groups = std::max(1, std::min(S, (3 * n_wg / 2 + gblk / 2) / std::max(1, gblk)));
+    *down_groups = std::max(1, std::min(S, n_wg / std::max(1, dblk)));
 }
 
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested) {
@@ -106,13 +106,13 @@ int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
                               ceil_div(s.H, cfg.rows_down);
     int64_t n = 1 + (int64_t)s.L * per_layer + ceil_div(s.V, cfg.rows_lm);
     if (s.max_batch > kMaxBatchValu) {
-        // matrix-core schedule: at most 2048 workgroups (down slot groups),
-        // gate/up tiles of at least 16 rows
+        // matrix-core schedule: expert tiles are (rows, slot group) pairs with
+        // at most min(E, B k) groups
         const int S = std::min(s.E, s.max_batch * s.K);
         const int64_t mm_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.mm_rows_qkv) +
                                  s.max_batch * (attn + comb) + ceil_div(s.H, cfg.mm_rows_o) +
-                                 ceil_div(s.E, cfg.mm_rows_router) + 1 + (int64_t)S * ceil_div(s.I, 16) +
-                                 (int64_t)ceil_div(s.H, 16) * std::min(S, 1024) + ceil_div(s.H, cfg.mm_rows_sum);
+                                 ceil_div(s.E, cfg.mm_rows_router) + 1 + (int64_t)S * ceil_div(s.I, 8) +
+                                 (int64_t)ceil_div(s.H, 16) * S + ceil_div(s.H, cfg.mm_rows_sum);
         const int64_t m = ceil_div(s.max_batch, cfg.mm_embed_tokens) + (int64_t)s.L * mm_layer +
                           ceil_div(s.V, cfg.mm_rows_lm);
         n = std::max(n, m);
@@ -266,9 +266,10 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
     const int no = ceil_div(s.H, cfg.mm_rows_o);
     const int nr = ceil_div(s.E, cfg.mm_rows_router);
     const int S = std::min(s.E, B * s.K);
-    int rows_gu = 16, Q = 1;
-    expert_rows_mm(s, n_wg, S, &rows_gu, &Q);
-    const int ngu = ceil_div(s.I, rows_gu);
+    int Qg = 1, Q = 1;
+    expert_groups_mm(s, n_wg, S, &Qg, &Q);
+    const int gblk = ceil_div(s.I, 8);
+    const int ngu = gblk * Qg;
     const int nblk = ceil_div(s.H, 16);
     const int nd = nblk * Q;
     const int ns = ceil_div(s.H, cfg.mm_rows_sum);
@@ -281,7 +282,7 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
         const int in_ctr = l == 0 ? cl.embed() : cl.moesum(l - 1);
         const int in_target = l == 0 ? ne : ns;
         const int defer_ctr = l == 0 ? -1 : cl.gateup(l - 1);
-        const int defer_target = l == 0 ? 0 : S * ngu;
+        const int defer_target = l == 0 ? 0 : ngu;
         for (int g = 0; g < s.Hkv; ++g) {
             for (int i = 0; i < nq; ++i) {
                 const int v0 = i * cfg.mm_rows_qkv, v1 = std::min(grows, v0 + cfg.mm_rows_qkv);
@@ -326,17 +327,17 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
         add(make_task(OP_ROUTE, l, 0, 1, 0, 0, -1, 0, cl.router(l), nr, cl.route(l), lv + 5), 4.0 * B * s.E,
             kDynamic);
         P.targets[cl.route(l)] = 1;
-        for (int sl = 0; sl < S; ++sl)
-            for (int i = 0; i < ngu; ++i) {
-                const int r0 = i * rows_gu, r1 = std::min(s.I, r0 + rows_gu);
-                add(make_task(OP_GATEUP, l, sl, r0, r1, 0, -1, 0, cl.route(l), 1, cl.gateup(l), lv + 6),
-                    4.0 * (r1 - r0) * s.H, kRouted);
+        for (int q = 0; q < Qg; ++q)
+            for (int i = 0; i < gblk; ++i) {
+                const int r0 = i * 8, r1 = std::min(s.I, r0 + 8);
+                add(make_task(OP_GATEUP, l, r0, r1, q, Qg, -1, 0, cl.route(l), 1, cl.gateup(l), lv + 6),
+                    4.0 * ceil_div(S - q, Qg) * (r1 - r0) * s.H, kRouted);
             }
-        P.targets[cl.gateup(l)] = S * ngu;
+        P.targets[cl.gateup(l)] = ngu;
         for (int q = 0; q < Q; ++q)
             for (int i = 0; i < nblk; ++i) {
                 const int r0 = i * 16, r1 = std::min(s.H, r0 + 16);
-                add(make_task(OP_DOWN, l, r0, r1, q, Q, -1, 0, cl.gateup(l), S * ngu, cl.down(l), lv + 7),
+                add(make_task(OP_DOWN, l, r0, r1, q, Q, -1, 0, cl.gateup(l), ngu, cl.down(l), lv + 7),
                     2.0 * ceil_div(S - q, Q) * (r1 - r0) * s.I, kRouted);
             }
         P.targets[cl.down(l)] = nd;
@@ -483,7 +484,12 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
             // one-/two-token down tiles carry their row count in a2 (the same for
             // every tile); matrix-core down tiles their slot group
             case OP_DOWN: ranges[std::make_tuple(t.op, t.layer, t.a2, 0)].push_back({t.a0, t.a1}); break;
-            case OP_GATEUP: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
+            // one-/two-token gate/up tiles: slot a0, rows a1..a2; matrix-core
+            // ones: rows a0..a1 of slot group a2
+            case OP_GATEUP:
+                if (P.B > kMaxBatchValu) ranges[std::make_tuple(t.op, t.layer, t.a2, 0)].push_back({t.a0, t.a1});
+                else ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2});
+                break;
             case OP_COMBINE: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a1 + 1}); break;
             default: break;
         }

@@ -68,8 +68,9 @@ struct Plan {
 // after them. Otherwise the configured sizes.
 void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down);
 
-// Batches of 3+: rows per gate/up tile (16 or 32), down tiles' slot groups.
-void expert_rows_mm(const ModelShape& s, int n_wg, int S, int* rows_gu, int* down_groups);
+// Batches of 3+: slot groups of the gate/up tiles (8-row blocks of the
+// expert width) and of the down tiles (16-row blocks of the hidden size).
+void expert_groups_mm(const ModelShape& s, int n_wg, int S, int* gu_groups, int* down_groups);
 
 // Attention chunk length for these contexts (tokens, multiple of 64).
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested);

@@ -248,7 +248,7 @@ __device__ __forceinline__ int nc8_tokens(int n) { return n <= 8 ? 8 : (n <= 16 
 
 template <int NC8>
 struct MmPfS {
-    static constexpr int v = NC8 == 1 ? 8 : (NC8 == 2 ? 6 : (NC8 == 4 ? 4 : 2));
+    static constexpr int v = NC8 == 1 ? 8 : (NC8 == 2 ? 6 : (NC8 == 4 ? 4 : 1));
 };
 
 // One wave's product over `nsteps` k-steps of 32 with split activations:
@@ -599,204 +599,250 @@ __device__ __forceinline__ bool tile_route(const Task& t, TileCtx& cx) {
     return true;
 }
 
-// ---------------------------------------------------------- expert gate/up
+// ------------------------------------------------------------ expert slots
 
-// Slot a0 of the routing table, rows a1..a2 (<= 32, a multiple of 8) of its
-// expert's gate and up matrices, for the tokens routed to it:
-// a = SiLU(W_gate h2) * (W_up h2), h2 = RMSNorm(x_mid) * g (split, from the
-// router tiles), written split to the (token, rank) row of the activations.
-// Row blocks: the gate rows first, then the up rows.
-__device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
-    const Params& p = cx.p;
-    const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1, H = p.H, K = p.K, I = p.I;
-    float* sPart = reinterpret_cast<float*>(cx.lds);
-    float* sSS = sPart + kMmPartFloats;
-    int* sList = reinterpret_cast<int*>(sSS + kMmSsFloats);
-    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
-    mark(cx, 0);
-    // slot count, the slot's expert and token count, and its token list in
-    // one round trip (sList[64..66] = count, expert, tokens)
-    const int32_t* rt = rtab_at(p, l);
-    {
-        const int tid = tid_();
-        int32_t v = 0;
-        if (tid < p.max_batch) v = ldg(rt + 64 + 2 * p.E + (int64_t)slot * p.max_batch + tid);
-        else if (tid >= 64 && tid < 67) v = ldg(rt + (tid == 64 ? 0 : 64 + (tid - 65) * p.E + slot));
-        if (tid < p.max_batch || (tid >= 64 && tid < 67)) sList[tid] = v;
+// Expert tiles for batches of 3+ are (rows, slot group) pairs: a tile takes
+// slots q0, q0 + Q, q0 + 2Q, ... of the routing table (however many experts
+// the step selected), and its waves take those slots in turn. The slots'
+// experts, token counts and token lists are read into LDS once per chunk of
+// slots; each wave then streams all its slots as one pipeline of load
+// batches, so the next slot's weight rows are in flight while the current
+// one finishes.
+constexpr int kDownLdsInts = 4096;
+static_assert(kDownLdsInts * 4 <= kRouteLdsBytes, "slot tables fit the general LDS region");
+
+struct SlotTables {
+    int* e;    // [chunk] expert of each slot
+    int* n;    // [chunk] tokens routed to it
+    int* ent;  // [chunk][max_batch] (token | rank << 16)
+    int chunk; // slots per LDS chunk
+};
+
+__device__ __forceinline__ SlotTables slot_tables(char* lds, int max_batch) {
+    SlotTables s;
+    s.chunk = (kDownLdsInts - 64) / (max_batch + 2);
+    s.e = reinterpret_cast<int*>(lds);
+    s.n = s.e + s.chunk;
+    s.ent = s.n + s.chunk;
+    return s;
+}
+
+// Read slots q0 + Q (c0 + i), i < mc, into LDS (one round trip), then barrier.
+__device__ __forceinline__ void load_slot_tables(const Params& p, const int32_t* rt, int q0, int Q, int c0, int mc,
+                                                 const SlotTables& s) {
+    const int tid = tid_(), maxB = p.max_batch;
+    for (int i = tid; i < mc; i += NT) {
+        const int sl = q0 + Q * (c0 + i);
+        s.e[i] = ldg(rt + 64 + sl);
+        s.n[i] = ldg(rt + 64 + p.E + sl);
+    }
+    for (int i = tid; i < mc * maxB; i += NT) {
+        const int j = i / maxB, c = i - j * maxB;
+        s.ent[i] = ldg(rt + 64 + 2 * p.E + (int64_t)(q0 + Q * (c0 + j)) * maxB + c);
     }
     __syncthreads();
-    if (slot >= sList[64]) {
-        block_signal(p, t.signal);
-        return true;
+}
+
+// One wave's slots (chunk indices wave, wave + 4, ...; mw of them) as one
+// stream of nsteps k-steps each: acc[cb] += A x B over the slot, then
+// flush(i, acc) at its end (acc: hi + lo summed on even columns; i: chunk
+// index). a_ptr(i, k) / x_ptr(i, cb, k): this lane's A row and B operand
+// (null: zero) at k-step k of slot i.
+template <int NC8, class APtr, class XPtr, class Flush>
+__device__ __forceinline__ void slot_stream(int mw, int nsteps, APtr&& a_ptr, XPtr&& x_ptr, Flush&& flush) {
+    constexpr int PF = MmPfS<NC8>::v;
+    const int wave = tid_() >> 6;
+    int spb = PF;   // k-steps per batch: the largest divisor of nsteps <= PF
+    while (nsteps % spb) --spb;
+    const int nbps = nsteps / spb, nbt = mw * nbps;
+    uint4 a0[PF], a1[PF], x0[PF][NC8], x1[PF][NC8];
+    auto loadA = [&](uint4(&a)[PF], int b) {
+        const int j = b / nbps;
+        const uint16_t* ap = a_ptr(wave + NWAVES * j, spb * (b - j * nbps));
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+            if (q < spb) a[q] = ld16s(ap + 32 * q);
+    };
+    auto loadX = [&](uint4(&x)[PF][NC8], int b) {
+        const int j = b / nbps;
+#pragma unroll
+        for (int cb = 0; cb < NC8; ++cb) {
+            const uint4* xp = x_ptr(wave + NWAVES * j, cb, spb * (b - j * nbps));
+#pragma unroll
+            for (int q = 0; q < PF; ++q)
+                x[q][cb] = (q < spb && xp != nullptr) ? ld16(xp + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    f32x4_t acc[NC8];
+#pragma unroll
+    for (int cb = 0; cb < NC8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const uint4(&a)[PF], const uint4(&x)[PF][NC8], int b) {
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+            if (q < spb) {
+#pragma unroll
+                for (int cb = 0; cb < NC8; ++cb) acc[cb] = mfma16x16x32(a[q], x[q][cb], acc[cb]);
+            }
+        if ((b + 1) % nbps == 0) {
+#pragma unroll
+            for (int cb = 0; cb < NC8; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[cb][q] += dpp_mov<0xB1>(acc[cb][q]);
+            flush(wave + NWAVES * (b / nbps), acc);
+#pragma unroll
+            for (int cb = 0; cb < NC8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    if (nbt > 0) {
+        loadA(a0, 0);
+        if (nbt > 1) loadA(a1, 1);
+        loadX(x0, 0);
+        for (int bt = 0; bt < nbt; bt += 2) {
+            if (bt + 1 < nbt) loadX(x1, bt + 1);
+            compute(a0, x0, bt);
+            if (bt + 2 < nbt) {
+                loadA(a0, bt + 2);
+                loadX(x0, bt + 2);
+            }
+            if (bt + 1 < nbt) {
+                compute(a1, x1, bt + 1);
+                if (bt + 3 < nbt) loadA(a1, bt + 3);
+            }
+        }
     }
-    const int e = sList[65], n = sList[66];
-    const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * I * H;
-    const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * I * H;
-    const int nrb = row_blocks(nrows), na = 2 * nrb;
-    const float* h2 = h2s_at(p, l);   // split form
-    const int nc = nc8_tokens(n);
-    with_nc8(n, [&](auto nn) {
-        mm_block_s<decltype(nn)::v>(
-            na, H,
-            [&](int blk, int r) {
-                const int up = blk >= nrb, rr = 16 * (up ? blk - nrb : blk) + r;
-                return (up ? Wu : Wg) + (int64_t)(r0 + (rr < nrows ? rr : nrows - 1)) * H;
+}
+
+// Runs body(tables, c0, mc, NC8 tag) per LDS chunk of this tile's slots, NC8
+// sized for the chunk's widest slot. Block-uniform.
+template <class Body>
+__device__ __forceinline__ void for_slot_chunks(const Params& p, const int32_t* rt, int q0, int Q, char* lds,
+                                                Body&& body) {
+    const int nact = ldg(rt);
+    const int mt = nact > q0 ? (nact - q0 + Q - 1) / Q : 0;
+    const SlotTables s = slot_tables(lds, p.max_batch);
+    const int lane = tid_() & 63;
+    for (int c0 = 0; c0 < mt; c0 += s.chunk) {
+        const int mc = min(s.chunk, mt - c0);
+        load_slot_tables(p, rt, q0, Q, c0, mc, s);
+        uint32_t mx = 0u;
+        for (int i = lane; i < mc; i += 64) mx = max(mx, (uint32_t)s.n[i]);
+        mx = wave_max_u32(mx);
+        with_nc8((int)mx, [&](auto nn) { body(s, mc, nn); });
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------- expert gate/up
+
+// Rows a0..a0+8 of the expert width, slots a2, a2 + a3, ... of the routing
+// table: a = SiLU(W_gate h2) * (W_up h2) for the tokens routed to each slot's
+// expert, h2 = RMSNorm(x_mid) * g (split, from the router tiles), written
+// split to the (token, rank) row of the activations. One MFMA block holds
+// the 8 gate rows (A rows 0-7) and the 8 up rows (A rows 8-15) of the slot's
+// expert, so SwiGLU pairs meet in one wave.
+__device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    const int l = t.layer, r0 = t.a0, q0 = t.a2, Q = t.a3, H = p.H, K = p.K, I = p.I;
+    const int lane = tid_() & 63, col = lane & 15, g4 = lane >> 4;
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    mark(cx, 0);
+    const int32_t* rt = rtab_at(p, l);
+    const uint16_t* Wg = wptr(p, l, W_GATE);
+    const uint16_t* Wu = wptr(p, l, W_UP);
+    const float* h2 = h2s_at(p, l);
+    float* act = act_at(p, l);
+    const int wave = tid_() >> 6;
+    for_slot_chunks(p, rt, q0, Q, cx.lds, [&](const SlotTables& s, int mc, auto nn) {
+        constexpr int NC8 = decltype(nn)::v;
+        const int mw = mc > wave ? (mc - wave + NWAVES - 1) / NWAVES : 0;
+        const uint16_t* Wrow = (col < 8 ? Wg : Wu) + (int64_t)(r0 + (col & 7)) * H + 8 * g4;
+        slot_stream<NC8>(
+            mw, H >> 5,
+            [&](int i, int k) { return Wrow + (int64_t)s.e[i] * I * H + 32 * k; },
+            [&](int i, int cb, int k) -> const uint4* {
+                const int c = 8 * cb + (col >> 1);
+                if (c >= s.n[i]) return nullptr;
+                return split_ptr(h2 + (int64_t)(s.ent[i * p.max_batch + c] & 0xffff) * H, 8 * g4 + 32 * k, col & 1);
             },
-            [&](int c) -> const float* { return c < n ? h2 + (int64_t)(sList[c] & 0xffff) * H : nullptr; }, [] {},
-            sPart);
+            [&](int i, f32x4_t(&acc)[NC8]) {
+                // lane (col, g4): rows 4 g4 + q; gate rows 0-7 in g4 0-1, up rows 8-15 in g4 2-3
+#pragma unroll
+                for (int cb = 0; cb < NC8; ++cb) {
+                    float a4[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float up = __shfl_xor(acc[cb][q], 32);
+                        const float g = acc[cb][q];
+                        a4[q] = (g / (1.0f + expf(-g))) * up;
+                    }
+                    const int c = 8 * cb + (col >> 1);
+                    if ((col & 1) == 0 && g4 < 2 && c < s.n[i]) {
+                        const int ent = s.ent[i * p.max_batch + c];
+                        // elements 4 g4 .. 4 g4 + 3 of the row's 8-group: half of its hi and of its lo half
+                        uint32_t hi0, lo0, hi1, lo1;
+                        split_pair(a4[0], a4[1], hi0, lo0);
+                        split_pair(a4[2], a4[3], hi1, lo1);
+                        uint32_t* d = reinterpret_cast<uint32_t*>(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I + r0);
+                        uint64_t* dh = reinterpret_cast<uint64_t*>(d + 2 * g4);
+                        uint64_t* dl = reinterpret_cast<uint64_t*>(d + 4 + 2 * g4);
+                        __hip_atomic_store(dh, (uint64_t)hi0 | ((uint64_t)hi1 << 32), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(dl, (uint64_t)lo0 | ((uint64_t)lo1 << 32), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            });
     });
     mark(cx, 1);
-    // outputs in split form, 8 rows per thread
-    float* act = act_at(p, l);
-    const int n8 = nrows >> 3;
-    for (int i = tid_(); i < n8 * n; i += NT) {
-        const int c = i / n8, r = 8 * (i - c * n8);
-        float a8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int rr = r + j;
-            const float gv = mm_c(sPart, nc, na, rr >> 4, rr & 15, c);
-            const float uv = mm_c(sPart, nc, na, nrb + (rr >> 4), rr & 15, c);
-            a8[j] = (gv / (1.0f + expf(-gv))) * uv;
-        }
-        const int ent = sList[c];
-        st_split8(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I + r0 + r, a8);
-    }
-    mark(cx, 2);
     block_signal(p, t.signal);
     return true;
 }
 
 // ------------------------------------------------------------ expert down
 
-// Rows a0..a1 (<= 16) of the hidden size, for slots a2, a2 + a3, a2 + 2 a3, ...
-// of the routing table: y = W_down a (a split, from the gate/up tiles) for
-// each token routed to the slot's expert, written to that token's
-// (token, rank) row of the expert outputs. The slots' tables are read into
-// LDS once; waves take the slots in turn.
-constexpr int kDownLdsInts = 4096;
-static_assert(kDownLdsInts * 4 <= kRouteLdsBytes, "down tile tables fit the general LDS region");
+// Rows a0..a1 (<= 16) of the hidden size, slots a2, a2 + a3, ... of the
+// routing table: y = W_down a (a split, from the gate/up tiles) for each
+// token routed to the slot's expert, written to that token's (token, rank)
+// row of the expert outputs.
 __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, q0 = t.a2, Q = t.a3;
-    const int H = p.H, K = p.K, I = p.I, maxB = p.max_batch;
-    const int tid = tid_(), wave = tid >> 6, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
+    const int H = p.H, K = p.K, I = p.I;
+    const int lane = tid_() & 63, col = lane & 15, g4 = lane >> 4, wave = tid_() >> 6;
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
     mark(cx, 0);
     const int32_t* rt = rtab_at(p, l);
-    const int nact = ldg(rt);
     const uint16_t* Wd = wptr(p, l, W_DOWN);
     const float* act = act_at(p, l);
     float* y = ybuf_at(p, l);
-    // this tile's slots q0 + Q i, i < mt, in chunks whose tables fit the LDS
-    const int mt = nact > q0 ? (nact - q0 + Q - 1) / Q : 0;
-    const int chunk = (kDownLdsInts - 64) / (maxB + 2);
-    int* sE = reinterpret_cast<int*>(cx.lds);
-    int* sN = sE + chunk;
-    int* sEnt = sN + chunk;
-    const int nsteps = I >> 5;
     const int rsel = col < nrows ? col : nrows - 1;
-    for (int c0 = 0; c0 < mt; c0 += chunk) {
-        const int mc = min(chunk, mt - c0);
-        // the chunk's experts, token counts and token lists: one round trip
-        for (int i = tid; i < mc; i += NT) {
-            const int s = q0 + Q * (c0 + i);
-            sE[i] = ldg(rt + 64 + s);
-            sN[i] = ldg(rt + 64 + p.E + s);
-        }
-        for (int i = tid; i < mc * maxB; i += NT) {
-            const int j = i / maxB, c = i - j * maxB;
-            sEnt[i] = ldg(rt + 64 + 2 * p.E + (int64_t)(q0 + Q * (c0 + j)) * maxB + c);
-        }
-        __syncthreads();
-        uint32_t mx = 0u;
-        for (int i = lane; i < mc; i += 64) mx = max(mx, (uint32_t)sN[i]);
-        mx = wave_max_u32(mx);
-        // wave w takes the chunk's slots w, w + 4, ...: all its slots form one
-        // pipeline of load batches, so the next slot's rows are in flight
-        // while the current one finishes
+    for_slot_chunks(p, rt, q0, Q, cx.lds, [&](const SlotTables& s, int mc, auto nn) {
+        constexpr int NC8 = decltype(nn)::v;
         const int mw = mc > wave ? (mc - wave + NWAVES - 1) / NWAVES : 0;
-        with_nc8((int)mx, [&](auto nn) {
-            constexpr int NC8 = decltype(nn)::v, PF = MmPfS<NC8>::v;
-            int spb = PF;   // k-steps per batch: the largest divisor of nsteps <= PF
-            while (nsteps % spb) --spb;
-            const int nbps = nsteps / spb, nbt = mw * nbps;
-            auto a_ptr = [&](int b) {
-                const int j = b / nbps, kb = b - j * nbps;
-                return Wd + ((int64_t)sE[wave + NWAVES * j] * H + h0 + rsel) * I + 8 * g4 + 32 * spb * kb;
-            };
-            auto x_ptr = [&](int b, int cb) -> const uint4* {
-                const int j = b / nbps, kb = b - j * nbps, i = wave + NWAVES * j;
+        const uint16_t* Wrow = Wd + (int64_t)(h0 + rsel) * I + 8 * g4;
+        slot_stream<NC8>(
+            mw, I >> 5,
+            [&](int i, int k) { return Wrow + (int64_t)s.e[i] * H * I + 32 * k; },
+            [&](int i, int cb, int k) -> const uint4* {
                 const int c = 8 * cb + (col >> 1);
-                if (c >= sN[i]) return nullptr;
-                const int ent = sEnt[i * maxB + c];
-                return split_ptr(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I, 8 * g4 + 32 * spb * kb, col & 1);
-            };
-            uint4 a0[PF], a1[PF], x0[PF][NC8], x1[PF][NC8];
-            auto loadA = [&](uint4(&a)[PF], int b) {
-                const uint16_t* ap = a_ptr(b);
-#pragma unroll
-                for (int j = 0; j < PF; ++j)
-                    if (j < spb) a[j] = ld16s(ap + 32 * j);
-            };
-            auto loadX = [&](uint4(&x)[PF][NC8], int b) {
+                if (c >= s.n[i]) return nullptr;
+                const int ent = s.ent[i * p.max_batch + c];
+                return split_ptr(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I, 8 * g4 + 32 * k, col & 1);
+            },
+            [&](int i, f32x4_t(&acc)[NC8]) {
 #pragma unroll
                 for (int cb = 0; cb < NC8; ++cb) {
-                    const uint4* xp = x_ptr(b, cb);
+                    const int c = 8 * cb + (col >> 1);
+                    if ((col & 1) == 0 && c < s.n[i]) {
+                        const int ent = s.ent[i * p.max_batch + c];
+                        float* yr = y + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * H + h0;
 #pragma unroll
-                    for (int j = 0; j < PF; ++j)
-                        x[j][cb] = (j < spb && xp != nullptr) ? ld16(xp + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
-                }
-            };
-            f32x4_t acc[NC8];
-#pragma unroll
-            for (int cb = 0; cb < NC8; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            auto compute = [&](const uint4(&a)[PF], const uint4(&x)[PF][NC8], int b) {
-#pragma unroll
-                for (int j = 0; j < PF; ++j)
-                    if (j < spb) {
-#pragma unroll
-                        for (int cb = 0; cb < NC8; ++cb) acc[cb] = mfma16x16x32(a[j], x[j][cb], acc[cb]);
-                    }
-                if ((b + 1) % nbps == 0) {
-                    // the slot's last batch: hi + lo, store, restart
-                    const int i = wave + NWAVES * (b / nbps);
-#pragma unroll
-                    for (int cb = 0; cb < NC8; ++cb) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[cb][q] += dpp_mov<0xB1>(acc[cb][q]);
-                        const int c = 8 * cb + (col >> 1);
-                        if ((col & 1) == 0 && c < sN[i]) {
-                            const int ent = sEnt[i * maxB + c];
-                            float* yr = y + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * H + h0;
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
-                        }
-                        acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        for (int q = 0; q < 4; ++q)
+                            if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
                     }
                 }
-            };
-            if (nbt > 0) {
-                loadA(a0, 0);
-                if (nbt > 1) loadA(a1, 1);
-                loadX(x0, 0);
-                for (int bt = 0; bt < nbt; bt += 2) {
-                    if (bt + 1 < nbt) loadX(x1, bt + 1);
-                    compute(a0, x0, bt);
-                    if (bt + 2 < nbt) {
-                        loadA(a0, bt + 2);
-                        loadX(x0, bt + 2);
-                    }
-                    if (bt + 1 < nbt) {
-                        compute(a1, x1, bt + 1);
-                        if (bt + 3 < nbt) loadA(a1, bt + 3);
-                    }
-                }
-            }
-        });
-        __syncthreads();
-    }
+            });
+    });
     mark(cx, 1);
     block_signal(p, t.signal);
     return true;

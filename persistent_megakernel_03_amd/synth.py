@@ -130,3 +130,111 @@ def make_tokens(n: int, vocab: int, seed: int = 3) -> np.ndarray:
 def bits(t: torch.Tensor) -> np.ndarray:
     """BF16 tensor -> uint16 numpy array of its bit patterns (host copy)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def zipf_router_bias(dims: dict, seed: int = 5, s: float = 1.1, n_tokens: int = 4096):
+    """Per-layer float32 router bias b_e = -alpha * s * ln(rank_e), rank_e a
+    seeded permutation of 1..E per layer, for a workload whose expert
+    popularity follows Zipf(s). alpha is set once by bisection so that, for
+    router logits drawn N(0, sigma^2) with sigma = 0.02 sqrt(H) (the spread a
+    N(0, 0.02) router gives a unit-RMS input), the selection counts of the
+    top-k experts, ordered by rank, fall off with a log-log slope of -s.
+    Returns (biases, alpha, fitted slope)."""
+    E, K, L, H = dims["n_experts"], dims["top_k"], dims["n_layers"], dims["hidden"]
+    sigma = 0.02 * float(np.sqrt(H))
+    rng = np.random.default_rng(tensor_seed(seed, "zipf.calib"))
+    logits = rng.standard_normal((n_tokens, E)) * sigma
+    lr = np.log(np.arange(1, E + 1, dtype=np.float64))
+
+    def slope(alpha):
+        z = logits - alpha * s * lr[None, :]
+        top = np.argpartition(-z, K - 1, axis=1)[:, :K]
+        cnt = np.bincount(top.ravel(), minlength=E).astype(np.float64)
+        keep = cnt > 0
+        return float(np.polyfit(lr[keep], np.log(cnt[keep]), 1)[0])
+
+    lo, hi = 0.0, 8.0
+    for _ in range(40):
+        mid = 0.5 * (lo + hi)
+        if slope(mid) > -s:
+            lo = mid
+        else:
+            hi = mid
+    alpha = 0.5 * (lo + hi)
+    biases = []
+    for l in range(L):
+        rank = np.random.default_rng(tensor_seed(seed, f"zipf.rank.{l}")).permutation(E) + 1
+        biases.append((-alpha * s * np.log(rank)).astype(np.float32))
+    return biases, alpha, slope(alpha)
+
+
+class RaggedBatch:
+    """A churning batch of `n_seqs` slots over a paged pool, as a serving
+    loop would run it: initial contexts log-uniform on [ctx_lo, ctx_hi];
+    every `every` steps `churn` seeded-random slots finish, their pages go
+    back to a free list, and new sequences take the slots with contexts
+    uniform on [join_lo, join_hi] (their cache pages hold the pool's random
+    prefill) and seeded first tokens. Pages are taken from the free list as
+    positions grow. Host bookkeeping only."""
+
+    def __init__(self, n_seqs: int, n_pages: int, page_size: int, max_pages: int, vocab: int, seed: int = 7,
+                 ctx_lo: int = 128, ctx_hi: int = 32768, join_lo: int = 128, join_hi: int = 2048,
+                 every: int = 8, churn: int = 4):
+        self.rng = np.random.default_rng(tensor_seed(seed, "ragged"))
+        self.P, self.max_pages, self.vocab = page_size, max_pages, vocab
+        self.every, self.churn, self.join = every, churn, (join_lo, join_hi)
+        # the page order has its own stream, so the schedule does not depend on the pool size
+        self.free = list(np.random.default_rng(tensor_seed(seed, "ragged.pages")).permutation(n_pages)[::-1])
+        self.pages_in_use = 0
+        self.peak_pages = 0
+        self.next_id = 0
+        self.ids, self.pos, self.pages = [], [], []
+        for _ in range(n_seqs):
+            ctx = int(np.exp(self.rng.uniform(np.log(ctx_lo), np.log(ctx_hi))))
+            self._admit(ctx)
+        self.tokens = [int(t) for t in self.rng.integers(0, vocab, size=n_seqs)]
+        self.step_no = 0
+
+    def _admit(self, ctx: int, slot: int = -1):
+        need = ctx // self.P + 1
+        if need > self.max_pages or need > len(self.free):
+            raise ValueError("pool or page table too small")
+        pages = [int(self.free.pop()) for _ in range(need)]
+        self._used(need)
+        if slot < 0:
+            self.ids.append(self.next_id); self.pos.append(ctx); self.pages.append(pages)
+        else:
+            self.ids[slot], self.pos[slot], self.pages[slot] = self.next_id, ctx, pages
+        self.next_id += 1
+
+    def _used(self, n: int):
+        self.pages_in_use += n
+        self.peak_pages = max(self.peak_pages, self.pages_in_use)
+
+    def tables(self) -> np.ndarray:
+        bt = np.zeros((len(self.pos), self.max_pages), np.int32)
+        for b, pg in enumerate(self.pages):
+            bt[b, :len(pg)] = pg
+        return bt
+
+    def advance(self):
+        """After a step: every position moves on by one (taking a page when it
+        crosses into a new one); on churn steps returns {slot: first token}
+        for the slots that new sequences took, else {}."""
+        self.step_no += 1
+        for b in range(len(self.pos)):
+            self.pos[b] += 1
+            if self.pos[b] // self.P >= len(self.pages[b]):
+                if self.pos[b] // self.P >= self.max_pages or not self.free:
+                    raise ValueError("pool or page table too small")
+                self.pages[b].append(int(self.free.pop()))
+                self._used(1)
+        joined = {}
+        if self.step_no % self.every == 0:
+            for b in sorted(self.rng.choice(len(self.pos), size=self.churn, replace=False).tolist()):
+                self.free.extend(self.pages[b])
+                self._used(-len(self.pages[b]))
+                ctx = int(self.rng.integers(self.join[0], self.join[1] + 1))
+                self._admit(ctx, b)
+                joined[b] = int(self.rng.integers(0, self.vocab))
+        return joined

@@ -33,14 +33,16 @@ class Setup:
     def fresh_pools(self):
         return self.k0.clone(), self.v0.clone()
 
-    def oracle_model(self, dtype=np.float32, lazy_experts: bool = False) -> DenseModel:
+    def oracle_model(self, dtype=np.float32, lazy_experts: bool = False, weights=None) -> DenseModel:
+        """weights: another name -> device tensor dict (default: this set-up's)."""
         cache = {}
+        wd = self.w_dev if weights is None else weights
 
         def src(name):
-            if name not in self.w_dev:
+            if name not in wd:
                 return None
             if name not in cache:
-                t = self.w_dev[name]
+                t = wd[name]
                 cache[name] = synth.bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
             return cache[name]
 
@@ -48,7 +50,7 @@ class Setup:
             return DenseModel(self.cfg, src, None, dtype)
 
         def esrc(layer, kind, e):
-            return synth.bits(self.w_dev[f"layers.{layer}.{kind}"][e])
+            return synth.bits(wd[f"layers.{layer}.{kind}"][e])
 
         def src_dense(name):
             if name.split(".")[-1] in ("w_gate", "w_up", "w_down"):

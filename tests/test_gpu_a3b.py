@@ -220,3 +220,49 @@ def test_a3b_batch_matches_oracle(weights, B):
         _check_against_oracle(s, bts[b], toks[b], row, ctx, written=written)
     del s, g, outs
     torch.cuda.empty_cache()
+
+
+def test_a3b_ragged_zipf_join_step(weights):
+    """The churning batch's shape on a join step: 32 sequences with contexts
+    log-uniform on [128, 32768] advanced 8 steps, so 4 have just joined with
+    short contexts, and a Zipf(1.1) router bias. The longest-context row and a
+    newly joined row are checked end to end against the oracle."""
+    B = 32
+    biases, _, _ = synth.zipf_router_bias(CFG)
+    w = dict(weights)
+    for l, b in enumerate(biases):
+        w[f"layers.{l}.router_bias"] = torch.as_tensor(b).cuda()
+    max_pages = 32768 // P + 4
+    rb = synth.RaggedBatch(B, 1 << 20, P, max_pages, CFG["vocab"])
+    joined = {}
+    for _ in range(8):
+        joined = rb.advance()
+    n_pages = rb.peak_pages + 8
+    rb = synth.RaggedBatch(B, n_pages, P, max_pages, CFG["vocab"])
+    for _ in range(8):
+        joined = rb.advance()
+    assert len(joined) == 4
+    print(f"a3b ragged: {B} sequences, contexts {min(rb.pos)}..{max(rb.pos)}, pool {n_pages} pages", flush=True)
+    s = Setup(CFG, n_pages=n_pages, seed=0, device_gen=True, weights=w)
+    toks = list(rb.tokens)
+    for b, tok in joined.items():
+        toks[b] = tok
+    k, v = s.fresh_pools()
+    dec = mk.Decoder(CFG, w, k, v, max_batch=B, max_pages_per_seq=max_pages)
+    tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, CFG["vocab"], dtype=torch.float32, device="cuda")
+    dec.step(rb.pos, rb.tables(), tokens, logits, seq_ids=rb.ids)
+    assert dec.sync_check() == mk.MK_OK
+    g = dict(logits=logits.cpu().numpy(), xs=x_layers(dec).cpu().numpy(), ids=route_ids(dec).cpu().numpy(),
+             k=k, v=v)
+    dec.close()
+    bts = rb.tables()
+    written = {(int(bts[b][rb.pos[b] // P]), rb.pos[b] % P) for b in range(B)}
+    # the oracle reads the biased router through the same weights dict
+    s.w_dev = w
+    for b in (int(np.argmax(rb.pos)), min(joined)):
+        row = dict(logits=g["logits"][b], xs=g["xs"][:, b], ids=g["ids"][:, b], k=g["k"], v=g["v"])
+        print(f"a3b ragged: oracle on row {b} at {rb.pos[b]} cached tokens", flush=True)
+        _check_against_oracle(s, [int(x) for x in bts[b]], toks[b], row, rb.pos[b], written=written)
+    del s, g
+    torch.cuda.empty_cache()

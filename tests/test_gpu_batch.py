@@ -12,7 +12,8 @@ equal to the per-op build bit for bit.
 Batches are ragged: seeded positions from 0 (empty cache) to 95, pages
 drawn from a shuffled pool. A batch of 64 identical sequences sends all 64
 tokens to the same two experts, which takes the expert tiles' widest token
-blocks (33-64 columns).
+blocks (33-64 columns). A churning batch (sequences leaving and joining,
+pages recycled through a free list) runs with a Zipf router bias.
 """
 
 import numpy as np
@@ -146,4 +147,46 @@ def test_batch_greedy_chain(setup):
         ol, _, _ = decode_step(model, kv, pos, bts, cur)
         assert np.max(np.abs(logits.cpu().numpy() - ol)) <= 5e-2
         tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+    dec.close()
+
+
+def test_churning_batch_with_zipf_bias(setup):
+    """Eight slots over 12 steps: every 4 steps three sequences finish and new
+    ones (new ids, recycled pages, fresh first tokens) take their slots; the
+    router carries a Zipf(1.1) bias. Each step is compared with the oracle
+    teacher-forced on the device's tokens and cache."""
+    s = setup
+    B = 8
+    biases, _, _ = synth.zipf_router_bias(CFG)
+    w = dict(s.w_dev)
+    for l, b in enumerate(biases):
+        w[f"layers.{l}.router_bias"] = torch.as_tensor(b).cuda()
+    rb = synth.RaggedBatch(B, N_PAGES, 16, PAGES_PER_SEQ, CFG["vocab"], seed=4, ctx_lo=2, ctx_hi=80,
+                           join_lo=0, join_hi=40, every=4, churn=3)
+    k, v = s.fresh_pools()
+    dec = mk.Decoder(CFG, w, k, v, max_batch=B, max_pages_per_seq=PAGES_PER_SEQ)
+    model = s.oracle_model(weights=w)
+    tokens = torch.tensor(rb.tokens, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, CFG["vocab"], device="cuda")
+    for st in range(12):
+        pos, bts, ids = list(rb.pos), rb.tables().tolist(), list(rb.ids)
+        cur = [int(x) for x in tokens.cpu().tolist()]
+        kv = s.oracle_kv(k, v)            # the cache as the device holds it before this step
+        print(f"churn step={st} ids={ids}", flush=True)
+        dec.step(pos, bts, tokens, logits, seq_ids=ids)
+        assert dec.sync_check() == mk.MK_OK
+        ol, tr, _ = decode_step(model, kv, pos, bts, cur)
+        gl = logits.cpu().numpy()
+        xs, rid = x_layers(dec).cpu().numpy(), route_ids(dec).cpu().numpy()
+        for b in range(B):
+            assert np.max(np.abs(gl[b] - ol[b])) <= 5e-2, ("logits", st, b)
+            for l in range(CFG["n_layers"]):
+                lt = tr[b].layers[l]
+                if not np.array_equal(rid[l, b], lt.ids):
+                    assert routing_margin(lt.router_logits, CFG["top_k"]) < 1e-4, ("routing", st, b, l)
+                    break
+                assert rel_l2(xs[2 * l + 2, b], lt.x_out) < 1e-2, ("x_out", st, b, l)
+        tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+        for b, tok in rb.advance().items():
+            tokens[b] = tok
     dec.close()
