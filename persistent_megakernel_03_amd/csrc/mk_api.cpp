@@ -184,7 +184,7 @@ struct mk_handle {
     // plan cache (the device holds the plan of the last key)
     bool have_plan = false;
     int plan_B = 0, plan_chunk = 0;
-    std::vector<int32_t> plan_chunks;
+    std::vector<int32_t> plan_chunks;   // attention chunks the plan reserves per sequence
     Plan plan;
     // pinned staging ring for per-step arrays and plans
     char* stage[kStageSlots] = {nullptr, nullptr, nullptr, nullptr};
@@ -351,7 +351,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         char* st = h->ws + h->lay.step;
         const int64_t B = d.max_batch;
         p.positions = reinterpret_cast<const int32_t*>(st);
-        p.n_chunks = reinterpret_cast<const int32_t*>(st + align256(B * 4));
+        p.seq_chunk = reinterpret_cast<const int32_t*>(st + align256(B * 4));
         p.rope = reinterpret_cast<const float*>(st + 2 * align256(B * 4));
         p.block_tables = reinterpret_cast<const int32_t*>(st + 2 * align256(B * 4) + align256(B * d.head_dim * 4));
         p.x = reinterpret_cast<float*>(h->ws + h->lay.x);
@@ -449,25 +449,56 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
                                 (long long)d.n_pages);
         }
 
-        // plan: rebuilt when the batch or a sequence's chunk count changes
+        // plan: reused while it still covers every sequence. A plan reserves
+        // attention chunks for kLookahead more tokens of each sequence (the
+        // chunks past a sequence's tokens run as empty tiles), and a
+        // sequence that outgrows its reservation (one that joined in the slot
+        // of a shorter one) stretches its own chunk length up to 2x the
+        // plan's. The plan is rebuilt when the batch size changes, a sequence
+        // would need more than that, the chunk length drifts a factor 2 from
+        // the balanced one, or reserved chunks exceed twice the needed ones.
         const ModelShape s = shape_of(d, h->lay.max_chunks);
         const TileConfig cfg = tile_config(h->o);
-        const int chunk = choose_chunk(s, h->n_wg, batch, positions, cfg.chunk);
-        std::vector<int32_t> nch(batch);
-        for (int b = 0; b < batch; ++b) nch[b] = (positions[b] + 1 + chunk - 1) / chunk;
-        if (!h->have_plan || h->plan_B != batch || h->plan_chunk != chunk || h->plan_chunks != nch) {
+        const int ideal = choose_chunk(s, h->n_wg, batch, positions, cfg.chunk);
+        bool reuse = h->have_plan && h->plan_B == batch;
+        if (reuse && (cfg.chunk > 0 ? h->plan_chunk != ideal
+                                     : (h->plan_chunk > 2 * ideal || 2 * h->plan_chunk < ideal)))
+            reuse = false;
+        int chunk = reuse ? h->plan_chunk : ideal;
+        auto seq_chunk = [&](int b) {
+            const int per = (positions[b] + h->plan_chunks[b]) / h->plan_chunks[b];   // ceil((pos + 1) / n)
+            return std::max(chunk, (per + 63) / 64 * 64);
+        };
+        if (reuse) {
+            int64_t planned = 0, needed = 0;
+            for (int b = 0; b < batch && reuse; ++b) {
+                if (seq_chunk(b) > 2 * chunk) reuse = false;
+                planned += h->plan_chunks[b];
+                needed += (positions[b] + chunk) / chunk;
+            }
+            if (planned > 2 * needed + batch) reuse = false;
+        }
+        if (!reuse) {
+            constexpr int kLookahead = 256;
+            chunk = ideal;
+            std::vector<int32_t> ppos(batch);
+            for (int b = 0; b < batch; ++b)
+                ppos[b] = std::max(positions[b], std::min(positions[b] + kLookahead, h->lay.max_chunks * chunk - 1));
             TileConfig c2 = cfg;
             c2.chunk = chunk;
-            const std::string err = build_plan(s, c2, h->n_wg, batch, positions, &h->plan);
+            const std::string err = build_plan(s, c2, h->n_wg, batch, ppos.data(), &h->plan);
             if (!err.empty()) return fail(MK_ERR_CAPACITY, "plan: %s", err.c_str());
             if ((int64_t)h->plan.tasks.size() > h->lay.cap_tasks) return fail(MK_ERR_CAPACITY, "too many tasks");
             mk_status st = upload_plan(h, stream);
             if (st != MK_OK) return st;
+            chunk = h->plan.chunk;
             h->have_plan = true;
             h->plan_B = batch;
             h->plan_chunk = chunk;
-            h->plan_chunks = nch;
+            h->plan_chunks = h->plan.n_chunks;
         }
+        std::vector<int32_t> nch(batch);
+        for (int b = 0; b < batch; ++b) nch[b] = seq_chunk(b);
 
         // per-step arrays through a pinned staging ring
         const int slot = h->stage_next;
@@ -477,7 +508,7 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
         const int64_t B = d.max_batch;
         memset(stg, 0, h->lay.step_bytes);
         int32_t* spos = reinterpret_cast<int32_t*>(stg);
-        int32_t* snch = reinterpret_cast<int32_t*>(stg + align256(B * 4));
+        int32_t* snch = reinterpret_cast<int32_t*>(stg + align256(B * 4));   // per-sequence chunk lengths
         float* srope = reinterpret_cast<float*>(stg + 2 * align256(B * 4));
         int32_t* sbt = reinterpret_cast<int32_t*>(stg + 2 * align256(B * 4) + align256(B * d.head_dim * 4));
         for (int b = 0; b < batch; ++b) {

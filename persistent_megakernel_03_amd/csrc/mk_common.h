@@ -118,7 +118,7 @@ struct Params {
     int32_t max_batch, max_pages, max_chunks;
     int64_t n_pages;
     // this step
-    int32_t B, chunk;
+    int32_t B, chunk;   // chunk: the plan's attention chunk length (a sequence may use a longer one)
     int32_t perop;      // 1: per-op launches (no counter waits / signals)
     int32_t trace_on;
     int64_t watchdog_ticks;
@@ -135,7 +135,7 @@ struct Params {
     const int32_t* positions;     // [max_batch]
     const int32_t* block_tables;  // [max_batch][max_pages]
     const float* rope;            // [max_batch][D/2][2] cos, sin
-    const int32_t* n_chunks;      // [max_batch]
+    const int32_t* seq_chunk;     // [max_batch] attention chunk length of each sequence (tokens)
     // workspace: every buffer exchanged between workgroups has one slice per
     // layer, so each is written at most once per step
     float* x;         // [2L+1][max_batch][H]

@@ -113,8 +113,9 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     const int quad = lane >> 4, col = lane & 15;
     const int G = p.G;
     const int pos = p.positions[b];
-    const int t0 = c * p.chunk;
-    const int t1 = min(t0 + p.chunk, pos + 1);
+    const int chunk = p.seq_chunk[b];
+    const int t0 = c * chunk;
+    const int t1 = min(t0 + chunk, pos + 1);
     const int t_old = min(t1, pos);
     const bool has_new = (t1 == pos + 1);
     const int* bt = p.block_tables + (int64_t)b * p.max_pages;
@@ -190,6 +191,22 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
         }
     };
 
+    if (t0 > pos) {
+        // a chunk the plan reserved past this sequence's tokens (plans are
+        // reused while sequences grow): an empty partial, weight 0 in the merge
+        float* part0 = part_at(p, l) + ((int64_t)b * p.Hq + g * G) * p.max_chunks * D;
+        float* ml0 = ml_at(p, l) + ((int64_t)b * p.Hq + g * G) * ml_row(p);
+        for (int i = tid; i < G * D; i += NT) {
+            const int h = i / D, d = i - h * D;
+            st_dev(part0 + ((int64_t)h * p.max_chunks + c) * D + d, 0.f);
+        }
+        if (tid < G) {
+            st_dev(ml0 + (int64_t)tid * ml_row(p) + 2 * c, -INFINITY);
+            st_dev(ml0 + (int64_t)tid * ml_row(p) + 2 * c + 1, 0.f);
+        }
+        block_signal(p, t.signal);
+        return true;
+    }
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
     load_kv(t0);
     // queries: lane (quad, col) holds head col's dims 32db + 8quad..+7 (zero

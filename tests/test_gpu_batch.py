@@ -190,3 +190,29 @@ def test_churning_batch_with_zipf_bias(setup):
         for b, tok in rb.advance().items():
             tokens[b] = tok
     dec.close()
+
+
+def test_longer_sequence_joins_a_reserved_slot(setup):
+    """A sequence of 500 cached tokens takes the slot of one of 10 in the
+    next step. The plan built for the first step reserved 3 chunks of 128
+    tokens for that slot (256 tokens of lookahead), so the step reuses it and
+    the new sequence spreads its 501 tokens over those 3 chunks (192 tokens
+    each). Both steps against the oracle, teacher-forced on the device's
+    cache."""
+    s = setup
+    pps = 40
+    bts = synth.make_block_tables(4, pps, N_PAGES, seed=31, shuffle=True).tolist()
+    k, v = s.fresh_pools()
+    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=3, max_pages_per_seq=pps)
+    model = s.oracle_model()
+    logits = torch.empty(3, CFG["vocab"], device="cuda")
+    steps = [([10, 20, 30], [bts[0], bts[1], bts[2]], [5, 6, 7], [1, 2, 3]),
+             ([500, 21, 31], [bts[3], bts[1], bts[2]], [9, 8, 4], [4, 2, 3])]
+    for pos, bt, toks, ids in steps:
+        kv = s.oracle_kv(k, v)
+        print(f"reserved-slot step pos={pos}", flush=True)
+        dec.step(pos, bt, torch.tensor(toks, dtype=torch.int32, device="cuda"), logits, seq_ids=ids)
+        assert dec.sync_check() == mk.MK_OK
+        ol, _, _ = decode_step(model, kv, pos, bt, toks)
+        assert np.max(np.abs(logits.cpu().numpy() - ol)) <= 5e-2
+    dec.close()
