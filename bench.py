@@ -13,7 +13,12 @@ build of the same tiles in the same harness, the roofline of the megakernel
 the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--sweep 4,16,64 [--sweep-steps K]]
+                       [--sweep 4,16,64 [--sweep-steps K]] [--long 32768,131072,262144]
+                       [--ragged]
+
+--long adds, under "long_context", batch 1 at other context lengths (e.g.
+32768,131072,262144; 32 timed steps each): megakernel and per-op tok/s, kernel
+time, algorithmic bytes per step and % of 8 TB/s.
 
 --ragged adds, under "ragged", the churning batch: 32 sequences with contexts
 log-uniform on [128, 32768], 4 of them replaced every 8 steps by new ones
@@ -93,6 +98,8 @@ def main():
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--sweep", type=str, default="", help="comma-separated batch sizes to measure as well")
     ap.add_argument("--sweep-steps", type=int, default=32)
+    ap.add_argument("--long", type=str, default="", help="comma-separated batch-1 context lengths to measure as well")
+    ap.add_argument("--long-steps", type=int, default=32)
     ap.add_argument("--ragged", action="store_true", help="also measure the churning 32-sequence batch")
     ap.add_argument("--ragged-steps", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true",
@@ -114,11 +121,11 @@ def main():
     log(f"generating weights ({cfg['n_layers']} layers) on device")
     weights = synth.make_model(cfg, 0, "cuda")
 
-    def make_inputs(B, steps, warmup):
+    def make_inputs(B, steps, warmup, ctx=ctx):
         total_tokens = ctx + warmup + steps + 16 + 1  # + the per-step kernel timing pass
         pages_per_seq = -(-total_tokens // P)
         n_pages = pages_per_seq * B + 1
-        log(f"batch {B}: KV for {B} x {ctx} tokens ({n_pages} pages) on device")
+        log(f"batch {B}: KV for {B} x {ctx} tokens ({n_pages} pages, {2 * k_bytes(n_pages) / 1e9:.1f} GB) on device")
         k_pool, v_oracle_layout = synth.make_kv_pool(cfg, n_pages, 1, "cuda")
         v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
         del v_oracle_layout
@@ -127,11 +134,14 @@ def main():
         tok0 = synth.make_tokens(B, cfg["vocab"], seed=3)
         return pages_per_seq, k_pool, v_pool, block_tables, tok0
 
+    def k_bytes(n_pages):
+        return cfg["n_layers"] * n_pages * cfg["n_kv_heads"] * P * cfg["head_dim"] * 2
+
     pages_per_seq, k_pool, v_pool, block_tables, tok0 = make_inputs(B, args.steps, args.warmup)
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
     def run(mode: int, steps: int, warmup: int, k, v, B=B, pages_per_seq=pages_per_seq, block_tables=block_tables,
-            tok0=tok0):
+            tok0=tok0, ctx=ctx):
         dec = mk.Decoder(cfg, weights, k, v, max_batch=B, max_pages_per_seq=pages_per_seq, mode=mode,
                          wg_per_cu=args.wg_per_cu, time_kernels=True)
         tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
@@ -226,6 +236,34 @@ def main():
                 f"(kernels {kms_p:.3f} ms)")
             sweep.append(rec)
 
+    long_ctx = []
+    if args.long:
+        if not args.sweep:
+            del k_pool, v_pool
+            torch.cuda.empty_cache()
+        for T in [int(x) for x in args.long.split(",") if x]:
+            steps_l, warm_l = args.long_steps, 3
+            pps, kp, vp, bts, tk = make_inputs(1, steps_l, warm_l, ctx=T)
+            el_l, kms_l, rid_l, pe_l = run(mk.MK_MODE_MEGAKERNEL, steps_l, warm_l, kp, vp, 1, pps, bts, tk, ctx=T)
+            del kp, vp
+            torch.cuda.empty_cache()
+            # the per-op build on a fresh pool of the same contents (the megakernel run appended to the first)
+            pps, kp, vp, bts, tk = make_inputs(1, steps_l, warm_l, ctx=T)
+            el_p, kms_p, _, _ = run(mk.MK_MODE_PEROP, max(4, steps_l // 4), 2, kp, vp, 1, pps, bts, tk, ctx=T)
+            del kp, vp
+            torch.cuda.empty_cache()
+            by = sol.step_bytes(cfg, [p - 1 for p in pe_l], distinct_experts(rid_l, 1), distinct_tokens=1)
+            ach = by / (kms_l * 1e-3) / 1e9
+            rec = {"context": T, "value": round(steps_l / el_l, 2), "unit": "tok/s",
+                   "ms_per_step": round(1e3 * el_l / steps_l, 4), "kernel_ms": round(kms_l, 4),
+                   "bytes_per_step": by, "achieved_gbs": round(ach, 1), "frac": round(ach / PEAK_GBS, 4),
+                   "sol_tok_s": round(sol.sol_tokens_per_s(by, 1), 1),
+                   "perop_value": round(max(4, steps_l // 4) / el_p, 2), "perop_kernel_ms": round(kms_p, 4),
+                   "steps": steps_l}
+            log(f"context {T}: {rec['value']:.1f} tok/s (kernel {kms_l:.3f} ms, {100 * rec['frac']:.1f}% of 8 TB/s); "
+                f"per-op {rec['perop_value']:.1f} tok/s (kernels {kms_p:.3f} ms)")
+            long_ctx.append(rec)
+
     out = {
         "metric": METRIC,
         "value": round(tok_s, 2),
@@ -254,8 +292,10 @@ def main():
     }
     if sweep:
         out["batch_sweep"] = sweep
+    if long_ctx:
+        out["long_context"] = long_ctx
     if args.ragged:
-        if not args.sweep:
+        if not args.sweep and not args.long:
             del k_pool, v_pool
             torch.cuda.empty_cache()
         out["ragged"] = run_ragged(cfg, weights, args.ragged_steps)
