@@ -12,9 +12,15 @@ build of the same tiles in the same harness, the roofline of the megakernel
 (algorithmic bytes per step / measured kernel time vs the 8 TB/s HBM peak) and
 the CPU oracle on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-schedule]
                        [--sweep 4,16,64 [--sweep-steps K]] [--long 32768,131072,262144]
                        [--ragged]
+
+"schedule" is one traced step of the same workload after the timed ones:
+the fraction of workgroup time spent waiting on dependency counters (with
+the loads issued before each wait), the fraction computing, the fraction of
+compute units with a workgroup computing, and the time each dependency level
+adds to a layer.
 
 --long adds, under "long_context", batch 1 at other context lengths (e.g.
 32768,131072,262144; 32 timed steps each): megakernel and per-op tok/s, kernel
@@ -95,6 +101,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-perop", action="store_true")
+    ap.add_argument("--no-schedule", action="store_true", help="skip the traced step (wait-stall and busy fractions)")
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--sweep", type=str, default="", help="comma-separated batch sizes to measure as well")
     ap.add_argument("--sweep-steps", type=int, default=32)
@@ -203,6 +210,12 @@ def main():
                  "kernel_ms": kms2, "steps": steps2, "kind": "per-op launches, same tiles, eager"}
         log(f"per-op: {perop['value']:.1f} tok/s, kernels {kms2:.3f} ms/step")
 
+    sched = None
+    if not args.no_schedule:
+        k3, v3 = k_pool.clone(), v_pool.clone()
+        sched = schedule_stats(cfg, weights, k3, v3, block_tables, tok0, ctx, B, pages_per_seq)
+        del k3, v3
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, args.cpu_steps)
@@ -288,6 +301,7 @@ def main():
         "sol": {"bytes_per_step": bytes_step, "sol_tok_s": round(sol.sol_tokens_per_s(bytes_step, B), 1),
                 "pct_sol_step": round(100 * tok_s / sol.sol_tokens_per_s(bytes_step, B), 2)},
         "perop_baseline": perop,
+        "schedule": sched,
         "cpu_baseline": cpu,
     }
     if sweep:
@@ -381,6 +395,83 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
     res["zipf"] = {"s": 1.1, "alpha": round(alpha, 5), "fitted_slope": round(slope, 4)}
     res["workload"] = "32 sequences, contexts log-uniform [128, 32768], 4 replaced every 8 steps (contexts [128, 2048])"
     return res
+
+
+OP_NAMES = ["embed", "qkv", "attention", "merge", "o_proj", "router", "routing", "gate_up", "down", "expert_sum",
+            "lm_head"]
+
+
+def schedule_stats(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, pages_per_seq, warmup=3):
+    """One traced megakernel step after a few untraced ones (the in-kernel
+    trace: per task its start, the end of its last counter wait and its end,
+    100 MHz wall clock). Reports, over the step's span and all workgroups,
+    the fraction of workgroup time spent before a task's last counter wait
+    ended (waiting, plus the weight loads issued before it), the fraction
+    after it (compute, stores, signal), the fraction of compute units with a
+    workgroup past its wait (workgroups w and w + n_wg/2 share a unit), and
+    per tile kind the median over the middle layers of the time from the
+    previous level's last tile to the level's last tile."""
+    import torch
+
+    from persistent_megakernel_03_amd import mk
+
+    dec = mk.Decoder(cfg, weights, k_pool, v_pool, max_batch=B, max_pages_per_seq=pages_per_seq, trace=True)
+    tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
+    pos = [ctx] * B
+    for _ in range(warmup + 1):
+        dec.step(pos, block_tables, tokens, logits)
+        tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+        pos = [p + 1 for p in pos]
+    torch.cuda.synchronize()
+    if dec.sync_check() != mk.MK_OK:
+        raise RuntimeError("device status after the traced step")
+    tr = mk.mk_get_trace(dec.handle)
+    tasks = mk.mk_get_plan(dec.handle)
+    dec.close()
+    idx = (tr[:, 0] & 0xffffffff).astype(np.int64)
+    wg = (tr[:, 0] >> 32).astype(np.int64)
+    t0 = int(tr[:, 1].min())
+    st = (tr[:, 1].astype(np.int64) - t0) / 100.0
+    wt = (tr[:, 2].astype(np.int64) - t0) / 100.0
+    en = (tr[:, 7].astype(np.int64) - t0) / 100.0
+    span = float(en.max())
+    n_wg = int(wg.max()) + 1
+    wait = float(np.sum(wt - st)) / (n_wg * span)
+    busy = float(np.sum(en - wt)) / (n_wg * span)
+    # compute units with a workgroup past its wait: union of the two
+    # workgroups' busy intervals per unit
+    half = n_wg // 2
+    cu = wg % half if n_wg % 2 == 0 else wg
+    busy_cu = 0.0
+    for c in np.unique(cu):
+        m = np.where(cu == c)[0]
+        iv = sorted(zip(wt[m], en[m]))
+        cur0, cur1 = iv[0]
+        for a, b in iv[1:]:
+            if a > cur1:
+                busy_cu += cur1 - cur0
+                cur0, cur1 = a, b
+            else:
+                cur1 = max(cur1, b)
+        busy_cu += cur1 - cur0
+    n_cu = len(np.unique(cu))
+    op, layer, level = tasks[idx, 0], tasks[idx, 1], tasks[idx, 11]
+    L = cfg["n_layers"]
+    ends = {}
+    for lv in np.unique(level):
+        ends[int(lv)] = float(en[level == lv].max())
+    order = sorted(ends)
+    per = {}
+    for i, lv in enumerate(order[1:], 1):
+        m = level == lv
+        o, l = int(op[m][0]), int(layer[m][0])
+        if L // 6 <= l < L - L // 6 and o not in (0, 10):
+            per.setdefault(OP_NAMES[o], []).append(ends[lv] - ends[order[i - 1]])
+    return {"traced_step_us": round(span, 1), "wait_stall_frac": round(wait, 4), "busy_wg_frac": round(busy, 4),
+            "busy_cu_frac": round(float(busy_cu) / (n_cu * span), 4), "n_wg": n_wg,
+            "level_us": {k: round(float(np.median(v)), 2) for k, v in per.items()},
+            "kind": "one traced step after the timed steps; layers %d-%d for level_us" % (L // 6, L - L // 6 - 1)}
 
 
 def cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, n_steps):

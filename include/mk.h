@@ -233,6 +233,17 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
 mk_status mk_get_trace(mk_handle* h, void* host_buf, size_t bytes, size_t* written);
 
 /*
+ * Task table of the plan the last step ran: the records that the task
+ * indices of mk_get_trace refer to, 12 int32 each as for mk_plan_build, in
+ * the order the last step's kernels indexed them (grouped per workgroup in
+ * the megakernel mode, per dependency level in the per-op mode). Host work
+ * only. *n_tasks is always set; with tasks NULL nothing is copied.
+ * Errors: MK_ERR_INVALID (null handle or n_tasks, no step run yet),
+ * MK_ERR_CAPACITY (tasks non-NULL and cap_tasks < *n_tasks; nothing copied).
+ */
+mk_status mk_get_plan(mk_handle* h, int32_t* tasks, int64_t cap_tasks, int64_t* n_tasks);
+
+/*
  * Device time of the last step's kernels in milliseconds, from HIP events
  * recorded on the step's stream immediately before the first and after the
  * last kernel of the step (per-step staging copies excluded). Needs

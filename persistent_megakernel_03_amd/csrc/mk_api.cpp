@@ -195,6 +195,7 @@ struct mk_handle {
     hipEvent_t plan_ev;
     bool plan_ev_used = false;
     int64_t last_n_tasks = 0;
+    bool last_perop = false;  // the last step ran the per-op launches
     hipEvent_t t_begin, t_end;
     bool timed = false;
 };
@@ -560,6 +561,7 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
         }
         h->bank = 1 - h->bank;
         h->last_n_tasks = (int64_t)h->plan.tasks.size();
+        h->last_perop = h->o.mode != MK_MODE_MEGAKERNEL;
         return MK_OK;
     } catch (const std::bad_alloc&) {
         return fail(MK_ERR_CAPACITY, "host allocation failed");
@@ -621,6 +623,18 @@ mk_status mk_get_trace(mk_handle* h, void* host_buf, size_t bytes, size_t* writt
     MK_HIP(hipDeviceSynchronize());
     MK_HIP(hipMemcpy(host_buf, h->ws + h->lay.trace, n, hipMemcpyDeviceToHost));
     *written = n;
+    return MK_OK;
+}
+
+mk_status mk_get_plan(mk_handle* h, int32_t* tasks, int64_t cap_tasks, int64_t* n_tasks) {
+    if (!h || !n_tasks) return fail(MK_ERR_INVALID, "null argument");
+    if (h->last_n_tasks == 0) return fail(MK_ERR_INVALID, "no step has run on this handle");
+    const std::vector<Task>& T = h->last_perop ? h->plan.level_tasks : h->plan.tasks;
+    *n_tasks = (int64_t)T.size();
+    if (!tasks) return MK_OK;
+    if (cap_tasks < (int64_t)T.size()) return fail(MK_ERR_CAPACITY, "task buffer holds %lld of %lld tasks",
+                                                   (long long)cap_tasks, (long long)T.size());
+    memcpy(tasks, T.data(), T.size() * sizeof(Task));
     return MK_OK;
 }
 

@@ -35,7 +35,7 @@ STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID", -2: "MK_ERR_UNSUPPORTED", -3: 
 
 # Every function declared in include/mk.h.
 EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_set_mode",
-           "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_get_trace", "mk_kernel_time",
+           "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_get_trace", "mk_get_plan", "mk_kernel_time",
            "mk_destroy", "mk_last_error"]
 
 
@@ -116,6 +116,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_plan_build.restype = c.c_int
     lib.mk_get_trace.argtypes = [c.c_void_p, c.c_void_p, c.c_size_t, c.POINTER(c.c_size_t)]
     lib.mk_get_trace.restype = c.c_int
+    lib.mk_get_plan.argtypes = [c.c_void_p, c.POINTER(c.c_int32), c.c_int64, c.POINTER(c.c_int64)]
+    lib.mk_get_plan.restype = c.c_int
     lib.mk_kernel_time.argtypes = [c.c_void_p, c.POINTER(c.c_float)]
     lib.mk_kernel_time.restype = c.c_int
     lib.mk_destroy.argtypes = [c.c_void_p]
@@ -223,6 +225,17 @@ def mk_get_trace(h: int) -> np.ndarray:
     buf = np.zeros(n.value // 8, np.uint64)
     _check(lib.mk_get_trace(ctypes.c_void_p(h), buf.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)))
     return buf.reshape(-1, 8)
+
+
+def mk_get_plan(h: int) -> np.ndarray:
+    """Task table [n_tasks][12] int32 of the plan the last step ran."""
+    lib = load()
+    n = ctypes.c_int64()
+    _check(lib.mk_get_plan(ctypes.c_void_p(h), None, 0, ctypes.byref(n)))
+    tasks = np.zeros((n.value, 12), np.int32)
+    _check(lib.mk_get_plan(ctypes.c_void_p(h), tasks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value,
+                           ctypes.byref(n)))
+    return tasks
 
 
 def mk_kernel_time(h: int) -> float:

@@ -118,6 +118,40 @@ def test_megakernel_equals_perop_bitwise(setup):
     assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
 
 
+@pytest.mark.parametrize("mode", [mk.MK_MODE_MEGAKERNEL, mk.MK_MODE_PEROP])
+def test_trace_refers_to_the_plan_of_the_last_step(setup, mode):
+    """mk_get_plan returns the task table the last step's trace indexes: every
+    task recorded exactly once, start <= end of wait <= end, tasks of one
+    workgroup (megakernel) or the whole table (per-op) in level order."""
+    s = setup
+    k, v = s.fresh_pools()
+    dec = _decoder(s, k, v, mode, trace=True)
+    with pytest.raises(mk.MkError):
+        mk.mk_get_plan(dec.handle)
+    tokens = torch.tensor([5], dtype=torch.int32, device="cuda")
+    logits = torch.empty(1, CFG["vocab"], device="cuda")
+    for step in range(2):
+        dec.step([CTX + step], [list(range(PAGES_PER_SEQ))], tokens, logits)
+    assert dec.sync_check() == mk.MK_OK
+    tasks = mk.mk_get_plan(dec.handle)
+    tr = mk.mk_get_trace(dec.handle)
+    dec.close()
+    assert tasks.shape == (tr.shape[0], 12)
+    idx = (tr[:, 0] & 0xffffffff).astype(np.int64)
+    wg = (tr[:, 0] >> 32).astype(np.int64)
+    assert np.array_equal(np.sort(idx), np.arange(len(tasks)))
+    assert np.all(tr[:, 1] <= tr[:, 2]) and np.all(tr[:, 2] <= tr[:, 7])
+    assert np.all((tasks[:, 0] >= 0) & (tasks[:, 0] <= 10))
+    level = tasks[:, 11]
+    if mode == mk.MK_MODE_PEROP:
+        assert np.all(np.diff(level) >= 0)
+    else:
+        for w in np.unique(wg):
+            mine = np.sort(idx[wg == w])
+            assert np.array_equal(mine, np.arange(mine[0], mine[0] + len(mine)))
+            assert np.all(np.diff(level[mine]) >= 0)
+
+
 def test_step_writes_exactly_the_new_slot(setup):
     s = setup
     k, v = s.fresh_pools()
