@@ -29,7 +29,9 @@ time, algorithmic bytes per step and % of 8 TB/s.
 --ragged adds, under "ragged", the churning batch: 32 sequences with contexts
 log-uniform on [128, 32768], 4 of them replaced every 8 steps by new ones
 (contexts uniform on [128, 2048]), a Zipf(1.1) router bias, 256 timed steps;
-the megakernel and the per-op build.
+the megakernel with fixed per-workgroup lists, the megakernel with shared
+levels (workgroups claim the attention, merge, output-projection and expert
+tiles from per-level pools), and the per-op build.
 
 --sweep adds, under "batch_sweep", the same measurement at other batch sizes
 (each sequence at the same context, pages from a shuffled pool, per-sequence
@@ -348,10 +350,14 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
     v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
     del v_oracle_layout
     res = {}
-    for mode, nsteps in ((mk.MK_MODE_MEGAKERNEL, steps), (mk.MK_MODE_PEROP, steps)):
+    for name, mode, shared in (("megakernel", mk.MK_MODE_MEGAKERNEL, False),
+                               ("megakernel_shared_levels", mk.MK_MODE_MEGAKERNEL, True),
+                               ("perop", mk.MK_MODE_PEROP, False)):
+        nsteps = steps
         k, v = k_pool.clone(), v_pool.clone()
         rb = synth.RaggedBatch(B, n_pages, P, max_pages, cfg["vocab"])
-        dec = mk.Decoder(cfg, w2, k, v, max_batch=B, max_pages_per_seq=max_pages, mode=mode, time_kernels=True)
+        dec = mk.Decoder(cfg, w2, k, v, max_batch=B, max_pages_per_seq=max_pages, mode=mode, time_kernels=True,
+                         shared_levels=shared)
         tokens = torch.tensor(rb.tokens, dtype=torch.int32, device="cuda")
         logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
 
@@ -383,7 +389,6 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
         del k, v
         nexp = distinct_experts(rid, B)
         by = sol.step_bytes(cfg, ctx, nexp, distinct_tokens=B)
-        name = "megakernel" if mode == mk.MK_MODE_MEGAKERNEL else "perop"
         res[name] = {"value": round(B * nsteps / el, 2), "unit": "tok/s", "steps": nsteps,
                      "ms_per_step": round(1e3 * el / nsteps, 4), "kernel_ms_sample": round(kms, 4),
                      "bytes_per_step_sample": by, "distinct_experts_mean": round(float(np.mean(nexp)), 2),

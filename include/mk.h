@@ -122,7 +122,10 @@ typedef struct mk_options {
     int32_t split_kv_tokens; /* attention chunk length in tokens (multiple of 64); 0 = auto */
     int32_t n_cu_override;   /* 0 = the device's compute-unit count */
     int32_t time_kernels;    /* nonzero: bracket each step's kernels with HIP events (mk_kernel_time) */
-    int32_t reserved[4];
+    int32_t shared_levels;   /* batches of 3+, megakernel mode: nonzero puts the attention, merge, output-
+                                projection and expert tiles of each level in a pool that workgroups claim
+                                from (claim tasks, see mk_plan_build) instead of fixed per-workgroup lists */
+    int32_t reserved[3];
 } mk_options;
 
 typedef struct mk_handle mk_handle;
@@ -203,6 +206,10 @@ mk_status mk_get_debug_ptrs(mk_handle* h, mk_debug_ptrs* out);
  * is 12 int32: {op, layer, a0, a1, a2, a3, pre_ctr, pre_target, ctr, target,
  * signal, level}; `wg_offsets` has n_wg + 1 entries (CSR: tasks of workgroup
  * w are [wg_offsets[w], wg_offsets[w + 1])). Pass NULL buffers to query sizes.
+ * Batches of 3+: tasks of op 11 (claim) in a workgroup's list stand for the
+ * tiles of one level held in a pool: tasks [a0, a0 + a1), which follow all
+ * the lists (from wg_offsets[n_wg] on); the workgroups holding a claim task
+ * for the level take the pool's tiles in order until none is left.
  */
 typedef struct mk_plan_info {
     int32_t n_wg;

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <new>
@@ -110,6 +111,7 @@ std::string check_dims(const mk_dims& d) {
 TileConfig tile_config(const mk_options& o) {
     TileConfig c;
     c.chunk = o.split_kv_tokens;
+    c.shared_levels = o.shared_levels != 0;
     return c;
 }
 
@@ -400,8 +402,10 @@ mk_status mk_set_mode(mk_handle* h, int32_t mode) {
 
 static mk_status upload_plan(mk_handle* h, hipStream_t stream) {
     const Plan& P = h->plan;
-    const size_t nt = P.tasks.size();
-    const size_t bytes = nt * sizeof(Task) * 2 + (P.wg_off.size()) * 4;
+    // the megakernel's table (lists, then the pools of shared levels) and the
+    // per-op table (every tile, level by level; no claim tasks)
+    const size_t nt = P.tasks.size(), nl = P.level_tasks.size();
+    const size_t bytes = (nt + nl) * sizeof(Task) + (P.wg_off.size()) * 4;
     if (h->plan_ev_used) MK_HIP(hipEventSynchronize(h->plan_ev));
     if (bytes > h->plan_stage_bytes) {
         if (h->plan_stage) MK_HIP(hipHostFree(h->plan_stage));
@@ -411,12 +415,12 @@ static mk_status upload_plan(mk_handle* h, hipStream_t stream) {
     }
     char* s = h->plan_stage;
     memcpy(s, P.tasks.data(), nt * sizeof(Task));
-    memcpy(s + nt * sizeof(Task), P.level_tasks.data(), nt * sizeof(Task));
-    memcpy(s + 2 * nt * sizeof(Task), P.wg_off.data(), P.wg_off.size() * 4);
+    memcpy(s + nt * sizeof(Task), P.level_tasks.data(), nl * sizeof(Task));
+    memcpy(s + (nt + nl) * sizeof(Task), P.wg_off.data(), P.wg_off.size() * 4);
     MK_HIP(hipMemcpyAsync(h->ws + h->lay.tasks, s, nt * sizeof(Task), hipMemcpyHostToDevice, stream));
-    MK_HIP(hipMemcpyAsync(h->ws + h->lay.level_tasks, s + nt * sizeof(Task), nt * sizeof(Task), hipMemcpyHostToDevice,
+    MK_HIP(hipMemcpyAsync(h->ws + h->lay.level_tasks, s + nt * sizeof(Task), nl * sizeof(Task), hipMemcpyHostToDevice,
                           stream));
-    MK_HIP(hipMemcpyAsync(h->ws + h->lay.wg_off, s + 2 * nt * sizeof(Task), P.wg_off.size() * 4,
+    MK_HIP(hipMemcpyAsync(h->ws + h->lay.wg_off, s + (nt + nl) * sizeof(Task), P.wg_off.size() * 4,
                           hipMemcpyHostToDevice, stream));
     MK_HIP(hipEventRecord(h->plan_ev, stream));
     h->plan_ev_used = true;
@@ -560,7 +564,7 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
             h->timed = true;
         }
         h->bank = 1 - h->bank;
-        h->last_n_tasks = (int64_t)h->plan.tasks.size();
+        h->last_n_tasks = (int64_t)(h->o.mode == MK_MODE_MEGAKERNEL ? h->plan.tasks.size() : h->plan.level_tasks.size());
         h->last_perop = h->o.mode != MK_MODE_MEGAKERNEL;
         return MK_OK;
     } catch (const std::bad_alloc&) {

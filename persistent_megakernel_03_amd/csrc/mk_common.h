@@ -33,7 +33,10 @@ enum Op : int32_t {
     OP_DOWN = 8,    // expert down rows (batches of 1-2: + weighted combine + residual)
     OP_MOESUM = 9,  // batches of 3+: weighted sum of the experts' outputs + residual
     OP_LMHEAD = 10, // fused final RMSNorm + LM-head rows
-    OP_COUNT = 11
+    OP_CLAIM = 11,  // not a tile: run tiles of one level from a shared pool
+                    // (a0: first pool task, a1: pool size, a2: the level,
+                    // whose claim counter hands out pool positions)
+    OP_COUNT = 12
 };
 
 // QKV, ATTN, COMBINE, OPROJ, ROUTER, ROUTE, GATEUP, DOWN, MOESUM; ROUTE and
@@ -101,7 +104,13 @@ struct CounterLayout {
     MK_HD int down(int l) const { return combine(l) + 5; }
     MK_HD int moesum(int l) const { return combine(l) + 6; }
     MK_HD int n_main() const { return 1 + n_layers * per_layer(); }
-    MK_HD int64_t bank_words() const { return ((int64_t)n_main() * kCtrSub * kCtrStride + 63) & ~(int64_t)63; }
+    // one claim counter per dependency level (a single line each), after the
+    // split counters
+    MK_HD int n_levels() const { return 2 + kLevelsPerLayer * n_layers; }
+    MK_HD int64_t claim_word(int level) const { return ((int64_t)n_main() * kCtrSub + level) * kCtrStride; }
+    MK_HD int64_t bank_words() const {
+        return (((int64_t)n_main() * kCtrSub + n_levels()) * kCtrStride + 63) & ~(int64_t)63;
+    }
 };
 
 // Exchange buffers are padded so that no 128-byte cache line holds words of

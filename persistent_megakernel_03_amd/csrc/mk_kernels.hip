@@ -23,10 +23,54 @@ __global__ void __launch_bounds__(NT, 2) k_persistent(Params p, int general) {
     for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < p.bank_words; i += (int64_t)gridDim.x * NT)
         p.ctr_other[i] = 0u;
     __syncthreads();
+    // The list is walked in order. A claim task stands for the tiles of one
+    // level held in a shared pool: the workgroup takes pool positions from
+    // the level's claim counter (one atomic per tile, largest tiles first)
+    // and runs them until the pool is exhausted, so the tiles of an
+    // irregular level go to whichever workgroups are free first. Claimed
+    // tiles wait only on lower levels and every list is in level order, so
+    // the lowest unfinished tile can always run. One call site of run_task
+    // keeps the tile code inlined once.
+    __shared__ int s_pos;
     const int beg = p.wg_off[blockIdx.x], end = p.wg_off[blockIdx.x + 1];
-    for (int i = beg; i < end; ++i) {
-        const Task t = p.tasks[i];
-        if (!run_task<S, NB>(t, i + 1 < end ? &p.tasks[i + 1] : nullptr, p, lds, general, i)) break;
+    int i = beg;
+    int claim = -1;   // list position of the claim task being drained
+    for (;;) {
+        int ti;
+        if (claim < 0) {
+            if (i >= end) break;
+            if (p.tasks[i].op == OP_CLAIM) {
+                claim = i;
+                if (p.trace_on && tid_() == 0) p.trace[(int64_t)i * 8 + 1] = wall_clock64();
+            }
+        }
+        if (claim >= 0) {
+            const Task ct = p.tasks[claim];
+            if (tid_() == 0)
+                s_pos = (int)__hip_atomic_fetch_add(p.ctr + p.cl.claim_word(ct.a2), 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const int j = s_pos;
+            __syncthreads();
+            if (j >= ct.a1) {
+                if (p.trace_on && tid_() == 0) {
+                    uint64_t* rec = p.trace + (int64_t)claim * 8;
+                    rec[0] = (uint64_t)(uint32_t)claim | ((uint64_t)blockIdx.x << 32);
+                    rec[2] = rec[1];
+                    rec[3] = rec[4] = rec[5] = rec[6] = 0;
+                    rec[7] = wall_clock64();
+                }
+                claim = -1;
+                ++i;
+                continue;
+            }
+            ti = ct.a0 + j;
+        } else {
+            ti = i;
+        }
+        const Task t = p.tasks[ti];
+        if (!run_task<S, NB>(t, nullptr, p, lds, general, ti)) break;
+        if (claim < 0) ++i;
         __syncthreads();
     }
 }

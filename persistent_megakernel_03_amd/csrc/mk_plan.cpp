@@ -115,7 +115,8 @@ int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
                                  (int64_t)ceil_div(s.H, 16) * S + ceil_div(s.H, cfg.mm_rows_sum);
         const int64_t m = ceil_div(s.max_batch, cfg.mm_embed_tokens) + (int64_t)s.L * mm_layer +
                           ceil_div(s.V, cfg.mm_rows_lm);
-        n = std::max(n, m);
+        // each claim task stands for at least one tile of its level
+        n = std::max(n, cfg.shared_levels ? 2 * m : m);
     }
     return n;
 }
@@ -424,11 +425,53 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
         level_end[lv] = tiles.empty() ? (lv > 0 ? level_end[lv - 1] : 0.0) : end;
     }
     P.model_us = level_end.back();
+
+    // Irregular levels of the matrix-core schedule (attention chunks of
+    // ragged sequences, expert tiles whose slots carry different token
+    // counts, and the levels that follow them) are shared: each workgroup
+    // the model placed tiles of such a level on gets one claim task instead,
+    // and the level's tiles go to a pool, largest first, that those
+    // workgroups drain in order.
+    std::vector<Task> pool;
+    std::vector<std::vector<int>> claim_pos(n_wg);   // list positions of claim tasks
+    if (cfg.shared_levels && P.B > kMaxBatchValu) {
+        auto shared_op = [](int op) {
+            return op == OP_ATTN || op == OP_COMBINE || op == OP_OPROJ || op == OP_GATEUP || op == OP_DOWN;
+        };
+        std::vector<int> pool_start(P.n_levels, -1), pool_size(P.n_levels, 0);
+        for (int lv = 0; lv < P.n_levels; ++lv) {
+            if (levels[lv].empty() || !shared_op(levels[lv][0].t.op)) continue;
+            std::vector<Tile> tiles = levels[lv];
+            std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& b) { return a.bytes > b.bytes; });
+            pool_start[lv] = (int)pool.size();
+            pool_size[lv] = (int)tiles.size();
+            for (const Tile& t : tiles) pool.push_back(t.t);
+        }
+        for (int w = 0; w < n_wg; ++w) {
+            std::vector<Task> out;
+            for (const Task& t : lists[w]) {
+                const int lv = t.level;
+                if (pool_start[lv] < 0) {
+                    out.push_back(t);
+                } else if (out.empty() || out.back().op != OP_CLAIM || out.back().level != lv) {
+                    claim_pos[w].push_back((int)out.size());
+                    out.push_back(make_task(OP_CLAIM, t.layer, pool_start[lv], pool_size[lv], lv, 0, -1, 0, -1, 0, -1,
+                                            lv));
+                }
+            }
+            lists[w].swap(out);
+        }
+    }
     P.wg_off.assign(n_wg + 1, 0);
     for (int w = 0; w < n_wg; ++w) {
         P.wg_off[w + 1] = P.wg_off[w] + (int)lists[w].size();
         P.tasks.insert(P.tasks.end(), lists[w].begin(), lists[w].end());
     }
+    // pool positions become task-table indices
+    const int list_end = P.wg_off[n_wg];
+    for (int w = 0; w < n_wg; ++w)
+        for (int i : claim_pos[w]) P.tasks[P.wg_off[w] + i].a0 += list_end;
+    P.tasks.insert(P.tasks.end(), pool.begin(), pool.end());
 }
 
 std::string validate_plan(const ModelShape& s, const Plan& P) {
@@ -436,8 +479,28 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
     const int n_main = cl.n_main();
     char buf[256];
     if ((int)P.wg_off.size() != P.n_wg + 1) return "wg_off size";
-    if (P.wg_off.back() != (int)P.tasks.size()) return "wg_off end";
-    if (P.level_tasks.size() != P.tasks.size()) return "task count differs between orders";
+    if (P.wg_off.back() > (int)P.tasks.size()) return "wg_off end";
+    // claim tasks: each names a pool range of tasks of its own level past the
+    // lists; every pool task lies in exactly one range (claimed ranges may be
+    // named by many claim tasks)
+    const int list_end = P.wg_off.back();
+    std::vector<int> in_pool(P.tasks.size(), 0);
+    std::set<std::pair<int, int>> ranges_seen;
+    int n_claim = 0;
+    for (int i = 0; i < list_end; ++i) {
+        const Task& t = P.tasks[i];
+        if (t.op != OP_CLAIM) continue;
+        ++n_claim;
+        if (t.a0 < list_end || t.a1 <= 0 || t.a0 + t.a1 > (int)P.tasks.size()) return "claim range out of the pool";
+        if (t.a2 != t.level) return "claim of another level";
+        for (int j = t.a0; j < t.a0 + t.a1; ++j)
+            if (P.tasks[j].level != t.level || P.tasks[j].op == OP_CLAIM) return "pool task of another level";
+        if (ranges_seen.insert({t.a0, t.a1}).second)
+            for (int j = t.a0; j < t.a0 + t.a1; ++j) in_pool[j]++;
+    }
+    for (int j = list_end; j < (int)P.tasks.size(); ++j)
+        if (in_pool[j] != 1) return "pool task claimed by no range or by two";
+    if (P.level_tasks.size() != P.tasks.size() - n_claim) return "task count differs between orders";
     // final counter values and producer levels
     std::vector<int> final_val(n_main, 0), prod_level(n_main, -1);
     for (const Task& t : P.tasks) {

@@ -66,7 +66,7 @@ class mk_options(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("trace", ctypes.c_int32), ("watchdog_ns", ctypes.c_int64),
                 ("wg_per_cu", ctypes.c_int32), ("split_kv_tokens", ctypes.c_int32),
                 ("n_cu_override", ctypes.c_int32), ("time_kernels", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("shared_levels", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class mk_debug_ptrs(ctypes.Structure):
@@ -146,11 +146,13 @@ def make_dims(cfg: dict, max_batch: int, max_pages_per_seq: int, n_pages: int) -
 
 
 def make_options(mode: int = MK_MODE_MEGAKERNEL, trace: bool = False, watchdog_ns: int = 0, wg_per_cu: int = 0,
-                 split_kv_tokens: int = 0, n_cu_override: int = 0, time_kernels: bool = False) -> mk_options:
+                 split_kv_tokens: int = 0, n_cu_override: int = 0, time_kernels: bool = False,
+                 shared_levels: bool = False) -> mk_options:
     o = mk_options()
     o.mode, o.trace, o.watchdog_ns = mode, int(bool(trace)), watchdog_ns
     o.wg_per_cu, o.split_kv_tokens, o.n_cu_override = wg_per_cu, split_kv_tokens, n_cu_override
     o.time_kernels = int(bool(time_kernels))
+    o.shared_levels = int(bool(shared_levels))
     return o
 
 
@@ -257,11 +259,11 @@ class Decoder:
     def __init__(self, cfg: dict, weights: Dict[str, "torch.Tensor"], k_pool, v_pool, max_batch: int,
                  max_pages_per_seq: int, mode: int = MK_MODE_MEGAKERNEL, trace: bool = False,
                  watchdog_ns: int = 0, wg_per_cu: int = 0, split_kv_tokens: int = 0, device: int = 0,
-                 time_kernels: bool = False):
+                 time_kernels: bool = False, shared_levels: bool = False):
         import torch
         self.cfg = dict(cfg)
         self.dims = make_dims(cfg, max_batch, max_pages_per_seq, k_pool.shape[1])
-        self.opts = make_options(mode, trace, watchdog_ns, wg_per_cu, split_kv_tokens, 0, time_kernels)
+        self.opts = make_options(mode, trace, watchdog_ns, wg_per_cu, split_kv_tokens, 0, time_kernels, shared_levels)
         L = cfg["n_layers"]
         self._keep: List = [weights, k_pool, v_pool]
 

@@ -14,7 +14,7 @@ from persistent_megakernel_03_amd import configs, mk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 (OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_ROUTER, OP_ROUTE, OP_GATEUP, OP_DOWN, OP_MOESUM,
- OP_LMHEAD) = range(11)
+ OP_LMHEAD, OP_CLAIM) = range(12)
 LEVELS_PER_LAYER = 9
 
 
@@ -44,19 +44,38 @@ def test_workspace_and_pool_sizes():
 
 def simulate(tasks, offs, targets, rng):
     """Run the per-workgroup lists with a random interleaving and the counter
-    protocol; return the final counters, or raise on deadlock."""
+    protocol; a claim task takes tiles from its level's pool (past the lists)
+    in pool order until none is left. Returns the final counters and the
+    number of tiles run, or raises on deadlock."""
     n_wg = len(offs) - 1
     ctr = defaultdict(int)
+    claimed = defaultdict(int)   # claim counter per level
     nxt = [int(offs[w]) for w in range(n_wg)]
+    cur = [None] * n_wg  # pool tile a claim task is running
     stage = [0] * n_wg  # 0: before pre-wait, 1: before compute wait
     live = [w for w in range(n_wg) if nxt[w] < offs[w + 1]]
     steps = 0
+
+    def advance(w):
+        nxt[w] += 1
+        if nxt[w] >= offs[w + 1]:
+            live.remove(w)
+
     while live:
         progressed = False
         rng.shuffle(live)
         for w in list(live):
             t = tasks[nxt[w]]
-            op, layer, a0, a1, a2, a3, pre_c, pre_t, c, tg, sig, lvl = [int(v) for v in t]
+            if int(t[0]) == OP_CLAIM and cur[w] is None:
+                j = claimed[int(t[4])]
+                claimed[int(t[4])] += 1
+                progressed = True
+                if j >= int(t[3]):
+                    advance(w)
+                    continue
+                cur[w] = int(t[2]) + j
+            tile = tasks[cur[w]] if cur[w] is not None else t
+            op, layer, a0, a1, a2, a3, pre_c, pre_t, c, tg, sig, lvl = [int(v) for v in tile]
             if stage[w] == 0:
                 if pre_c >= 0 and ctr[pre_c] < pre_t:
                     continue
@@ -66,12 +85,13 @@ def simulate(tasks, offs, targets, rng):
             # run the tile
             if sig >= 0:
                 ctr[sig] += 1
-            nxt[w] += 1
             stage[w] = 0
             progressed = True
             steps += 1
-            if nxt[w] >= offs[w + 1]:
-                live.remove(w)
+            if cur[w] is not None:
+                cur[w] = None
+            else:
+                advance(w)
         if not progressed:
             raise RuntimeError("deadlock")
     return ctr, steps
@@ -87,19 +107,24 @@ def simulate(tasks, offs, targets, rng):
     ("TINY", 8, [5, 70, 64, 63, 1, 0, 127, 300], 512),
     ("A3B", 4, [8192, 100, 3000, 5], 512),
 ])
-def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
+@pytest.mark.parametrize("shared", [False, True])
+def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg, shared):
     cfg = configs.dims_of(cfg_name)
     d = mk.make_dims(cfg, max(2, batch), 600, 1200)
-    info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), n_wg, positions)
-    assert info.n_tasks == len(tasks) and offs[-1] == len(tasks)
+    info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(shared_levels=shared), n_wg, positions)
+    assert info.n_tasks == len(tasks) and offs[-1] <= len(tasks)
     # each workgroup list is in non-decreasing dependency level
     for w in range(n_wg):
         lv = tasks[offs[w]:offs[w + 1], 11]
         assert np.all(np.diff(lv) >= 0)
+    # claim tasks (batches of 3+ only) name pools past the lists
+    claims = tasks[:offs[-1]][tasks[:offs[-1], 0] == OP_CLAIM]
+    assert (len(claims) > 0) == (shared and batch > 2) and np.all(claims[:, 2] >= offs[-1])
+    n_tiles = len(tasks) - len(claims)
     # the counters reach exactly their targets, whatever the interleaving
     for seed in range(1 if batch > 2 and cfg_name == "A3B" else (2 if cfg_name == "A3B" else 5)):
         ctr, steps = simulate(tasks, offs, targets, random.Random(seed))
-        assert steps == len(tasks)
+        assert steps == n_tiles
         for c, t in enumerate(targets):
             assert ctr[c] == t, (c, ctr[c], t)
     # attention chunks cover every cached token plus the new one
@@ -114,7 +139,8 @@ def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg):
 def test_plan_counts_for_the_30b_shape():
     d = mk.make_dims(configs.A3B, 1, 520, 520)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192])
-    ops = np.bincount(tasks[:, 0], minlength=11)
+    ops = np.bincount(tasks[:, 0], minlength=12)
+    assert ops[OP_CLAIM] == 0                  # one- and two-token plans are fully static
     assert ops[OP_EMBED] == 1
     assert ops[OP_QKV] == 48 * 4 * 54          # 1280 rows per KV group, 24 per tile
     assert ops[OP_ATTN] == 48 * 4 * 65         # 8193 tokens in 128-token chunks
@@ -134,7 +160,7 @@ def test_plan_counts_for_30b_batches(batch):
     # routing tile; gate/up tiles are (8 rows, one of 8 slot groups) pairs
     d = mk.make_dims(configs.A3B, batch, 520, 520 * batch)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192] * batch)
-    ops = np.bincount(tasks[:, 0], minlength=11)
+    ops = np.bincount(tasks[:, 0], minlength=12)
     assert ops[OP_EMBED] == -(-batch // 4)
     assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
     assert ops[OP_COMBINE] == 48 * 32 * batch

@@ -46,13 +46,14 @@ def _batch(B, seed):
     return positions, bts, toks
 
 
-def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1):
+def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=False):
     B = len(positions)
     k, v = s.fresh_pools()
-    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=max(B, 3), max_pages_per_seq=PAGES_PER_SEQ, mode=mode)
+    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=max(B, 3), max_pages_per_seq=PAGES_PER_SEQ, mode=mode,
+                     shared_levels=shared)
     tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
     logits = torch.empty(B, CFG["vocab"], device="cuda")
-    print(f"batch B={B} mode={mode} steps={steps}", flush=True)
+    print(f"batch B={B} mode={mode} shared={shared} steps={steps}", flush=True)
     for st in range(steps):
         dec.step([p + st for p in positions], bts, tokens, logits, seq_ids=list(range(100, 100 + B)))
         assert dec.sync_check() == mk.MK_OK
@@ -109,6 +110,22 @@ def test_batch_megakernel_equals_perop_bitwise(setup):
     assert np.array_equal(a["xs"], b["xs"])
     assert np.array_equal(a["ids"], b["ids"])
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+
+
+@pytest.mark.parametrize("B", [8, 64])
+def test_shared_levels_equal_static_lists_bitwise(setup, B):
+    """Tiles claimed from shared pools compute exactly what the same tiles
+    compute from fixed lists (placement decides only where a tile runs), and
+    the shared-level step matches the oracle."""
+    positions, bts, toks = _batch(B, 11)
+    a = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2)
+    b = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2, shared=True)
+    assert np.array_equal(a["logits"], b["logits"])
+    assert np.array_equal(a["xs"], b["xs"])
+    assert np.array_equal(a["ids"], b["ids"])
+    assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+    g = _run(setup, positions, bts, toks, shared=True)
+    _check_rows(setup, positions, bts, toks, g)
 
 
 def test_identical_sequences_share_experts(setup):
