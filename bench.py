@@ -29,9 +29,10 @@ time, algorithmic bytes per step and % of 8 TB/s.
 --ragged adds, under "ragged", the churning batch: 32 sequences with contexts
 log-uniform on [128, 32768], 4 of them replaced every 8 steps by new ones
 (contexts uniform on [128, 2048]), a Zipf(1.1) router bias, 256 timed steps;
-the megakernel with fixed per-workgroup lists, the megakernel with shared
-levels (workgroups claim the attention, merge, output-projection and expert
-tiles from per-level pools), and the per-op build.
+the megakernel (its default: the ragged contexts make it share the
+attention, merge, output-projection and expert levels, whose tiles workgroups
+then claim from per-level pools), the megakernel with fixed per-workgroup
+lists only, and the per-op build.
 
 --sweep adds, under "batch_sweep", the same measurement at other batch sizes
 (each sequence at the same context, pages from a shuffled pool, per-sequence
@@ -350,9 +351,9 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
     v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
     del v_oracle_layout
     res = {}
-    for name, mode, shared in (("megakernel", mk.MK_MODE_MEGAKERNEL, False),
-                               ("megakernel_shared_levels", mk.MK_MODE_MEGAKERNEL, True),
-                               ("perop", mk.MK_MODE_PEROP, False)):
+    for name, mode, shared in (("megakernel", mk.MK_MODE_MEGAKERNEL, 0),
+                               ("megakernel_fixed_lists", mk.MK_MODE_MEGAKERNEL, -1),
+                               ("perop", mk.MK_MODE_PEROP, 0)):
         nsteps = steps
         k, v = k_pool.clone(), v_pool.clone()
         rb = synth.RaggedBatch(B, n_pages, P, max_pages, cfg["vocab"])

@@ -122,9 +122,11 @@ typedef struct mk_options {
     int32_t split_kv_tokens; /* attention chunk length in tokens (multiple of 64); 0 = auto */
     int32_t n_cu_override;   /* 0 = the device's compute-unit count */
     int32_t time_kernels;    /* nonzero: bracket each step's kernels with HIP events (mk_kernel_time) */
-    int32_t shared_levels;   /* batches of 3+, megakernel mode: nonzero puts the attention, merge, output-
-                                projection and expert tiles of each level in a pool that workgroups claim
-                                from (claim tasks, see mk_plan_build) instead of fixed per-workgroup lists */
+    int32_t shared_levels;   /* batches of 3+, megakernel mode: levels whose tiles workgroups claim from a
+                                pool (claim tasks, see mk_plan_build) instead of fixed per-workgroup
+                                lists. 0 = the attention, merge, output-projection and expert levels when
+                                the sequences need different numbers of attention chunks, else none;
+                                1 = the attention level; 2 = those five levels always; -1 = none */
     int32_t reserved[3];
 } mk_options;
 

@@ -111,7 +111,7 @@ std::string check_dims(const mk_dims& d) {
 TileConfig tile_config(const mk_options& o) {
     TileConfig c;
     c.chunk = o.split_kv_tokens;
-    c.shared_levels = o.shared_levels != 0;
+    c.shared_levels = o.shared_levels;
     return c;
 }
 

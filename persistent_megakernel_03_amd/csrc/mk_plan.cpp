@@ -116,7 +116,7 @@ int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
         const int64_t m = ceil_div(s.max_batch, cfg.mm_embed_tokens) + (int64_t)s.L * mm_layer +
                           ceil_div(s.V, cfg.mm_rows_lm);
         // each claim task stands for at least one tile of its level
-        n = std::max(n, cfg.shared_levels ? 2 * m : m);
+        n = std::max(n, 2 * m);
     }
     return n;
 }
@@ -426,18 +426,26 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     }
     P.model_us = level_end.back();
 
-    // Irregular levels of the matrix-core schedule (attention chunks of
-    // ragged sequences, expert tiles whose slots carry different token
-    // counts, and the levels that follow them) are shared: each workgroup
-    // the model placed tiles of such a level on gets one claim task instead,
-    // and the level's tiles go to a pool, largest first, that those
-    // workgroups drain in order.
+    // Shared levels (batches of 3+): each workgroup the model placed tiles of
+    // such a level on gets one claim task instead, and the level's tiles go to
+    // a pool, largest first, that those workgroups drain in order. By default
+    // the attention, merge, output-projection and expert levels are shared
+    // when the sequences need different numbers of attention chunks (ragged
+    // contexts): the attention tiles then differ in length and the levels
+    // after them start unevenly, which the timing model places worse than
+    // first-free claiming does. Uniform batches keep fixed lists (claiming
+    // costs one atomic round trip per tile).
     std::vector<Task> pool;
     std::vector<std::vector<int>> claim_pos(n_wg);   // list positions of claim tasks
-    if (cfg.shared_levels && P.B > kMaxBatchValu) {
-        auto shared_op = [](int op) {
+    bool ragged = false;
+    for (int b = 1; b < P.B; ++b) ragged = ragged || P.n_chunks[b] != P.n_chunks[0];
+    auto shared_op = [&](int op) {
+        if (cfg.shared_levels < 0 || P.B <= kMaxBatchValu) return false;
+        if (cfg.shared_levels >= 2 || (cfg.shared_levels == 0 && ragged))
             return op == OP_ATTN || op == OP_COMBINE || op == OP_OPROJ || op == OP_GATEUP || op == OP_DOWN;
-        };
+        return op == OP_ATTN && cfg.shared_levels == 1;
+    };
+    {
         std::vector<int> pool_start(P.n_levels, -1), pool_size(P.n_levels, 0);
         for (int lv = 0; lv < P.n_levels; ++lv) {
             if (levels[lv].empty() || !shared_op(levels[lv][0].t.op)) continue;

@@ -40,9 +40,12 @@ struct TileConfig {
     int mm_rows_lm = 32;
     int mm_embed_tokens = 4;
     int chunk = 0;  // attention chunk in tokens (multiple of 64); 0 = choose
-    // batches of 3+: attention, merge, output-projection and expert levels as
-    // shared pools that workgroups claim tiles from (claim tasks)
-    bool shared_levels = false;
+    // batches of 3+, levels whose tiles workgroups claim from a shared pool
+    // (claim tasks) instead of fixed lists: -1 none; 0 the attention, merge,
+    // output-projection and expert levels when the sequences need different
+    // numbers of attention chunks, else none; 1 the attention level; 2 the
+    // attention, merge, output-projection and expert levels
+    int shared_levels = 0;
     // timing model used to place tiles on workgroups
     double model_bw_bytes_per_us = 5.6e6;  // whole-device HBM bandwidth
     double model_task_us = 2.5;            // fixed cost of a task after its inputs are ready

@@ -147,12 +147,12 @@ def make_dims(cfg: dict, max_batch: int, max_pages_per_seq: int, n_pages: int) -
 
 def make_options(mode: int = MK_MODE_MEGAKERNEL, trace: bool = False, watchdog_ns: int = 0, wg_per_cu: int = 0,
                  split_kv_tokens: int = 0, n_cu_override: int = 0, time_kernels: bool = False,
-                 shared_levels: bool = False) -> mk_options:
+                 shared_levels: int = 0) -> mk_options:
     o = mk_options()
     o.mode, o.trace, o.watchdog_ns = mode, int(bool(trace)), watchdog_ns
     o.wg_per_cu, o.split_kv_tokens, o.n_cu_override = wg_per_cu, split_kv_tokens, n_cu_override
     o.time_kernels = int(bool(time_kernels))
-    o.shared_levels = int(bool(shared_levels))
+    o.shared_levels = int(shared_levels)
     return o
 
 
@@ -259,7 +259,7 @@ class Decoder:
     def __init__(self, cfg: dict, weights: Dict[str, "torch.Tensor"], k_pool, v_pool, max_batch: int,
                  max_pages_per_seq: int, mode: int = MK_MODE_MEGAKERNEL, trace: bool = False,
                  watchdog_ns: int = 0, wg_per_cu: int = 0, split_kv_tokens: int = 0, device: int = 0,
-                 time_kernels: bool = False, shared_levels: bool = False):
+                 time_kernels: bool = False, shared_levels: int = 0):
         import torch
         self.cfg = dict(cfg)
         self.dims = make_dims(cfg, max_batch, max_pages_per_seq, k_pool.shape[1])

@@ -107,7 +107,7 @@ def simulate(tasks, offs, targets, rng):
     ("TINY", 8, [5, 70, 64, 63, 1, 0, 127, 300], 512),
     ("A3B", 4, [8192, 100, 3000, 5], 512),
 ])
-@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("shared", [-1, 0, 2])
 def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg, shared):
     cfg = configs.dims_of(cfg_name)
     d = mk.make_dims(cfg, max(2, batch), 600, 1200)
@@ -119,7 +119,11 @@ def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg, share
         assert np.all(np.diff(lv) >= 0)
     # claim tasks (batches of 3+ only) name pools past the lists
     claims = tasks[:offs[-1]][tasks[:offs[-1], 0] == OP_CLAIM]
-    assert (len(claims) > 0) == (shared and batch > 2) and np.all(claims[:, 2] >= offs[-1])
+    assert np.all(claims[:, 2] >= offs[-1])
+    if shared != 0:
+        assert (len(claims) > 0) == (shared > 0 and batch > 2)
+    if shared == 0 and len(claims):   # ragged contexts only
+        assert OP_ATTN in set(tasks[claims[:, 2], 0])
     n_tiles = len(tasks) - len(claims)
     # the counters reach exactly their targets, whatever the interleaving
     for seed in range(1 if batch > 2 and cfg_name == "A3B" else (2 if cfg_name == "A3B" else 5)):

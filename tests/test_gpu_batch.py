@@ -46,7 +46,7 @@ def _batch(B, seed):
     return positions, bts, toks
 
 
-def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=False):
+def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=0):
     B = len(positions)
     k, v = s.fresh_pools()
     dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=max(B, 3), max_pages_per_seq=PAGES_PER_SEQ, mode=mode,
@@ -118,13 +118,13 @@ def test_shared_levels_equal_static_lists_bitwise(setup, B):
     compute from fixed lists (placement decides only where a tile runs), and
     the shared-level step matches the oracle."""
     positions, bts, toks = _batch(B, 11)
-    a = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2)
-    b = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2, shared=True)
+    a = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2, shared=-1)
+    b = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2, shared=2)
     assert np.array_equal(a["logits"], b["logits"])
     assert np.array_equal(a["xs"], b["xs"])
     assert np.array_equal(a["ids"], b["ids"])
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
-    g = _run(setup, positions, bts, toks, shared=True)
+    g = _run(setup, positions, bts, toks, shared=2)
     _check_rows(setup, positions, bts, toks, g)
 
 
