@@ -405,6 +405,7 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
 
 OP_NAMES = ["embed", "qkv", "attention", "merge", "o_proj", "router", "routing", "gate_up", "down", "expert_sum",
             "lm_head"]
+OP_CLAIM = 11
 
 
 def schedule_stats(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, pages_per_seq, warmup=3):
@@ -435,6 +436,15 @@ def schedule_stats(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, pag
     tr = mk.mk_get_trace(dec.handle)
     tasks = mk.mk_get_plan(dec.handle)
     dec.close()
+    return schedule_from_trace(tr, tasks, cfg["n_layers"])
+
+
+def schedule_from_trace(tr, tasks, L):
+    """The schedule figures of one traced step from its trace records
+    ({task | workgroup << 32, start, end of last wait, 4 marks, end}, 100 MHz
+    ticks) and the task table they index (see schedule_stats). Records of
+    claim tasks (which span the tiles they drain) are left out."""
+    tr = tr[tasks[(tr[:, 0] & 0xffffffff).astype(np.int64), 0] != OP_CLAIM]
     idx = (tr[:, 0] & 0xffffffff).astype(np.int64)
     wg = (tr[:, 0] >> 32).astype(np.int64)
     t0 = int(tr[:, 1].min())
@@ -463,7 +473,6 @@ def schedule_stats(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, pag
         busy_cu += cur1 - cur0
     n_cu = len(np.unique(cu))
     op, layer, level = tasks[idx, 0], tasks[idx, 1], tasks[idx, 11]
-    L = cfg["n_layers"]
     ends = {}
     for lv in np.unique(level):
         ends[int(lv)] = float(en[level == lv].max())
