@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(NT, 2) k_persistent(Params p, int general) {
             ti = i;
         }
         const Task t = p.tasks[ti];
-        if (!run_task<S, NB>(t, nullptr, p, lds, general, ti)) break;
+        if (!run_task<S, NB>(t, p, lds, general, ti)) break;
         if (claim < 0) ++i;
         __syncthreads();
     }
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(NT, 2) k_perop(Params p, int general, int firs
     const int i = first + blockIdx.x;
     const Task t = p.tasks[i];
     __syncthreads();
-    run_task<S, NB>(t, nullptr, p, lds, general, i);
+    run_task<S, NB>(t, p, lds, general, i);
 }
 
 __global__ void k_fill_u32(uint32_t* dst, int64_t n, uint32_t v) {

@@ -34,7 +34,6 @@ struct TileCtx {
     int general;      // bytes of the general LDS region
     uint64_t* t_wait; // trace: when the compute wait ended
     uint64_t* marks;  // trace: four phase stamps inside the tile
-    const Task* next; // the workgroup's next task (persistent mode), else null
 };
 
 // Trace stamp k (0..3) of the current tile (thread 0, tracing on).

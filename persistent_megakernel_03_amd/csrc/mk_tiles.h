@@ -913,12 +913,12 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
 // Run one task; with tracing on, thread 0 records {task | wg << 32, start,
 // end of the compute wait, four phase stamps, end}.
 template <class S, int NB>
-__device__ __forceinline__ bool run_task(const Task& t, const Task* next, const Params& p, char* lds, int general,
+__device__ __forceinline__ bool run_task(const Task& t, const Params& p, char* lds, int general,
                                          int idx) {
     uint64_t t_start = 0, t_wait = 0;
     uint64_t marks[4] = {0, 0, 0, 0};
     if (p.trace_on && tid_() == 0) t_start = t_wait = wall_clock64();
-    TileCtx cx{p, lds, general, &t_wait, marks, next};
+    TileCtx cx{p, lds, general, &t_wait, marks};
     const bool ok = dispatch_tile<S, NB>(t, cx);
     if (p.trace_on && tid_() == 0) {
         uint64_t* rec = p.trace + (int64_t)idx * 8;
