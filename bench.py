@@ -209,9 +209,21 @@ def main():
         steps2 = max(8, args.steps // 4)
         el2, kms2, _, _ = run(mk.MK_MODE_PEROP, steps2, 3, k2, v2)
         del k2, v2
-        perop = {"value": B * steps2 / el2, "unit": "tok/s", "ms_per_step": 1e3 * el2 / steps2,
-                 "kernel_ms": kms2, "steps": steps2, "kind": "per-op launches, same tiles, eager"}
-        log(f"per-op: {perop['value']:.1f} tok/s, kernels {kms2:.3f} ms/step")
+        eager = {"value": round(B * steps2 / el2, 2), "ms_per_step": round(1e3 * el2 / steps2, 4),
+                 "kernel_ms": round(kms2, 4), "steps": steps2}
+        log(f"per-op: {eager['value']:.1f} tok/s, kernels {kms2:.3f} ms/step")
+        k2, v2 = k_pool.clone(), v_pool.clone()
+        try:
+            graph = perop_graph(cfg, weights, k2, v2, block_tables, tok0, ctx, B, pages_per_seq, steps2, 3)
+            log(f"per-op as a HIP graph: {graph['value']:.1f} tok/s, {graph['ms_per_step']:.3f} ms/step")
+        except RuntimeError as e:   # capture refused: the eager figure stands
+            graph = {"value": 0.0, "error": str(e)[:200]}
+            log(f"per-op as a HIP graph: not measured ({graph['error']})")
+        del k2, v2
+        best = graph if graph["value"] > eager["value"] else eager
+        perop = {"value": best["value"], "unit": "tok/s", "ms_per_step": best["ms_per_step"],
+                 "kind": "per-op launches, same tiles; the better of eager launches and one captured HIP graph "
+                         "per step", "eager": eager, "graph": graph}
 
     sched = None
     if not args.no_schedule:
@@ -401,6 +413,46 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
     res["zipf"] = {"s": 1.1, "alpha": round(alpha, 5), "fitted_slope": round(slope, 4)}
     res["workload"] = "32 sequences, contexts log-uniform [128, 32768], 4 replaced every 8 steps (contexts [128, 2048])"
     return res
+
+
+def perop_graph(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, pages_per_seq, steps, warmup):
+    """The per-op build's step captured once as a HIP graph (its staging copy
+    and every level's launch), then replayed: each replay is the captured
+    step at the same positions (the same cache slot rewritten), with the
+    caller's greedy argmax between replays as in the eager loop."""
+    import torch
+
+    from persistent_megakernel_03_amd import mk
+
+    dec = mk.Decoder(cfg, weights, k_pool, v_pool, max_batch=B, max_pages_per_seq=pages_per_seq,
+                     mode=mk.MK_MODE_PEROP)
+    tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
+    pos = [ctx] * B
+    dec.step(pos, block_tables, tokens, logits)   # builds and uploads the plan outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        dec.step(pos, block_tables, tokens, logits)
+    torch.cuda.synchronize()
+
+    def one():
+        g.replay()
+        tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    if dec.sync_check() != mk.MK_OK:
+        raise RuntimeError("device status after the per-op graph replays")
+    del g
+    dec.close()
+    return {"value": round(B * steps / el, 2), "ms_per_step": round(1e3 * el / steps, 4), "steps": steps}
 
 
 OP_NAMES = ["embed", "qkv", "attention", "merge", "o_proj", "router", "routing", "gate_up", "down", "expert_sum",

@@ -152,6 +152,34 @@ def test_trace_refers_to_the_plan_of_the_last_step(setup, mode):
             assert np.all(np.diff(level[mine]) >= 0)
 
 
+def test_perop_step_replays_as_a_graph(setup):
+    """The per-op step (staging copy and every level's launch) captured as a
+    HIP graph: each replay, with eager work and synchronisation between
+    replays, gives the eager step's logits bit for bit."""
+    s = setup
+    k, v = s.fresh_pools()
+    dec = _decoder(s, k, v, mk.MK_MODE_PEROP)
+    tokens = torch.tensor([5], dtype=torch.int32, device="cuda")
+    logits = torch.empty(1, CFG["vocab"], device="cuda")
+    bt = [list(range(PAGES_PER_SEQ))]
+    dec.step([CTX], bt, tokens, logits)
+    assert dec.sync_check() == mk.MK_OK
+    eager = logits.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        dec.step([CTX], bt, tokens, logits)
+    torch.cuda.synchronize()
+    for r in range(3):
+        logits.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert dec.sync_check() == mk.MK_OK
+        assert torch.equal(logits, eager), r
+        assert torch.isfinite((logits * 2).sum()).item()
+    del g
+    dec.close()
+
+
 def test_step_writes_exactly_the_new_slot(setup):
     s = setup
     k, v = s.fresh_pools()
