@@ -501,10 +501,14 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         ++n_claim;
         if (t.a0 < list_end || t.a1 <= 0 || t.a0 + t.a1 > (int)P.tasks.size()) return "claim range out of the pool";
         if (t.a2 != t.level) return "claim of another level";
-        for (int j = t.a0; j < t.a0 + t.a1; ++j)
-            if (P.tasks[j].level != t.level || P.tasks[j].op == OP_CLAIM) return "pool task of another level";
-        if (ranges_seen.insert({t.a0, t.a1}).second)
-            for (int j = t.a0; j < t.a0 + t.a1; ++j) in_pool[j]++;
+        if (ranges_seen.insert({t.a0, t.a1}).second) {
+            for (int j = t.a0; j < t.a0 + t.a1; ++j) {
+                if (P.tasks[j].level != t.level || P.tasks[j].op == OP_CLAIM) return "pool task of another level";
+                in_pool[j]++;
+            }
+        } else if (P.tasks[t.a0].level != t.level) {
+            return "pool task of another level";
+        }
     }
     for (int j = list_end; j < (int)P.tasks.size(); ++j)
         if (in_pool[j] != 1) return "pool task claimed by no range or by two";
