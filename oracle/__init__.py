@@ -37,4 +37,5 @@ from .decode import (  # noqa: F401
     PagedKV,
     decode_step,
     decode_sequence,
+    prefill,
 )

@@ -430,10 +430,38 @@ def decode_step(model: DenseModel, kv: PagedKV, positions: Sequence[int],
     return logits, traces, touched
 
 
+def prefill(model: DenseModel, kv: PagedKV, pos0: int, block_table, tokens: Sequence[int],
+            dtype=np.float32):
+    """A block of T new tokens of one sequence at positions pos0 .. pos0+T-1
+    (a prompt being ingested, or any step that feeds a sequence several
+    tokens at once).
+
+    The pages describe a server that takes new requests into a running batch
+    over a paged KV cache ("Cohere Publishes One-Kernel Server for North Mini
+    Code, Claims 1.58x vLLM Speedup", opening section; "Cohere fuses an entire
+    decode step into one GPU program", paragraph 4), so a prompt has to be
+    written into the cache before its sequence decodes. They say nothing of
+    how; the plainest reading is causal attention over the block: token i
+    writes its K/V slot pos0+i and attends over positions 0..pos0+i (the
+    cached prefix and new tokens 0..i). That is exactly T decode steps in
+    order, which is how it is written here.
+
+    Returns ``(logits [T][V], traces)``: every token's logits (the last row
+    predicts the token after the block)."""
+    out, traces = [], []
+    for i, tok in enumerate(tokens):
+        lg, tr = _decode_one(model, kv, int(pos0) + i, block_table, int(tok), dtype)
+        out.append(lg)
+        traces.append(tr)
+    return np.stack(out), traces
+
+
 def decode_sequence(model: DenseModel, kv: PagedKV, pos0: int, block_table,
                     token0: int, n_steps: int, dtype=np.float32):
-    """Free-running greedy decode of one sequence: each step's token is the
-    argmax of the previous logits (lowest index on ties)."""
+    """Free-running greedy decode of one sequence: step i feeds token i at
+    position pos0 + i (writing that KV slot), and token i+1 is the argmax of
+    step i's logits (lowest index on ties). Returns (logits [n][V], the
+    n + 1 tokens, traces)."""
     toks, all_logits, traces = [int(token0)], [], []
     pos = int(pos0)
     for _ in range(n_steps):
