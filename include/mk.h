@@ -34,7 +34,11 @@
  *    and reported by mk_sync_check.
  *  - No C++ exception crosses this boundary. mk_last_error() returns a
  *    thread-local message for the last failing call on the calling thread.
- *  - A handle is used by one host thread and one stream at a time.
+ *  - A handle is used by one host thread at a time. Its steps may be enqueued
+ *    on different streams: a step enqueued on another stream than the
+ *    previous one first waits for the previous step (the workspace holds one
+ *    step's inputs at a time). During a stream capture nothing is waited on:
+ *    the caller orders graph replays against other steps of the handle.
  */
 #ifndef MK_H
 #define MK_H
@@ -127,7 +131,14 @@ typedef struct mk_options {
                                 lists. 0 = the attention, merge, output-projection and expert levels when
                                 the sequences need different numbers of attention chunks, else none;
                                 1 = the attention level; 2 = those five levels always; -1 = none */
-    int32_t reserved[3];
+    int32_t validate_plans;  /* nonzero: check every plan mk_decode_step builds with the same checks as
+                                mk_plan_build before using it (MK_ERR_INVALID if one fails) */
+    int32_t mfma_min_batch;  /* smallest batch run by the matrix-core schedule (every weight product on
+                                MFMA, a routing level and an expert-sum level); smaller batches run the
+                                one- and two-token schedule (GEMV tiles on packed BF16 dot products).
+                                0 = 3; 1..3 allowed: the one- and two-token kernels are compiled for
+                                exactly one or two tokens, so the threshold can be lowered, not raised */
+    int32_t reserved[1];
 } mk_options;
 
 typedef struct mk_handle mk_handle;
@@ -174,6 +185,29 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* weights, void* k_pool
 mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids,
                          const int32_t* positions, const int32_t* block_tables,
                          const int32_t* tokens, float* logits, void* stream);
+
+/*
+ * Enqueue one multi-token step: a batch whose rows may feed several new
+ * tokens of one sequence at once (a prompt block being ingested, or a mix of
+ * prompt blocks and decode rows). The pages' server admits new requests into
+ * a running batch over a paged KV cache ("Cohere Publishes One-Kernel Server
+ * for North Mini Code, Claims 1.58x vLLM Speedup", opening section; "Cohere
+ * fuses an entire decode step into one GPU program", paragraph 4), so a
+ * prompt's tokens have to reach the cache through the same kernel; they are
+ * computed causally, which is exactly sequential decoding of those tokens.
+ *   seq_ids      host [B], required: rows with equal ids must be adjacent, at
+ *                consecutive positions, with equal block-table entries over
+ *                the pages they share; distinct runs have distinct ids
+ *   positions, block_tables, tokens, logits: as for mk_decode_step, per row
+ * Row b writes the KV slot at positions[b] and attends over positions
+ * 0..positions[b] of its sequence: the cached prefix plus the rows of its run
+ * up to itself. Every row gets its logits. Runs of one row are decode rows,
+ * so mk_decode_step is this call with distinct seq_ids. Errors as for
+ * mk_decode_step, plus MK_ERR_INVALID for a malformed run.
+ */
+mk_status mk_forward_step(mk_handle* h, int32_t batch, const int32_t* seq_ids,
+                          const int32_t* positions, const int32_t* block_tables,
+                          const int32_t* tokens, float* logits, void* stream);
 
 /* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PEROP for later steps. */
 mk_status mk_set_mode(mk_handle* h, int32_t mode);

@@ -86,8 +86,11 @@ int max_chunks_for(const mk_dims& d) {
     return (int)std::min<int64_t>(kMaxChunksCap, (ctx + 127) / 128);
 }
 
+// Smallest batch that runs the matrix-core schedule (mk_options.mfma_min_batch).
+int mm_min_of(const mk_options& o) { return o.mfma_min_batch > 0 ? o.mfma_min_batch : kMaxBatchValu + 1; }
+
 // Host-checkable support conditions. Empty string = supported.
-std::string check_dims(const mk_dims& d) {
+std::string check_dims(const mk_dims& d, int mm_min = kMaxBatchValu + 1) {
     if (d.n_layers <= 0 || d.hidden <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.n_experts <= 0 ||
         d.top_k <= 0 || d.moe_inter <= 0 || d.vocab <= 0 || d.max_batch <= 0 || d.max_pages_per_seq <= 0 ||
         d.n_pages <= 0)
@@ -100,9 +103,9 @@ std::string check_dims(const mk_dims& d) {
     if (d.n_experts > 256) return "n_experts must be <= 256";
     if (d.hidden % 8 || d.moe_inter % 8) return "hidden and moe_inter must be multiples of 8";
     if (d.max_batch > kMaxBatchMM) return "max_batch above 64";
-    if (d.max_batch > kMaxBatchValu &&
+    if (d.max_batch >= mm_min &&
         (d.hidden % 128 || (d.n_q_heads * d.head_dim) % 128 || d.moe_inter % 32))
-        return "batches above 2 need hidden and n_q_heads*head_dim multiples of 128, moe_inter of 32";
+        return "the matrix-core schedule needs hidden and n_q_heads*head_dim multiples of 128, moe_inter of 32";
     if (find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts) < 0)
         return "no kernel build for this (hidden, attention width, expert width, head_dim)";
     return std::string();
@@ -112,6 +115,7 @@ TileConfig tile_config(const mk_options& o) {
     TileConfig c;
     c.chunk = o.split_kv_tokens;
     c.shared_levels = o.shared_levels;
+    c.mm_min_batch = mm_min_of(o);
     return c;
 }
 
@@ -147,14 +151,14 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
     L.route_w = take((size_t)d.n_layers * B * d.top_k * 4);
     L.act = take(Ln * pad64(B * d.top_k * d.moe_inter) * 4);
     // batches of 3+: routing tables and per-(token, rank) expert outputs
-    const bool mm = d.max_batch > kMaxBatchValu;
+    const bool mm = d.max_batch >= mm_min_of(o);
     L.rtab = take(mm ? Ln * rtab_words(d.n_experts, d.top_k, d.max_batch) * 4 : 0);
     L.ybuf = take(mm ? Ln * pad64(B * d.top_k * H) * 4 : 0);
     L.h2s = take(mm ? Ln * pad64(B * H) * 4 : 0);
     L.wtab = take((size_t)d.n_layers * W_NKINDS * 8);
     // per-step arrays: positions, chunk counts, rotary table, block tables
     L.step_bytes = align256((size_t)B * 4) * 2 + align256((size_t)B * d.head_dim * 4) +
-                   align256((size_t)B * d.max_pages_per_seq * 4);
+                   align256((size_t)B * d.max_pages_per_seq * 4) + align256((size_t)B * 8);
     L.step = take(L.step_bytes);
     L.tasks = take((size_t)L.cap_tasks * sizeof(Task));
     L.wg_off = take((size_t)(max_wg + 1) * 4);
@@ -174,7 +178,8 @@ struct mk_handle {
     int wg_per_cu = 0;
     int n_wg = 0;
     int shape = -1;
-    // [1], [2]: the one- and two-token kernels; [0]: batches of 3+ (if max_batch > 2)
+    int mm_min = kMaxBatchValu + 1;   // smallest batch on the matrix-core kernels
+    // [1], [2]: the one- and two-token kernels; [0]: the matrix-core kernels (if max_batch >= mm_min)
     KernelPair kern[kMaxBatchValu + 1];
     size_t lds_bytes[kMaxBatchValu + 1] = {0, 0, 0};
     int general[kMaxBatchValu + 1] = {0, 0, 0};
@@ -200,6 +205,12 @@ struct mk_handle {
     bool last_perop = false;  // the last step ran the per-op launches
     hipEvent_t t_begin, t_end;
     bool timed = false;
+    // the last step's completion on the stream it was enqueued on: a step
+    // enqueued on another stream waits for it (the workspace's per-step
+    // arrays and task table are single-buffered)
+    hipEvent_t step_ev;
+    bool step_ev_used = false;
+    hipStream_t last_stream = nullptr;
 };
 
 extern "C" {
@@ -216,7 +227,7 @@ size_t mk_workspace_bytes(const mk_dims* d, const mk_options* o) {
     mk_options oo;
     memset(&oo, 0, sizeof oo);
     if (o) oo = *o;
-    if (!check_dims(*d).empty()) return 0;
+    if (!check_dims(*d, mm_min_of(oo)).empty()) return 0;
     // sized for up to 8 workgroups on each of 256 compute units
     return make_layout(*d, oo, 256 * 8).total;
 }
@@ -226,13 +237,15 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
     try {
         if (!dims || !w || !k_pool || !v_pool || !workspace || !out) return fail(MK_ERR_INVALID, "null argument");
         *out = nullptr;
-        const std::string why = check_dims(*dims);
-        if (!why.empty()) return fail(MK_ERR_UNSUPPORTED, "%s", why.c_str());
         mk_options o;
         memset(&o, 0, sizeof o);
         if (opts) o = *opts;
+        const std::string why = check_dims(*dims, mm_min_of(o));
+        if (!why.empty()) return fail(MK_ERR_UNSUPPORTED, "%s", why.c_str());
         if (o.mode != MK_MODE_MEGAKERNEL && o.mode != MK_MODE_PEROP) return fail(MK_ERR_INVALID, "bad mode");
         if (o.split_kv_tokens < 0 || o.split_kv_tokens % 64) return fail(MK_ERR_INVALID, "split_kv_tokens must be a multiple of 64");
+        if (o.mfma_min_batch < 0 || o.mfma_min_batch > kMaxBatchValu + 1)
+            return fail(MK_ERR_INVALID, "mfma_min_batch must be 0 (default) or 1..%d", kMaxBatchValu + 1);
         if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return fail(MK_ERR_INVALID, "workspace not 256-byte aligned");
         const mk_dims& d = *dims;
         if (!w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wqkv || !w->wo || !w->ffn_norm ||
@@ -252,9 +265,13 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         h->device = device;
         h->n_cu = o.n_cu_override > 0 ? o.n_cu_override : prop.multiProcessorCount;
         h->shape = find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts);
-        const bool mm = d.max_batch > kMaxBatchValu;
-        for (int nb = mm ? 0 : 1; nb <= kMaxBatchValu; ++nb)
-            if (!get_kernels(h->shape, nb, &h->kern[nb])) return fail(MK_ERR_UNSUPPORTED, "no kernels");
+        h->mm_min = mm_min_of(o);
+        const bool mm = d.max_batch >= h->mm_min;
+        // kernels a step may launch: the matrix-core ones for batches >= mm_min,
+        // the one- and two-token ones below it
+        auto used = [&](int nb) { return nb == 0 ? mm : (nb <= d.max_batch && nb < h->mm_min); };
+        for (int nb = 0; nb <= kMaxBatchValu; ++nb)
+            if (used(nb) && !get_kernels(h->shape, nb, &h->kern[nb])) return fail(MK_ERR_UNSUPPORTED, "no kernels");
 
         // LDS: general region (attention tiles + query fragments, combine
         // coefficients, or the down tile's staged activations and outputs),
@@ -274,13 +291,13 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         // matrix-core tiles: block-product partials or the routing tile's tables
         const size_t gen_m = align256(std::max(std::max(attn, comb), (size_t)std::max(kMmLdsBytes, kRouteLdsBytes)));
         int occ = 1 << 30;
-        for (int nb = mm ? 0 : 1; nb <= kMaxBatchValu; ++nb) {
+        for (int nb = 0; nb <= kMaxBatchValu; ++nb) {
+            if (!used(nb)) continue;
             h->general[nb] = (int)(nb == 0 ? gen_m : gen_v);
             h->lds_bytes[nb] = h->general[nb] + 1024 + 1024;
             if (h->lds_bytes[nb] > (size_t)prop.sharedMemPerBlock && h->lds_bytes[nb] > 160 * 1024)
                 return fail(MK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", h->lds_bytes[nb]);
             MK_HIP(set_kernel_attributes(h->kern[nb], h->lds_bytes[nb]));
-            if (nb > d.max_batch) continue;
             int o2 = 0;
             MK_HIP(persistent_occupancy(h->kern[nb], h->lds_bytes[nb], &o2));
             occ = std::min(occ, o2);
@@ -357,6 +374,8 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         p.seq_chunk = reinterpret_cast<const int32_t*>(st + align256(B * 4));
         p.rope = reinterpret_cast<const float*>(st + 2 * align256(B * 4));
         p.block_tables = reinterpret_cast<const int32_t*>(st + 2 * align256(B * 4) + align256(B * d.head_dim * 4));
+        p.seq_first = reinterpret_cast<const int32_t*>(st + 2 * align256(B * 4) + align256(B * d.head_dim * 4) +
+                                                       align256(B * d.max_pages_per_seq * 4));
         p.x = reinterpret_cast<float*>(h->ws + h->lay.x);
         p.qkv = reinterpret_cast<float*>(h->ws + h->lay.qkv);
         p.att_part = reinterpret_cast<float*>(h->ws + h->lay.att_part);
@@ -380,6 +399,7 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
             MK_HIP(hipEventRecord(h->stage_ev[i], nullptr));
         }
         MK_HIP(hipEventCreateWithFlags(&h->plan_ev, hipEventDisableTiming));
+        MK_HIP(hipEventCreateWithFlags(&h->step_ev, hipEventDisableTiming));
         if (o.time_kernels) {
             MK_HIP(hipEventCreate(&h->t_begin));
             MK_HIP(hipEventCreate(&h->t_end));
@@ -427,8 +447,15 @@ static mk_status upload_plan(mk_handle* h, hipStream_t stream) {
     return MK_OK;
 }
 
-mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
-                         const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream_) {
+}  // extern "C"
+
+// One step over `batch` rows (mk_decode_step, mk_forward_step). With
+// multi_token, adjacent rows of equal seq_id form a run at consecutive
+// positions: each row's first[] entry names the run's first position and the
+// row that feeds it; otherwise every row is its own run.
+static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
+                           const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream_,
+                           bool multi_token) {
     try {
         if (!h) return fail(MK_ERR_INVALID, "null handle");
         if (!positions || !block_tables || !tokens || !logits) return fail(MK_ERR_INVALID, "null argument");
@@ -436,7 +463,22 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
         if (batch <= 0) return fail(MK_ERR_INVALID, "batch must be positive");
         if (batch > d.max_batch) return fail(MK_ERR_CAPACITY, "batch %d > max_batch %d", batch, d.max_batch);
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        if (seq_ids) {
+        std::vector<int32_t> first_row(batch);
+        for (int b = 0; b < batch; ++b) first_row[b] = b;
+        if (multi_token) {
+            if (!seq_ids) return fail(MK_ERR_INVALID, "a multi-token step needs seq_ids");
+            std::set<int32_t> seen;
+            for (int b = 0; b < batch; ++b) {
+                if (b > 0 && seq_ids[b] == seq_ids[b - 1]) {
+                    if (positions[b] != positions[b - 1] + 1)
+                        return fail(MK_ERR_INVALID, "rows %d and %d of sequence %d are not at consecutive positions",
+                                    b - 1, b, seq_ids[b]);
+                    first_row[b] = first_row[b - 1];
+                } else if (!seen.insert(seq_ids[b]).second) {
+                    return fail(MK_ERR_INVALID, "the rows of sequence %d are not adjacent", seq_ids[b]);
+                }
+            }
+        } else if (seq_ids) {
             std::set<int32_t> ids(seq_ids, seq_ids + batch);
             if ((int)ids.size() != batch) return fail(MK_ERR_INVALID, "seq_ids must be distinct");
         }
@@ -452,7 +494,25 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
                 if (bt[i] < 0 || bt[i] >= d.n_pages)
                     return fail(MK_ERR_BAD_PAGE, "sequence %d block %d names page %d (pool has %lld)", b, i, bt[i],
                                 (long long)d.n_pages);
+            // rows of one sequence share its pages: the earlier row's table
+            // must agree with this one over every page it uses
+            if (first_row[b] != b) {
+                const int32_t* prev = bt - d.max_pages_per_seq;
+                for (int i = 0; i <= positions[b - 1] / P; ++i)
+                    if (prev[i] != bt[i])
+                        return fail(MK_ERR_INVALID, "rows %d and %d of one sequence differ at block %d", b - 1, b, i);
+            }
         }
+
+        // Order this step after the previous one when the caller switched
+        // streams. Inside a stream capture the caller orders the replays
+        // (capture requires the work before it to be complete), so nothing
+        // is waited on or recorded there.
+        hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+        MK_HIP(hipStreamIsCapturing(stream, &capture));
+        const bool capturing = capture != hipStreamCaptureStatusNone;
+        if (!capturing && h->step_ev_used && stream != h->last_stream)
+            MK_HIP(hipStreamWaitEvent(stream, h->step_ev, 0));
 
         // plan: reused while it still covers every sequence. A plan reserves
         // attention chunks for kLookahead more tokens of each sequence (the
@@ -493,6 +553,13 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
             c2.chunk = chunk;
             const std::string err = build_plan(s, c2, h->n_wg, batch, ppos.data(), &h->plan);
             if (!err.empty()) return fail(MK_ERR_CAPACITY, "plan: %s", err.c_str());
+            if (h->o.validate_plans) {
+                const std::string verr = validate_plan(s, h->plan);
+                if (!verr.empty()) {
+                    h->have_plan = false;
+                    return fail(MK_ERR_INVALID, "plan invalid: %s", verr.c_str());
+                }
+            }
             if ((int64_t)h->plan.tasks.size() > h->lay.cap_tasks) return fail(MK_ERR_CAPACITY, "too many tasks");
             mk_status st = upload_plan(h, stream);
             if (st != MK_OK) return st;
@@ -516,9 +583,13 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
         int32_t* snch = reinterpret_cast<int32_t*>(stg + align256(B * 4));   // per-sequence chunk lengths
         float* srope = reinterpret_cast<float*>(stg + 2 * align256(B * 4));
         int32_t* sbt = reinterpret_cast<int32_t*>(stg + 2 * align256(B * 4) + align256(B * d.head_dim * 4));
+        int32_t* sfirst = reinterpret_cast<int32_t*>(stg + 2 * align256(B * 4) + align256(B * d.head_dim * 4) +
+                                                     align256(B * d.max_pages_per_seq * 4));
         for (int b = 0; b < batch; ++b) {
             spos[b] = positions[b];
             snch[b] = nch[b];
+            sfirst[2 * b] = positions[first_row[b]];
+            sfirst[2 * b + 1] = first_row[b];
             for (int i = 0; i < d.head_dim / 2; ++i) {
                 const double ang = (double)positions[b] * h->inv_freq[i];
                 srope[(int64_t)b * d.head_dim + 2 * i] = (float)std::cos(ang);
@@ -538,7 +609,8 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
         uint32_t* banks = reinterpret_cast<uint32_t*>(h->ws + h->lay.banks);
         p.ctr = banks + (int64_t)h->bank * h->lay.bank_words;
         p.ctr_other = banks + (int64_t)(1 - h->bank) * h->lay.bank_words;
-        const int nb = batch <= kMaxBatchValu ? batch : 0;
+        const int nb = batch >= h->mm_min ? 0 : batch;
+        p.mm = nb == 0 ? 1 : 0;
         const KernelPair& k = h->kern[nb];
         const int general = h->general[nb];
         const size_t lds_bytes = h->lds_bytes[nb];
@@ -563,6 +635,13 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
             MK_HIP(hipEventRecord(h->t_end, stream));
             h->timed = true;
         }
+        if (!capturing) {
+            MK_HIP(hipEventRecord(h->step_ev, stream));
+            h->step_ev_used = true;
+            h->last_stream = stream;
+        } else {
+            h->step_ev_used = false;
+        }
         h->bank = 1 - h->bank;
         h->last_n_tasks = (int64_t)(h->o.mode == MK_MODE_MEGAKERNEL ? h->plan.tasks.size() : h->plan.level_tasks.size());
         h->last_perop = h->o.mode != MK_MODE_MEGAKERNEL;
@@ -570,8 +649,20 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
     } catch (const std::bad_alloc&) {
         return fail(MK_ERR_CAPACITY, "host allocation failed");
     } catch (...) {
-        return fail(MK_ERR_INVALID, "unexpected exception in mk_decode_step");
+        return fail(MK_ERR_INVALID, "unexpected exception in a step");
     }
+}
+
+extern "C" {
+
+mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
+                         const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream) {
+    return step_impl(h, batch, seq_ids, positions, block_tables, tokens, logits, stream, false);
+}
+
+mk_status mk_forward_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
+                          const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream) {
+    return step_impl(h, batch, seq_ids, positions, block_tables, tokens, logits, stream, true);
 }
 
 mk_status mk_sync_check(mk_handle* h, void* stream) {
@@ -589,6 +680,8 @@ mk_status mk_sync_check(mk_handle* h, void* stream) {
             MK_HIP(hipDeviceSynchronize());
             return fail(MK_ERR_TIMEOUT, "device watchdog: wait on counter %d timed out", e[1]);
         }
+        if (e[0] == kErrBadTask)
+            return fail(MK_ERR_DEVICE, "device found a task with unknown operation %d in the plan", e[1]);
         return fail(MK_ERR_DEVICE, "device reported bad input (token %d)", e[1]);
     }
     return MK_OK;
@@ -647,11 +740,13 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
                         int32_t* wg_offsets, int32_t* counter_targets) {
     try {
         if (!dims || !positions || !info) return fail(MK_ERR_INVALID, "null argument");
-        const std::string why = check_dims(*dims);
-        if (!why.empty()) return fail(MK_ERR_UNSUPPORTED, "%s", why.c_str());
         mk_options o;
         memset(&o, 0, sizeof o);
         if (opts) o = *opts;
+        if (o.mfma_min_batch < 0 || o.mfma_min_batch > kMaxBatchValu + 1)
+            return fail(MK_ERR_INVALID, "mfma_min_batch must be 0 (default) or 1..%d", kMaxBatchValu + 1);
+        const std::string why = check_dims(*dims, mm_min_of(o));
+        if (!why.empty()) return fail(MK_ERR_UNSUPPORTED, "%s", why.c_str());
         if (batch <= 0 || batch > dims->max_batch) return fail(MK_ERR_CAPACITY, "batch out of range");
         const ModelShape s = shape_of(*dims, max_chunks_for(*dims));
         Plan P;
@@ -691,6 +786,8 @@ void mk_destroy(mk_handle* h) {
     }
     if (h->plan_ev_used) (void)hipEventSynchronize(h->plan_ev);
     (void)hipEventDestroy(h->plan_ev);
+    if (h->step_ev_used) (void)hipEventSynchronize(h->step_ev);
+    (void)hipEventDestroy(h->step_ev);
     if (h->plan_stage) (void)hipHostFree(h->plan_stage);
     if (h->o.time_kernels) {
         (void)hipEventDestroy(h->t_begin);

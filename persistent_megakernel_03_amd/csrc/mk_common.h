@@ -129,6 +129,7 @@ struct Params {
     // this step
     int32_t B, chunk;   // chunk: the plan's attention chunk length (a sequence may use a longer one)
     int32_t perop;      // 1: per-op launches (no counter waits / signals)
+    int32_t mm;         // 1: the matrix-core schedule (its tiles take split-form inputs)
     int32_t trace_on;
     int64_t watchdog_ticks;
     // weights
@@ -145,6 +146,9 @@ struct Params {
     const int32_t* block_tables;  // [max_batch][max_pages]
     const float* rope;            // [max_batch][D/2][2] cos, sin
     const int32_t* seq_chunk;     // [max_batch] attention chunk length of each sequence (tokens)
+    const int32_t* seq_first;     // [max_batch][2] (first position this step writes for the row's sequence,
+                                  // the row that feeds it): a multi-token step's rows of one sequence
+                                  // take each other's new K/V from the qkv buffer, not the pool
     // workspace: every buffer exchanged between workgroups has one slice per
     // layer, so each is written at most once per step
     float* x;         // [2L+1][max_batch][H]
@@ -178,8 +182,10 @@ MK_HD inline int64_t rtab_words(int E, int K, int max_batch) {
     return pad64(64 + 2 * (int64_t)E + (int64_t)E * max_batch + (int64_t)max_batch * K);
 }
 
-// Device error codes (mirror mk_status values).
+// Device error codes: the first two mirror mk_status values; a task record
+// with an unknown operation is reported to the caller as MK_ERR_DEVICE.
 constexpr int32_t kErrTimeout = -6;
 constexpr int32_t kErrDevice = -7;
+constexpr int32_t kErrBadTask = -8;
 
 }  // namespace mk

@@ -105,7 +105,7 @@ int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
                               (int64_t)std::min(s.E, bv * s.K) * ceil_div(s.I, cfg.rows_gateup) +
                               ceil_div(s.H, cfg.rows_down);
     int64_t n = 1 + (int64_t)s.L * per_layer + ceil_div(s.V, cfg.rows_lm);
-    if (s.max_batch > kMaxBatchValu) {
+    if (s.max_batch >= cfg.mm_min_batch) {
         // matrix-core schedule: expert tiles are (rows, slot group) pairs with
         // at most min(E, B k) groups
         const int S = std::min(s.E, s.max_batch * s.K);
@@ -130,6 +130,8 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     P = Plan();
     P.n_wg = n_wg;
     P.B = B;
+    P.mm = B >= cfg.mm_min_batch;
+    if (!P.mm && B > kMaxBatchValu) return "batch above the one- and two-token schedule";
     P.chunk = choose_chunk(s, n_wg, B, positions, cfg.chunk);
     P.n_levels = 2 + kLevelsPerLayer * s.L;
     P.targets.assign(cl.n_main(), 0);
@@ -141,7 +143,7 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     }
 
     std::vector<std::vector<Tile>> levels(P.n_levels);
-    if (B > kMaxBatchValu) {
+    if (P.mm) {
         build_levels_mm(s, cfg, n_wg, B, positions, P, levels);
     } else {
         build_levels_valu(s, cfg, n_wg, B, positions, P, levels);
@@ -388,7 +390,7 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     typedef std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> Heap;
     // (one- and two-token schedule only; the matrix-core expert tiles are many
     // more than the workgroups and go wherever a workgroup is free first)
-    const int half = (n_wg % 2 == 0 && P.B <= kMaxBatchValu) ? n_wg / 2 : 0;
+    const int half = (n_wg % 2 == 0 && !P.mm) ? n_wg / 2 : 0;
     Heap heaps[2];   // [0]: workgroups below `half`, [1]: the rest
     for (int w = 0; w < n_wg; ++w) heaps[w >= half ? 1 : 0].push({0.0, w});
     std::vector<double> level_end(P.n_levels, 0.0);
@@ -440,7 +442,7 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     bool ragged = false;
     for (int b = 1; b < P.B; ++b) ragged = ragged || P.n_chunks[b] != P.n_chunks[0];
     auto shared_op = [&](int op) {
-        if (cfg.shared_levels < 0 || P.B <= kMaxBatchValu) return false;
+        if (cfg.shared_levels < 0 || !P.mm) return false;
         if (cfg.shared_levels >= 2 || (cfg.shared_levels == 0 && ragged))
             return op == OP_ATTN || op == OP_COMBINE || op == OP_OPROJ || op == OP_GATEUP || op == OP_DOWN;
         return op == OP_ATTN && cfg.shared_levels == 1;
@@ -562,7 +564,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
             // one-/two-token gate/up tiles: slot a0, rows a1..a2; matrix-core
             // ones: rows a0..a1 of slot group a2
             case OP_GATEUP:
-                if (P.B > kMaxBatchValu) ranges[std::make_tuple(t.op, t.layer, t.a2, 0)].push_back({t.a0, t.a1});
+                if (P.mm) ranges[std::make_tuple(t.op, t.layer, t.a2, 0)].push_back({t.a0, t.a1});
                 else ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2});
                 break;
             case OP_COMBINE: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a1 + 1}); break;

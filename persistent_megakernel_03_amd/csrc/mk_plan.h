@@ -46,6 +46,8 @@ struct TileConfig {
     // numbers of attention chunks, else none; 1 the attention level; 2 the
     // attention, merge, output-projection and expert levels
     int shared_levels = 0;
+    // smallest batch that runs the matrix-core schedule (1..kMaxBatchValu + 1)
+    int mm_min_batch = kMaxBatchValu + 1;
     // timing model used to place tiles on workgroups
     double model_bw_bytes_per_us = 5.6e6;  // whole-device HBM bandwidth
     double model_task_us = 2.5;            // fixed cost of a task after its inputs are ready
@@ -55,6 +57,7 @@ struct TileConfig {
 struct Plan {
     int n_wg = 0;
     int B = 0;
+    bool mm = false;                  // the matrix-core schedule (else the one- and two-token tiles)
     int chunk = 0;
     int n_levels = 0;
     std::vector<Task> tasks;          // grouped per workgroup (CSR)

@@ -90,8 +90,13 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
 
 // -------------------------------------------------------------- attention
 
-// One chunk of split-KV paged attention for sequence b, KV head g, chunk c:
-// tokens [c*chunk, min((c+1)*chunk, pos+1)). Each wave owns 16-token blocks
+// One chunk of split-KV paged attention for row b, KV head g, chunk c:
+// tokens [c*chunk, min((c+1)*chunk, pos+1)). In a multi-token step the rows
+// of one sequence sit at consecutive positions p0.. and each attends
+// causally over the cached prefix and the rows up to itself: tokens before
+// p0 come from the pool, tokens p0..pos-1 from the qkv rows of the earlier
+// rows (written in this step, so not yet in the pool), rotated and rounded
+// to BF16 exactly as the tile that owns them writes them. Each wave owns 16-token blocks
 // of the chunk (one cache page each) and runs a complete online softmax over
 // them on the matrix cores: scores transposed, S^T = K Q^T (BF16 MFMA
 // 16x16x32, the G query heads of the KV head as the N dimension), then
@@ -116,8 +121,11 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
     const int chunk = p.seq_chunk[b];
     const int t0 = c * chunk;
     const int t1 = min(t0 + chunk, pos + 1);
-    const int t_old = min(t1, pos);
+    const int p0 = p.seq_first[2 * b];          // first position written in this step (pos for decode)
+    const int r0 = p.seq_first[2 * b + 1];      // the row that feeds position p0
+    const int t_old = min(t1, p0);              // tokens read from the pool
     const bool has_new = (t1 == pos + 1);
+    const bool multi = p0 < pos && t1 > p0;     // earlier rows of this step inside the chunk
     const int* bt = p.block_tables + (int64_t)b * p.max_pages;
     const int64_t hstride = (int64_t)16 * D;
     const int64_t layer_pages = (int64_t)l * p.n_pages;
@@ -159,10 +167,57 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
             }
         }
     };
-    // After the loads land, in the (at most one per wave) block that reaches
-    // past the cached tokens: zero the values of slots at or past t_old (their
-    // probabilities are 0, but the slots may hold any bits) and insert the
-    // new token's k and v.
+    // Multi-token steps: the keys and values of positions p0..pos-1 in block
+    // i (first token blk) from the qkv rows that feed them -- RoPE at the
+    // token's own position, then BF16 rounding, the same arithmetic as the
+    // new-token path below.
+    auto fix_kv_rows = [&](int i, int blk) {
+        const float* qkv0 = qkv_at(p, l);
+        const int tk = blk + col;
+        if (tk >= p0 && tk < pos && tk < t1) {
+            const int row = r0 + (tk - p0);
+            const float* kp = qkv0 + (int64_t)row * p.QKVD + p.Hq * D + g * D + quad * 8;
+            const float* rp = p.rope + (int64_t)row * D + 2 * (quad * 8);
+#pragma unroll
+            for (int db = 0; db < NDB / 2; ++db) {
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int j2 = 0; j2 < 4; ++j2) {
+                    uint32_t r[2][2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int j = 2 * j2 + e;
+                        const float a = ld_dev(kp + db * 32 + j), bb = ld_dev(kp + (db + NDB / 2) * 32 + j);
+                        const float cs = ldg(rp + 2 * (db * 32 + j)), sn = ldg(rp + 2 * (db * 32 + j) + 1);
+                        r[0][e] = f2bf(a * cs - bb * sn);
+                        r[1][e] = f2bf(a * sn + bb * cs);
+                    }
+                    lo[j2] = r[0][0] | (r[0][1] << 16);
+                    hi[j2] = r[1][0] | (r[1][1] << 16);
+                }
+                kf[i][db] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                kf[i][db + NDB / 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tv = blk + 4 * quad + j;
+            if (tv >= p0 && tv < pos && tv < t1) {
+                const float* vp = qkv0 + (int64_t)(r0 + (tv - p0)) * p.QKVD + (p.Hq + p.Hkv) * D + g * D + col;
+                const int sh = 16 * (j & 1);
+#pragma unroll
+                for (int dv = 0; dv < NDV; ++dv) {
+                    const uint32_t val = f2bf(ld_dev(vp + dv * 16)) << sh;
+                    if (j & 2) vf[i][dv].y |= val;
+                    else vf[i][dv].x |= val;
+                }
+            }
+        }
+    };
+    // After the loads land, in the block that reaches past the cached tokens
+    // (at most one per wave, or several in a multi-token step): zero the
+    // values of slots at or past t_old (their probabilities are 0, but the
+    // slots may hold any bits) and insert the new tokens' k and v.
     auto fix_kv = [&](int st0) {
 #pragma unroll
         for (int i = 0; i < NTBW; ++i) {
@@ -187,6 +242,7 @@ __device__ __forceinline__ bool tile_attn(const Task& t, TileCtx& cx) {
                         else vf[i][dv].x |= val;
                     }
                 }
+                if (multi) fix_kv_rows(i, blk);
             }
         }
     };
@@ -503,8 +559,8 @@ __device__ __forceinline__ bool tile_combine(const Task& t, TileCtx& cx) {
     __syncthreads();
     mark(cx, 1);
     float* out = attout_at(p, l) + row * D;
-    if (p.B > kMaxBatchValu) {
-        // batches of 3+: the output projection takes it split (see st_split8)
+    if (p.mm) {
+        // matrix-core schedule: the output projection takes it split (see st_split8)
         if (tid < D / 8) {
             float o8[8];
 #pragma unroll
@@ -875,6 +931,15 @@ struct Pf {
     static constexpr int v = NB == 1 ? (NCH <= 2 ? 8 : (NCH <= 4 ? 4 : 2)) : (NCH <= 1 ? 8 : (NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1)));
 };
 
+// A task record whose operation this schedule does not run (a corrupted or
+// foreign task table): report it and abort the step, so every workgroup
+// leaves its waits at once instead of timing out on counters that will
+// never be bumped.
+__device__ __forceinline__ bool bad_task(const Task& t, TileCtx& cx) {
+    if (tid_() == 0) raise_error(cx.p, kErrBadTask, t.op, true);
+    return false;
+}
+
 // NB = 1, 2: the one- and two-token tiles; NB = 0: the matrix-core tiles of
 // batches of 3 or more (attention, its merge and the embedding are shared).
 template <class S, int NB>
@@ -892,7 +957,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
             case OP_DOWN: return tile_down_mm(t, cx);
             case OP_MOESUM: return tile_moesum(t, cx);
             case OP_LMHEAD: return tile_lmhead_mm(t, cx);
-            default: return false;
+            default: return bad_task(t, cx);
         }
     } else {
         switch (t.op) {
@@ -905,7 +970,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
             case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 7 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
             case OP_DOWN: return tile_down<8 * S::NCHP_I, NB, S::NE>(t, cx);
             case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
-            default: return false;
+            default: return bad_task(t, cx);
         }
     }
 }

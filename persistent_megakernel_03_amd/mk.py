@@ -34,7 +34,7 @@ STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID", -2: "MK_ERR_UNSUPPORTED", -3: 
                 -4: "MK_ERR_BAD_PAGE", -5: "MK_ERR_HIP", -6: "MK_ERR_TIMEOUT", -7: "MK_ERR_DEVICE"}
 
 # Every function declared in include/mk.h.
-EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_set_mode",
+EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_forward_step", "mk_set_mode",
            "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_get_trace", "mk_get_plan", "mk_kernel_time",
            "mk_destroy", "mk_last_error"]
 
@@ -66,7 +66,8 @@ class mk_options(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("trace", ctypes.c_int32), ("watchdog_ns", ctypes.c_int64),
                 ("wg_per_cu", ctypes.c_int32), ("split_kv_tokens", ctypes.c_int32),
                 ("n_cu_override", ctypes.c_int32), ("time_kernels", ctypes.c_int32),
-                ("shared_levels", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("shared_levels", ctypes.c_int32), ("validate_plans", ctypes.c_int32),
+                ("mfma_min_batch", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class mk_debug_ptrs(ctypes.Structure):
@@ -104,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_decode_step.argtypes = [c.c_void_p, c.c_int32, c.POINTER(c.c_int32), c.POINTER(c.c_int32),
                                    c.POINTER(c.c_int32), c.c_void_p, c.c_void_p, c.c_void_p]
     lib.mk_decode_step.restype = c.c_int
+    lib.mk_forward_step.argtypes = lib.mk_decode_step.argtypes
+    lib.mk_forward_step.restype = c.c_int
     lib.mk_set_mode.argtypes = [c.c_void_p, c.c_int32]
     lib.mk_set_mode.restype = c.c_int
     lib.mk_sync_check.argtypes = [c.c_void_p, c.c_void_p]
@@ -147,12 +150,14 @@ def make_dims(cfg: dict, max_batch: int, max_pages_per_seq: int, n_pages: int) -
 
 def make_options(mode: int = MK_MODE_MEGAKERNEL, trace: bool = False, watchdog_ns: int = 0, wg_per_cu: int = 0,
                  split_kv_tokens: int = 0, n_cu_override: int = 0, time_kernels: bool = False,
-                 shared_levels: int = 0) -> mk_options:
+                 shared_levels: int = 0, validate_plans: bool = False, mfma_min_batch: int = 0) -> mk_options:
     o = mk_options()
     o.mode, o.trace, o.watchdog_ns = mode, int(bool(trace)), watchdog_ns
     o.wg_per_cu, o.split_kv_tokens, o.n_cu_override = wg_per_cu, split_kv_tokens, n_cu_override
     o.time_kernels = int(bool(time_kernels))
     o.shared_levels = int(shared_levels)
+    o.validate_plans = int(bool(validate_plans))
+    o.mfma_min_batch = int(mfma_min_batch)
     return o
 
 
@@ -182,6 +187,15 @@ def mk_decode_step(h: int, batch: int, seq_ids, positions, block_tables, tokens:
     b_arr, b_p = _i32(block_tables)
     _check(load().mk_decode_step(ctypes.c_void_p(h), batch, s_p, p_p, b_p, ctypes.c_void_p(tokens),
                                  ctypes.c_void_p(logits), ctypes.c_void_p(stream)))
+
+
+def mk_forward_step(h: int, batch: int, seq_ids, positions, block_tables, tokens: int, logits: int,
+                    stream: int) -> None:
+    s_arr, s_p = _i32(seq_ids)
+    p_arr, p_p = _i32(positions)
+    b_arr, b_p = _i32(block_tables)
+    _check(load().mk_forward_step(ctypes.c_void_p(h), batch, s_p, p_p, b_p, ctypes.c_void_p(tokens),
+                                  ctypes.c_void_p(logits), ctypes.c_void_p(stream)))
 
 
 def mk_set_mode(h: int, mode: int) -> None:
@@ -252,6 +266,46 @@ def mk_destroy(h: int) -> None:
 
 # ------------------------------------------------------------ convenience --
 
+def check_step_args(dims: mk_dims, vocab: int, positions, block_tables, tokens, logits, device, seq_ids=None):
+    """Shapes, dtypes and placement of one step's arguments, checked before
+    the C ABI sees raw pointers (it trusts them: block-table rows are read
+    max_pages_per_seq entries long, logits are written batch x vocab floats).
+    Returns the positions and block tables as contiguous int32 arrays.
+    Raises MkError(MK_ERR_INVALID)."""
+    import torch
+
+    def bad(msg):
+        raise MkError(MK_ERR_INVALID, msg)
+
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(-1))
+    B = int(pos.shape[0])
+    if B <= 0:
+        bad("batch must be positive")
+    if np.any(pos > np.iinfo(np.int32).max):
+        bad("position out of int32 range")
+    bt = np.asarray(block_tables)
+    if bt.ndim != 2 or bt.shape[0] < B or bt.shape[1] != dims.max_pages_per_seq:
+        bad(f"block_tables must be [batch >= {B}][max_pages_per_seq = {dims.max_pages_per_seq}], got {bt.shape}")
+    if not np.issubdtype(bt.dtype, np.integer):
+        bad("block_tables must hold integers")
+    if seq_ids is not None and len(seq_ids) < B:
+        bad(f"seq_ids holds {len(seq_ids)} entries for a batch of {B}")
+    for name, t, dt, n in (("tokens", tokens, torch.int32, B), ("logits", logits, torch.float32, B * vocab)):
+        if not isinstance(t, torch.Tensor):
+            bad(f"{name} must be a torch tensor")
+        if t.dtype != dt:
+            bad(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != torch.device(device):
+            bad(f"{name} must be on {device}, got {t.device}")
+        if not t.is_contiguous():
+            bad(f"{name} must be contiguous")
+        if t.numel() < n:
+            bad(f"{name} holds {t.numel()} elements, the step needs {n}")
+    if logits.dim() == 2 and logits.shape[1] != vocab:
+        bad(f"logits rows must be vocab = {vocab} wide, got {logits.shape[1]}")
+    return pos.astype(np.int32), np.ascontiguousarray(bt[:B], dtype=np.int32)
+
+
 class Decoder:
     """Owns the torch tensors a handle points into (weights dict, KV pools,
     workspace) and forwards calls to the C ABI. No arithmetic happens here."""
@@ -259,11 +313,13 @@ class Decoder:
     def __init__(self, cfg: dict, weights: Dict[str, "torch.Tensor"], k_pool, v_pool, max_batch: int,
                  max_pages_per_seq: int, mode: int = MK_MODE_MEGAKERNEL, trace: bool = False,
                  watchdog_ns: int = 0, wg_per_cu: int = 0, split_kv_tokens: int = 0, device: int = 0,
-                 time_kernels: bool = False, shared_levels: int = 0):
+                 time_kernels: bool = False, shared_levels: int = 0, validate_plans: bool = False,
+                 mfma_min_batch: int = 0):
         import torch
         self.cfg = dict(cfg)
         self.dims = make_dims(cfg, max_batch, max_pages_per_seq, k_pool.shape[1])
-        self.opts = make_options(mode, trace, watchdog_ns, wg_per_cu, split_kv_tokens, 0, time_kernels, shared_levels)
+        self.opts = make_options(mode, trace, watchdog_ns, wg_per_cu, split_kv_tokens, 0, time_kernels, shared_levels,
+                                 validate_plans, mfma_min_batch)
         L = cfg["n_layers"]
         self._keep: List = [weights, k_pool, v_pool]
 
@@ -294,9 +350,23 @@ class Decoder:
         import torch
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
-        positions = np.asarray(positions, np.int32)
-        mk_decode_step(self.handle, len(positions), seq_ids, positions, np.asarray(block_tables, np.int32),
+        positions, block_tables = check_step_args(self.dims, self.cfg["vocab"], positions, block_tables, tokens,
+                                                  logits, self.k_pool.device, seq_ids)
+        mk_decode_step(self.handle, len(positions), seq_ids, positions, block_tables,
                        tokens.data_ptr(), logits.data_ptr(), stream)
+
+    def forward(self, seq_ids, positions, block_tables, tokens, logits, stream=None):
+        """A multi-token step (mk_forward_step): rows of one sequence are
+        adjacent with equal seq_ids at consecutive positions."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        if seq_ids is None:
+            raise MkError(MK_ERR_INVALID, "a multi-token step needs seq_ids")
+        positions, block_tables = check_step_args(self.dims, self.cfg["vocab"], positions, block_tables, tokens,
+                                                  logits, self.k_pool.device, seq_ids)
+        mk_forward_step(self.handle, len(positions), seq_ids, positions, block_tables,
+                        tokens.data_ptr(), logits.data_ptr(), stream)
 
     def set_mode(self, mode: int):
         mk_set_mode(self.handle, mode)

@@ -46,14 +46,14 @@ def _batch(B, seed):
     return positions, bts, toks
 
 
-def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=0):
+def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=0, mfma_min_batch=0):
     B = len(positions)
     k, v = s.fresh_pools()
     dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=max(B, 3), max_pages_per_seq=PAGES_PER_SEQ, mode=mode,
-                     shared_levels=shared)
+                     shared_levels=shared, validate_plans=True, mfma_min_batch=mfma_min_batch)
     tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
     logits = torch.empty(B, CFG["vocab"], device="cuda")
-    print(f"batch B={B} mode={mode} shared={shared} steps={steps}", flush=True)
+    print(f"batch B={B} mode={mode} shared={shared} steps={steps} mfma_min_batch={mfma_min_batch}", flush=True)
     for st in range(steps):
         dec.step([p + st for p in positions], bts, tokens, logits, seq_ids=list(range(100, 100 + B)))
         assert dec.sync_check() == mk.MK_OK
@@ -100,6 +100,19 @@ def test_batch_step_matches_oracle(setup, B):
     positions, bts, toks = _batch(B, B)
     g = _run(setup, positions, bts, toks)
     _check_rows(setup, positions, bts, toks, g)
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_matrix_core_schedule_at_one_and_two_tokens(setup, B):
+    """mfma_min_batch = 1: one- and two-token batches on the matrix-core
+    schedule (every weight product on MFMA, routing and expert-sum levels)
+    match the oracle at the same bars, in both modes, and the megakernel
+    equals the per-op build bit for bit."""
+    positions, bts, toks = _batch(B, 40 + B)
+    a = _run(setup, positions, bts, toks, mfma_min_batch=1)
+    _check_rows(setup, positions, bts, toks, a)
+    b = _run(setup, positions, bts, toks, mk.MK_MODE_PEROP, mfma_min_batch=1)
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["xs"], b["xs"])
 
 
 def test_batch_megakernel_equals_perop_bitwise(setup):
