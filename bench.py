@@ -14,7 +14,7 @@ the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-schedule]
                        [--sweep 4,16,64 [--sweep-steps K]] [--long 32768,131072,262144]
-                       [--ragged]
+                       [--ragged] [--prefill 512,2048 [--prefill-prefix N]]
 
 "schedule" is one traced step of the same workload after the timed ones:
 the fraction of workgroup time spent waiting on dependency counters (with
@@ -33,6 +33,11 @@ the megakernel (its default: the ragged contexts make it share the
 attention, merge, output-projection and expert levels, whose tiles workgroups
 then claim from per-level pools), the megakernel with fixed per-workgroup
 lists only, and the per-op build.
+
+--prefill adds, under "prefill", prompt ingestion: each prompt length in
+multi-token steps of up to 64 rows of one sequence (one launch per block,
+causal attention over the cache and the earlier rows), prompt tok/s over the
+whole prompt and the blocks' bytes against 8 TB/s, megakernel and per-op.
 
 --sweep adds, under "batch_sweep", the same measurement at other batch sizes
 (each sequence at the same context, pages from a shuffled pool, per-sequence
@@ -112,6 +117,9 @@ def main():
     ap.add_argument("--long-steps", type=int, default=32)
     ap.add_argument("--ragged", action="store_true", help="also measure the churning 32-sequence batch")
     ap.add_argument("--ragged-steps", type=int, default=256)
+    ap.add_argument("--prefill", type=str, default="",
+                    help="prompt lengths to ingest (multi-token steps of up to 64 rows), e.g. 512,2048")
+    ap.add_argument("--prefill-prefix", type=int, default=0, help="tokens already cached before each prompt")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -334,6 +342,14 @@ def main():
             del k_pool, v_pool
             torch.cuda.empty_cache()
         out["ragged"] = run_ragged(cfg, weights, args.ragged_steps)
+    if args.prefill:
+        try:
+            del k_pool, v_pool
+        except NameError:
+            pass
+        torch.cuda.empty_cache()
+        out["prefill"] = [run_prefill(cfg, weights, int(T), args.prefill_prefix)
+                          for T in args.prefill.split(",") if T]
     print(json.dumps(out), flush=True)
 
     if args.calib_copy:
@@ -345,11 +361,30 @@ def main():
         log("calibration copy of 1 GiB done (3 launches)")
 
 
+def churn_pool_pages(cfg, B, max_pages, steps, seed_pages=(1 << 22)):
+    """Pages the churning workload holds at its peak, from a dry run of the
+    host scheduler (host bookkeeping only), plus a margin."""
+    from persistent_megakernel_03_amd import mk, synth
+
+    sch = mk.Scheduler(B, B, cfg["page_size"], max_pages, seed_pages, reserve_full=False)
+    run = synth.ChurnRun(sch, synth.ChurnWorkload(B, cfg["vocab"]), max_len=max_pages * cfg["page_size"])
+    low = seed_pages
+    for _ in range(steps):
+        n = sch.next()
+        low = min(low, sch.stats()["free_pages"])
+        sch.commit(np.zeros(n, np.int32))
+        run.advance()
+    sch.close()
+    return seed_pages - low + 64
+
+
 def run_ragged(cfg, weights, steps, warmup=8, B=32):
     """The churning batch (see the module docstring), megakernel then per-op,
-    each over the same schedule from the same initial state. Throughput is
-    tokens over wall time of the timed steps (host scheduling, plan rebuilds
-    and joins included)."""
+    each over the same schedule from the same initial state. The host
+    continuous-batching scheduler (mk.Scheduler) owns the requests, slots and
+    pages; the workload's draws (synth.ChurnWorkload) say which requests end
+    and which join. Throughput is tokens over wall time of the timed steps
+    (host scheduling, plan rebuilds and joins included)."""
     import torch
 
     from persistent_megakernel_03_amd import mk, sol, synth
@@ -360,64 +395,139 @@ def run_ragged(cfg, weights, steps, warmup=8, B=32):
         w2[f"layers.{l}.router_bias"] = torch.as_tensor(b).cuda()
     P = cfg["page_size"]
     max_pages = 32768 // P + (steps + warmup) // P + 2
-    probe = synth.RaggedBatch(B, 1 << 20, P, max_pages, cfg["vocab"])
-    for _ in range(steps + warmup + 16):
-        probe.advance()
-    n_pages = probe.peak_pages + 64
+    n_pages = churn_pool_pages(cfg, B, max_pages, steps + warmup + 2)
     log(f"ragged: Zipf bias alpha {alpha:.4f} (fitted slope {slope:.3f}); pool of {n_pages} pages")
     k_pool, v_oracle_layout = synth.make_kv_pool(cfg, n_pages, 1, "cuda")
     v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
     del v_oracle_layout
+    order = np.random.default_rng(synth.tensor_seed(7, "ragged.pages")).permutation(n_pages)
     res = {}
     for name, mode, shared in (("megakernel", mk.MK_MODE_MEGAKERNEL, 0),
                                ("megakernel_fixed_lists", mk.MK_MODE_MEGAKERNEL, -1),
                                ("perop", mk.MK_MODE_PEROP, 0)):
         nsteps = steps
         k, v = k_pool.clone(), v_pool.clone()
-        rb = synth.RaggedBatch(B, n_pages, P, max_pages, cfg["vocab"])
+        sch = mk.Scheduler(B, B, P, max_pages, n_pages, reserve_full=False, page_order=order)
+        run = synth.ChurnRun(sch, synth.ChurnWorkload(B, cfg["vocab"]), max_len=max_pages * P)
         dec = mk.Decoder(cfg, w2, k, v, max_batch=B, max_pages_per_seq=max_pages, mode=mode, time_kernels=True,
                          shared_levels=shared)
-        tokens = torch.tensor(rb.tokens, dtype=torch.int32, device="cuda")
+        tokens = torch.empty(B, dtype=torch.int32, device="cuda")
         logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
+        nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+        host_next = torch.empty(B, dtype=torch.int32, pin_memory=True)
 
         def one():
-            dec.step(rb.pos, rb.tables(), tokens, logits, seq_ids=rb.ids)
-            tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
-            for b, tok in rb.advance().items():
-                tokens[b] = tok
+            n = sch.next()
+            tokens[:n].copy_(torch.from_numpy(sch.tokens[:n]), non_blocking=False)
+            dec.forward(sch.seq_ids[:n], sch.positions[:n], sch.block_tables[:n], tokens[:n], logits[:n])
+            nxt[:n].copy_(torch.argmax(logits[:n], dim=1).to(torch.int32))
+            host_next[:n].copy_(nxt[:n])
+            sch.commit(host_next[:n].numpy())
+            run.advance()
+            return n
 
         for _ in range(warmup):
             one()
         torch.cuda.synchronize()
         assert dec.sync_check() == mk.MK_OK
         t0 = time.perf_counter()
+        toks = 0
         for _ in range(nsteps):
-            one()
+            toks += one()
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         if dec.sync_check() != mk.MK_OK:
             raise RuntimeError("device status after the ragged run")
-        ctx = list(rb.pos)
-        dec.step(rb.pos, rb.tables(), tokens, logits, seq_ids=rb.ids)
+        n = sch.next()
+        ctx = [int(x) for x in sch.positions[:n]]
+        tokens[:n].copy_(torch.from_numpy(sch.tokens[:n]))
+        dec.forward(sch.seq_ids[:n], sch.positions[:n], sch.block_tables[:n], tokens[:n], logits[:n])
         kms = dec.kernel_ms()
         dbg = dec.debug()
         off = dbg.route_ids - dec.workspace.data_ptr()
-        n = cfg["n_layers"] * B * cfg["top_k"]
-        rid = dec.workspace[off:off + 4 * n].view(torch.int32).view(cfg["n_layers"], B, cfg["top_k"]).cpu().numpy()
+        n_ids = cfg["n_layers"] * B * cfg["top_k"]
+        rid = dec.workspace[off:off + 4 * n_ids].view(torch.int32).view(cfg["n_layers"], B, cfg["top_k"]).cpu().numpy()
+        st = sch.stats()
         dec.close()
+        sch.close()
         del k, v
-        nexp = distinct_experts(rid, B)
-        by = sol.step_bytes(cfg, ctx, nexp, distinct_tokens=B)
-        res[name] = {"value": round(B * nsteps / el, 2), "unit": "tok/s", "steps": nsteps,
+        nexp = distinct_experts(rid, n)
+        by = sol.step_bytes(cfg, ctx, nexp, distinct_tokens=n)
+        res[name] = {"value": round(toks / el, 2), "unit": "tok/s", "steps": nsteps,
                      "ms_per_step": round(1e3 * el / nsteps, 4), "kernel_ms_sample": round(kms, 4),
                      "bytes_per_step_sample": by, "distinct_experts_mean": round(float(np.mean(nexp)), 2),
                      "frac_sample": round(by / (kms * 1e-3) / 1e9 / PEAK_GBS, 4),
-                     "mean_context": round(float(np.mean(ctx)), 1)}
+                     "mean_context": round(float(np.mean(ctx)), 1),
+                     "scheduler": {"admitted": st["admitted"], "released": st["finished"], "steps": st["steps"]}}
         log(f"ragged {name}: {res[name]['value']:.1f} tok/s over {nsteps} steps ({res[name]['ms_per_step']:.2f} ms/step); "
             f"sample step kernel {kms:.3f} ms, {res[name]['distinct_experts_mean']} experts/layer, "
             f"{100 * res[name]['frac_sample']:.1f}% of 8 TB/s")
     res["zipf"] = {"s": 1.1, "alpha": round(alpha, 5), "fitted_slope": round(slope, 4)}
-    res["workload"] = "32 sequences, contexts log-uniform [128, 32768], 4 replaced every 8 steps (contexts [128, 2048])"
+    res["workload"] = ("32 sequences, contexts log-uniform [128, 32768], 4 replaced every 8 steps (contexts [128, 2048]); "
+                       "requests, slots and pages owned by the host scheduler (libmk mk_sched)")
+    return res
+
+
+def run_prefill(cfg, weights, T, prefix, block=64):
+    """Ingest one prompt of T tokens after `prefix` cached ones, in
+    multi-token steps of up to `block` rows (mk_forward_step: one launch per
+    block, the rows attending causally over the cache and each other), then
+    decode nothing. Reports prompt tokens per second over the whole prompt
+    (wall time, blocks back to back), per-block kernel time, and the
+    algorithmic bytes of the blocks (weights and routed experts once per
+    block, the sequence's cache read once per block) against 8 TB/s; the
+    per-op build in the same harness."""
+    import torch
+
+    from persistent_megakernel_03_amd import mk, sol, synth
+
+    P = cfg["page_size"]
+    pages = (prefix + T) // P + 2
+    k_pool, v_oracle_layout = synth.make_kv_pool(cfg, pages + 1, 1, "cuda")
+    v_pool = v_oracle_layout.transpose(-1, -2).contiguous()
+    del v_oracle_layout
+    bt = synth.make_block_tables(1, pages, pages + 1, shuffle=True)[0]
+    prompt = synth.make_tokens(T, cfg["vocab"], seed=17)
+    blocks = [(s0, min(T, s0 + block)) for s0 in range(0, T, block)]
+    res = {"prompt_tokens": T, "prefix": prefix, "block_rows": block}
+    for name, mode in (("megakernel", mk.MK_MODE_MEGAKERNEL), ("perop", mk.MK_MODE_PEROP)):
+        dec = mk.Decoder(cfg, weights, k_pool.clone(), v_pool.clone(), max_batch=block, max_pages_per_seq=pages,
+                         mode=mode, time_kernels=True)
+        logits = torch.empty(block, cfg["vocab"], dtype=torch.float32, device="cuda")
+        toks = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+
+        def one(s0, s1):
+            n = s1 - s0
+            dec.forward([0] * n, [prefix + s0 + i for i in range(n)], [bt] * n, toks[s0:s1], logits[:n])
+
+        for s0, s1 in blocks:       # warm pass (plans built, code paged in)
+            one(s0, s1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s0, s1 in blocks:
+            one(s0, s1)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if dec.sync_check() != mk.MK_OK:
+            raise RuntimeError("device status after the prefill run")
+        kms, by = [], []
+        for s0, s1 in blocks:
+            one(s0, s1)
+            kms.append(dec.kernel_ms())
+            dbg = dec.debug()
+            off = dbg.route_ids - dec.workspace.data_ptr()
+            n_ids = cfg["n_layers"] * block * cfg["top_k"]
+            rid = dec.workspace[off:off + 4 * n_ids].view(torch.int32).view(cfg["n_layers"], block,
+                                                                           cfg["top_k"]).cpu().numpy()
+            by.append(sol.forward_step_bytes(cfg, [(prefix + s0, s1 - s0)], distinct_experts(rid, s1 - s0),
+                                             distinct_tokens=len(set(prompt[s0:s1].tolist()))))
+        dec.close()
+        ach = sum(by) / (sum(kms) * 1e-3) / 1e9
+        res[name] = {"value": round(T / el, 1), "unit": "prompt tok/s", "ms_per_prompt": round(1e3 * el, 3),
+                     "kernel_ms_per_block": [round(x, 4) for x in kms], "bytes_per_block": by,
+                     "achieved_gbs": round(ach, 1), "frac": round(ach / PEAK_GBS, 4)}
+        log(f"prefill {name}: {T} tokens after {prefix}: {res[name]['value']:.0f} prompt tok/s, "
+            f"{sum(kms):.2f} ms of kernels in {len(blocks)} blocks, {100 * ach / PEAK_GBS:.1f}% of 8 TB/s")
     return res
 
 

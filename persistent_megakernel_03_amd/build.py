@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["mk_kernels.hip", "mk_api.cpp", "mk_plan.cpp"]
+SOURCES = ["mk_kernels.hip", "mk_api.cpp", "mk_plan.cpp", "mk_sched.cpp"]
 ARCH = "gfx950"
 
 

@@ -23,6 +23,7 @@
 
 #include "../../include/mk.h"
 #include "mk_common.h"
+#include "mk_host.h"
 #include "mk_kernels.h"
 #include "mk_plan.h"
 
@@ -169,6 +170,18 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
 }
 
 }  // namespace
+
+namespace mk {
+mk_status host_fail(mk_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+}  // namespace mk
 
 struct mk_handle {
     mk_dims d;

@@ -36,7 +36,10 @@ STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID", -2: "MK_ERR_UNSUPPORTED", -3: 
 # Every function declared in include/mk.h.
 EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_forward_step", "mk_set_mode",
            "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_get_trace", "mk_get_plan", "mk_kernel_time",
-           "mk_destroy", "mk_last_error"]
+           "mk_destroy", "mk_last_error",
+           # include/mk_sched.h
+           "mk_sched_create", "mk_sched_destroy", "mk_sched_submit", "mk_sched_release", "mk_sched_next",
+           "mk_sched_commit", "mk_sched_get_stats", "mk_sched_tokens"]
 
 
 class MkError(RuntimeError):
@@ -79,6 +82,18 @@ class mk_debug_ptrs(ctypes.Structure):
 class mk_plan_info(ctypes.Structure):
     _fields_ = [("n_wg", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("n_counters", ctypes.c_int32),
                 ("n_levels", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+class mk_sched_config(ctypes.Structure):
+    _fields_ = [("max_seqs", ctypes.c_int32), ("max_rows", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("n_pages", ctypes.c_int64), ("reserve_full", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+
+class mk_sched_stats(ctypes.Structure):
+    _fields_ = [("queued", ctypes.c_int32), ("running", ctypes.c_int32), ("free_pages", ctypes.c_int32),
+                ("reserved_pages", ctypes.c_int32), ("admitted", ctypes.c_int64), ("finished", ctypes.c_int64),
+                ("steps", ctypes.c_int64), ("rows", ctypes.c_int64), ("prompt_rows", ctypes.c_int64)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -127,6 +142,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_destroy.restype = None
     lib.mk_last_error.argtypes = []
     lib.mk_last_error.restype = c.c_char_p
+    I32P, I64P = c.POINTER(c.c_int32), c.POINTER(c.c_int64)
+    lib.mk_sched_create.argtypes = [c.POINTER(mk_sched_config), I32P, c.POINTER(c.c_void_p)]
+    lib.mk_sched_destroy.argtypes = [c.c_void_p]
+    lib.mk_sched_destroy.restype = None
+    lib.mk_sched_submit.argtypes = [c.c_void_p, c.c_int64, c.c_int32, I32P, c.c_int32, c.c_int32]
+    lib.mk_sched_release.argtypes = [c.c_void_p, c.c_int64]
+    lib.mk_sched_next.argtypes = [c.c_void_p, I32P, I32P, I32P, I32P, I32P, I32P, I64P]
+    lib.mk_sched_commit.argtypes = [c.c_void_p, I32P, I32P, I64P, c.c_int32]
+    lib.mk_sched_get_stats.argtypes = [c.c_void_p, c.POINTER(mk_sched_stats)]
+    lib.mk_sched_tokens.argtypes = [c.c_void_p, c.c_int64, I32P, c.c_int32, I32P]
+    for n in ("mk_sched_create", "mk_sched_submit", "mk_sched_release", "mk_sched_next", "mk_sched_commit",
+              "mk_sched_get_stats", "mk_sched_tokens"):
+        getattr(lib, n).restype = c.c_int
     _lib = lib
     return lib
 
@@ -386,6 +414,87 @@ class Decoder:
     def close(self):
         if getattr(self, "handle", None):
             mk_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------- scheduler --
+
+class Scheduler:
+    """The host continuous-batching scheduler (include/mk_sched.h): request
+    queue, admission, page allocator and the rows of each step. Argument
+    marshalling only; the policy lives in libmk."""
+
+    def __init__(self, max_seqs: int, max_rows: int, page_size: int, max_pages_per_seq: int, n_pages: int,
+                 reserve_full: bool = True, page_order=None):
+        cfg = mk_sched_config(max_seqs, max_rows, page_size, max_pages_per_seq, n_pages, int(bool(reserve_full)))
+        self.max_rows, self.max_pages = max_rows, max_pages_per_seq
+        order = None
+        if page_order is not None:
+            self._order, order = _i32(page_order)
+        h = ctypes.c_void_p()
+        _check(load().mk_sched_create(ctypes.byref(cfg), order, ctypes.byref(h)))
+        self.handle = h.value
+        R, M = max_rows, max_pages_per_seq
+        self.seq_ids = np.zeros(R, np.int32)
+        self.positions = np.zeros(R, np.int32)
+        self.block_tables = np.zeros((R, M), np.int32)
+        self.tokens = np.zeros(R, np.int32)
+        self.sample = np.zeros(R, np.int32)
+        self.request_ids = np.zeros(R, np.int64)
+        self._fin = np.zeros(R, np.int64)
+
+    @staticmethod
+    def _p(a):
+        return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32 if a.dtype == np.int32 else ctypes.c_int64))
+
+    def submit(self, request_id: int, prompt, max_new_tokens: int, cached_len: int = 0) -> None:
+        arr, ptr = _i32(prompt)
+        _check(load().mk_sched_submit(ctypes.c_void_p(self.handle), int(request_id), int(cached_len), ptr, len(arr),
+                                      int(max_new_tokens)))
+
+    def release(self, request_id: int) -> None:
+        _check(load().mk_sched_release(ctypes.c_void_p(self.handle), int(request_id)))
+
+    def next(self) -> int:
+        """Lay out the next step; returns the number of rows (views of the
+        arrays above hold them)."""
+        n = ctypes.c_int32()
+        _check(load().mk_sched_next(ctypes.c_void_p(self.handle), ctypes.byref(n), self._p(self.seq_ids),
+                                    self._p(self.positions), self._p(self.block_tables), self._p(self.tokens),
+                                    self._p(self.sample), self._p(self.request_ids)))
+        return int(n.value)
+
+    def commit(self, next_tokens) -> list:
+        """next_tokens: one per row of the step (read where sample == 1).
+        Returns the ids of the requests that finished."""
+        arr, ptr = _i32(next_tokens)
+        nf = ctypes.c_int32()
+        _check(load().mk_sched_commit(ctypes.c_void_p(self.handle), ptr, ctypes.byref(nf), self._p(self._fin),
+                                      len(self._fin)))
+        return [int(x) for x in self._fin[:min(nf.value, len(self._fin))]]
+
+    def stats(self) -> dict:
+        st = mk_sched_stats()
+        _check(load().mk_sched_get_stats(ctypes.c_void_p(self.handle), ctypes.byref(st)))
+        return {k: int(getattr(st, k)) for k, _ in mk_sched_stats._fields_}
+
+    def tokens_of(self, request_id: int) -> list:
+        n = ctypes.c_int32()
+        _check(load().mk_sched_tokens(ctypes.c_void_p(self.handle), int(request_id), None, 0, ctypes.byref(n)))
+        out = np.zeros(max(1, n.value), np.int32)
+        _check(load().mk_sched_tokens(ctypes.c_void_p(self.handle), int(request_id), self._p(out), n.value,
+                                      ctypes.byref(n)))
+        return [int(x) for x in out[:n.value]]
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load().mk_sched_destroy(ctypes.c_void_p(self.handle))
             self.handle = None
 
     def __del__(self):  # pragma: no cover

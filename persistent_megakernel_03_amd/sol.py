@@ -45,6 +45,23 @@ def step_bytes(dims: dict, contexts: Sequence[int], distinct_experts: Sequence[i
     return int(dense + experts + head + kv_read + kv_write + logits)
 
 
+def forward_step_bytes(dims: dict, runs: Sequence[tuple], distinct_experts: Sequence[int],
+                       distinct_tokens: int | None = None, router_bias: bool = False) -> int:
+    """Bytes a multi-token step must move. runs[i] = (first position, rows)
+    of one sequence: the run reads that sequence's cache once (the cached
+    prefix and its own new entries, positions 0 .. first + rows - 1), writes
+    one KV slot and one logits row per row. Dense weights, routed experts and
+    the LM head count once, as in step_bytes."""
+    L, V = dims["n_layers"], dims["vocab"]
+    kv_token = L * 2 * dims["n_kv_heads"] * dims["head_dim"] * 2
+    rows = sum(int(n) for _, n in runs)
+    if distinct_tokens is None:
+        distinct_tokens = rows
+    base = step_bytes(dims, [], distinct_experts, distinct_tokens, router_bias)
+    kv_read = sum((int(p0) + int(n)) * kv_token for p0, n in runs)
+    return int(base + kv_read + rows * kv_token + rows * V * 4)
+
+
 def weight_bytes(dims: dict, distinct_experts: Sequence[int]) -> int:
     """The weight part of step_bytes (dense, routed experts, LM head)."""
     return step_bytes(dims, [], distinct_experts, 0) - 0

@@ -168,73 +168,61 @@ def zipf_router_bias(dims: dict, seed: int = 5, s: float = 1.1, n_tokens: int = 
     return biases, alpha, slope(alpha)
 
 
-class RaggedBatch:
-    """A churning batch of `n_seqs` slots over a paged pool, as a serving
-    loop would run it: initial contexts log-uniform on [ctx_lo, ctx_hi];
-    every `every` steps `churn` seeded-random slots finish, their pages go
-    back to a free list, and new sequences take the slots with contexts
-    uniform on [join_lo, join_hi] (their cache pages hold the pool's random
-    prefill) and seeded first tokens. Pages are taken from the free list as
-    positions grow. Host bookkeeping only."""
+class ChurnWorkload:
+    """Seeded draws of a churning batch, as a serving loop would see it:
+    `n_seqs` requests with initial contexts log-uniform on [ctx_lo, ctx_hi]
+    (their cache pages hold the pool's random prefill) and seeded first
+    tokens; after every `every` steps, `churn` seeded-random slots finish and
+    new requests with contexts uniform on [join_lo, join_hi] and seeded first
+    tokens take them. Draws only: the scheduler (mk.Scheduler) owns slots,
+    pages and positions."""
 
-    def __init__(self, n_seqs: int, n_pages: int, page_size: int, max_pages: int, vocab: int, seed: int = 7,
-                 ctx_lo: int = 128, ctx_hi: int = 32768, join_lo: int = 128, join_hi: int = 2048,
-                 every: int = 8, churn: int = 4):
+    def __init__(self, n_seqs: int, vocab: int, seed: int = 7, ctx_lo: int = 128, ctx_hi: int = 32768,
+                 join_lo: int = 128, join_hi: int = 2048, every: int = 8, churn: int = 4):
         self.rng = np.random.default_rng(tensor_seed(seed, "ragged"))
-        self.P, self.max_pages, self.vocab = page_size, max_pages, vocab
-        self.every, self.churn, self.join = every, churn, (join_lo, join_hi)
-        # the page order has its own stream, so the schedule does not depend on the pool size
-        self.free = list(np.random.default_rng(tensor_seed(seed, "ragged.pages")).permutation(n_pages)[::-1])
-        self.pages_in_use = 0
-        self.peak_pages = 0
-        self.next_id = 0
-        self.ids, self.pos, self.pages = [], [], []
-        for _ in range(n_seqs):
-            ctx = int(np.exp(self.rng.uniform(np.log(ctx_lo), np.log(ctx_hi))))
-            self._admit(ctx)
-        self.tokens = [int(t) for t in self.rng.integers(0, vocab, size=n_seqs)]
-        self.step_no = 0
+        self.n_seqs, self.vocab, self.every, self.churn, self.join = n_seqs, vocab, every, churn, (join_lo, join_hi)
+        ctx = [int(np.exp(self.rng.uniform(np.log(ctx_lo), np.log(ctx_hi)))) for _ in range(n_seqs)]
+        toks = [int(t) for t in self.rng.integers(0, vocab, size=n_seqs)]
+        self.initial = list(zip(ctx, toks))
 
-    def _admit(self, ctx: int, slot: int = -1):
-        need = ctx // self.P + 1
-        if need > self.max_pages or need > len(self.free):
-            raise ValueError("pool or page table too small")
-        pages = [int(self.free.pop()) for _ in range(need)]
-        self._used(need)
-        if slot < 0:
-            self.ids.append(self.next_id); self.pos.append(ctx); self.pages.append(pages)
-        else:
-            self.ids[slot], self.pos[slot], self.pages[slot] = self.next_id, ctx, pages
+    def after_step(self, step: int):
+        """Slots replaced after `step` steps (counted from 1): [(slot,
+        context, first token)] in ascending slot order, or []."""
+        if step % self.every:
+            return []
+        out = []
+        for b in sorted(self.rng.choice(self.n_seqs, size=self.churn, replace=False).tolist()):
+            out.append((int(b), int(self.rng.integers(self.join[0], self.join[1] + 1)),
+                        int(self.rng.integers(0, self.vocab))))
+        return out
+
+
+class ChurnRun:
+    """A ChurnWorkload played on a scheduler: request b (b < n_seqs) starts
+    in slot b; every churn releases the requests of the chosen slots and
+    submits the new ones, which the scheduler admits into those slots (lowest
+    free slot first, in submission order). Each request's length limit is
+    max_len positions; it ends earlier only by churn."""
+
+    def __init__(self, sched, workload: ChurnWorkload, max_len: int):
+        self.sched, self.w, self.max_len = sched, workload, max_len
+        self.step_no, self.next_id = 0, 0
+        self.req_of_slot = {}
+        for b, (ctx, tok) in enumerate(workload.initial):
+            self._submit(b, ctx, tok)
+
+    def _submit(self, slot, ctx, tok):
+        self.sched.submit(self.next_id, [tok], self.max_len - ctx, cached_len=ctx)
+        self.req_of_slot[slot] = self.next_id
         self.next_id += 1
 
-    def _used(self, n: int):
-        self.pages_in_use += n
-        self.peak_pages = max(self.peak_pages, self.pages_in_use)
-
-    def tables(self) -> np.ndarray:
-        bt = np.zeros((len(self.pos), self.max_pages), np.int32)
-        for b, pg in enumerate(self.pages):
-            bt[b, :len(pg)] = pg
-        return bt
-
     def advance(self):
-        """After a step: every position moves on by one (taking a page when it
-        crosses into a new one); on churn steps returns {slot: first token}
-        for the slots that new sequences took, else {}."""
+        """After a committed step: apply the workload's churn. Returns the
+        slots that new requests took."""
         self.step_no += 1
-        for b in range(len(self.pos)):
-            self.pos[b] += 1
-            if self.pos[b] // self.P >= len(self.pages[b]):
-                if self.pos[b] // self.P >= self.max_pages or not self.free:
-                    raise ValueError("pool or page table too small")
-                self.pages[b].append(int(self.free.pop()))
-                self._used(1)
-        joined = {}
-        if self.step_no % self.every == 0:
-            for b in sorted(self.rng.choice(len(self.pos), size=self.churn, replace=False).tolist()):
-                self.free.extend(self.pages[b])
-                self._used(-len(self.pages[b]))
-                ctx = int(self.rng.integers(self.join[0], self.join[1] + 1))
-                self._admit(ctx, b)
-                joined[b] = int(self.rng.integers(0, self.vocab))
-        return joined
+        ev = self.w.after_step(self.step_no)
+        for slot, _, _ in ev:
+            self.sched.release(self.req_of_slot[slot])
+        for slot, ctx, tok in ev:
+            self._submit(slot, ctx, tok)
+        return [slot for slot, _, _ in ev]

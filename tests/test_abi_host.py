@@ -19,7 +19,8 @@ LEVELS_PER_LAYER = 9
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    import glob
+    text = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", text)))
 

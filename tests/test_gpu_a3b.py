@@ -41,8 +41,8 @@ def weights():
     return synth.make_model(CFG, 0, "cuda")
 
 
-def _case(weights, ctx):
-    pages = ctx // P + 2
+def _case(weights, ctx, extra_tokens=0):
+    pages = (ctx + extra_tokens) // P + 2
     n_pages = pages + 7
     print(f"a3b: cache for {ctx} tokens ({n_pages} pages)", flush=True)
     s = Setup(CFG, n_pages=n_pages, seed=0, device_gen=True, weights=weights)
@@ -114,12 +114,15 @@ def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True, written=None):
         del kv
         kv2, layers = s.oracle_kv(), SAMPLED
     else:
-        # a one-layer cache for layer 0
-        kv2 = PagedKV(synth.bits(s.k0[0:1]), synth.bits(s.v0[0:1].transpose(-1, -2)), P)
-        layers = (0,)
+        # very long caches: every sampled layer with a one-layer host copy of
+        # its pages, loaded one layer at a time
+        kv2, layers = None, SAMPLED
 
     # sampled layers teacher-forced from the device's residuals
     for l in layers:
+        if not end_to_end:
+            print(f"a3b: layer {l} cache to the host", flush=True)
+            kv2 = _LayerKV(l, synth.bits(s.k0[l:l + 1]), synth.bits(s.v0[l:l + 1].transpose(-1, -2)), P)
         xa, lt = attention_block(model, kv2, l, g["xs"][2 * l].astype(np.float32), CTX, bt, cos, sin)
         assert rel_l2(xa, g["xs"][2 * l + 1]) <= 1e-3, ("teacher-forced attention", l)
         lt2 = LayerTrace()
@@ -136,8 +139,9 @@ def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True, written=None):
         # same products, to within one BF16 ulp wherever the value is not
         # tiny (fp32 summation-order differences can move a near-zero value
         # by more ulps than that) and to BF16 noise overall
-        for got, want in ((synth.bits(g["k"][l, page, :, slot, :]), kv2.k[l, page, :, slot, :]),
-                          (synth.bits(g["v"][l, page, :, :, slot]), kv2.v[l, page, :, slot, :])):
+        li = 0 if isinstance(kv2, _LayerKV) else l
+        for got, want in ((synth.bits(g["k"][l, page, :, slot, :]), kv2.k[li, page, :, slot, :]),
+                          (synth.bits(g["v"][l, page, :, :, slot]), kv2.v[li, page, :, slot, :])):
             gf, wf = bf16_to_f32(got), bf16_to_f32(want)
             big_ = np.abs(wf) >= 0.1 * np.max(np.abs(wf))
             assert np.abs(got.astype(np.int32) - want.astype(np.int32))[big_].max() <= 1
@@ -148,6 +152,110 @@ def _check_against_oracle(s, bt, tok, g, CTX, end_to_end=True, written=None):
     cv = {tuple(int(t) for t in x) for x in torch.nonzero(torch.any(g["v"] != s.v0, dim=3).any(dim=2)).tolist()}
     want = {(l, pg, sl) for l in range(L) for pg, sl in (written or {(page, slot)})}
     assert ck == want and cv == want
+
+
+class _LayerKV(PagedKV):
+    """The pages of one layer l, held as a one-layer pool: layer l's reads
+    and writes go to index 0."""
+
+    def __init__(self, layer, k, v, page_size):
+        super().__init__(k, v, page_size)
+        self.layer = layer
+
+    def append(self, layer, block_table, pos, k_bf16, v_bf16):
+        assert layer == self.layer
+        super().append(0, block_table, pos, k_bf16, v_bf16)
+
+    def read(self, layer, block_table, n_tokens):
+        assert layer == self.layer
+        return super().read(0, block_table, n_tokens)
+
+
+class _Snapshot:
+    """A Setup whose 'initial' pools are the device cache as a chain left it."""
+
+    def __init__(self, s, k, v):
+        self.cfg, self.w_dev, self.k0, self.v0 = s.cfg, s.w_dev, k, v
+        self.oracle_model = s.oracle_model
+        self.oracle_kv = lambda k_dev=None, v_dev=None: Setup.oracle_kv(self, k_dev, v_dev)
+
+
+def test_a3b_greedy_chain_steps_0_1_and_32(weights):
+    """A 33-step greedy chain at 8192 cached tokens (argmax fed back on the
+    device). Steps 0, 1 and 32 are checked as in test_a3b_step_matches_oracle,
+    each teacher-forced on the cache the device left behind: the keys and
+    values the earlier steps appended are what the oracle reads."""
+    s, bt, tok, pages = _case(weights, 8192, extra_tokens=48)
+    k, v = s.fresh_pools()
+    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=1, max_pages_per_seq=pages)
+    tokens = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    logits = torch.empty(1, CFG["vocab"], dtype=torch.float32, device="cuda")
+    for step in range(33):
+        check = step in (0, 1, 32)
+        if check:
+            snap = _Snapshot(s, k.clone(), v.clone())
+            fed = int(tokens[0])
+        dec.step([8192 + step], [bt], tokens, logits)
+        if check:
+            assert dec.sync_check() == mk.MK_OK
+            g = dict(logits=logits.cpu().numpy()[0], xs=x_layers(dec).cpu().numpy()[:, 0],
+                     ids=route_ids(dec).cpu().numpy()[:, 0], k=k, v=v)
+            print(f"a3b chain: step {step} (position {8192 + step}, token {fed}) against the oracle", flush=True)
+            _check_against_oracle(snap, bt, fed, g, 8192 + step)
+            del snap
+        tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
+    assert dec.sync_check() == mk.MK_OK
+    dec.close()
+
+
+def test_a3b_prompt_block(weights):
+    """A multi-token step at full scale: 8 prompt tokens at positions
+    100..107 of one sequence in one launch (mk_forward_step). The oracle
+    runs the rows in order on one cache with the device's expert choice
+    adopted per row (routing is discontinuous, as for single steps); every
+    row's residual after every block and its logits are compared, and every
+    disagreement with the oracle's own top-k must be a near tie."""
+    p0, n, ctx = 100, 8, 108
+    pages = ctx // P + 2
+    s = Setup(CFG, n_pages=pages + 3, seed=0, device_gen=True, weights=weights)
+    bt = [int(x) for x in synth.make_block_tables(1, pages, pages + 3, shuffle=True)[0]]
+    toks = [int(t) for t in synth.make_tokens(n, CFG["vocab"], seed=31)]
+    k, v = s.fresh_pools()
+    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=n, max_pages_per_seq=pages, validate_plans=True)
+    tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
+    logits = torch.empty(n, CFG["vocab"], dtype=torch.float32, device="cuda")
+    print(f"a3b prompt block: {n} rows at {p0}..{p0 + n - 1}", flush=True)
+    dec.forward([7] * n, list(range(p0, p0 + n)), [bt] * n, tokens, logits)
+    assert dec.sync_check() == mk.MK_OK
+    gl, gx, gi = logits.cpu().numpy(), x_layers(dec).cpu().numpy(), route_ids(dec).cpu().numpy()
+    dec.close()
+    model, kv = s.oracle_model(lazy_experts=True), s.oracle_kv()
+    L = CFG["n_layers"]
+    for i in range(n):
+        pos = p0 + i
+        cos, sin = rope_cos_sin(pos, CFG["head_dim"], CFG["rope_theta"])
+        x = model.rows("embed", toks[i]).astype(np.float32)
+        for l in range(L):
+            x, lt = attention_block(model, kv, l, x, pos, bt, cos, sin)
+            assert rel_l2(x, gx[2 * l + 1, i]) <= 1e-2, ("after attention", i, l)
+            x = moe_block(model, l, x, lt, force_ids=gi[l, i])
+            assert rel_l2(x, gx[2 * l + 2, i]) <= 1e-2, ("after experts", i, l)
+            own, _ = route_topk(lt.router_logits, CFG["top_k"])
+            if set(own.tolist()) != set(gi[l, i].tolist()):
+                kth = np.sort(np.asarray(lt.router_logits, np.float64))[::-1]
+                tol = 1e-2 * max(1.0, float(np.max(np.abs(lt.router_logits))))
+                assert kth[CFG["top_k"] - 1] - kth[CFG["top_k"]] < tol, ("routing", i, l)
+        err = float(np.max(np.abs(final_logits(model, x) - gl[i])))
+        print(f"a3b prompt block: row {i} logits max-abs {err:.3e}", flush=True)
+        assert err <= 5e-2
+    # the device cache holds the block's keys and values where the oracle wrote them
+    for l in (0, 23, 47):
+        for i in range(n):
+            pg, sl = bt[(p0 + i) // P], (p0 + i) % P
+            assert rel_l2(bf16_to_f32(synth.bits(k[l, pg, :, sl, :])), bf16_to_f32(kv.k[l, pg, :, sl, :])) <= 1e-2
+            assert rel_l2(bf16_to_f32(synth.bits(v[l, pg, :, :, sl])), bf16_to_f32(kv.v[l, pg, :, sl, :])) <= 1e-2
+    del s
+    torch.cuda.empty_cache()
 
 
 def test_a3b_step_matches_oracle(big):
@@ -166,11 +274,12 @@ def test_a3b_megakernel_equals_perop_bitwise(big):
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
 
 
-@pytest.mark.parametrize("ctx", [32768, 262144])
+@pytest.mark.parametrize("ctx", [32768, 131072, 262144])
 def test_a3b_long_context(weights, ctx):
-    """Long contexts: 32K end to end against the oracle; 256K (25.8 GB of
-    cache, attention split over many more chunks) with the sampled layers
-    teacher-forced, plus megakernel == per-op bit for bit."""
+    """Long contexts: 32K end to end against the oracle; 128K and 256K
+    (12.9 and 25.8 GB of cache, attention split over many more chunks) with
+    the sampled layers (0, 1, 23, 46, 47) teacher-forced, each from a
+    one-layer host copy of its pages, plus megakernel == per-op bit for bit."""
     s, bt, tok, pages = _case(weights, ctx)
     a = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL, ctx, pages)
     assert np.all(np.isfinite(a["logits"]))
@@ -182,12 +291,12 @@ def test_a3b_long_context(weights, ctx):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("B", [4, 16, 64])
+@pytest.mark.parametrize("B", [2, 4, 16, 64])
 def test_a3b_batch_matches_oracle(weights, B):
     """The batch sweep's shape: B sequences at 8192 cached tokens each, pages
     from a shuffled pool, per-sequence seeded first tokens. Rows 0 and B-1
-    are checked end to end against the oracle as above; B = 4 also
-    megakernel == per-op bit for bit."""
+    are checked end to end against the oracle as above; B = 2 (the two-token
+    schedule) and B = 4 also megakernel == per-op bit for bit."""
     ctx = 8192
     pages = ctx // P + 2
     n_pages = B * pages + 7
@@ -196,7 +305,7 @@ def test_a3b_batch_matches_oracle(weights, B):
     bts = [[int(x) for x in r] for r in synth.make_block_tables(B, pages, n_pages, seed=B, shuffle=True)]
     toks = [int(t) for t in synth.make_tokens(B, CFG["vocab"], seed=100 + B)]
     outs = []
-    for mode in ([mk.MK_MODE_MEGAKERNEL, mk.MK_MODE_PEROP] if B == 4 else [mk.MK_MODE_MEGAKERNEL]):
+    for mode in ([mk.MK_MODE_MEGAKERNEL, mk.MK_MODE_PEROP] if B <= 4 else [mk.MK_MODE_MEGAKERNEL]):
         k, v = s.fresh_pools()
         dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=B, max_pages_per_seq=pages, mode=mode)
         tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
@@ -223,46 +332,49 @@ def test_a3b_batch_matches_oracle(weights, B):
 
 
 def test_a3b_ragged_zipf_join_step(weights):
-    """The churning batch's shape on a join step: 32 sequences with contexts
-    log-uniform on [128, 32768] advanced 8 steps, so 4 have just joined with
-    short contexts, and a Zipf(1.1) router bias. The longest-context row and a
-    newly joined row are checked end to end against the oracle."""
+    """The churning batch's shape on a join step: 32 requests with contexts
+    log-uniform on [128, 32768] run 8 steps through the host scheduler (the
+    host side only), so 4 have just joined with short contexts, and a
+    Zipf(1.1) router bias. The longest-context row and a newly joined row of
+    that step are checked end to end against the oracle."""
     B = 32
     biases, _, _ = synth.zipf_router_bias(CFG)
     w = dict(weights)
     for l, b in enumerate(biases):
         w[f"layers.{l}.router_bias"] = torch.as_tensor(b).cuda()
     max_pages = 32768 // P + 4
-    rb = synth.RaggedBatch(B, 1 << 20, P, max_pages, CFG["vocab"])
-    joined = {}
+    w0 = synth.ChurnWorkload(B, CFG["vocab"])
+    n_pages = sum(ctx // P + 2 for ctx, _ in w0.initial) + 4 * (2048 // P + 2) + 64
+    sch = mk.Scheduler(B, B, P, max_pages, n_pages, reserve_full=False,
+                       page_order=np.random.default_rng(7).permutation(n_pages))
+    run = synth.ChurnRun(sch, synth.ChurnWorkload(B, CFG["vocab"]), max_len=max_pages * P)
+    joined = []
     for _ in range(8):
-        joined = rb.advance()
-    n_pages = rb.peak_pages + 8
-    rb = synth.RaggedBatch(B, n_pages, P, max_pages, CFG["vocab"])
-    for _ in range(8):
-        joined = rb.advance()
+        n = sch.next()
+        sch.commit(np.zeros(n, np.int32))
+        joined = run.advance()
     assert len(joined) == 4
-    print(f"a3b ragged: {B} sequences, contexts {min(rb.pos)}..{max(rb.pos)}, pool {n_pages} pages", flush=True)
+    n = sch.next()
+    assert n == B
+    pos, bts, toks = sch.positions[:n].tolist(), sch.block_tables[:n].copy(), sch.tokens[:n].tolist()
+    print(f"a3b ragged: {B} requests, contexts {min(pos)}..{max(pos)}, pool {n_pages} pages", flush=True)
     s = Setup(CFG, n_pages=n_pages, seed=0, device_gen=True, weights=w)
-    toks = list(rb.tokens)
-    for b, tok in joined.items():
-        toks[b] = tok
     k, v = s.fresh_pools()
     dec = mk.Decoder(CFG, w, k, v, max_batch=B, max_pages_per_seq=max_pages)
     tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
     logits = torch.empty(B, CFG["vocab"], dtype=torch.float32, device="cuda")
-    dec.step(rb.pos, rb.tables(), tokens, logits, seq_ids=rb.ids)
+    dec.forward(sch.seq_ids[:n].copy(), pos, bts, tokens, logits)
     assert dec.sync_check() == mk.MK_OK
     g = dict(logits=logits.cpu().numpy(), xs=x_layers(dec).cpu().numpy(), ids=route_ids(dec).cpu().numpy(),
              k=k, v=v)
     dec.close()
-    bts = rb.tables()
-    written = {(int(bts[b][rb.pos[b] // P]), rb.pos[b] % P) for b in range(B)}
+    sch.close()
+    written = {(int(bts[b][pos[b] // P]), pos[b] % P) for b in range(B)}
     # the oracle reads the biased router through the same weights dict
     s.w_dev = w
-    for b in (int(np.argmax(rb.pos)), min(joined)):
+    for b in (int(np.argmax(pos)), min(joined)):
         row = dict(logits=g["logits"][b], xs=g["xs"][:, b], ids=g["ids"][:, b], k=g["k"], v=g["v"])
-        print(f"a3b ragged: oracle on row {b} at {rb.pos[b]} cached tokens", flush=True)
-        _check_against_oracle(s, [int(x) for x in bts[b]], toks[b], row, rb.pos[b], written=written)
+        print(f"a3b ragged: oracle on row {b} at {pos[b]} cached tokens", flush=True)
+        _check_against_oracle(s, [int(x) for x in bts[b]], toks[b], row, pos[b], written=written)
     del s, g
     torch.cuda.empty_cache()

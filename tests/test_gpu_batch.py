@@ -181,9 +181,10 @@ def test_batch_greedy_chain(setup):
 
 
 def test_churning_batch_with_zipf_bias(setup):
-    """Eight slots over 12 steps: every 4 steps three sequences finish and new
-    ones (new ids, recycled pages, fresh first tokens) take their slots; the
-    router carries a Zipf(1.1) bias. Each step is compared with the oracle
+    """Eight slots over 12 steps, driven by the host scheduler: every 4 steps
+    three requests end and new ones (new ids, pages recycled through the
+    scheduler's free list, fresh first tokens) take their slots; the router
+    carries a Zipf(1.1) bias. Each step is compared with the oracle
     teacher-forced on the device's tokens and cache."""
     s = setup
     B = 8
@@ -191,19 +192,24 @@ def test_churning_batch_with_zipf_bias(setup):
     w = dict(s.w_dev)
     for l, b in enumerate(biases):
         w[f"layers.{l}.router_bias"] = torch.as_tensor(b).cuda()
-    rb = synth.RaggedBatch(B, N_PAGES, 16, PAGES_PER_SEQ, CFG["vocab"], seed=4, ctx_lo=2, ctx_hi=80,
-                           join_lo=0, join_hi=40, every=4, churn=3)
+    sch = mk.Scheduler(B, B, 16, PAGES_PER_SEQ, N_PAGES, reserve_full=False,
+                       page_order=np.random.default_rng(4).permutation(N_PAGES))
+    run = synth.ChurnRun(sch, synth.ChurnWorkload(B, CFG["vocab"], seed=4, ctx_lo=2, ctx_hi=80, join_lo=0,
+                                                  join_hi=40, every=4, churn=3), max_len=PAGES_PER_SEQ * 16)
     k, v = s.fresh_pools()
     dec = mk.Decoder(CFG, w, k, v, max_batch=B, max_pages_per_seq=PAGES_PER_SEQ)
     model = s.oracle_model(weights=w)
-    tokens = torch.tensor(rb.tokens, dtype=torch.int32, device="cuda")
+    tokens = torch.empty(B, dtype=torch.int32, device="cuda")
     logits = torch.empty(B, CFG["vocab"], device="cuda")
     for st in range(12):
-        pos, bts, ids = list(rb.pos), rb.tables().tolist(), list(rb.ids)
-        cur = [int(x) for x in tokens.cpu().tolist()]
+        n = sch.next()
+        assert n == B
+        pos, bts, ids = sch.positions[:n].tolist(), sch.block_tables[:n].tolist(), sch.seq_ids[:n].tolist()
+        cur = sch.tokens[:n].tolist()
+        tokens.copy_(torch.tensor(cur, dtype=torch.int32))
         kv = s.oracle_kv(k, v)            # the cache as the device holds it before this step
-        print(f"churn step={st} ids={ids}", flush=True)
-        dec.step(pos, bts, tokens, logits, seq_ids=ids)
+        print(f"churn step={st} requests={sch.request_ids[:n].tolist()}", flush=True)
+        dec.forward(ids, pos, bts, tokens, logits)
         assert dec.sync_check() == mk.MK_OK
         ol, tr, _ = decode_step(model, kv, pos, bts, cur)
         gl = logits.cpu().numpy()
@@ -216,10 +222,10 @@ def test_churning_batch_with_zipf_bias(setup):
                     assert routing_margin(lt.router_logits, CFG["top_k"]) < 1e-4, ("routing", st, b, l)
                     break
                 assert rel_l2(xs[2 * l + 2, b], lt.x_out) < 1e-2, ("x_out", st, b, l)
-        tokens.copy_(torch.argmax(logits, dim=1).to(torch.int32))
-        for b, tok in rb.advance().items():
-            tokens[b] = tok
+        sch.commit(np.argmax(gl, axis=1).astype(np.int32))
+        run.advance()
     dec.close()
+    sch.close()
 
 
 def test_longer_sequence_joins_a_reserved_slot(setup):

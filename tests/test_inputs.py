@@ -19,22 +19,16 @@ def test_zipf_bias_slope_and_determinism():
         assert np.array_equal(np.sort(np.rint(rank)), np.arange(1, 129))
 
 
-def test_ragged_batch_pages_and_churn():
-    rb = synth.RaggedBatch(32, 20000, 16, 2200, 1000, seed=3)
-    ctx0 = list(rb.pos)
-    assert min(ctx0) >= 128 and max(ctx0) <= 32768
-    seen_ids = set(rb.ids)
+def test_churn_workload_draws():
+    w = synth.ChurnWorkload(32, 1000, seed=3)
+    ctx0 = [c for c, _ in w.initial]
+    assert len(ctx0) == 32 and min(ctx0) >= 128 and max(ctx0) <= 32768
+    assert len(set(ctx0)) > 20     # log-uniform spread, not a constant
+    w2 = synth.ChurnWorkload(32, 1000, seed=3)
     for step in range(1, 41):
-        joined = rb.advance()
-        assert (len(joined) == 4) == (step % 8 == 0)
-        for b in joined:
-            assert 128 <= rb.pos[b] <= 2048 and rb.ids[b] not in seen_ids
-        seen_ids |= set(rb.ids)
-        # every sequence holds exactly the pages its next slot needs, no page twice
-        owned = [p for pg in rb.pages for p in pg]
-        assert len(owned) == len(set(owned))
-        assert not set(owned) & set(rb.free)
-        for b in range(32):
-            assert len(rb.pages[b]) == rb.pos[b] // 16 + 1
-        bt = rb.tables()
-        assert bt.shape == (32, 2200)
+        ev, ev2 = w.after_step(step), w2.after_step(step)
+        assert ev == ev2
+        assert (len(ev) == 4) == (step % 8 == 0)
+        assert [s for s, _, _ in ev] == sorted({s for s, _, _ in ev})
+        for slot, ctx, tok in ev:
+            assert 0 <= slot < 32 and 128 <= ctx <= 2048 and 0 <= tok < 1000
