@@ -268,6 +268,26 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
                         int64_t cap_tasks, int32_t* wg_offsets, int32_t* counter_targets);
 
 /*
+ * Check a task table against the plan builder's invariants without a
+ * device: the table (12 int32 per task, as mk_plan_build writes it) and
+ * per-workgroup offsets for n_wg workgroups, for this batch and these
+ * positions. MK_OK, or MK_ERR_INVALID with the first violated rule in
+ * mk_last_error: counter targets equal to their producer counts, every wait
+ * on a lower level, workgroup lists in level order (deadlock freedom with
+ * all workgroups resident), each operation's output covered exactly once,
+ * and read coverage: every range a tile reads (residual stream, QKV rows of
+ * its KV group, attention partials of its head, routing, expert
+ * activations) is written by tiles whose completion its waits imply,
+ * directly or through the waits of the tiles it waits on. This is the "no
+ * missing dependency" property of tile-level scheduling ("Cohere Publishes
+ * One-Kernel Server for North Mini Code, Claims 1.58x vLLM Speedup",
+ * section "What the scheduling change is meant to avoid").
+ */
+mk_status mk_plan_check(const mk_dims* dims, const mk_options* opts, int32_t n_wg, int32_t batch,
+                        const int32_t* positions, const int32_t* tasks, int64_t n_tasks,
+                        const int32_t* wg_offsets);
+
+/*
  * Per-task timestamps of the last step (when mk_options.trace was set): one
  * record of 8 uint64 per task, {task index | workgroup << 32, t_start,
  * t_after_wait, four phase stamps inside the tile (0 if unused), t_end}, in

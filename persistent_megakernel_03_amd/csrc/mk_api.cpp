@@ -787,6 +787,39 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
     }
 }
 
+mk_status mk_plan_check(const mk_dims* dims, const mk_options* opts, int32_t n_wg, int32_t batch,
+                        const int32_t* positions, const int32_t* tasks, int64_t n_tasks, const int32_t* wg_offsets) {
+    try {
+        if (!dims || !positions || !tasks || !wg_offsets) return fail(MK_ERR_INVALID, "null argument");
+        mk_options o;
+        memset(&o, 0, sizeof o);
+        if (opts) o = *opts;
+        const std::string why = check_dims(*dims, mm_min_of(o));
+        if (!why.empty()) return fail(MK_ERR_UNSUPPORTED, "%s", why.c_str());
+        if (batch <= 0 || batch > dims->max_batch || n_wg <= 0 || n_tasks < 0) return fail(MK_ERR_INVALID, "bad sizes");
+        const ModelShape s = shape_of(*dims, max_chunks_for(*dims));
+        Plan P;
+        const std::string err = build_plan(s, tile_config(o), n_wg, batch, positions, &P);
+        if (!err.empty()) return fail(MK_ERR_CAPACITY, "%s", err.c_str());
+        // the caller's task table and lists in place of the built ones
+        P.tasks.assign(reinterpret_cast<const Task*>(tasks), reinterpret_cast<const Task*>(tasks) + n_tasks);
+        P.wg_off.assign(wg_offsets, wg_offsets + n_wg + 1);
+        if (P.wg_off.front() != 0 || P.wg_off.back() > n_tasks) return fail(MK_ERR_INVALID, "plan invalid: offsets");
+        for (int w = 0; w < n_wg; ++w)
+            if (P.wg_off[w + 1] < P.wg_off[w]) return fail(MK_ERR_INVALID, "plan invalid: offsets");
+        for (const Task& t : P.tasks)
+            if (t.op < 0 || t.op >= OP_COUNT || t.level < 0 || t.level >= P.n_levels)
+                return fail(MK_ERR_INVALID, "plan invalid: task op or level out of range");
+        const std::string verr = validate_plan(s, P);
+        if (!verr.empty()) return fail(MK_ERR_INVALID, "plan invalid: %s", verr.c_str());
+        return MK_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(MK_ERR_CAPACITY, "host allocation failed");
+    } catch (...) {
+        return fail(MK_ERR_INVALID, "unexpected exception in mk_plan_check");
+    }
+}
+
 void mk_destroy(mk_handle* h) {
     if (!h) return;
     (void)hipSetDevice(h->device);

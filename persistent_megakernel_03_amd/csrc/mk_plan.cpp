@@ -484,6 +484,125 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     P.tasks.insert(P.tasks.end(), pool.begin(), pool.end());
 }
 
+// Read coverage ("no missing dependency"): every exchange-buffer range a
+// tile reads was written by tiles whose completion the tile's waits imply.
+// deps(c) is the set of counters whose producers have all finished once
+// counter c reached its target: c itself and, recursively, the counters its
+// producers waited on. For each tile, the counters signalled by the tiles
+// that write what it reads must lie in deps(ctr) | deps(pre_ctr). Writes
+// are looked up per producing operation: which counters its tiles signal,
+// for a whole layer or for one KV group, hidden-row range or sequence.
+static std::string check_reads(const ModelShape& s, const Plan& P, const std::vector<int>& prod_level) {
+    const CounterLayout cl{s.L, s.Hkv, s.max_batch};
+    const int n_main = cl.n_main();
+    const int W = (n_main + 63) / 64;
+    typedef std::vector<uint64_t> Bits;
+    // producers' waits per counter
+    std::vector<std::set<std::pair<int, int>>> pw(n_main);
+    for (const Task& t : P.tasks)
+        if (t.op != OP_CLAIM && t.signal >= 0) pw[t.signal].insert({t.ctr, t.pre_ctr});
+    // deps in counter order of producer level (lower levels first)
+    std::vector<int> order(n_main);
+    for (int c = 0; c < n_main; ++c) order[c] = c;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return prod_level[a] < prod_level[b]; });
+    std::vector<Bits> deps(n_main, Bits(W, 0));
+    for (int c : order) {
+        if (prod_level[c] < 0) continue;
+        Bits& d = deps[c];
+        d[c / 64] |= 1ull << (c % 64);
+        for (const auto& w : pw[c])
+            for (int x : {w.first, w.second})
+                if (x >= 0)
+                    for (int i = 0; i < W; ++i) d[i] |= deps[x][i];
+    }
+    auto has = [&](const Bits& d, int c) { return c >= 0 && ((d[c / 64] >> (c % 64)) & 1ull); };
+    // writers: per (op, layer) the counters signalled, whole and per selector
+    struct Key {
+        int op, layer, sel;
+        bool operator<(const Key& o) const { return std::tie(op, layer, sel) < std::tie(o.op, o.layer, o.sel); }
+    };
+    std::map<Key, std::set<int>> wr;          // sel -1: every tile of the op
+    std::map<std::pair<int, int>, std::vector<std::tuple<int, int, int>>> rows;   // (op, layer) -> (r0, r1, signal)
+    const int G = s.Hq / s.Hkv;
+    for (const Task& t : P.tasks) {
+        if (t.op == OP_CLAIM) continue;
+        wr[{t.op, t.layer, -1}].insert(t.signal);
+        if (t.op == OP_QKV) wr[{t.op, t.layer, t.a0}].insert(t.signal);                    // KV group
+        if (t.op == OP_ATTN) wr[{t.op, t.layer, t.a0 * s.Hkv + t.a1}].insert(t.signal);   // (sequence, group)
+        if (t.op == OP_OPROJ || (t.op == OP_DOWN && !P.mm) || t.op == OP_MOESUM)
+            rows[{t.op, t.layer}].push_back(std::make_tuple(t.a0, t.a1, t.signal));
+    }
+    const int x_op = P.mm ? OP_MOESUM : OP_DOWN;   // writes the layer output
+    char buf[256];
+    auto need = [&](const Task& t, const Bits& d, int op, int layer, int sel) -> std::string {
+        auto it = wr.find({op, layer, sel});
+        if (it == wr.end()) {
+            snprintf(buf, sizeof buf, "op %d layer %d reads what no op-%d tile (layer %d, part %d) writes", t.op,
+                     t.layer, op, layer, sel);
+            return buf;
+        }
+        for (int c : it->second)
+            if (!has(d, c)) {
+                snprintf(buf, sizeof buf, "op %d layer %d reads op %d layer %d output without waiting on counter %d",
+                         t.op, t.layer, op, layer, c);
+                return buf;
+            }
+        return std::string();
+    };
+    auto need_rows = [&](const Task& t, const Bits& d, int op, int layer, int r0, int r1) -> std::string {
+        for (const auto& w : rows[{op, layer}])
+            if (std::get<0>(w) < r1 && r0 < std::get<1>(w) && !has(d, std::get<2>(w))) {
+                snprintf(buf, sizeof buf, "op %d layer %d reads rows %d..%d of op %d without waiting on counter %d",
+                         t.op, t.layer, r0, r1, op, std::get<2>(w));
+                return buf;
+            }
+        return std::string();
+    };
+    // the residual stream entering layer l: the embedding or the previous layer's output
+    auto x_in = [&](const Task& t, const Bits& d, int l) {
+        return l == 0 ? need(t, d, OP_EMBED, 0, -1) : need(t, d, x_op, l - 1, -1);
+    };
+    for (const Task& t : P.tasks) {
+        if (t.op == OP_CLAIM) continue;
+        Bits d(W, 0);
+        for (int c : {t.ctr, t.pre_ctr})
+            if (c >= 0)
+                for (int i = 0; i < W; ++i) d[i] |= deps[c][i];
+        const int l = t.layer;
+        std::string e;
+        switch (t.op) {
+            case OP_EMBED: break;
+            case OP_QKV: e = x_in(t, d, l); break;
+            case OP_ATTN: e = need(t, d, OP_QKV, l, t.a1); break;
+            case OP_COMBINE: e = need(t, d, OP_ATTN, l, t.a0 * s.Hkv + t.a1 / G); break;
+            case OP_OPROJ:
+                e = need(t, d, OP_COMBINE, l, -1);
+                if (e.empty()) e = l == 0 ? need(t, d, OP_EMBED, 0, -1) : need_rows(t, d, x_op, l - 1, t.a0, t.a1);
+                break;
+            case OP_ROUTER: e = need(t, d, OP_OPROJ, l, -1); break;
+            case OP_ROUTE: e = need(t, d, OP_ROUTER, l, -1); break;
+            case OP_GATEUP:
+                e = need(t, d, OP_ROUTER, l, -1);
+                if (e.empty()) e = P.mm ? need(t, d, OP_ROUTE, l, -1) : need(t, d, OP_OPROJ, l, -1);
+                break;
+            case OP_DOWN:
+                e = need(t, d, OP_GATEUP, l, -1);
+                if (e.empty()) e = P.mm ? need(t, d, OP_ROUTE, l, -1) : need(t, d, OP_ROUTER, l, -1);
+                if (e.empty() && !P.mm) e = need_rows(t, d, OP_OPROJ, l, t.a0, t.a1);
+                break;
+            case OP_MOESUM:
+                e = need(t, d, OP_DOWN, l, -1);
+                if (e.empty()) e = need(t, d, OP_ROUTE, l, -1);
+                if (e.empty()) e = need_rows(t, d, OP_OPROJ, l, t.a0, t.a1);
+                break;
+            case OP_LMHEAD: e = need(t, d, x_op, s.L - 1, -1); break;
+            default: break;
+        }
+        if (!e.empty()) return e;
+    }
+    return std::string();
+}
+
 std::string validate_plan(const ModelShape& s, const Plan& P) {
     const CounterLayout cl{s.L, s.Hkv, s.max_batch};
     const int n_main = cl.n_main();
@@ -595,7 +714,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         }
         if (end != want) return "tile ranges do not cover the operation";
     }
-    return std::string();
+    return check_reads(s, P, prod_level);
 }
 
 }  // namespace mk

@@ -35,7 +35,7 @@ STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID", -2: "MK_ERR_UNSUPPORTED", -3: 
 
 # Every function declared in include/mk.h.
 EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_forward_step", "mk_set_mode",
-           "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_get_trace", "mk_get_plan", "mk_kernel_time",
+           "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_plan_check", "mk_get_trace", "mk_get_plan", "mk_kernel_time",
            "mk_destroy", "mk_last_error",
            # include/mk_sched.h
            "mk_sched_create", "mk_sched_destroy", "mk_sched_submit", "mk_sched_release", "mk_sched_next",
@@ -132,6 +132,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                   c.POINTER(c.c_int32), c.POINTER(mk_plan_info), c.POINTER(c.c_int32), c.c_int64,
                                   c.POINTER(c.c_int32), c.POINTER(c.c_int32)]
     lib.mk_plan_build.restype = c.c_int
+    lib.mk_plan_check.argtypes = [c.POINTER(mk_dims), c.POINTER(mk_options), c.c_int32, c.c_int32,
+                                  c.POINTER(c.c_int32), c.POINTER(c.c_int32), c.c_int64, c.POINTER(c.c_int32)]
+    lib.mk_plan_check.restype = c.c_int
     lib.mk_get_trace.argtypes = [c.c_void_p, c.c_void_p, c.c_size_t, c.POINTER(c.c_size_t)]
     lib.mk_get_trace.restype = c.c_int
     lib.mk_get_plan.argtypes = [c.c_void_p, c.POINTER(c.c_int32), c.c_int64, c.POINTER(c.c_int64)]
@@ -260,6 +263,16 @@ def mk_plan_build(dims: mk_dims, opts: mk_options, n_wg: int, positions: Sequenc
                              offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                              targets.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
     return info, tasks, offs, targets
+
+
+def mk_plan_check(dims: mk_dims, opts: mk_options, n_wg: int, positions: Sequence[int], tasks: np.ndarray,
+                  offs: np.ndarray) -> None:
+    """Raises MkError(MK_ERR_INVALID) naming the first rule the task table breaks."""
+    p_arr, p_p = _i32(positions)
+    t_arr = np.ascontiguousarray(tasks, dtype=np.int32)
+    o_arr, o_p = _i32(offs)
+    _check(load().mk_plan_check(ctypes.byref(dims), ctypes.byref(opts), n_wg, len(p_arr), p_p,
+                                t_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), t_arr.shape[0], o_p))
 
 
 def mk_get_trace(h: int) -> np.ndarray:

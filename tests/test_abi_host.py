@@ -192,3 +192,50 @@ def test_plan_rejects_bad_input():
     with pytest.raises(mk.MkError) as e:
         mk.mk_plan_build(bad, mk.make_options(), 8, [1])
     assert e.value.status == mk.MK_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("cfg_name,batch,positions,shared", [
+    ("A3B", 1, [8192], 0), ("TINY", 2, [5, 70], 0), ("TINY", 8, [5, 70, 64, 63, 1, 0, 127, 300], 2),
+    ("A3B", 4, [8192, 100, 3000, 5], 0)])
+def test_plan_check_accepts_built_plans_and_finds_missing_dependencies(cfg_name, batch, positions, shared):
+    """mk_plan_check passes the builder's own plans; planted mistakes that keep
+    every counter target and level order intact (so only the read-coverage
+    rule can see them) are rejected: an attention tile waiting on another KV
+    group's QKV counter, a down tile waiting on the router instead of the
+    gate/up tiles, a merge tile waiting on another group's attention."""
+    cfg = configs.dims_of(cfg_name)
+    d = mk.make_dims(cfg, max(2, batch), 600, 1200)
+    o = mk.make_options(shared_levels=shared)
+    info, tasks, offs, targets = mk.mk_plan_build(d, o, 512, positions)
+    mk.mk_plan_check(d, o, 512, positions, tasks, offs)
+    Hkv, L = cfg["n_kv_heads"], cfg["n_layers"]
+    per = 2 * Hkv + 7
+    qkv_ctr = lambda l, g: 1 + l * per + g
+    attn_ctr = lambda l, g: 1 + l * per + Hkv + g
+    router_ctr = lambda l: 1 + l * per + 2 * Hkv + 2
+    l = L - 1
+
+    def planted(pick, change):
+        t = tasks.copy()
+        idx = [i for i in range(len(t)) if pick(t[i])]
+        assert idx
+        change(t[idx[0]])
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_plan_check(d, o, 512, positions, t, offs)
+        assert e.value.status == mk.MK_ERR_INVALID and "reads" in str(e.value)
+
+    def other_group(t):
+        t[8] = qkv_ctr(t[1], (t[3] + 1) % Hkv)
+
+    planted(lambda t: t[0] == OP_ATTN and t[1] == l and t[8] == qkv_ctr(l, t[3]), other_group)
+
+    def to_other_attn(t):
+        g = t[8] - (1 + t[1] * per + Hkv)
+        t[8] = attn_ctr(t[1], (g + 1) % Hkv)
+        t[9] = int(targets[t[8]])
+
+    planted(lambda t: t[0] == OP_COMBINE and t[1] == l, to_other_attn)
+    if batch <= 2:
+        def down_on_router(t):
+            t[8], t[9] = router_ctr(t[1]), int(targets[router_ctr(t[1])])
+        planted(lambda t: t[0] == OP_DOWN and t[1] == l, down_on_router)
