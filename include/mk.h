@@ -209,6 +209,30 @@ mk_status mk_forward_step(mk_handle* h, int32_t batch, const int32_t* seq_ids,
                           const int32_t* positions, const int32_t* block_tables,
                           const int32_t* tokens, float* logits, void* stream);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): mk_decode_step with the
+ * step's counters and exchange buffers (the residual stream, attention
+ * partials, router logits, expert activations and the like) in the library's
+ * static device scratch instead of the handle's workspace. Same arguments,
+ * same results (the same kernels and plan), and like every step it calls no
+ * hipMalloc, hipFree, hipHostMalloc or other device or pinned allocator; the
+ * plan's host bookkeeping uses ordinary heap memory.
+ *  - The scratch is 64 MiB per device, held from the library's first use on
+ *    that device until the process ends. A handle whose step needs more
+ *    (mk_workspace_bytes minus the task tables, about the per-layer
+ *    attention partials for its max_batch and max_pages_per_seq) gets
+ *    MK_ERR_CAPACITY, before anything is enqueued.
+ *  - Every call on a device shares that device's scratch, which keeps the
+ *    last call's contents; each call clears the counters it needs with a
+ *    fill kernel on `stream`. Calls that overlap on one device (other
+ *    streams, other handles) race: order them.
+ *  - mk_get_debug_ptrs refers to the handle's workspace, not to the scratch.
+ */
+mk_status mk_decode_step_noalloc(mk_handle* h, int32_t batch, const int32_t* seq_ids,
+                                 const int32_t* positions, const int32_t* block_tables,
+                                 const int32_t* tokens, float* logits, void* stream);
+
 /* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PEROP for later steps. */
 mk_status mk_set_mode(mk_handle* h, int32_t mode);
 

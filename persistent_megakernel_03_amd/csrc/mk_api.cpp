@@ -413,6 +413,10 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         }
         MK_HIP(hipEventCreateWithFlags(&h->plan_ev, hipEventDisableTiming));
         MK_HIP(hipEventCreateWithFlags(&h->step_ev, hipEventDisableTiming));
+        // plan staging for the largest plan (both task orders and the
+        // offsets), so that no step allocates pinned memory
+        h->plan_stage_bytes = (size_t)2 * h->lay.cap_tasks * sizeof(Task) + (size_t)(h->lay.max_wg + 1) * 4;
+        MK_HIP(hipHostMalloc(reinterpret_cast<void**>(&h->plan_stage), h->plan_stage_bytes, hipHostMallocDefault));
         if (o.time_kernels) {
             MK_HIP(hipEventCreate(&h->t_begin));
             MK_HIP(hipEventCreate(&h->t_end));
@@ -440,12 +444,7 @@ static mk_status upload_plan(mk_handle* h, hipStream_t stream) {
     const size_t nt = P.tasks.size(), nl = P.level_tasks.size();
     const size_t bytes = (nt + nl) * sizeof(Task) + (P.wg_off.size()) * 4;
     if (h->plan_ev_used) MK_HIP(hipEventSynchronize(h->plan_ev));
-    if (bytes > h->plan_stage_bytes) {
-        if (h->plan_stage) MK_HIP(hipHostFree(h->plan_stage));
-        h->plan_stage = nullptr;
-        MK_HIP(hipHostMalloc(reinterpret_cast<void**>(&h->plan_stage), bytes, hipHostMallocDefault));
-        h->plan_stage_bytes = bytes;
-    }
+    if (bytes > h->plan_stage_bytes) return fail(MK_ERR_CAPACITY, "plan of %zu bytes exceeds its staging", bytes);
     char* s = h->plan_stage;
     memcpy(s, P.tasks.data(), nt * sizeof(Task));
     memcpy(s + nt * sizeof(Task), P.level_tasks.data(), nl * sizeof(Task));
@@ -468,7 +467,7 @@ static mk_status upload_plan(mk_handle* h, hipStream_t stream) {
 // row that feeds it; otherwise every row is its own run.
 static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
                            const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream_,
-                           bool multi_token) {
+                           bool multi_token, bool use_scratch = false) {
     try {
         if (!h) return fail(MK_ERR_INVALID, "null handle");
         if (!positions || !block_tables || !tokens || !logits) return fail(MK_ERR_INVALID, "null argument");
@@ -476,6 +475,18 @@ static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, 
         if (batch <= 0) return fail(MK_ERR_INVALID, "batch must be positive");
         if (batch > d.max_batch) return fail(MK_ERR_CAPACITY, "batch %d > max_batch %d", batch, d.max_batch);
         hipStream_t stream = static_cast<hipStream_t>(stream_);
+        // the static scratch: counter banks and exchange buffers, laid out as
+        // in the workspace (regions banks .. wtab)
+        char* scratch = nullptr;
+        const size_t scratch_need = h->lay.wtab - h->lay.banks;
+        if (use_scratch) {
+            if (scratch_need > kScratchBytes)
+                return fail(MK_ERR_CAPACITY, "this handle's step needs %zu bytes of scratch, the library holds %zu",
+                            scratch_need, (size_t)kScratchBytes);
+            void* sp = nullptr;
+            MK_HIP(scratch_address(h->device, &sp));
+            scratch = static_cast<char*>(sp);
+        }
         std::vector<int32_t> first_row(batch);
         for (int b = 0; b < batch; ++b) first_row[b] = b;
         if (multi_token) {
@@ -622,6 +633,28 @@ static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, 
         uint32_t* banks = reinterpret_cast<uint32_t*>(h->ws + h->lay.banks);
         p.ctr = banks + (int64_t)h->bank * h->lay.bank_words;
         p.ctr_other = banks + (int64_t)(1 - h->bank) * h->lay.bank_words;
+        if (use_scratch) {
+            // every pointer into banks .. wtab moves to the same offset in the
+            // scratch; both counter banks start at zero (a fill kernel, so the
+            // step can be captured), the step uses bank 0
+            auto at = [&](size_t off) { return scratch + (off - h->lay.banks); };
+            banks = reinterpret_cast<uint32_t*>(at(h->lay.banks));
+            MK_HIP(launch_fill(banks, 2 * h->lay.bank_words, 0u, stream));
+            p.ctr = banks;
+            p.ctr_other = banks + h->lay.bank_words;
+            p.x = reinterpret_cast<float*>(at(h->lay.x));
+            p.qkv = reinterpret_cast<float*>(at(h->lay.qkv));
+            p.att_part = reinterpret_cast<float*>(at(h->lay.att_part));
+            p.att_ml = reinterpret_cast<float*>(at(h->lay.att_ml));
+            p.att_out = reinterpret_cast<float*>(at(h->lay.att_out));
+            p.rlogits = reinterpret_cast<float*>(at(h->lay.rlogits));
+            p.route_ids = reinterpret_cast<int32_t*>(at(h->lay.route_ids));
+            p.route_w = reinterpret_cast<float*>(at(h->lay.route_w));
+            p.act = reinterpret_cast<float*>(at(h->lay.act));
+            p.rtab = reinterpret_cast<int32_t*>(at(h->lay.rtab));
+            p.ybuf = reinterpret_cast<float*>(at(h->lay.ybuf));
+            p.h2s = reinterpret_cast<float*>(at(h->lay.h2s));
+        }
         const int nb = batch >= h->mm_min ? 0 : batch;
         p.mm = nb == 0 ? 1 : 0;
         const KernelPair& k = h->kern[nb];
@@ -655,7 +688,7 @@ static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, 
         } else {
             h->step_ev_used = false;
         }
-        h->bank = 1 - h->bank;
+        if (!use_scratch) h->bank = 1 - h->bank;
         h->last_n_tasks = (int64_t)(h->o.mode == MK_MODE_MEGAKERNEL ? h->plan.tasks.size() : h->plan.level_tasks.size());
         h->last_perop = h->o.mode != MK_MODE_MEGAKERNEL;
         return MK_OK;
@@ -676,6 +709,11 @@ mk_status mk_decode_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, co
 mk_status mk_forward_step(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
                           const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream) {
     return step_impl(h, batch, seq_ids, positions, block_tables, tokens, logits, stream, true);
+}
+
+mk_status mk_decode_step_noalloc(mk_handle* h, int32_t batch, const int32_t* seq_ids, const int32_t* positions,
+                                 const int32_t* block_tables, const int32_t* tokens, float* logits, void* stream) {
+    return step_impl(h, batch, seq_ids, positions, block_tables, tokens, logits, stream, false, true);
 }
 
 mk_status mk_sync_check(mk_handle* h, void* stream) {

@@ -30,4 +30,10 @@ hipError_t launch_perop_level(const KernelPair& k, const Params& p, int general,
                               int count, hipStream_t stream);
 hipError_t launch_fill(uint32_t* dst, int64_t n, uint32_t v, hipStream_t stream);
 
+// The library's static device scratch (mk_decode_step_noalloc): its size, and
+// its device address on `device` (looked up once per device, then cached).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_address(int device, void** out);
+
 }  // namespace mk

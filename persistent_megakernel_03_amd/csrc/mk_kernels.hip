@@ -11,6 +11,8 @@
 // stream's kernel boundaries are the only synchronisation -- the conventional
 // pipeline the pages compare against (same page, section "The delay is
 // between operations").
+#include <mutex>
+
 #include "mk_kernels.h"
 #include "mk_tiles.h"
 
@@ -82,6 +84,32 @@ __global__ void __launch_bounds__(NT, 2) k_perop(Params p, int general, int firs
     const Task t = p.tasks[i];
     __syncthreads();
     run_task<S, NB>(t, p, lds, general, i);
+}
+
+// Device scratch of mk_decode_step_noalloc: the step's counters and exchange
+// buffers for callers that cannot allocate. In host code `scratch` names a
+// host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(int device, void** out) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        int prev = 0;
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess) return e;
+        if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (prev != device) (void)hipSetDevice(prev);
+        if (e != hipSuccess) return e;
+        addr[device] = p;
+    }
+    *out = addr[device];
+    return hipSuccess;
 }
 
 __global__ void k_fill_u32(uint32_t* dst, int64_t n, uint32_t v) {

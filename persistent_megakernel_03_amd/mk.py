@@ -34,7 +34,8 @@ STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID", -2: "MK_ERR_UNSUPPORTED", -3: 
                 -4: "MK_ERR_BAD_PAGE", -5: "MK_ERR_HIP", -6: "MK_ERR_TIMEOUT", -7: "MK_ERR_DEVICE"}
 
 # Every function declared in include/mk.h.
-EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_forward_step", "mk_set_mode",
+EXPORTS = ["mk_kv_pool_bytes", "mk_workspace_bytes", "mk_create", "mk_decode_step", "mk_forward_step",
+           "mk_decode_step_noalloc", "mk_set_mode",
            "mk_sync_check", "mk_get_debug_ptrs", "mk_plan_build", "mk_plan_check", "mk_get_trace", "mk_get_plan", "mk_kernel_time",
            "mk_destroy", "mk_last_error",
            # include/mk_sched.h
@@ -122,6 +123,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_decode_step.restype = c.c_int
     lib.mk_forward_step.argtypes = lib.mk_decode_step.argtypes
     lib.mk_forward_step.restype = c.c_int
+    lib.mk_decode_step_noalloc.argtypes = lib.mk_decode_step.argtypes
+    lib.mk_decode_step_noalloc.restype = c.c_int
     lib.mk_set_mode.argtypes = [c.c_void_p, c.c_int32]
     lib.mk_set_mode.restype = c.c_int
     lib.mk_sync_check.argtypes = [c.c_void_p, c.c_void_p]
@@ -227,6 +230,15 @@ def mk_forward_step(h: int, batch: int, seq_ids, positions, block_tables, tokens
     b_arr, b_p = _i32(block_tables)
     _check(load().mk_forward_step(ctypes.c_void_p(h), batch, s_p, p_p, b_p, ctypes.c_void_p(tokens),
                                   ctypes.c_void_p(logits), ctypes.c_void_p(stream)))
+
+
+def mk_decode_step_noalloc(h: int, batch: int, seq_ids, positions, block_tables, tokens: int, logits: int,
+                           stream: int) -> None:
+    s_arr, s_p = _i32(seq_ids) if seq_ids is not None else (None, None)
+    p_arr, p_p = _i32(positions)
+    b_arr, b_p = _i32(block_tables)
+    _check(load().mk_decode_step_noalloc(ctypes.c_void_p(h), batch, s_p, p_p, b_p, ctypes.c_void_p(tokens),
+                                         ctypes.c_void_p(logits), ctypes.c_void_p(stream)))
 
 
 def mk_set_mode(h: int, mode: int) -> None:
