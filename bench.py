@@ -697,13 +697,24 @@ def cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, n_ste
     kv_k, kv_v = kv.k.copy(), kv.v.copy()
     decode_step(model, PagedKV(kv_k, kv_v, cfg["page_size"]), pos, block_tables, toks)
     del kv_k, kv_v
-    threads = len(os.sched_getaffinity(0))
+    cores_visible = len(os.sched_getaffinity(0))
+    threads, blas_threads, blas_lib = cores_visible, None, None
     try:
         from threadpoolctl import threadpool_info
-        blas = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         if blas:
-            threads = max(blas)
+            blas_threads = max(int(i.get("num_threads", 0)) for i in blas)
+            blas_lib = blas[0].get("internal_api")
+            threads = blas_threads
     except Exception:
+        pass
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
         pass
     t0 = time.perf_counter()
     for _ in range(n_steps):
@@ -714,7 +725,9 @@ def cpu_baseline(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, n_ste
     log(f"cpu oracle: {B * n_steps / el:.3f} tok/s over {n_steps} steps ({el:.1f}s, {threads} cores)")
     return {"value": round(B * n_steps / el, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_steps} greedy steps of the same workload from its first position, after one untimed "
-                      f"pass that decodes the touched weights; numpy float32"}
+                      f"pass that decodes the touched weights; numpy float32",
+            "cpu_model": cpu_model, "cores_visible": cores_visible, "blas_threads": blas_threads,
+            "blas": blas_lib}
 
 
 if __name__ == "__main__":

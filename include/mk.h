@@ -277,7 +277,9 @@ typedef struct mk_plan_info {
     int32_t n_counters;
     int32_t n_levels;
     int32_t chunk_tokens;
-    int32_t reserved[3];
+    int32_t cap_tasks; /* tasks a handle of these dims and options reserves for
+                          any batch on at most n_wg workgroups (n_tasks <= it) */
+    int32_t reserved[2];
 } mk_plan_info;
 
 /*

@@ -129,7 +129,7 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
     const TileConfig cfg = tile_config(o);
     const CounterLayout cl{d.n_layers, d.n_kv_heads, d.max_batch};
     L.bank_words = cl.bank_words();
-    L.cap_tasks = max_tasks(s, cfg);
+    L.cap_tasks = max_tasks(s, cfg, max_wg);
     L.max_wg = max_wg;
     const int64_t B = d.max_batch, H = d.hidden, QKVD = (int64_t)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
     size_t off = 0;
@@ -811,6 +811,7 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
         info->n_counters = (int32_t)P.targets.size();
         info->n_levels = P.n_levels;
         info->chunk_tokens = P.chunk;
+        info->cap_tasks = (int32_t)std::min<int64_t>(max_tasks(s, tile_config(o), n_wg), INT32_MAX);
         if (tasks) {
             if (cap_tasks < (int64_t)P.tasks.size()) return fail(MK_ERR_CAPACITY, "task buffer too small");
             memcpy(tasks, P.tasks.data(), P.tasks.size() * sizeof(Task));

@@ -383,6 +383,25 @@ __device__ __forceinline__ void load_row(uint4 (&w)[NCH], const uint16_t* row, i
     }
 }
 
+// The byte offsets of this lane's chunks in a row (the clamp of load_row),
+// computed once per tile so that each further row costs one address add
+// per chunk instead of recomputing the lane's chunk indices.
+template <int NCH>
+__device__ __forceinline__ void chunk_offsets(int (&off)[NCH], int K8) {
+    const int lane = tid_() & 63;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int ch = lane + 64 * c;
+        off[c] = (ch < K8 ? ch : K8 - 1) * 16;
+    }
+}
+template <int NCH>
+__device__ __forceinline__ void load_row_at(uint4 (&w)[NCH], const uint16_t* row, const int (&off)[NCH]) {
+    const char* r = reinterpret_cast<const char*>(row);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) w[c] = ld16s(r + off[c]);
+}
+
 // Wave-level streaming matrix-vector product over split activation slices hx
 // (split_x) that the caller holds. The wave owns `nmine` row-vectors;
 // rowptr(i) returns the i-th. The first PF rows are loaded before ready()
@@ -401,8 +420,10 @@ __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine,
     }
     uint4 buf[PF][NCH];
     const int last = nmine - 1;
+    int off[NCH];
+    chunk_offsets<NCH>(off, K8);
 #pragma unroll
-    for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], rowptr(s < last ? s : last), K8);
+    for (int s = 0; s < PF; ++s) load_row_at<NCH>(buf[s], rowptr(s < last ? s : last), off);
     ready();
     for (int i0 = 0; i0 < nmine; i0 += PF) {
 #pragma unroll
@@ -417,7 +438,7 @@ __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine,
                 acc[b] = wave_sum(a);
             }
             const int nx = i + PF;
-            if (i0 + PF < nmine) load_row<NCH>(buf[s], rowptr(nx < last ? nx : last), K8);
+            if (i0 + PF < nmine) load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
             if (i < nmine) emit(i, acc);
         }
     }
@@ -441,8 +462,10 @@ __device__ __forceinline__ void gemv_rows_warm(uint32_t (&hx)[NB][NCH][8], int n
     }
     uint4 buf[PF][NCH];
     const int last = nmine - 1;
+    int off[NCH];
+    chunk_offsets<NCH>(off, K8);
 #pragma unroll
-    for (int s = 0; s < PF; ++s) load_row<NCH>(buf[s], rowptr(s < last ? s : last), K8);
+    for (int s = 0; s < PF; ++s) load_row_at<NCH>(buf[s], rowptr(s < last ? s : last), off);
 #pragma clang loop unroll(disable)
     for (int pass = 0; pass < 2; ++pass) {
         ready(pass);
@@ -459,7 +482,7 @@ __device__ __forceinline__ void gemv_rows_warm(uint32_t (&hx)[NB][NCH][8], int n
                     acc[b] = wave_sum(a);
                 }
                 const int nx = i + PF;
-                if (pass == 1 && i0 + PF < nmine) load_row<NCH>(buf[s], rowptr(nx < last ? nx : last), K8);
+                if (pass == 1 && i0 + PF < nmine) load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
                 if (pass == 1 && i < nmine) emit(i, acc);
             }
             if (pass == 0) break;   // the first PF rows are enough to warm the loop body
@@ -492,6 +515,7 @@ struct RouteLds {
     int32_t slot_e[kMaxSlots];         // expert of each slot, ascending ids
     int32_t slot_mask[kMaxSlots];      // tokens routed to the slot's expert
     int8_t slot_rank[kMaxSlots][kMaxBatch]; // rank of the expert in that token's top-k
+    int32_t tag;                       // which layer's routing this holds (-1: none)
 };
 
 // Order-preserving map of a float to an unsigned key (larger float, larger
@@ -601,9 +625,21 @@ __device__ __forceinline__ void compute_routing(const Params& p, const float* rl
             }
             base += __popcll(m);
         }
-        if (lane == 0) r->nslots = base;
+        if (lane == 0) {
+            r->nslots = base;
+            r->tag = (int32_t)(rl - p.rlogits);
+        }
     }
     __syncthreads();
+}
+
+// The routing of the layer whose router logits start at rl, computed here
+// unless this workgroup's LDS already holds it (an expert tile of the same
+// layer ran just before; LDS persists across the tasks of a workgroup, and
+// the tag is cleared when the kernel starts).
+template <int NE>
+__device__ __forceinline__ void routing_for(const Params& p, const float* rl, RouteLds* r) {
+    if (r->tag != (int32_t)(rl - p.rlogits)) compute_routing<NE>(p, rl, r);
 }
 
 }  // namespace mk

@@ -34,6 +34,7 @@ __global__ void __launch_bounds__(NT, 2) k_persistent(Params p, int general) {
     // the lowest unfinished tile can always run. One call site of run_task
     // keeps the tile code inlined once.
     __shared__ int s_pos;
+    if (threadIdx.x == 0) route_lds(lds, general)->tag = -1;   // no routing held yet
     const int beg = p.wg_off[blockIdx.x], end = p.wg_off[blockIdx.x + 1];
     int i = beg;
     int claim = -1;   // list position of the claim task being drained
@@ -82,6 +83,7 @@ __global__ void __launch_bounds__(NT, 2) k_perop(Params p, int general, int firs
     extern __shared__ __align__(16) char lds[];
     const int i = first + blockIdx.x;
     const Task t = p.tasks[i];
+    if (threadIdx.x == 0) route_lds(lds, general)->tag = -1;
     __syncthreads();
     run_task<S, NB>(t, p, lds, general, i);
 }

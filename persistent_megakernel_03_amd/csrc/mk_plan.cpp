@@ -61,9 +61,13 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
     while (rd > 1 && rd * std::max(1, S) > 64) rd >>= 1;
     if (rd < cfg.rows_down) return;
     const int n_down = ceil_div(s.H, rd);
-    const int per_slot = (n_wg - n_down) / std::max(1, S);
+    // gate/up tiles go to every workgroup when the down tiles fill at most
+    // half of them (one gate/up tile each, its rows in flight at once), else
+    // to the workgroups the down tiles leave
+    const bool spread = 2 * n_down <= n_wg;
+    const int per_slot = (spread ? n_wg : n_wg - n_down) / std::max(1, S);
     if (per_slot < 1) return;
-    int rg = std::max(cfg.rows_gateup, ceil_div(s.I, per_slot));
+    int rg = spread ? ceil_div(s.I, per_slot) : std::max(cfg.rows_gateup, ceil_div(s.I, per_slot));
     rg = ceil_div(rg, 4) * 4;
     *rows_gu = rg;
     *rows_down = rd;
@@ -95,14 +99,16 @@ int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions,
     return chunk;
 }
 
-int64_t max_tasks(const ModelShape& s, const TileConfig& cfg) {
+int64_t max_tasks(const ModelShape& s, const TileConfig& cfg, int n_wg) {
     const int G = s.Hq / s.Hkv;
     const int bv = std::min(s.max_batch, kMaxBatchValu);
     const int64_t attn = (int64_t)s.Hkv * s.max_chunks, comb = s.Hq;
     const int64_t per_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.rows_qkv) + bv * (attn + comb) +
                               ceil_div(s.H, cfg.rows_o) +
                               ceil_div(s.E, cfg.rows_router) +
-                              (int64_t)std::min(s.E, bv * s.K) * ceil_div(s.I, cfg.rows_gateup) +
+                              // spread gate/up rows give each slot at most n_wg / S tiles
+                              std::max<int64_t>((int64_t)std::min(s.E, bv * s.K) * ceil_div(s.I, cfg.rows_gateup),
+                                                n_wg) +
                               ceil_div(s.H, cfg.rows_down);
     int64_t n = 1 + (int64_t)s.L * per_layer + ceil_div(s.V, cfg.rows_lm);
     if (s.max_batch >= cfg.mm_min_batch) {
@@ -381,9 +387,11 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     //
     // The expert tiles stream most of a layer's bytes once the routing is
     // known, so they are spread evenly over compute units: with two
-    // workgroups per unit, workgroups w and w + n_wg/2 share one, so the
-    // gate/up tiles go to the upper half and the down tiles to the lower half
-    // (one of each per unit when both counts equal n_wg/2).
+    // workgroups per unit, workgroups w and w + n_wg/2 share one. The down
+    // tiles go to the lower half; the gate/up tiles to every workgroup when
+    // there is one per workgroup (each then holds all its rows in flight, and
+    // the down tile that follows on a lower workgroup reuses its routing),
+    // else to the upper half.
     std::vector<std::vector<Task>> lists(n_wg);
     P.wg_bytes.assign(n_wg, 0.0);
     typedef std::pair<double, int> Slot;
@@ -407,7 +415,7 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
         double end = 0.0;
         for (const Tile& t : tiles) {
             int hsel;
-            if (half > 0 && op == OP_GATEUP) hsel = 1;
+            if (half > 0 && op == OP_GATEUP && (int)tiles.size() < n_wg) hsel = 1;
             else if (half > 0 && op == OP_DOWN) hsel = 0;
             else if (heaps[0].empty()) hsel = 1;
             else if (heaps[1].empty()) hsel = 0;

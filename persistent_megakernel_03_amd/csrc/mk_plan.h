@@ -95,7 +95,7 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
 // tile of the step appears exactly once. Empty string = valid.
 std::string validate_plan(const ModelShape& s, const Plan& plan);
 
-// Upper bound on tasks for any batch <= max_batch.
-int64_t max_tasks(const ModelShape& s, const TileConfig& cfg);
+// Upper bound on tasks for any batch <= max_batch on at most n_wg workgroups.
+int64_t max_tasks(const ModelShape& s, const TileConfig& cfg, int n_wg);
 
 }  // namespace mk

@@ -694,7 +694,7 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
         split_x<NB, NCH>(h, hx);
     }
     if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
-    compute_routing<NE>(p, rlogits_at(p, l), rt);
+    routing_for<NE>(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
@@ -764,7 +764,7 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
     const int col = lane & 15, g4 = lane >> 4;
     RouteLds* rt = route_lds(cx.lds, cx.general);
     if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
-    compute_routing<NE>(p, rlogits_at(p, l), rt);
+    routing_for<NE>(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     const int I = p.I, K = p.K, B = p.B;
     const int K8 = I >> 3, nks = I >> 5;
@@ -967,7 +967,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
             case OP_COMBINE: return tile_combine<S::D>(t, cx);
             case OP_OPROJ: return tile_oproj<S::NCH_O, Pf<S::NCH_O, NB>::v, NB>(t, cx);
             case OP_ROUTER: return tile_router<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
-            case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 7 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
+            case OP_GATEUP: return tile_gateup<S::NCH_H, (NB == 1 && S::NCH_H <= 4 ? 6 : Pf<S::NCH_H, NB>::v), NB, S::NE>(t, cx);
             case OP_DOWN: return tile_down<8 * S::NCHP_I, NB, S::NE>(t, cx);
             case OP_LMHEAD: return tile_lmhead<S::NCH_H, Pf<S::NCH_H, NB>::v, NB>(t, cx);
             default: return bad_task(t, cx);

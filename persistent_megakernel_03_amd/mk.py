@@ -82,7 +82,8 @@ class mk_debug_ptrs(ctypes.Structure):
 
 class mk_plan_info(ctypes.Structure):
     _fields_ = [("n_wg", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("n_counters", ctypes.c_int32),
-                ("n_levels", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("n_levels", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32), ("cap_tasks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class mk_sched_config(ctypes.Structure):

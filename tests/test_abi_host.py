@@ -152,8 +152,15 @@ def test_plan_counts_for_the_30b_shape():
     assert ops[OP_COMBINE] == 48 * 32          # one merge per query head
     assert ops[OP_OPROJ] == 48 * 256
     assert ops[OP_ROUTER] == 48 * 16
-    assert ops[OP_GATEUP] == 48 * 8 * 32       # 8 slots x 768 rows / 24 (gate/up and down fit 512 workgroups)
+    assert ops[OP_GATEUP] == 48 * 8 * 64       # 8 slots x 768 rows / 12: one per workgroup
     assert ops[OP_DOWN] == 48 * 256            # 2048 rows / 8: 8 experts x 8 rows per tile held in registers
+    # every workgroup one gate/up tile per layer, the down tiles on the lower half
+    wg = np.repeat(np.arange(512), np.diff(offs))
+    for l in (0, 20, 47):
+        gu = wg[(tasks[:, 0] == OP_GATEUP) & (tasks[:, 1] == l)]
+        dn = wg[(tasks[:, 0] == OP_DOWN) & (tasks[:, 1] == l)]
+        assert sorted(gu.tolist()) == list(range(512))
+        assert sorted(dn.tolist()) == list(range(256))
     assert ops[OP_LMHEAD] == -(-151936 // 64)
     assert ops[OP_ROUTE] == 0 and ops[OP_MOESUM] == 0
     assert info.n_levels == 2 + LEVELS_PER_LAYER * 48
@@ -239,3 +246,22 @@ def test_plan_check_accepts_built_plans_and_finds_missing_dependencies(cfg_name,
         def down_on_router(t):
             t[8], t[9] = router_ctr(t[1]), int(targets[router_ctr(t[1])])
         planted(lambda t: t[0] == OP_DOWN and t[1] == l, down_on_router)
+
+
+@pytest.mark.parametrize("cfg_name", ["TINY", "A3B"])
+@pytest.mark.parametrize("max_batch", [1, 2, 3, 8])
+@pytest.mark.parametrize("mmb", [0, 1, 3])
+def test_every_plan_fits_the_task_capacity(cfg_name, max_batch, mmb):
+    # the task buffer a handle reserves is sized once, for any batch and
+    # context; the plans of every batch up to max_batch at the longest and
+    # shortest contexts fit it on every workgroup count
+    cfg = configs.dims_of(cfg_name)
+    max_pages = 520 if cfg_name == "A3B" else 40
+    d = mk.make_dims(cfg, max_batch, max_pages, max_pages * max_batch)
+    o = mk.make_options(mfma_min_batch=mmb)
+    longest = max_pages * cfg["page_size"] - 1
+    for n_wg in (7, 64, 256, 512):
+        for b in sorted({1, 2, max_batch} & set(range(1, max_batch + 1))):
+            for pos in ([0] * b, [longest] * b, [longest] + [0] * (b - 1)):
+                info, tasks, offs, targets = mk.mk_plan_build(d, o, n_wg, pos)
+                assert 0 < info.n_tasks <= info.cap_tasks, (n_wg, b, pos[0], info.n_tasks, info.cap_tasks)
