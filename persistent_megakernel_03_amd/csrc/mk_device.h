@@ -91,19 +91,6 @@ __device__ __forceinline__ float dot2bf(uint32_t w, uint32_t x, float acc) {
                                            false);
 }
 
-// acc + sum_j w_j x_j over one chunk of eight BF16 weights and split activations.
-__device__ __forceinline__ float dot8(const uint4 w, const uint32_t (&x)[8], float acc) {
-    acc = dot2bf(w.x, x[0], acc);
-    acc = dot2bf(w.y, x[1], acc);
-    acc = dot2bf(w.z, x[2], acc);
-    acc = dot2bf(w.w, x[3], acc);
-    acc = dot2bf(w.x, x[4], acc);
-    acc = dot2bf(w.y, x[5], acc);
-    acc = dot2bf(w.z, x[6], acc);
-    acc = dot2bf(w.w, x[7], acc);
-    return acc;
-}
-
 // DPP move within rows of 16 lanes (compile-time control word).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -122,6 +109,23 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_mov<0x141>(v);  // row_half_mirror
     v += dpp_mov<0x140>(v);  // row_mirror
     return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+// wave_sum of N values at once, each step issued for all of them before the
+// next step, so the DPP and lane-read latencies of one value hide behind the
+// others. Each value is summed in exactly wave_sum's order.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0xB1>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0x4E>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0x141>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0x140>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (readlane(v[i], 0) + readlane(v[i], 16)) + (readlane(v[i], 32) + readlane(v[i], 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -402,15 +406,44 @@ __device__ __forceinline__ void load_row_at(uint4 (&w)[NCH], const uint16_t* row
     for (int c = 0; c < NCH; ++c) w[c] = ld16s(r + off[c]);
 }
 
+// The wave-reduced dot products of the PF row-vectors in buf with the NB
+// split activation slices. A row's products accumulate in a fixed order
+// (chunks in order; within a chunk the four hi pairs, then the four lo
+// pairs), one chain per (row, token); the chains are interleaved
+// instruction by instruction, so consecutive dot-product instructions are
+// independent, and the PF * NB reductions run together (wave_sum_n).
+template <int NCH, int PF, int NB>
+__device__ __forceinline__ void dot_rows(const uint4 (&buf)[PF][NCH], const uint32_t (&hx)[NB][NCH][8],
+                                         float (&acc)[PF][NB]) {
+    float a[PF * NB];
+#pragma unroll
+    for (int i = 0; i < PF * NB; ++i) a[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int s = 0; s < PF; ++s) {
+                const uint4 w = buf[s][c];
+                const uint32_t wj = (j & 3) == 0 ? w.x : (j & 3) == 1 ? w.y : (j & 3) == 2 ? w.z : w.w;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) a[s * NB + b] = dot2bf(wj, hx[b][c][j], a[s * NB + b]);
+            }
+    wave_sum_n<PF * NB>(a);
+#pragma unroll
+    for (int s = 0; s < PF; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[s][b] = a[s * NB + b];
+}
+
 // Wave-level streaming matrix-vector product over split activation slices hx
 // (split_x) that the caller holds. The wave owns `nmine` row-vectors;
 // rowptr(i) returns the i-th. The first PF rows are loaded before ready()
 // runs (ready holds any dependency wait and may fill hx); then rows are
-// consumed in order while the row PF places ahead is in flight.
-// emit(i, acc) receives the wave-reduced dot products (every lane has them).
-// Loads are unconditional (slots past the last row re-read the last row,
-// which is in flight already), so the wait before each row covers that row
-// only and the stream stays PF rows deep.
+// consumed PF at a time (dot_rows), the next PF rows' loads issued before
+// the results are emitted. emit(i, acc) receives the wave-reduced dot
+// products (every lane has them). Loads are unconditional (slots past the
+// last row re-read the last row, which is in flight already).
 template <int NCH, int PF, int NB, class RowPtr, class Ready, class Emit>
 __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine, int K8, RowPtr rowptr, Ready ready,
                                           Emit emit) {
@@ -426,21 +459,18 @@ __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine,
     for (int s = 0; s < PF; ++s) load_row_at<NCH>(buf[s], rowptr(s < last ? s : last), off);
     ready();
     for (int i0 = 0; i0 < nmine; i0 += PF) {
+        float acc[PF][NB];
+        dot_rows<NCH, PF, NB>(buf, hx, acc);
+        if (i0 + PF < nmine) {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) {
-            const int i = i0 + s;
-            float acc[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                float a = 0.f;
-#pragma unroll
-                for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], hx[b][c], a);
-                acc[b] = wave_sum(a);
+            for (int s = 0; s < PF; ++s) {
+                const int nx = i0 + PF + s;
+                load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
             }
-            const int nx = i + PF;
-            if (i0 + PF < nmine) load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
-            if (i < nmine) emit(i, acc);
         }
+#pragma unroll
+        for (int s = 0; s < PF; ++s)
+            if (i0 + s < nmine) emit(i0 + s, acc[s]);
     }
 }
 
@@ -470,22 +500,19 @@ __device__ __forceinline__ void gemv_rows_warm(uint32_t (&hx)[NB][NCH][8], int n
     for (int pass = 0; pass < 2; ++pass) {
         ready(pass);
         for (int i0 = 0; i0 < nmine; i0 += PF) {
-#pragma unroll
-            for (int s = 0; s < PF; ++s) {
-                const int i = i0 + s;
-                float acc[NB];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    float a = 0.f;
-#pragma unroll
-                    for (int c = 0; c < NCH; ++c) a = dot8(buf[s][c], hx[b][c], a);
-                    acc[b] = wave_sum(a);
-                }
-                const int nx = i + PF;
-                if (pass == 1 && i0 + PF < nmine) load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
-                if (pass == 1 && i < nmine) emit(i, acc);
-            }
+            float acc[PF][NB];
+            dot_rows<NCH, PF, NB>(buf, hx, acc);
             if (pass == 0) break;   // the first PF rows are enough to warm the loop body
+            if (i0 + PF < nmine) {
+#pragma unroll
+                for (int s = 0; s < PF; ++s) {
+                    const int nx = i0 + PF + s;
+                    load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < PF; ++s)
+                if (i0 + s < nmine) emit(i0 + s, acc[s]);
         }
     }
 }

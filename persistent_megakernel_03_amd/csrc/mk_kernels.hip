@@ -190,7 +190,8 @@ hipError_t launch_perop_level(const KernelPair& k, const Params& p, int general,
 
 hipError_t launch_fill(uint32_t* dst, int64_t n, uint32_t v, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const int blocks = (int)(n + 255) / 256 < 1024 ? (int)((n + 255) / 256) : 1024;
+    const int64_t need = (n + 255) / 256;
+    const int blocks = need < 1024 ? (int)need : 1024;
     hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, stream, dst, n, v);
     return hipGetLastError();
 }
