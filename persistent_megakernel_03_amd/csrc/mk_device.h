@@ -436,14 +436,35 @@ __device__ __forceinline__ void dot_rows(const uint4 (&buf)[PF][NCH], const uint
         for (int b = 0; b < NB; ++b) acc[s][b] = a[s * NB + b];
 }
 
+// Row i0 + s of a group of PF rows is emitted by lane i0 + s, which picks
+// that row's values out of acc (every lane holds all of them), so a group
+// leaves in one store instruction per token instead of one per row.
+// emit(i, v, vx): row i (= the lane), its values v and those of row i ^ 1
+// (for tiles that pair adjacent rows).
+template <int PF, int NB, class Emit>
+__device__ __forceinline__ void lane_emit(int i0, int nmine, const float (&acc)[PF][NB], Emit& emit) {
+    const int lane = tid_() & 63;
+    const int s = lane - i0;
+    float v[NB], vx[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float x = acc[0][b];
+#pragma unroll
+        for (int k = 1; k < PF; ++k) x = s == k ? acc[k][b] : x;
+        v[b] = x;
+        vx[b] = __shfl_xor(x, 1);
+    }
+    if (s >= 0 && s < PF && lane < nmine) emit(lane, v, vx);
+}
+
 // Wave-level streaming matrix-vector product over split activation slices hx
 // (split_x) that the caller holds. The wave owns `nmine` row-vectors;
 // rowptr(i) returns the i-th. The first PF rows are loaded before ready()
 // runs (ready holds any dependency wait and may fill hx); then rows are
 // consumed PF at a time (dot_rows), the next PF rows' loads issued before
-// the results are emitted. emit(i, acc) receives the wave-reduced dot
-// products (every lane has them). Loads are unconditional (slots past the
-// last row re-read the last row, which is in flight already).
+// the results are emitted (lane_emit: row i by lane i, so a wave holds at
+// most 64 rows). Loads are unconditional (slots past the last row re-read
+// the last row, which is in flight already).
 template <int NCH, int PF, int NB, class RowPtr, class Ready, class Emit>
 __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine, int K8, RowPtr rowptr, Ready ready,
                                           Emit emit) {
@@ -468,9 +489,7 @@ __device__ __forceinline__ void gemv_rows(uint32_t (&hx)[NB][NCH][8], int nmine,
                 load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
             }
         }
-#pragma unroll
-        for (int s = 0; s < PF; ++s)
-            if (i0 + s < nmine) emit(i0 + s, acc[s]);
+        lane_emit<PF, NB>(i0, nmine, acc, emit);
     }
 }
 
@@ -510,9 +529,7 @@ __device__ __forceinline__ void gemv_rows_warm(uint32_t (&hx)[NB][NCH][8], int n
                     load_row_at<NCH>(buf[s], rowptr(nx < last ? nx : last), off);
                 }
             }
-#pragma unroll
-            for (int s = 0; s < PF; ++s)
-                if (i0 + s < nmine) emit(i0 + s, acc[s]);
+            lane_emit<PF, NB>(i0, nmine, acc, emit);
         }
     }
 }

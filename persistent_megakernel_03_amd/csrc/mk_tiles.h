@@ -49,7 +49,7 @@ template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, g = t.a0, v0 = t.a1, nrows = t.a2 - t.a1;
-    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int wave = tid_() >> 6;
     const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     const uint16_t* W = wptr(p, l, W_QKV);
     const int H = p.H, D = p.D, GD = p.G * p.D;
@@ -74,13 +74,11 @@ __device__ __forceinline__ bool tile_qkv(const Task& t, TileCtx& cx) {
             split_x<NB, NCH>(h, hx);
             if (pass) mark(cx, 0);
         },
-        [&](int i, const float(&acc)[NB]) {
-            if (lane == 0) {
-                const int row = phys(v0 + wave + i * NWAVES);
+        [&](int i, const float(&acc)[NB], const float(&)[NB]) {
+            const int row = phys(v0 + wave + i * NWAVES);
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    if (b < p.B) st_dev(qkv_at(p, l) + (int64_t)b * p.QKVD + row, acc[b]);
-            }
+            for (int b = 0; b < NB; ++b)
+                if (b < p.B) st_dev(qkv_at(p, l) + (int64_t)b * p.QKVD + row, acc[b]);
         });
     if (!ok) return false;
     mark(cx, 1);
@@ -619,13 +617,12 @@ __device__ __forceinline__ bool tile_oproj(const Task& t, TileCtx& cx) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, attout_at(p, l), K, p.B, K, nullptr, 0.f, 0.f);
         },
-        [&](int i, const float(&acc)[NB]) {
-            if (lane == i) {
-                const int row = r0 + wave + i * NWAVES;
+        [&](int i, const float(&acc)[NB], const float(&)[NB]) {
+            // lane i holds row i's residual
+            const int row = r0 + wave + i * NWAVES;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    if (b < p.B) st_dev(xmid + (int64_t)b * p.H + row, xres[b] + acc[b]);
-            }
+            for (int b = 0; b < NB; ++b)
+                if (b < p.B) st_dev(xmid + (int64_t)b * p.H + row, xres[b] + acc[b]);
         });
     if (!ok) return false;
     mark(cx, 1);
@@ -639,7 +636,7 @@ template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0;
-    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int wave = tid_() >> 6;
     const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     const int H = p.H;
     const uint16_t* W = wptr(p, l, W_ROUTER);
@@ -653,8 +650,8 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps, p.inv_h);
         },
-        [&](int i, const float(&acc)[NB]) {
-            if (lane == 0) {
+        [&](int i, const float(&acc)[NB], const float(&)[NB]) {
+            {
                 const int row = r0 + wave + i * NWAVES;
                 const float bv = bias != nullptr ? ldg(bias + row) : 0.f;
 #pragma unroll
@@ -681,7 +678,7 @@ template <int NCH, int PF, int NB, int NE>
 __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, slot = t.a0, r0 = t.a1, nrows = t.a2 - t.a1;
-    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int wave = tid_() >> 6;
     const int H = p.H;
     RouteLds* rt = route_lds(cx.lds, cx.general);
     uint32_t hx[NB][NCH][8];
@@ -712,16 +709,13 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const uint16_t* Wg = wptr(p, l, W_GATE) + (int64_t)e * p.I * H;
     const uint16_t* Wu = wptr(p, l, W_UP) + (int64_t)e * p.I * H;
     const int npair = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
-    float gate[NB];
     gemv_rows<NCH, PF, NB>(
         hx, 2 * npair, H >> 3,
         [&](int i) { return ((i & 1) ? Wu : Wg) + (int64_t)(r0 + wave + (i >> 1) * NWAVES) * H; },
         [&]() { mark(cx, 1); },
-        [&](int i, const float(&acc)[NB]) {
-            if ((i & 1) == 0) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) gate[b] = acc[b];
-            } else if (lane == 0) {
+        [&](int i, const float(&acc)[NB], const float(&gate)[NB]) {
+            // row-vector i odd: up row, its gate row's products from lane i - 1
+            if (i & 1) {
                 const int row = r0 + wave + (i >> 1) * NWAVES;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -884,7 +878,7 @@ template <int NCH, int PF, int NB>
 __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int r0 = t.a0, nrows = t.a1 - t.a0;
-    const int wave = tid_() >> 6, lane = tid_() & 63;
+    const int wave = tid_() >> 6;
     const int nmine = nrows > wave ? (nrows - wave + NWAVES - 1) / NWAVES : 0;
     const int H = p.H;
     bool ok = true;
@@ -896,13 +890,11 @@ __device__ __forceinline__ bool tile_lmhead(const Task& t, TileCtx& cx) {
             ok = block_wait(p, t.ctr, t.target, cx.t_wait);
             load_x<NCH, NB>(h, x_at(p, 2 * p.L), H, p.B, H, gn, p.eps, p.inv_h);
         },
-        [&](int i, const float(&acc)[NB]) {
-            if (lane == 0) {
-                const int row = r0 + wave + i * NWAVES;
+        [&](int i, const float(&acc)[NB], const float(&)[NB]) {
+            const int row = r0 + wave + i * NWAVES;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    if (b < p.B) p.logits[(int64_t)b * p.V + row] = acc[b];
-            }
+            for (int b = 0; b < NB; ++b)
+                if (b < p.B) p.logits[(int64_t)b * p.V + row] = acc[b];
         });
     if (!ok) return false;
     mark(cx, 1);
