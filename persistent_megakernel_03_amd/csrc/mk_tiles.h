@@ -826,16 +826,25 @@ __device__ __forceinline__ bool tile_down(const Task& t, TileCtx& cx) {
             // B operands eight k-steps at a time (their LDS reads in flight
             // together), two accumulators (independent matrix-core chains)
             f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            auto ksteps = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-            for (int k0 = 0; k0 < KS; k0 += 8) {
-                uint4 bv[8];
+                for (int k0 = 0; k0 < KS; k0 += 8) {
+                    uint4 bv[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    bv[j] = (k0 + j < nks && rank >= 0) ? bsrc[8 * (k0 + j)] : make_uint4(0u, 0u, 0u, 0u);
+                    for (int j = 0; j < 8; ++j)
+                        bv[j] = ((FULL || k0 + j < nks) && rank >= 0) ? bsrc[8 * (k0 + j)]
+                                                                      : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (k0 + j < KS && k0 + j < nks) acc2[j & 1] = mfma16x16x32(wb[k0 + j], bv[j], acc2[j & 1]);
-            }
+                    for (int j = 0; j < 8; ++j)
+                        if (k0 + j < KS && (FULL || k0 + j < nks))
+                            acc2[j & 1] = mfma16x16x32(wb[k0 + j], bv[j], acc2[j & 1]);
+                }
+            };
+            // an expert width of exactly the compiled k-steps (the shape the
+            // kernel is built for) runs without a bound check per step
+            if (nks == KS) ksteps(std::true_type{});
+            else ksteps(std::false_type{});
             f32x4_t acc = acc2[0] + acc2[1];
             // hi + lo (adjacent columns); lane (col, g4) holds A-rows 4 g4 + q
 #pragma unroll
