@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--prefill", type=str, default="",
                     help="prompt lengths to ingest (multi-token steps of up to 64 rows), e.g. 512,2048")
     ap.add_argument("--prefill-prefix", type=int, default=0, help="tokens already cached before each prompt")
+    ap.add_argument("--calib-lmhead", action="store_true",
+                    help="also run one per-op step, whose LM-head level is a single dispatch reading exactly the "
+                         "V x H BF16 LM-head matrix through the kernels' own weight loads (HBM counter calibration)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -210,6 +213,13 @@ def main():
     achieved = bytes_step / (kms * 1e-3) / 1e9
     log(f"megakernel: {tok_s:.1f} tok/s, {ms_per_step:.3f} ms/step, kernel {kms:.3f} ms, "
         f"{achieved:.0f} GB/s ({100 * achieved / PEAK_GBS:.1f}% of 8 TB/s)")
+
+    if args.calib_lmhead:
+        k2, v2 = k_pool.clone(), v_pool.clone()
+        run(mk.MK_MODE_PEROP, 1, 0, k2, v2)
+        del k2, v2
+        log(f"calibration: two per-op steps run; each LM-head level dispatch reads "
+            f"{cfg['vocab'] * cfg['hidden'] * 2} bytes of weights")
 
     perop = None
     if not args.no_perop:

@@ -149,18 +149,22 @@ typedef struct mk_handle mk_handle;
  *   K: [L][n_pages][Hkv][P][D]  BF16 (token-major inside a page)
  *   V: [L][n_pages][Hkv][D][P]  BF16 (dimension-major inside a page)
  * Token t of a sequence with block table bt lives in page bt[t / P], slot
- * t % P (first page, opening section: paged attention). Returns the bytes of
- * one pool (K and V are the same size).
+ * t % P: the paged KV cache of "Cohere Publishes One-Kernel Server for North Mini Code, Claims 1.58x vLLM Speedup",
+ * opening section. Returns the bytes of one pool (K and V are the same size).
  */
 size_t mk_kv_pool_bytes(const mk_dims* dims);
 
-/* Bytes of device workspace mk_create needs for these dims and options
- * (activations, attention partials, counters, task lists). 0 on bad input. */
+/* Bytes of device workspace mk_create needs for these dims and options: the
+ * counters in global memory and the task lists of the resident program (same
+ * page, section "One resident program, many small tasks"), the exchanged
+ * activations and attention partials. 0 on bad input. */
 size_t mk_workspace_bytes(const mk_dims* dims, const mk_options* opts);
 
 /*
- * Create a handle on `device` (HIP ordinal). Validates the dims, queries the
- * device, carves `workspace` (device memory of at least mk_workspace_bytes,
+ * Create a handle on `device` (HIP ordinal): the state of the one resident
+ * program that runs every step ("Cohere Publishes One-Kernel Server ...",
+ * section "One resident program, many small tasks"). Validates the dims,
+ * queries the device, carves `workspace` (device memory of at least mk_workspace_bytes,
  * 256-byte aligned, owned by the caller) and clears its counters with a
  * synchronous launch on the null stream. Returns MK_ERR_UNSUPPORTED for dims
  * outside the supported set and MK_ERR_CAPACITY for a short workspace.
@@ -170,7 +174,11 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* weights, void* k_pool
                     mk_handle** out);
 
 /*
- * Enqueue one decode step for `batch` sequences on `stream` and return.
+ * Enqueue one decode step for `batch` sequences on `stream` and return: the
+ * whole step, embedding to logits, as one launch of the resident program
+ * ("Cohere Publishes One-Kernel Server ...", section "One resident program,
+ * many small tasks"; "Cohere fuses an entire decode step into one GPU
+ * program", paragraphs 1-2), or as the per-op chain (mk_set_mode).
  *   seq_ids      host [B]: distinct ids (tracing only)
  *   positions    host [B]: tokens already cached; the new token's KV goes to
  *                that position and attention covers positions 0..positions[b]
@@ -233,16 +241,23 @@ mk_status mk_decode_step_noalloc(mk_handle* h, int32_t batch, const int32_t* seq
                                  const int32_t* positions, const int32_t* block_tables,
                                  const int32_t* tokens, float* logits, void* stream);
 
-/* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PEROP for later steps. */
+/* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PEROP for later steps. The
+ * per-op mode is the conventional chain of one kernel per operation that the
+ * pages measure against ("Cohere Publishes One-Kernel Server ...", section
+ * "The delay is between operations"), running the same tiles. */
 mk_status mk_set_mode(mk_handle* h, int32_t mode);
 
 /* Synchronize `stream`, then report and clear the device error word:
- * MK_OK, MK_ERR_TIMEOUT or MK_ERR_DEVICE. */
+ * MK_OK, MK_ERR_TIMEOUT or MK_ERR_DEVICE. Not an operation of the pages (they
+ * describe no error handling): the boundary's report of a watchdog timeout on
+ * a counter wait, a token out of range or a task the kernel cannot run. */
 mk_status mk_sync_check(mk_handle* h, void* stream);
 
 /*
  * Device addresses of per-step results kept in the workspace, for checking
- * and tracing. Valid until mk_destroy; contents refer to the last step.
+ * and tracing (not an operation of the pages: parity and tracing access to
+ * the exchange buffers the resident program's tiles pass between them).
+ * Valid until mk_destroy; contents refer to the last step.
  * Slices are padded: pad64(n) is n rounded up to a multiple of 64 floats.
  *   x_layers: fp32 [2L + 1] slices of stride pad64(max_batch * H), each
  *             [max_batch][H]: the residual stream; slice 0 is the embedding,
@@ -284,7 +299,10 @@ typedef struct mk_plan_info {
 
 /*
  * Build a plan on the host without a device or handle (CPU testing of the
- * task-graph builder). `n_wg` workgroups; positions host [batch].
+ * task-graph builder): the per-workgroup task lists and counter targets the
+ * host prepares for the resident program ("Cohere Publishes One-Kernel Server
+ * for North Mini Code, Claims 1.58x vLLM Speedup", section "One resident
+ * program, many small tasks"). `n_wg` workgroups; positions host [batch].
  * `tasks` (12 * n_tasks int32), `wg_offsets` (n_wg + 1 int32) and
  * `counter_targets` (n_counters int32: the value each counter reaches when
  * the step completes) may be NULL to query sizes; `cap_tasks` bounds tasks.
@@ -314,7 +332,10 @@ mk_status mk_plan_check(const mk_dims* dims, const mk_options* opts, int32_t n_w
                         const int32_t* wg_offsets);
 
 /*
- * Per-task timestamps of the last step (when mk_options.trace was set): one
+ * Per-task timestamps of the last step (when mk_options.trace was set), the
+ * measure of the idle time between dependent tiles that the scheduling change
+ * targets ("Cohere Publishes One-Kernel Server ...", section "What the
+ * scheduling change is meant to avoid"): one
  * record of 8 uint64 per task, {task index | workgroup << 32, t_start,
  * t_after_wait, four phase stamps inside the tile (0 if unused), t_end}, in
  * the device's constant wall clock (100 MHz ticks).
@@ -322,7 +343,9 @@ mk_status mk_plan_check(const mk_dims* dims, const mk_options* opts, int32_t n_w
 mk_status mk_get_trace(mk_handle* h, void* host_buf, size_t bytes, size_t* written);
 
 /*
- * Task table of the plan the last step ran: the records that the task
+ * Task table of the plan the last step ran (the host-prepared task list of
+ * "Cohere Publishes One-Kernel Server ...", section "One resident program,
+ * many small tasks"): the records that the task
  * indices of mk_get_trace refer to, 12 int32 each as for mk_plan_build, in
  * the order the last step's kernels indexed them (grouped per workgroup in
  * the megakernel mode, per dependency level in the per-op mode). Host work
@@ -333,15 +356,22 @@ mk_status mk_get_trace(mk_handle* h, void* host_buf, size_t bytes, size_t* writt
 mk_status mk_get_plan(mk_handle* h, int32_t* tasks, int64_t cap_tasks, int64_t* n_tasks);
 
 /*
- * Device time of the last step's kernels in milliseconds, from HIP events
+ * Device time of the last step's kernels in milliseconds (the step time
+ * behind the pages' speed-of-light accounting, "Inside the Megakernel
+ * Serving Engine for North Mini Code", paragraph 2), from HIP events
  * recorded on the step's stream immediately before the first and after the
  * last kernel of the step (per-step staging copies excluded). Needs
  * mk_options.time_kernels; waits for the step to finish.
  */
 mk_status mk_kernel_time(mk_handle* h, float* ms);
 
+/* Release the handle: its pinned staging, events and host plan. The caller's
+ * device buffers are untouched. Not an operation of the pages (handle
+ * lifetime). NULL is a no-op. */
 void mk_destroy(mk_handle* h);
 
+/* Thread-local message of the calling thread's last failing call (never
+ * NULL). Not an operation of the pages (the boundary's error text). */
 const char* mk_last_error(void);
 
 #ifdef __cplusplus
