@@ -592,7 +592,7 @@ def perop_graph(cfg, weights, k_pool, v_pool, block_tables, tok0, ctx, B, pages_
 
 
 OP_NAMES = ["embed", "qkv", "attention", "merge", "o_proj", "router", "routing", "gate_up", "down", "expert_sum",
-            "lm_head"]
+            "lm_head", "claim", "final_norm"]
 OP_CLAIM = 11
 
 
@@ -669,7 +669,7 @@ def schedule_from_trace(tr, tasks, L):
     for i, lv in enumerate(order[1:], 1):
         m = level == lv
         o, l = int(op[m][0]), int(layer[m][0])
-        if L // 6 <= l < L - L // 6 and o not in (0, 10):
+        if L // 6 <= l < L - L // 6 and o not in (0, 10, 12):
             per.setdefault(OP_NAMES[o], []).append(ends[lv] - ends[order[i - 1]])
     return {"traced_step_us": round(span, 1), "wait_stall_frac": round(wait, 4), "busy_wg_frac": round(busy, 4),
             "busy_cu_frac": round(float(busy_cu) / (n_cu * span), 4), "n_wg": n_wg,

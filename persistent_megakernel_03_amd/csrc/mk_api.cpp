@@ -155,7 +155,7 @@ Layout make_layout(const mk_dims& d, const mk_options& o, int max_wg) {
     const bool mm = d.max_batch >= mm_min_of(o);
     L.rtab = take(mm ? Ln * rtab_words(d.n_experts, d.top_k, d.max_batch) * 4 : 0);
     L.ybuf = take(mm ? Ln * pad64(B * d.top_k * H) * 4 : 0);
-    L.h2s = take(mm ? Ln * pad64(B * H) * 4 : 0);
+    L.h2s = take(mm ? (Ln + 1) * pad64(B * H) * 4 : 0);   // + the final norm's output
     L.wtab = take((size_t)d.n_layers * W_NKINDS * 8);
     // per-step arrays: positions, chunk counts, rotary table, block tables
     L.step_bytes = align256((size_t)B * 4) * 2 + align256((size_t)B * d.head_dim * 4) +

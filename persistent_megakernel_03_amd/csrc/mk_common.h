@@ -32,11 +32,12 @@ enum Op : int32_t {
     OP_GATEUP = 7,  // expert gate/up rows + SwiGLU (batches of 1-2: also the top-k)
     OP_DOWN = 8,    // expert down rows (batches of 1-2: + weighted combine + residual)
     OP_MOESUM = 9,  // batches of 3+: weighted sum of the experts' outputs + residual
-    OP_LMHEAD = 10, // fused final RMSNorm + LM-head rows
+    OP_LMHEAD = 10, // LM-head rows (batches of 1-2: with the final RMSNorm fused)
     OP_CLAIM = 11,  // not a tile: run tiles of one level from a shared pool
                     // (a0: first pool task, a1: pool size, a2: the level,
                     // whose claim counter hands out pool positions)
-    OP_COUNT = 12
+    OP_FNORM = 12,  // batches of 3+: the final RMSNorm of tokens a0..a1, stored split for the LM head
+    OP_COUNT = 13
 };
 
 // QKV, ATTN, COMBINE, OPROJ, ROUTER, ROUTE, GATEUP, DOWN, MOESUM; ROUTE and
@@ -55,10 +56,12 @@ constexpr int kMaxBatchMM = 64;
 constexpr int kMmLdsBytes = (4 * 16 * 64 + 4 * 64 + 128) * 4;
 constexpr int kRouteLdsBytes = 2 * 256 * 4 + kMaxBatchMM * 256 + 16;
 
-// Dependency level of an op in layer l (0 = embedding, last = LM head).
+// Dependency level of an op in layer l (0 = embedding; after the layers the
+// final norm, empty at batches of 1-2, then the LM head).
 inline int op_level(int op, int layer, int n_layers) {
     if (op == OP_EMBED) return 0;
-    if (op == OP_LMHEAD) return 1 + kLevelsPerLayer * n_layers;
+    if (op == OP_FNORM) return 1 + kLevelsPerLayer * n_layers;
+    if (op == OP_LMHEAD) return 2 + kLevelsPerLayer * n_layers;
     return 1 + kLevelsPerLayer * layer + (op - OP_QKV);
 }
 
@@ -103,10 +106,11 @@ struct CounterLayout {
     MK_HD int gateup(int l) const { return combine(l) + 4; }
     MK_HD int down(int l) const { return combine(l) + 5; }
     MK_HD int moesum(int l) const { return combine(l) + 6; }
-    MK_HD int n_main() const { return 1 + n_layers * per_layer(); }
+    MK_HD int fnorm() const { return 1 + n_layers * per_layer(); }
+    MK_HD int n_main() const { return 2 + n_layers * per_layer(); }
     // one claim counter per dependency level (a single line each), after the
     // split counters
-    MK_HD int n_levels() const { return 2 + kLevelsPerLayer * n_layers; }
+    MK_HD int n_levels() const { return 3 + kLevelsPerLayer * n_layers; }
     MK_HD int64_t claim_word(int level) const { return ((int64_t)n_main() * kCtrSub + level) * kCtrStride; }
     MK_HD int64_t bank_words() const {
         return (((int64_t)n_main() * kCtrSub + n_levels()) * kCtrStride + 63) & ~(int64_t)63;
@@ -162,7 +166,8 @@ struct Params {
     float* act;          // [L][max_batch*K][I] (split form for batches of 3+)
     int32_t* rtab;       // [L][rtab_words]: batches of 3+, routing table (see rtab_words)
     float* ybuf;         // [L][max_batch*K][H]: batches of 3+, each expert's output per (token, rank)
-    float* h2s;          // [L][max_batch][H]: batches of 3+, the experts' normalised input, split
+    float* h2s;          // [L+1][max_batch][H]: batches of 3+, the experts' normalised input, split;
+                         // slice L: the final norm's output (the LM head's input), split
     uint32_t* ctr;       // this step's counter bank
     uint32_t* ctr_other; // the bank the next step uses (cleared by this step)
     int64_t bank_words;

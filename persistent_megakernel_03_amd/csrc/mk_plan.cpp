@@ -120,7 +120,7 @@ int64_t max_tasks(const ModelShape& s, const TileConfig& cfg, int n_wg) {
                                  ceil_div(s.E, cfg.mm_rows_router) + 1 + (int64_t)S * ceil_div(s.I, 8) +
                                  (int64_t)ceil_div(s.H, 16) * S + ceil_div(s.H, cfg.mm_rows_sum);
         const int64_t m = ceil_div(s.max_batch, cfg.mm_embed_tokens) + (int64_t)s.L * mm_layer +
-                          ceil_div(s.V, cfg.mm_rows_lm);
+                          s.max_batch + ceil_div(s.V, cfg.mm_rows_lm);
         // each claim task stands for at least one tile of its level
         n = std::max(n, 2 * m);
     }
@@ -139,7 +139,7 @@ std::string build_plan(const ModelShape& s, const TileConfig& cfg, int n_wg, int
     P.mm = B >= cfg.mm_min_batch;
     if (!P.mm && B > kMaxBatchValu) return "batch above the one- and two-token schedule";
     P.chunk = choose_chunk(s, n_wg, B, positions, cfg.chunk);
-    P.n_levels = 2 + kLevelsPerLayer * s.L;
+    P.n_levels = 3 + kLevelsPerLayer * s.L;
     P.targets.assign(cl.n_main(), 0);
     P.n_chunks.resize(B);
     for (int b = 0; b < B; ++b) {
@@ -357,9 +357,16 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
         }
         P.targets[cl.moesum(l)] = ns;
     }
+    // the final RMSNorm once per token, stored split: the LM-head tiles then
+    // stream their rows against a ready operand instead of each normalising
+    // every token's residual again
+    for (int b = 0; b < B; ++b)
+        add(make_task(OP_FNORM, 0, b, b + 1, 0, 0, -1, 0, cl.moesum(s.L - 1), ns, cl.fnorm(), P.n_levels - 2),
+            8.0 * s.H, kStatic);
+    P.targets[cl.fnorm()] = B;
     for (int i = 0; i < nl; ++i) {
         const int r0 = i * cfg.mm_rows_lm, r1 = std::min(s.V, r0 + cfg.mm_rows_lm);
-        add(make_task(OP_LMHEAD, 0, r0, r1, 0, 0, -1, 0, cl.moesum(s.L - 1), ns, -1, P.n_levels - 1),
+        add(make_task(OP_LMHEAD, 0, r0, r1, 0, 0, -1, 0, cl.fnorm(), B, -1, P.n_levels - 1),
             2.0 * (r1 - r0) * s.H, kStatic);
     }
 }
@@ -603,7 +610,8 @@ static std::string check_reads(const ModelShape& s, const Plan& P, const std::ve
                 if (e.empty()) e = need(t, d, OP_ROUTE, l, -1);
                 if (e.empty()) e = need_rows(t, d, OP_OPROJ, l, t.a0, t.a1);
                 break;
-            case OP_LMHEAD: e = need(t, d, x_op, s.L - 1, -1); break;
+            case OP_FNORM: e = need(t, d, x_op, s.L - 1, -1); break;
+            case OP_LMHEAD: e = P.mm ? need(t, d, OP_FNORM, 0, -1) : need(t, d, x_op, s.L - 1, -1); break;
             default: break;
         }
         if (!e.empty()) return e;
@@ -684,6 +692,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
             case OP_ROUTER:
             case OP_ROUTE:
             case OP_MOESUM:
+            case OP_FNORM:
             case OP_LMHEAD: ranges[std::make_tuple(t.op, t.layer, 0, 0)].push_back({t.a0, t.a1}); break;
             // one-/two-token down tiles carry their row count in a2 (the same for
             // every tile); matrix-core down tiles their slot group
@@ -710,7 +719,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         const int op = std::get<0>(kv.first);
         int want = 0;
         switch (op) {
-            case OP_EMBED: want = P.B; break;
+            case OP_EMBED: case OP_FNORM: want = P.B; break;
             case OP_ROUTE: want = 1; break;
             case OP_QKV: want = (G + 2) * s.D; break;
             case OP_ATTN: want = P.n_chunks[std::get<2>(kv.first)]; break;

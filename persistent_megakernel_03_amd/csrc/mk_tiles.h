@@ -957,6 +957,7 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
             case OP_GATEUP: return tile_gateup_mm(t, cx);
             case OP_DOWN: return tile_down_mm(t, cx);
             case OP_MOESUM: return tile_moesum(t, cx);
+            case OP_FNORM: return tile_fnorm(t, cx);
             case OP_LMHEAD: return tile_lmhead_mm(t, cx);
             default: return bad_task(t, cx);
         }

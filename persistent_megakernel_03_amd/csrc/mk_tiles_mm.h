@@ -879,33 +879,88 @@ __device__ __forceinline__ bool tile_moesum(const Task& t, TileCtx& cx) {
     return true;
 }
 
+// ------------------------------------------------------------- final norm
+
+// Tokens a0..a1: the final RMSNorm of the last layer's output,
+// (x / sqrt(mean(x^2) + eps)) * g, stored split (st_split8) into slice L of
+// the experts'-input buffer, where every LM-head tile reads it as its
+// matrix-core operand. Each thread takes 8 consecutive elements per round
+// (the supported hidden sizes fit in kRounds rounds).
+__device__ __forceinline__ bool tile_fnorm(const Task& t, TileCtx& cx) {
+    const Params& p = cx.p;
+    constexpr int kRounds = 4;
+    const int H8 = p.H >> 3, tid = tid_(), lane = tid & 63, wave = tid >> 6;
+    float* sred = reinterpret_cast<float*>(cx.lds);
+    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
+    const float* xf = x_at(p, 2 * p.L);
+    float* hf = h2s_at(p, p.L);
+    for (int b = t.a0; b < t.a1; ++b) {
+        float v[kRounds][8];
+        float ss = 0.f;
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int e8 = tid + r * NT;
+            if (e8 < H8) {
+                const float* src = xf + (int64_t)b * p.H + 8 * e8;
+                const float4 u = ldf4(src), w = ldf4(src + 4);
+                v[r][0] = u.x; v[r][1] = u.y; v[r][2] = u.z; v[r][3] = u.w;
+                v[r][4] = w.x; v[r][5] = w.y; v[r][6] = w.z; v[r][7] = w.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[r][j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = fmaf(v[r][j], v[r][j], ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) sred[wave] = ss;
+        __syncthreads();
+        const float inv = 1.0f / sqrtf((((sred[0] + sred[1]) + sred[2]) + sred[3]) * p.inv_h + p.eps);
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int e8 = tid + r * NT;
+            if (e8 < H8) {
+                const uint4 gw = ld16(p.final_norm + 8 * e8);
+                const float gv[8] = {bflo(gw.x), bfhi(gw.x), bflo(gw.y), bfhi(gw.y),
+                                     bflo(gw.z), bfhi(gw.z), bflo(gw.w), bfhi(gw.w)};
+                float o[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = (v[r][j] * inv) * gv[j];
+                st_split8(hf + (int64_t)b * p.H + 8 * e8, o);
+            }
+        }
+        __syncthreads();   // sred is written again for the next token
+    }
+    block_signal(p, t.signal);
+    return true;
+}
+
 // ---------------------------------------------------------------- LM head
 
-// Rows a0..a1 (<= 64) of the LM head: logits = W_lm (g o x) / rms(x).
+// Rows a0..a1 (<= 64) of the LM head: logits = W_lm h over the normalised
+// final residual h that the final-norm tiles stored split.
 __device__ __forceinline__ bool tile_lmhead_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int r0 = t.a0, nrows = t.a1 - t.a0, B = p.B, H = p.H;
     float* sPart = reinterpret_cast<float*>(cx.lds);
-    float* sSS = sPart + kMmPartFloats;
     bool ok = true;
-    const float* xf = x_at(p, 2 * p.L);
+    const float* hf = h2s_at(p, p.L);   // normalised final residual, split (tile_fnorm)
     const int na = row_blocks(nrows);
-    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
-    with_ncb(ncb, [&](auto n) {
-        mm_block<decltype(n)::v, true>(
+    const int nc = nc8_tokens(B);
+    with_nc8(B, [&](auto n) {
+        mm_block_s<decltype(n)::v>(
             na, H,
             [&](int blk, int r) {
                 const int rr = 16 * blk + r;
                 return p.lm_head + (int64_t)(r0 + (rr < nrows ? rr : nrows - 1)) * H;
             },
-            [&](int c) -> const float* { return c < B ? xf + (int64_t)c * H : nullptr; }, p.final_norm,
-            [&]() { ok = block_wait(p, t.ctr, t.target, cx.t_wait); }, sPart, sSS);
+            [&](int c) -> const float* { return c < B ? hf + (int64_t)c * H : nullptr; },
+            [&]() { ok = block_wait(p, t.ctr, t.target, cx.t_wait); }, sPart);
     });
     if (!ok) return false;
     for (int i = tid_(); i < nrows * B; i += NT) {
         const int r = i / B, b = i - r * B;
-        p.logits[(int64_t)b * p.V + r0 + r] =
-            mm_c(sPart, nc, na, r >> 4, r & 15, b) * rms_scale(p, mm_ss(sSS, nc, na, b));
+        p.logits[(int64_t)b * p.V + r0 + r] = mm_c(sPart, nc, na, r >> 4, r & 15, b);
     }
     mark(cx, 1);
     block_signal(p, t.signal);

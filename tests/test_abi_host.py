@@ -14,7 +14,7 @@ from persistent_megakernel_03_amd import configs, mk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 (OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_ROUTER, OP_ROUTE, OP_GATEUP, OP_DOWN, OP_MOESUM,
- OP_LMHEAD, OP_CLAIM) = range(12)
+ OP_LMHEAD, OP_CLAIM, OP_FNORM) = range(13)
 LEVELS_PER_LAYER = 9
 
 
@@ -144,7 +144,7 @@ def test_plan_is_valid_and_deadlock_free(cfg_name, batch, positions, n_wg, share
 def test_plan_counts_for_the_30b_shape():
     d = mk.make_dims(configs.A3B, 1, 520, 520)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192])
-    ops = np.bincount(tasks[:, 0], minlength=12)
+    ops = np.bincount(tasks[:, 0], minlength=13)
     assert ops[OP_CLAIM] == 0                  # one- and two-token plans are fully static
     assert ops[OP_EMBED] == 1
     assert ops[OP_QKV] == 48 * 4 * 54          # 1280 rows per KV group, 24 per tile
@@ -162,8 +162,8 @@ def test_plan_counts_for_the_30b_shape():
         assert sorted(gu.tolist()) == list(range(512))
         assert sorted(dn.tolist()) == list(range(256))
     assert ops[OP_LMHEAD] == -(-151936 // 64)
-    assert ops[OP_ROUTE] == 0 and ops[OP_MOESUM] == 0
-    assert info.n_levels == 2 + LEVELS_PER_LAYER * 48
+    assert ops[OP_ROUTE] == 0 and ops[OP_MOESUM] == 0 and ops[OP_FNORM] == 0
+    assert info.n_levels == 3 + LEVELS_PER_LAYER * 48   # the final-norm level is empty here
 
 
 @pytest.mark.parametrize("batch", [4, 16, 64])
@@ -172,7 +172,7 @@ def test_plan_counts_for_30b_batches(batch):
     # routing tile; gate/up tiles are (8 rows, one of 8 slot groups) pairs
     d = mk.make_dims(configs.A3B, batch, 520, 520 * batch)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192] * batch)
-    ops = np.bincount(tasks[:, 0], minlength=12)
+    ops = np.bincount(tasks[:, 0], minlength=13)
     assert ops[OP_EMBED] == -(-batch // 4)
     assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
     assert ops[OP_COMBINE] == 48 * 32 * batch
@@ -182,6 +182,7 @@ def test_plan_counts_for_30b_batches(batch):
     assert ops[OP_GATEUP] == 48 * 96 * 8
     assert ops[OP_DOWN] == 48 * 128 * 4        # 16-row blocks x 4 slot groups
     assert ops[OP_MOESUM] == 48 * 128
+    assert ops[OP_FNORM] == batch                  # the final norm, one tile per token
     assert ops[OP_LMHEAD] == -(-151936 // 32)
     att = tasks[tasks[:, 0] == OP_ATTN]
     assert len(att) == 48 * batch * 4 * att[0, 5]
