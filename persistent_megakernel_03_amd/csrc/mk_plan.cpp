@@ -61,10 +61,11 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
     while (rd > 1 && rd * std::max(1, S) > 64) rd >>= 1;
     if (rd < cfg.rows_down) return;
     const int n_down = ceil_div(s.H, rd);
-    // gate/up tiles go to every workgroup when the down tiles fill at most
-    // half of them (one gate/up tile each, its rows in flight at once), else
-    // to the workgroups the down tiles leave
-    const bool spread = 2 * n_down <= n_wg;
+    // gate/up tiles go to every workgroup (one each, its rows in flight at
+    // once) when there are at most as many down tiles as workgroups, so that
+    // no workgroup runs two expert tiles of one kind; else to the workgroups
+    // the down tiles leave
+    const bool spread = n_down <= n_wg;
     const int per_slot = (spread ? n_wg : n_wg - n_down) / std::max(1, S);
     if (per_slot < 1) return;
     int rg = spread ? ceil_div(s.I, per_slot) : std::max(cfg.rows_gateup, ceil_div(s.I, per_slot));
@@ -395,7 +396,9 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
     // The expert tiles stream most of a layer's bytes once the routing is
     // known, so they are spread evenly over compute units: with two
     // workgroups per unit, workgroups w and w + n_wg/2 share one. The down
-    // tiles go to the lower half; the gate/up tiles to every workgroup when
+    // tiles go to the lower half (to either half when there are more of them
+    // than lower workgroups, so that none runs two while an upper one runs
+    // none); the gate/up tiles to every workgroup when
     // there is one per workgroup (each then holds all its rows in flight, and
     // the down tile that follows on a lower workgroup reuses its routing),
     // else to the upper half.
@@ -423,7 +426,7 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
         for (const Tile& t : tiles) {
             int hsel;
             if (half > 0 && op == OP_GATEUP && (int)tiles.size() < n_wg) hsel = 1;
-            else if (half > 0 && op == OP_DOWN) hsel = 0;
+            else if (half > 0 && op == OP_DOWN && (int)tiles.size() <= half) hsel = 0;
             else if (heaps[0].empty()) hsel = 1;
             else if (heaps[1].empty()) hsel = 0;
             else hsel = heaps[1].top() < heaps[0].top() ? 1 : 0;
