@@ -333,13 +333,11 @@ __device__ __forceinline__ void load_gain(uint4 (&g)[NCH], const uint16_t* gain,
 // x / sqrt(mean(x^2) + eps) * gain, the mean as sum(x^2) * inv_k (inv_k =
 // 1/K, a kernel argument, so no per-tile division is needed).
 template <int NCH, int NB>
-__device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, int64_t stride, int nb,
-                                       int K, const uint4* g, float eps, float inv_k) {
+__device__ __forceinline__ void load_x_raw(float (&h)[NB][NCH][8], const float* x, int64_t stride, int nb, int K) {
     const int lane = tid_() & 63;
     const int K8 = K >> 3;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        float ss = 0.f;
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int ch = lane + 64 * c;
@@ -351,21 +349,39 @@ __device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, i
 #pragma unroll
                 for (int j = 0; j < 8; ++j) h[b][c][j] = 0.f;
             }
+        }
+}
+// RMSNorm of loaded slices in place (gain g per this lane's positions).
+template <int NCH, int NB>
+__device__ __forceinline__ void norm_x(float (&h)[NB][NCH][8], int K, const uint4* g, float eps, float inv_k) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
 #pragma unroll
             for (int j = 0; j < 8; ++j) ss = fmaf(h[b][c][j], h[b][c][j], ss);
-        }
-        if (g != nullptr) {
-            ss = wave_sum(ss);
-            const float inv = 1.0f / sqrtf(ss * inv_k + eps);
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss * inv_k + eps);
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const uint4 gw = g[c];
-                const float gv[8] = {bflo(gw.x), bfhi(gw.x), bflo(gw.y), bfhi(gw.y),
-                                     bflo(gw.z), bfhi(gw.z), bflo(gw.w), bfhi(gw.w)};
+        for (int c = 0; c < NCH; ++c) {
+            const uint4 gw = g[c];
+            const float gv[8] = {bflo(gw.x), bfhi(gw.x), bflo(gw.y), bfhi(gw.y),
+                                 bflo(gw.z), bfhi(gw.z), bflo(gw.w), bfhi(gw.w)};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) h[b][c][j] = (h[b][c][j] * inv) * gv[j];
-            }
+            for (int j = 0; j < 8; ++j) h[b][c][j] = (h[b][c][j] * inv) * gv[j];
         }
+    }
+}
+template <int NCH, int NB>
+__device__ __forceinline__ void load_x(float (&h)[NB][NCH][8], const float* x, int64_t stride, int nb,
+                                       int K, const uint4* g, float eps, float inv_k) {
+    load_x_raw<NCH, NB>(h, x, stride, nb, K);
+    if (g != nullptr) {
+        norm_x<NCH, NB>(h, K, g, eps, inv_k);
+    } else {
+        (void)eps;
+        (void)inv_k;
     }
 }
 

@@ -234,8 +234,10 @@ static void build_levels_valu(const ModelShape& s, const TileConfig& cfg, int n_
         for (int sl = 0; sl < S; ++sl)
             for (int i = 0; i < ngu; ++i) {
                 const int r0 = i * rows_gu, r1 = std::min(s.I, r0 + rows_gu);
-                add(make_task(OP_GATEUP, l, sl, r0, r1, (sl == 0 && i == 0) ? 1 : 0, cl.oproj(l), no, cl.router(l),
-                              nr, cl.gateup(l), lv + 5),
+                // waits on the router only: the router tiles waited on the
+                // output projection, whose residual this tile also reads
+                add(make_task(OP_GATEUP, l, sl, r0, r1, (sl == 0 && i == 0) ? 1 : 0, -1, 0, cl.router(l), nr,
+                              cl.gateup(l), lv + 5),
                     4.0 * (r1 - r0) * s.H, kRouted);
             }
         P.targets[cl.gateup(l)] = S * ngu;

@@ -669,11 +669,14 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
 
 // Slot a0 (the a0-th distinct selected expert, ascending id), rows a1..a2 of
 // its gate and up matrices; a = SiLU(W_gate h2) * (W_up h2) for every token
-// routed to it. The post-attention residual is ready one level before the
-// router logits, so the tile waits for it first (pre counter), normalizes it,
-// then waits for the logits (main counter) and computes the routing; only
-// then are the expert's rows known and streamed. Task a3 != 0: also store the
-// routing of this layer.
+// routed to it. The tile waits for the router logits only (they imply the
+// post-attention residual, which the router tiles read): an earlier wait on
+// the residual's counter would have ~250 tiles polling it while the output
+// projection stores it. Then the residual's loads are issued, the routing is
+// computed (its logits loads queue behind them, so the two round trips
+// overlap) and the residual normalized; only then are the expert's rows known
+// and streamed. The task's pre counter (the output projection) is implied by
+// the main one. Task a3 != 0: also store the routing of this layer.
 template <int NCH, int PF, int NB, int NE>
 __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
@@ -685,13 +688,13 @@ __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     {
         uint4 gn[NCH];
         load_gain<NCH>(gn, wptr(p, l, W_FFN_NORM), H);
-        if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+        if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
         float h[NB][NCH][8];
-        load_x<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H, gn, p.eps, p.inv_h);
+        load_x_raw<NCH, NB>(h, x_at(p, 2 * l + 1), H, p.B, H);
+        routing_for<NE>(p, rlogits_at(p, l), rt);
+        norm_x<NCH, NB>(h, H, gn, p.eps, p.inv_h);
         split_x<NB, NCH>(h, hx);
     }
-    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
-    routing_for<NE>(p, rlogits_at(p, l), rt);
     mark(cx, 0);
     if (t.a3 != 0) {
         for (int i = tid_(); i < p.B * p.K; i += NT) {
