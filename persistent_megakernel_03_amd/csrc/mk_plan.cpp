@@ -118,7 +118,8 @@ int64_t max_tasks(const ModelShape& s, const TileConfig& cfg, int n_wg) {
         const int S = std::min(s.E, s.max_batch * s.K);
         const int64_t mm_layer = (int64_t)s.Hkv * ceil_div((G + 2) * s.D, cfg.mm_rows_qkv) +
                                  s.max_batch * (attn + comb) + ceil_div(s.H, cfg.mm_rows_o) +
-                                 ceil_div(s.E, cfg.mm_rows_router) + 1 + (int64_t)S * ceil_div(s.I, 8) +
+                                 (int64_t)ceil_div(s.E, cfg.mm_rows_router) * ceil_div(s.max_batch, 16) + 1 +
+                                 (int64_t)S * ceil_div(s.I, 8) +
                                  (int64_t)ceil_div(s.H, 16) * S + ceil_div(s.H, cfg.mm_rows_sum);
         const int64_t m = ceil_div(s.max_batch, cfg.mm_embed_tokens) + (int64_t)s.L * mm_layer +
                           s.max_batch + ceil_div(s.V, cfg.mm_rows_lm);
@@ -277,6 +278,7 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
     const int nq = ceil_div(grows, cfg.mm_rows_qkv);
     const int no = ceil_div(s.H, cfg.mm_rows_o);
     const int nr = ceil_div(s.E, cfg.mm_rows_router);
+    const int ntb = ceil_div(B, 16);   // router tiles per row block: one per 16-token block
     const int S = std::min(s.E, B * s.K);
     int Qg = 1, Q = 1;
     expert_groups_mm(s, n_wg, S, &Qg, &Q);
@@ -326,17 +328,21 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
                 2.0 * (r1 - r0) * s.Hq * s.D, kStatic);
         }
         P.targets[cl.oproj(l)] = no;
-        // router tile i also writes 8-element groups [g0, g1) of the experts'
-        // normalised input
+        // router tile (i, tb): expert rows of block i for the tokens of
+        // 16-token block tb (each tile reads only those tokens' residual
+        // rows), and the 8-element groups [g0, g1) of those tokens' expert
+        // input; tb rides in the upper half of a2 and a3
         const int ng = s.H / 8, gs = ceil_div(ng, nr);
-        for (int i = 0; i < nr; ++i) {
-            const int r0 = i * cfg.mm_rows_router, r1 = std::min(s.E, r0 + cfg.mm_rows_router);
-            const int g0 = std::min(ng, i * gs), g1 = std::min(ng, g0 + gs);
-            add(make_task(OP_ROUTER, l, r0, r1, g0, g1, -1, 0, cl.oproj(l), no, cl.router(l), lv + 4),
-                2.0 * (r1 - r0) * s.H, kStatic);
-        }
-        P.targets[cl.router(l)] = nr;
-        add(make_task(OP_ROUTE, l, 0, 1, 0, 0, -1, 0, cl.router(l), nr, cl.route(l), lv + 5), 4.0 * B * s.E,
+        for (int tb = 0; tb < ntb; ++tb)
+            for (int i = 0; i < nr; ++i) {
+                const int r0 = i * cfg.mm_rows_router, r1 = std::min(s.E, r0 + cfg.mm_rows_router);
+                const int g0 = std::min(ng, i * gs), g1 = std::min(ng, g0 + gs);
+                add(make_task(OP_ROUTER, l, r0, r1, g0 | (tb << 16), g1 | (tb << 16), -1, 0, cl.oproj(l), no,
+                              cl.router(l), lv + 4),
+                    2.0 * (r1 - r0) * s.H, kStatic);
+            }
+        P.targets[cl.router(l)] = nr * ntb;
+        add(make_task(OP_ROUTE, l, 0, 1, 0, 0, -1, 0, cl.router(l), nr * ntb, cl.route(l), lv + 5), 4.0 * B * s.E,
             kDynamic);
         P.targets[cl.route(l)] = 1;
         for (int q = 0; q < Qg; ++q)
@@ -692,9 +698,14 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
         switch (t.op) {
             case OP_QKV: ranges[std::make_tuple(t.op, t.layer, t.a0, 0)].push_back({t.a1, t.a2}); break;
             case OP_ATTN: ranges[std::make_tuple(t.op, t.layer, t.a0, t.a1)].push_back({t.a2, t.a2 + 1}); break;
+            // router tiles: per 16-token block (upper half of a2), and the
+            // token blocks themselves once, under the first row block
+            case OP_ROUTER:
+                ranges[std::make_tuple(t.op, t.layer, t.a2 >> 16, 0)].push_back({t.a0, t.a1});
+                if (t.a0 == 0) ranges[std::make_tuple(OP_COUNT + OP_ROUTER, t.layer, 0, 0)].push_back({t.a2 >> 16, (t.a2 >> 16) + 1});
+                break;
             case OP_EMBED:
             case OP_OPROJ:
-            case OP_ROUTER:
             case OP_ROUTE:
             case OP_MOESUM:
             case OP_FNORM:
@@ -731,6 +742,7 @@ std::string validate_plan(const ModelShape& s, const Plan& P) {
             case OP_COMBINE: want = s.Hq; break;
             case OP_OPROJ: case OP_DOWN: case OP_MOESUM: want = s.H; break;
             case OP_ROUTER: want = s.E; break;
+            case OP_COUNT + OP_ROUTER: want = P.mm ? ceil_div(P.B, 16) : 1; break;
             case OP_GATEUP: want = s.I; break;
             case OP_LMHEAD: want = s.V; break;
         }

@@ -433,37 +433,38 @@ __device__ __forceinline__ bool tile_oproj_mm(const Task& t, TileCtx& cx) {
 // tiles normalise it: (x * rs) * g.
 __device__ __forceinline__ bool tile_router_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
-    const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0, B = p.B, H = p.H;
+    const int l = t.layer, r0 = t.a0, nrows = t.a1 - t.a0, H = p.H;
+    // tokens of 16-token block tb only: a tile that read every token's
+    // residual row would stream B x H fp32 through one workgroup
+    const int tb = t.a2 >> 16, b0 = 16 * tb, nb = min(16, p.B - b0);
     const uint16_t* W = wptr(p, l, W_ROUTER);
     const float* bias = reinterpret_cast<const float*>(p.wtab[l * W_NKINDS + W_RBIAS]);
     float* sPart = reinterpret_cast<float*>(cx.lds);
     float* sSS = sPart + kMmPartFloats;
     bool ok = true;
-    const float* xm = x_at(p, 2 * l + 1);
-    const int ncb = (B + 15) >> 4, nc = ncb_cols(ncb);
-    with_ncb(ncb, [&](auto n) {
-        mm_block<decltype(n)::v, true>(
-            1, H, [&](int, int r) { return W + (int64_t)(r0 + (r < nrows ? r : nrows - 1)) * H; },
-            [&](int c) -> const float* { return c < B ? xm + (int64_t)c * H : nullptr; }, wptr(p, l, W_FFN_NORM),
-            [&]() {
-                ok = block_wait(p, t.ctr, t.target, cx.t_wait);
-                mark(cx, 0);
-            },
-            sPart, sSS);
-    });
+    const float* xm = x_at(p, 2 * l + 1) + (int64_t)b0 * H;
+    const int nc = ncb_cols(1);
+    mm_block<1, true>(
+        1, H, [&](int, int r) { return W + (int64_t)(r0 + (r < nrows ? r : nrows - 1)) * H; },
+        [&](int c) -> const float* { return c < nb ? xm + (int64_t)c * H : nullptr; }, wptr(p, l, W_FFN_NORM),
+        [&]() {
+            ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+            mark(cx, 0);
+        },
+        sPart, sSS);
     if (!ok) return false;
-    float* out = rlogits_at(p, l);
-    for (int i = tid_(); i < nrows * B; i += NT) {
-        const int r = i / B, b = i - r * B;
+    float* out = rlogits_at(p, l) + (int64_t)b0 * p.E;
+    for (int i = tid_(); i < nrows * nb; i += NT) {
+        const int r = i / nb, b = i - r * nb;
         const float v = mm_c(sPart, nc, 1, 0, r, b) * rms_scale(p, mm_ss(sSS, nc, 1, b));
         st_dev(out + (int64_t)b * p.E + r0 + r, bias != nullptr ? v + ldg(bias + r0 + r) : v);
     }
     // this tile's share of the expert input h2 = RMSNorm(x_mid) * g, split:
-    // groups of 8 elements [t.a2, t.a3)
+    // groups of 8 elements [g0, g1) of its tokens
     const uint16_t* gn = wptr(p, l, W_FFN_NORM);
-    float* h2 = h2s_at(p, l);
-    const int g0 = t.a2, ng = t.a3 - t.a2;
-    for (int i = tid_(); i < ng * B; i += NT) {
+    float* h2 = h2s_at(p, l) + (int64_t)b0 * H;
+    const int g0 = t.a2 & 0xffff, ng = (t.a3 & 0xffff) - g0;
+    for (int i = tid_(); i < ng * nb; i += NT) {
         const int b = i / ng, k = 8 * (g0 + i - b * ng);
         const float rs = rms_scale(p, mm_ss(sSS, nc, 1, b));
         const float4 u = ldf4(xm + (int64_t)b * H + k), v = ldf4(xm + (int64_t)b * H + k + 4);

@@ -169,7 +169,8 @@ def test_plan_counts_for_the_30b_shape():
 @pytest.mark.parametrize("batch", [4, 16, 64])
 def test_plan_counts_for_30b_batches(batch):
     # batches of 3+: every weight product in 16-row matrix-core blocks, one
-    # routing tile; gate/up tiles are (8 rows, one of 8 slot groups) pairs
+    # routing tile; gate/up tiles are (8 rows, one of 8 slot groups) pairs;
+    # router tiles are (8 expert rows, one 16-token block) pairs
     d = mk.make_dims(configs.A3B, batch, 520, 520 * batch)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192] * batch)
     ops = np.bincount(tasks[:, 0], minlength=13)
@@ -177,7 +178,10 @@ def test_plan_counts_for_30b_batches(batch):
     assert ops[OP_QKV] == 48 * 4 * 80          # 1280 rows per KV group, 16 per tile
     assert ops[OP_COMBINE] == 48 * 32 * batch
     assert ops[OP_OPROJ] == 48 * 256           # 8 rows per tile
-    assert ops[OP_ROUTER] == 48 * 16
+    assert ops[OP_ROUTER] == 48 * 16 * -(-batch // 16)
+    rt = tasks[(tasks[:, 0] == OP_ROUTER) & (tasks[:, 1] == 0)]
+    assert set((rt[:, 4] >> 16).tolist()) == set(range(-(-batch // 16)))   # token blocks
+    assert set((rt[:, 4] & 0xffff).tolist()) == set(range(0, 256, 16))   # 8-element groups of the expert input
     assert ops[OP_ROUTE] == 48
     assert ops[OP_GATEUP] == 48 * 96 * 8
     assert ops[OP_DOWN] == 48 * 128 * 4        # 16-row blocks x 4 slot groups
@@ -266,3 +270,20 @@ def test_every_plan_fits_the_task_capacity(cfg_name, max_batch, mmb):
             for pos in ([0] * b, [longest] * b, [longest] + [0] * (b - 1)):
                 info, tasks, offs, targets = mk.mk_plan_build(d, o, n_wg, pos)
                 assert 0 < info.n_tasks <= info.cap_tasks, (n_wg, b, pos[0], info.n_tasks, info.cap_tasks)
+
+
+def test_plan_check_rejects_router_token_blocks():
+    # batches above 16 tokens: router tiles per 16-token block; a tile moved
+    # to another block leaves its own block's expert rows uncovered
+    d = mk.make_dims(configs.A3B, 32, 520, 520 * 32)
+    o = mk.make_options()
+    positions = [8192] * 32
+    info, tasks, offs, targets = mk.mk_plan_build(d, o, 512, positions)
+    mk.mk_plan_check(d, o, 512, positions, tasks, offs)
+    t = tasks.copy()
+    i = int(np.flatnonzero((t[:, 0] == OP_ROUTER) & ((t[:, 4] >> 16) == 1))[0])
+    t[i, 4] &= 0xffff
+    t[i, 5] &= 0xffff
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_check(d, o, 512, positions, t, offs)
+    assert e.value.status == mk.MK_ERR_INVALID
