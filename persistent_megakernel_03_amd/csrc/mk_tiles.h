@@ -675,8 +675,9 @@ __device__ __forceinline__ bool tile_router(const Task& t, TileCtx& cx) {
 // projection stores it. Then the residual's loads are issued, the routing is
 // computed (its logits loads queue behind them, so the two round trips
 // overlap) and the residual normalized; only then are the expert's rows known
-// and streamed. The task's pre counter (the output projection) is implied by
-// the main one. Task a3 != 0: also store the routing of this layer.
+// and streamed. The plan gives the task no pre counter: the output
+// projection is implied by the main one. Task a3 != 0: also store the
+// routing of this layer.
 template <int NCH, int PF, int NB, int NE>
 __device__ __forceinline__ bool tile_gateup(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
