@@ -138,7 +138,16 @@ typedef struct mk_options {
                                 one- and two-token schedule (GEMV tiles on packed BF16 dot products).
                                 0 = 3; 1..3 allowed: the one- and two-token kernels are compiled for
                                 exactly one or two tokens, so the threshold can be lowered, not raised */
-    int32_t reserved[1];
+    int32_t poison_exchange; /* debug: nonzero fills the buffers that carry floating-point data between
+                                tiles (activations, query/key/value rows, attention partials, router
+                                logits, expert activations and outputs) with NaN before each step, with a
+                                fill kernel on the step's stream. A tile that read such data before its
+                                producer wrote it in this step would turn the step's outputs into NaN;
+                                with every read covered by a wait, outputs are bit-identical to a step
+                                without it (the pages' counters mark inputs ready: "Cohere Publishes
+                                One-Kernel Server for North Mini Code, Claims 1.58x vLLM Speedup",
+                                "One resident program, many small tasks"). Costs the fill (up to the
+                                attention partials' size) per step. */
 } mk_options;
 
 typedef struct mk_handle mk_handle;

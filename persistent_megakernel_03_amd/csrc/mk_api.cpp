@@ -655,6 +655,16 @@ static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, 
             p.ybuf = reinterpret_cast<float*>(at(h->lay.ybuf));
             p.h2s = reinterpret_cast<float*>(at(h->lay.h2s));
         }
+        if (h->o.poison_exchange) {
+            // NaN in fp32 and in both BF16 halves; the integer routing tables
+            // and the host-read routing output are left alone
+            const uint32_t nan2 = 0x7FC07FC0u;
+            const Layout& L = h->lay;
+            MK_HIP(launch_fill(reinterpret_cast<uint32_t*>(p.x), (int64_t)(L.route_ids - L.x) / 4, nan2, stream));
+            MK_HIP(launch_fill(reinterpret_cast<uint32_t*>(p.act), (int64_t)(L.rtab - L.act) / 4, nan2, stream));
+            if (L.wtab > L.ybuf)
+                MK_HIP(launch_fill(reinterpret_cast<uint32_t*>(p.ybuf), (int64_t)(L.wtab - L.ybuf) / 4, nan2, stream));
+        }
         const int nb = batch >= h->mm_min ? 0 : batch;
         p.mm = nb == 0 ? 1 : 0;
         const KernelPair& k = h->kern[nb];

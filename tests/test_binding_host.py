@@ -2,6 +2,7 @@
 pointers (block-table rows are read max_pages_per_seq entries long, logits
 written batch x vocab floats), so Decoder.step checks shapes, dtypes and
 placement first and raises MkError before any call."""
+import ctypes
 
 import numpy as np
 import pytest
@@ -59,4 +60,7 @@ def test_bad_arguments_raise_before_the_call(what):
 
 def test_plan_validation_option_is_in_the_options_struct():
     o = mk.make_options(validate_plans=True)
-    assert o.validate_plans == 1 and o.mfma_min_batch == 0 and list(o.reserved) == [0]
+    assert o.validate_plans == 1 and o.mfma_min_batch == 0 and o.poison_exchange == 0
+    assert mk.make_options(poison_exchange=True).poison_exchange == 1
+    # the debug word took the place of the reserved one: the struct's size is unchanged
+    assert ctypes.sizeof(mk.mk_options) == 48

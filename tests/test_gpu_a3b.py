@@ -56,9 +56,9 @@ def big(weights):
     return _case(weights, 8192)
 
 
-def _run(s, bt, tok, mode, ctx=8192, pages=8192 // 16 + 2):
+def _run(s, bt, tok, mode, ctx=8192, pages=8192 // 16 + 2, poison=False):
     k, v = s.fresh_pools()
-    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=1, max_pages_per_seq=pages, mode=mode)
+    dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=1, max_pages_per_seq=pages, mode=mode, poison_exchange=poison)
     tokens = torch.tensor([tok], dtype=torch.int32, device="cuda")
     logits = torch.empty(1, CFG["vocab"], dtype=torch.float32, device="cuda")
     print(f"a3b: one step at {ctx} cached tokens, mode {mode}", flush=True)
@@ -272,6 +272,40 @@ def test_a3b_megakernel_equals_perop_bitwise(big):
     assert np.array_equal(a["xs"], b["xs"])
     assert np.array_equal(a["ids"], b["ids"])
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+
+
+def test_a3b_poisoned_step_equals_plain(big, weights):
+    """Read-before-write check at full scale: the float exchange buffers
+    filled with NaN before the step (mk_options.poison_exchange) give the same
+    step bit for bit, at one token (8K cache) and for a batch of 4."""
+    s, bt, tok, pages = big
+    a = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL, 8192, pages, poison=True)
+    b = _run(s, bt, tok, mk.MK_MODE_MEGAKERNEL, 8192, pages)
+    assert np.all(np.isfinite(a["logits"])) and np.all(np.isfinite(a["xs"]))
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["xs"], b["xs"])
+    assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+    del a, b
+    B, ctx = 4, 2048
+    pages = ctx // P + 2
+    n_pages = B * pages + 7
+    s4 = Setup(CFG, n_pages=n_pages, seed=0, device_gen=True, weights=weights)
+    bts = [[int(x) for x in r] for r in synth.make_block_tables(B, pages, n_pages, seed=3, shuffle=True)]
+    toks = [int(t) for t in synth.make_tokens(B, CFG["vocab"], seed=33)]
+    outs = []
+    for poison in (True, False):
+        k, v = s4.fresh_pools()
+        dec = mk.Decoder(CFG, s4.w_dev, k, v, max_batch=B, max_pages_per_seq=pages, poison_exchange=poison)
+        tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
+        logits = torch.empty(B, CFG["vocab"], dtype=torch.float32, device="cuda")
+        print(f"a3b poison={poison}: batch {B} at {ctx} cached tokens", flush=True)
+        dec.step([ctx, ctx - 100, ctx - 1000, 17], bts, tokens, logits)
+        assert dec.sync_check() == mk.MK_OK
+        outs.append((logits.cpu().numpy(), x_layers(dec).cpu().numpy()))
+        dec.close()
+    assert np.all(np.isfinite(outs[0][0]))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    del s4, outs
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("ctx", [32768, 131072, 262144])
