@@ -518,6 +518,72 @@ static void place_tiles(const TileConfig& cfg, int n_wg, std::vector<std::vector
 // that write what it reads must lie in deps(ctr) | deps(pre_ctr). Writes
 // are looked up per producing operation: which counters its tiles signal,
 // for a whole layer or for one KV group, hidden-row range or sequence.
+// What task t reads, by producer: need(op, layer, sel) for every tile of op
+// in layer (sel -1) or the tiles of one KV group (QKV, sel = group) or of one
+// (sequence, group) (attention, sel = b * Hkv + g); need_rows(op, layer, r0,
+// r1) for the tiles of op writing rows [r0, r1) of the residual. Returns the
+// first non-empty result. One definition for the validator and the thread
+// executor.
+template <class Need, class NeedRows>
+static std::string for_each_read(const ModelShape& s, const Plan& P, const Task& t, Need&& need, NeedRows&& need_rows) {
+    const int G = s.Hq / s.Hkv;
+    const int x_op = P.mm ? OP_MOESUM : OP_DOWN;   // writes the layer output
+    const int l = t.layer;
+    // the residual stream entering layer l: the embedding or the previous layer's output
+    auto x_in = [&](int layer) { return layer == 0 ? need(OP_EMBED, 0, -1) : need(x_op, layer - 1, -1); };
+    std::string e;
+    switch (t.op) {
+        case OP_EMBED: break;
+        case OP_QKV: e = x_in(l); break;
+        case OP_ATTN: e = need(OP_QKV, l, t.a1); break;
+        case OP_COMBINE: e = need(OP_ATTN, l, t.a0 * s.Hkv + t.a1 / G); break;
+        case OP_OPROJ:
+            e = need(OP_COMBINE, l, -1);
+            if (e.empty()) e = l == 0 ? need(OP_EMBED, 0, -1) : need_rows(x_op, l - 1, t.a0, t.a1);
+            break;
+        case OP_ROUTER: e = need(OP_OPROJ, l, -1); break;
+        case OP_ROUTE: e = need(OP_ROUTER, l, -1); break;
+        case OP_GATEUP:
+            e = need(OP_ROUTER, l, -1);
+            if (e.empty()) e = P.mm ? need(OP_ROUTE, l, -1) : need(OP_OPROJ, l, -1);
+            break;
+        case OP_DOWN:
+            e = need(OP_GATEUP, l, -1);
+            if (e.empty()) e = P.mm ? need(OP_ROUTE, l, -1) : need(OP_ROUTER, l, -1);
+            if (e.empty() && !P.mm) e = need_rows(OP_OPROJ, l, t.a0, t.a1);
+            break;
+        case OP_MOESUM:
+            e = need(OP_DOWN, l, -1);
+            if (e.empty()) e = need(OP_ROUTE, l, -1);
+            if (e.empty()) e = need_rows(OP_OPROJ, l, t.a0, t.a1);
+            break;
+        case OP_FNORM: e = need(x_op, s.L - 1, -1); break;
+        case OP_LMHEAD: e = P.mm ? need(OP_FNORM, 0, -1) : need(x_op, s.L - 1, -1); break;
+        default: break;
+    }
+    return e;
+}
+
+// Writers of each (op, layer, selector) and of residual rows, as task
+// indices or as the counters they signal (see for_each_read).
+struct WriterKey {
+    int op, layer, sel;
+    bool operator<(const WriterKey& o) const { return std::tie(op, layer, sel) < std::tie(o.op, o.layer, o.sel); }
+};
+template <class F>
+static void for_each_writer(const ModelShape& s, const Plan& P, F&& f) {
+    for (int i = 0; i < (int)P.tasks.size(); ++i) {
+        const Task& t = P.tasks[i];
+        if (t.op == OP_CLAIM) continue;
+        f(WriterKey{t.op, t.layer, -1}, i);
+        if (t.op == OP_QKV) f(WriterKey{t.op, t.layer, t.a0}, i);                    // KV group
+        if (t.op == OP_ATTN) f(WriterKey{t.op, t.layer, t.a0 * s.Hkv + t.a1}, i);   // (sequence, group)
+    }
+}
+static bool writes_rows(const Plan& P, const Task& t) {
+    return t.op == OP_OPROJ || (t.op == OP_DOWN && !P.mm) || t.op == OP_MOESUM;
+}
+
 static std::string check_reads(const ModelShape& s, const Plan& P, const std::vector<int>& prod_level) {
     const CounterLayout cl{s.L, s.Hkv, s.max_batch};
     const int n_main = cl.n_main();
@@ -543,91 +609,73 @@ static std::string check_reads(const ModelShape& s, const Plan& P, const std::ve
     }
     auto has = [&](const Bits& d, int c) { return c >= 0 && ((d[c / 64] >> (c % 64)) & 1ull); };
     // writers: per (op, layer) the counters signalled, whole and per selector
-    struct Key {
-        int op, layer, sel;
-        bool operator<(const Key& o) const { return std::tie(op, layer, sel) < std::tie(o.op, o.layer, o.sel); }
-    };
-    std::map<Key, std::set<int>> wr;          // sel -1: every tile of the op
+    std::map<WriterKey, std::set<int>> wr;   // sel -1: every tile of the op
+    for_each_writer(s, P, [&](const WriterKey& k, int i) { wr[k].insert(P.tasks[i].signal); });
     std::map<std::pair<int, int>, std::vector<std::tuple<int, int, int>>> rows;   // (op, layer) -> (r0, r1, signal)
-    const int G = s.Hq / s.Hkv;
-    for (const Task& t : P.tasks) {
-        if (t.op == OP_CLAIM) continue;
-        wr[{t.op, t.layer, -1}].insert(t.signal);
-        if (t.op == OP_QKV) wr[{t.op, t.layer, t.a0}].insert(t.signal);                    // KV group
-        if (t.op == OP_ATTN) wr[{t.op, t.layer, t.a0 * s.Hkv + t.a1}].insert(t.signal);   // (sequence, group)
-        if (t.op == OP_OPROJ || (t.op == OP_DOWN && !P.mm) || t.op == OP_MOESUM)
-            rows[{t.op, t.layer}].push_back(std::make_tuple(t.a0, t.a1, t.signal));
-    }
-    const int x_op = P.mm ? OP_MOESUM : OP_DOWN;   // writes the layer output
+    for (const Task& t : P.tasks)
+        if (t.op != OP_CLAIM && writes_rows(P, t)) rows[{t.op, t.layer}].push_back(std::make_tuple(t.a0, t.a1, t.signal));
     char buf[256];
-    auto need = [&](const Task& t, const Bits& d, int op, int layer, int sel) -> std::string {
-        auto it = wr.find({op, layer, sel});
-        if (it == wr.end()) {
-            snprintf(buf, sizeof buf, "op %d layer %d reads what no op-%d tile (layer %d, part %d) writes", t.op,
-                     t.layer, op, layer, sel);
-            return buf;
-        }
-        for (int c : it->second)
-            if (!has(d, c)) {
-                snprintf(buf, sizeof buf, "op %d layer %d reads op %d layer %d output without waiting on counter %d",
-                         t.op, t.layer, op, layer, c);
-                return buf;
-            }
-        return std::string();
-    };
-    auto need_rows = [&](const Task& t, const Bits& d, int op, int layer, int r0, int r1) -> std::string {
-        for (const auto& w : rows[{op, layer}])
-            if (std::get<0>(w) < r1 && r0 < std::get<1>(w) && !has(d, std::get<2>(w))) {
-                snprintf(buf, sizeof buf, "op %d layer %d reads rows %d..%d of op %d without waiting on counter %d",
-                         t.op, t.layer, r0, r1, op, std::get<2>(w));
-                return buf;
-            }
-        return std::string();
-    };
-    // the residual stream entering layer l: the embedding or the previous layer's output
-    auto x_in = [&](const Task& t, const Bits& d, int l) {
-        return l == 0 ? need(t, d, OP_EMBED, 0, -1) : need(t, d, x_op, l - 1, -1);
-    };
     for (const Task& t : P.tasks) {
         if (t.op == OP_CLAIM) continue;
         Bits d(W, 0);
         for (int c : {t.ctr, t.pre_ctr})
             if (c >= 0)
                 for (int i = 0; i < W; ++i) d[i] |= deps[c][i];
-        const int l = t.layer;
-        std::string e;
-        switch (t.op) {
-            case OP_EMBED: break;
-            case OP_QKV: e = x_in(t, d, l); break;
-            case OP_ATTN: e = need(t, d, OP_QKV, l, t.a1); break;
-            case OP_COMBINE: e = need(t, d, OP_ATTN, l, t.a0 * s.Hkv + t.a1 / G); break;
-            case OP_OPROJ:
-                e = need(t, d, OP_COMBINE, l, -1);
-                if (e.empty()) e = l == 0 ? need(t, d, OP_EMBED, 0, -1) : need_rows(t, d, x_op, l - 1, t.a0, t.a1);
-                break;
-            case OP_ROUTER: e = need(t, d, OP_OPROJ, l, -1); break;
-            case OP_ROUTE: e = need(t, d, OP_ROUTER, l, -1); break;
-            case OP_GATEUP:
-                e = need(t, d, OP_ROUTER, l, -1);
-                if (e.empty()) e = P.mm ? need(t, d, OP_ROUTE, l, -1) : need(t, d, OP_OPROJ, l, -1);
-                break;
-            case OP_DOWN:
-                e = need(t, d, OP_GATEUP, l, -1);
-                if (e.empty()) e = P.mm ? need(t, d, OP_ROUTE, l, -1) : need(t, d, OP_ROUTER, l, -1);
-                if (e.empty() && !P.mm) e = need_rows(t, d, OP_OPROJ, l, t.a0, t.a1);
-                break;
-            case OP_MOESUM:
-                e = need(t, d, OP_DOWN, l, -1);
-                if (e.empty()) e = need(t, d, OP_ROUTE, l, -1);
-                if (e.empty()) e = need_rows(t, d, OP_OPROJ, l, t.a0, t.a1);
-                break;
-            case OP_FNORM: e = need(t, d, x_op, s.L - 1, -1); break;
-            case OP_LMHEAD: e = P.mm ? need(t, d, OP_FNORM, 0, -1) : need(t, d, x_op, s.L - 1, -1); break;
-            default: break;
-        }
+        auto need = [&](int op, int layer, int sel) -> std::string {
+            auto it = wr.find({op, layer, sel});
+            if (it == wr.end()) {
+                snprintf(buf, sizeof buf, "op %d layer %d reads what no op-%d tile (layer %d, part %d) writes", t.op,
+                         t.layer, op, layer, sel);
+                return buf;
+            }
+            for (int c : it->second)
+                if (!has(d, c)) {
+                    snprintf(buf, sizeof buf, "op %d layer %d reads op %d layer %d output without waiting on counter %d",
+                             t.op, t.layer, op, layer, c);
+                    return buf;
+                }
+            return std::string();
+        };
+        auto need_rows = [&](int op, int layer, int r0, int r1) -> std::string {
+            for (const auto& w : rows[{op, layer}])
+                if (std::get<0>(w) < r1 && r0 < std::get<1>(w) && !has(d, std::get<2>(w))) {
+                    snprintf(buf, sizeof buf, "op %d layer %d reads rows %d..%d of op %d without waiting on counter %d",
+                             t.op, t.layer, r0, r1, op, std::get<2>(w));
+                    return buf;
+                }
+            return std::string();
+        };
+        const std::string e = for_each_read(s, P, t, need, need_rows);
         if (!e.empty()) return e;
     }
     return std::string();
+}
+
+std::vector<std::vector<int>> read_producers(const ModelShape& s, const Plan& P) {
+    std::map<WriterKey, std::vector<int>> wr;
+    for_each_writer(s, P, [&](const WriterKey& k, int i) { wr[k].push_back(i); });
+    std::map<std::pair<int, int>, std::vector<std::tuple<int, int, int>>> rows;   // (op, layer) -> (r0, r1, task)
+    for (int i = 0; i < (int)P.tasks.size(); ++i)
+        if (P.tasks[i].op != OP_CLAIM && writes_rows(P, P.tasks[i]))
+            rows[{P.tasks[i].op, P.tasks[i].layer}].push_back(std::make_tuple(P.tasks[i].a0, P.tasks[i].a1, i));
+    std::vector<std::vector<int>> out(P.tasks.size());
+    for (int i = 0; i < (int)P.tasks.size(); ++i) {
+        const Task& t = P.tasks[i];
+        if (t.op == OP_CLAIM) continue;
+        std::vector<int>& o = out[i];
+        auto need = [&](int op, int layer, int sel) -> std::string {
+            auto it = wr.find({op, layer, sel});
+            if (it != wr.end()) o.insert(o.end(), it->second.begin(), it->second.end());
+            return std::string();
+        };
+        auto need_rows = [&](int op, int layer, int r0, int r1) -> std::string {
+            for (const auto& w : rows[{op, layer}])
+                if (std::get<0>(w) < r1 && r0 < std::get<1>(w)) o.push_back(std::get<2>(w));
+            return std::string();
+        };
+        for_each_read(s, P, t, need, need_rows);
+    }
+    return out;
 }
 
 std::string validate_plan(const ModelShape& s, const Plan& P) {

@@ -81,6 +81,11 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
 // expert width) and of the down tiles (16-row blocks of the hidden size).
 void expert_groups_mm(const ModelShape& s, int n_wg, int S, int* gu_groups, int* down_groups);
 
+// For each task of P (by index), the tasks whose outputs it reads: the
+// relation validate_plan proves covered by waits, as task indices (used by
+// the host thread executor of the tests).
+std::vector<std::vector<int>> read_producers(const ModelShape& s, const Plan& P);
+
 // Attention chunk length for these contexts (tokens, multiple of 64).
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested);
 
