@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--wg-per-cu", type=int, default=0, help="persistent workgroups per compute unit (0 = auto, 2)")
     ap.add_argument("--mfma-min-batch", type=int, default=0,
                     help="smallest batch on the matrix-core schedule (0 = default 3; 1 or 2 move those batches to it)")
+    ap.add_argument("--mm-row-blocks", type=int, default=0,
+                    help="row blocks per matrix-core expert tile (0 = chosen per step; 1 or 2 force it)")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated batch sizes to measure as well")
     ap.add_argument("--sweep-steps", type=int, default=32)
     ap.add_argument("--long", type=str, default="", help="comma-separated batch-1 context lengths to measure as well")
@@ -166,7 +168,8 @@ def main():
     def run(mode: int, steps: int, warmup: int, k, v, B=B, pages_per_seq=pages_per_seq, block_tables=block_tables,
             tok0=tok0, ctx=ctx):
         dec = mk.Decoder(cfg, weights, k, v, max_batch=B, max_pages_per_seq=pages_per_seq, mode=mode,
-                         wg_per_cu=args.wg_per_cu, mfma_min_batch=args.mfma_min_batch, time_kernels=True)
+                         wg_per_cu=args.wg_per_cu, mfma_min_batch=args.mfma_min_batch,
+                         mm_row_blocks=args.mm_row_blocks, time_kernels=True)
         tokens = torch.tensor(tok0, dtype=torch.int32, device="cuda")
         logits = torch.empty(B, cfg["vocab"], dtype=torch.float32, device="cuda")
         pos = [ctx] * B
@@ -336,10 +339,12 @@ def main():
                    "top_k": cfg["top_k"], "parallelism": "single GPU",
                    **({"wg_per_cu": args.wg_per_cu} if args.wg_per_cu else {}),
                    **({"mfma_min_batch": args.mfma_min_batch} if args.mfma_min_batch else {}),
+                   **({"mm_row_blocks": args.mm_row_blocks} if args.mm_row_blocks else {}),
                    "precision": "BF16 weights and KV; fp32 activations, entering weight products as two BF16 parts; fp32 accumulation"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": measured_traffic(B, ctx) if not (args.wg_per_cu or args.mfma_min_batch) else None,
+                     "traffic": (measured_traffic(B, ctx)
+                                 if not (args.wg_per_cu or args.mfma_min_batch or args.mm_row_blocks) else None),
                      "kernel": "k_persistent (one launch per step)", "bytes_per_launch": bytes_step,
                      "kernel_ms": round(kms, 4)},
         "sol": {"bytes_per_step": bytes_step, "sol_tok_s": round(sol.sol_tokens_per_s(bytes_step, B), 1),

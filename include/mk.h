@@ -148,6 +148,14 @@ typedef struct mk_options {
                                 One-Kernel Server for North Mini Code, Claims 1.58x vLLM Speedup",
                                 "One resident program, many small tasks"). Costs the fill (up to the
                                 attention partials' size) per step. */
+    int32_t mm_row_blocks;   /* batches of 3+: row blocks per expert tile (8-row blocks of the expert width
+                                per gate/up tile, 16-row blocks of the hidden size per down tile), so that
+                                a wave multiplies one load of its tokens' activations by that many blocks
+                                of an expert's weights. 0 = choose per step (2 when the expected number of
+                                distinct experts gives each wave of a tile about two slots, else 1); 1 or 2
+                                force it. Results are bit-identical either way: each output row sums the
+                                same products in the same order. */
+    int32_t reserved0;       /* must be 0 */
 } mk_options;
 
 typedef struct mk_handle mk_handle;

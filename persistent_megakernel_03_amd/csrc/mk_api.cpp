@@ -117,6 +117,7 @@ TileConfig tile_config(const mk_options& o) {
     c.chunk = o.split_kv_tokens;
     c.shared_levels = o.shared_levels;
     c.mm_min_batch = mm_min_of(o);
+    c.mm_row_blocks = o.mm_row_blocks;
     return c;
 }
 
@@ -193,9 +194,9 @@ struct mk_handle {
     int shape = -1;
     int mm_min = kMaxBatchValu + 1;   // smallest batch on the matrix-core kernels
     // [1], [2]: the one- and two-token kernels; [0]: the matrix-core kernels (if max_batch >= mm_min)
-    KernelPair kern[kMaxBatchValu + 1];
-    size_t lds_bytes[kMaxBatchValu + 1] = {0, 0, 0};
-    int general[kMaxBatchValu + 1] = {0, 0, 0};
+    KernelPair kern[kNbCount];
+    size_t lds_bytes[kNbCount] = {};
+    int general[kNbCount] = {};
     Layout lay;
     char* ws = nullptr;
     int bank = 0;
@@ -259,6 +260,8 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         if (o.split_kv_tokens < 0 || o.split_kv_tokens % 64) return fail(MK_ERR_INVALID, "split_kv_tokens must be a multiple of 64");
         if (o.mfma_min_batch < 0 || o.mfma_min_batch > kMaxBatchValu + 1)
             return fail(MK_ERR_INVALID, "mfma_min_batch must be 0 (default) or 1..%d", kMaxBatchValu + 1);
+        if (o.mm_row_blocks < 0 || o.mm_row_blocks > kMmMaxRowBlocks)
+            return fail(MK_ERR_INVALID, "mm_row_blocks must be 0 (choose) or 1..%d", kMmMaxRowBlocks);
         if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return fail(MK_ERR_INVALID, "workspace not 256-byte aligned");
         const mk_dims& d = *dims;
         if (!w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wqkv || !w->wo || !w->ffn_norm ||
@@ -280,10 +283,13 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         h->shape = find_shape(d.hidden, d.n_q_heads * d.head_dim, d.moe_inter, d.head_dim, d.n_experts);
         h->mm_min = mm_min_of(o);
         const bool mm = d.max_batch >= h->mm_min;
-        // kernels a step may launch: the matrix-core ones for batches >= mm_min,
-        // the one- and two-token ones below it
-        auto used = [&](int nb) { return nb == 0 ? mm : (nb <= d.max_batch && nb < h->mm_min); };
-        for (int nb = 0; nb <= kMaxBatchValu; ++nb)
+        // kernels a step may launch: the matrix-core ones (one or two row
+        // blocks per expert tile) for batches >= mm_min, the one- and
+        // two-token ones below it
+        auto used = [&](int nb) {
+            return nb == 0 || nb == kNbMmWide ? mm : (nb <= d.max_batch && nb < h->mm_min);
+        };
+        for (int nb = 0; nb < kNbCount; ++nb)
             if (used(nb) && !get_kernels(h->shape, nb, &h->kern[nb])) return fail(MK_ERR_UNSUPPORTED, "no kernels");
 
         // LDS: general region (attention tiles + query fragments, combine
@@ -304,9 +310,9 @@ mk_status mk_create(const mk_dims* dims, const mk_weights* w, void* k_pool, void
         // matrix-core tiles: block-product partials or the routing tile's tables
         const size_t gen_m = align256(std::max(std::max(attn, comb), (size_t)std::max(kMmLdsBytes, kRouteLdsBytes)));
         int occ = 1 << 30;
-        for (int nb = 0; nb <= kMaxBatchValu; ++nb) {
+        for (int nb = 0; nb < kNbCount; ++nb) {
             if (!used(nb)) continue;
-            h->general[nb] = (int)(nb == 0 ? gen_m : gen_v);
+            h->general[nb] = (int)(nb == 0 || nb == kNbMmWide ? gen_m : gen_v);
             h->lds_bytes[nb] = h->general[nb] + 1024 + 1024;
             if (h->lds_bytes[nb] > (size_t)prop.sharedMemPerBlock && h->lds_bytes[nb] > 160 * 1024)
                 return fail(MK_ERR_UNSUPPORTED, "needs %zu bytes of LDS", h->lds_bytes[nb]);
@@ -665,8 +671,8 @@ static mk_status step_impl(mk_handle* h, int32_t batch, const int32_t* seq_ids, 
             if (L.wtab > L.ybuf)
                 MK_HIP(launch_fill(reinterpret_cast<uint32_t*>(p.ybuf), (int64_t)(L.wtab - L.ybuf) / 4, nan2, stream));
         }
-        const int nb = batch >= h->mm_min ? 0 : batch;
-        p.mm = nb == 0 ? 1 : 0;
+        const int nb = batch >= h->mm_min ? (h->plan.rb > 1 ? kNbMmWide : 0) : batch;
+        p.mm = batch >= h->mm_min ? 1 : 0;
         const KernelPair& k = h->kern[nb];
         const int general = h->general[nb];
         const size_t lds_bytes = h->lds_bytes[nb];
@@ -806,6 +812,8 @@ mk_status mk_plan_build(const mk_dims* dims, const mk_options* opts, int32_t n_w
         if (opts) o = *opts;
         if (o.mfma_min_batch < 0 || o.mfma_min_batch > kMaxBatchValu + 1)
             return fail(MK_ERR_INVALID, "mfma_min_batch must be 0 (default) or 1..%d", kMaxBatchValu + 1);
+        if (o.mm_row_blocks < 0 || o.mm_row_blocks > kMmMaxRowBlocks)
+            return fail(MK_ERR_INVALID, "mm_row_blocks must be 0 (choose) or 1..%d", kMmMaxRowBlocks);
         const std::string why = check_dims(*dims, mm_min_of(o));
         if (!why.empty()) return fail(MK_ERR_UNSUPPORTED, "%s", why.c_str());
         if (batch <= 0 || batch > dims->max_batch) return fail(MK_ERR_CAPACITY, "batch out of range");

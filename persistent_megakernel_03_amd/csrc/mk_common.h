@@ -49,6 +49,19 @@ constexpr int kLevelsPerLayer = 9;
 constexpr int kMaxBatchValu = 2;
 constexpr int kMaxBatchMM = 64;
 
+// Matrix-core expert tiles: at most this many 8-row blocks of the expert
+// width per gate/up tile and 16-row blocks of the hidden size per down tile,
+// so that a wave can multiply one load of its tokens' activations by several
+// blocks of one expert's weights.
+constexpr int kMmMaxRowBlocks = 2;
+
+// Kernel flavours (template argument NB): 0 the matrix-core schedule, 1 and
+// 2 the one- and two-token schedules, kNbMmWide the matrix-core schedule
+// with kMmMaxRowBlocks row blocks per expert tile (a kernel of its own, so
+// that each build holds one variant of the expert stream in its registers).
+constexpr int kNbMmWide = kMaxBatchValu + 1;
+constexpr int kNbCount = kNbMmWide + 1;
+
 // LDS of the matrix-core tiles (general region): a block product's per-wave
 // partials [4][16][64] and sums of squares [4][64] fp32 plus 128 words of
 // token list and routing-table entries; the routing tile's token masks [256][2], ranks [64][256] (bytes)

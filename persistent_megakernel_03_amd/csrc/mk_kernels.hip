@@ -135,9 +135,12 @@ void fill_pair(int nb, KernelPair* out) {
     } else if (nb == 1) {
         out->persistent = reinterpret_cast<const void*>(&k_persistent<S, 1>);
         out->perop = reinterpret_cast<const void*>(&k_perop<S, 1>);
-    } else {
+    } else if (nb == 2) {
         out->persistent = reinterpret_cast<const void*>(&k_persistent<S, 2>);
         out->perop = reinterpret_cast<const void*>(&k_perop<S, 2>);
+    } else {
+        out->persistent = reinterpret_cast<const void*>(&k_persistent<S, kNbMmWide>);
+        out->perop = reinterpret_cast<const void*>(&k_perop<S, kNbMmWide>);
     }
 }
 }  // namespace
@@ -154,7 +157,7 @@ int find_shape(int hidden, int attn_width, int moe_inter, int head_dim, int n_ex
 }
 
 bool get_kernels(int shape, int nb, KernelPair* out) {
-    if (nb < 0 || nb > kMaxBatchValu) return false;
+    if (nb < 0 || nb >= kNbCount) return false;
     switch (shape) {
         case 0: fill_pair<ShapeSmall>(nb, out); return true;
         case 1: fill_pair<ShapeA3B>(nb, out); return true;
@@ -208,5 +211,9 @@ template __global__ void k_perop<ShapeSmall, 1>(Params, int, int);
 template __global__ void k_perop<ShapeSmall, 2>(Params, int, int);
 template __global__ void k_perop<ShapeA3B, 1>(Params, int, int);
 template __global__ void k_perop<ShapeA3B, 2>(Params, int, int);
+template __global__ void k_persistent<ShapeSmall, kNbMmWide>(Params, int);
+template __global__ void k_persistent<ShapeA3B, kNbMmWide>(Params, int);
+template __global__ void k_perop<ShapeSmall, kNbMmWide>(Params, int, int);
+template __global__ void k_perop<ShapeA3B, kNbMmWide>(Params, int, int);
 
 }  // namespace mk

@@ -2,6 +2,7 @@
 #include "mk_plan.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <map>
 #include <queue>
@@ -74,13 +75,26 @@ void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, in
     *rows_down = rd;
 }
 
-void expert_groups_mm(const ModelShape& s, int n_wg, int S, int* gu_groups, int* down_groups) {
-    // gate/up: 8-row blocks of the expert width, the slots in groups so that
-    // there are about 1.5 tiles per workgroup; down: 16-row blocks of the
-    // hidden size, about one tile per workgroup
-    const int gblk = ceil_div(s.I, 8), dblk = ceil_div(s.H, 16);
+void expert_groups_mm(const ModelShape& s, int n_wg, int S, int rb, int* gu_groups, int* down_groups) {
+    // gate/up: rb 8-row blocks of the expert width per tile, the slots in
+    // groups so that there are about 1.5 tiles per workgroup; down: rb 16-row
+    // blocks of the hidden size, about one tile per workgroup
+    const int gblk = ceil_div(s.I, 8 * rb), dblk = ceil_div(s.H, 16 * rb);
     *gu_groups = std::max(1, std::min(S, (3 * n_wg / 2 + gblk / 2) / std::max(1, gblk)));
     *down_groups = std::max(1, std::min(S, n_wg / std::max(1, dblk)));
+}
+
+int mm_row_blocks(const ModelShape& s, int n_wg, int B) {
+    // Two blocks per tile halve the tiles per slot group, so the slots are
+    // spread over twice the groups: worth it only when the tile's four waves
+    // still get about two slots each. The count of distinct experts is
+    // unknown until routing; its expectation under uniform routing,
+    // E (1 - (1 - k/E)^B), stands in for it.
+    const int S = std::min(s.E, B * s.K);
+    int qg = 1, q = 1;
+    expert_groups_mm(s, n_wg, S, kMmMaxRowBlocks, &qg, &q);
+    const double distinct = s.E * (1.0 - std::pow(1.0 - (double)s.K / s.E, B));
+    return distinct >= 7.0 * qg ? kMmMaxRowBlocks : 1;
 }
 
 int choose_chunk(const ModelShape& s, int n_wg, int B, const int32_t* positions, int requested) {
@@ -281,10 +295,12 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
     const int ntb = ceil_div(B, 16);   // router tiles per row block: one per 16-token block
     const int S = std::min(s.E, B * s.K);
     int Qg = 1, Q = 1;
-    expert_groups_mm(s, n_wg, S, &Qg, &Q);
-    const int gblk = ceil_div(s.I, 8);
+    const int rb = cfg.mm_row_blocks > 0 ? cfg.mm_row_blocks : mm_row_blocks(s, n_wg, B);
+    P.rb = rb;
+    expert_groups_mm(s, n_wg, S, rb, &Qg, &Q);
+    const int gblk = ceil_div(s.I, 8 * rb);
     const int ngu = gblk * Qg;
-    const int nblk = ceil_div(s.H, 16);
+    const int nblk = ceil_div(s.H, 16 * rb);
     const int nd = nblk * Q;
     const int ns = ceil_div(s.H, cfg.mm_rows_sum);
     const int nl = ceil_div(s.V, cfg.mm_rows_lm);
@@ -347,14 +363,14 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
         P.targets[cl.route(l)] = 1;
         for (int q = 0; q < Qg; ++q)
             for (int i = 0; i < gblk; ++i) {
-                const int r0 = i * 8, r1 = std::min(s.I, r0 + 8);
+                const int r0 = i * 8 * rb, r1 = std::min(s.I, r0 + 8 * rb);
                 add(make_task(OP_GATEUP, l, r0, r1, q, Qg, -1, 0, cl.route(l), 1, cl.gateup(l), lv + 6),
                     4.0 * ceil_div(S - q, Qg) * (r1 - r0) * s.H, kRouted);
             }
         P.targets[cl.gateup(l)] = ngu;
         for (int q = 0; q < Q; ++q)
             for (int i = 0; i < nblk; ++i) {
-                const int r0 = i * 16, r1 = std::min(s.H, r0 + 16);
+                const int r0 = i * 16 * rb, r1 = std::min(s.H, r0 + 16 * rb);
                 add(make_task(OP_DOWN, l, r0, r1, q, Q, -1, 0, cl.gateup(l), ngu, cl.down(l), lv + 7),
                     2.0 * ceil_div(S - q, Q) * (r1 - r0) * s.I, kRouted);
             }

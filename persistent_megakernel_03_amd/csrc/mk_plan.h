@@ -48,6 +48,8 @@ struct TileConfig {
     int shared_levels = 0;
     // smallest batch that runs the matrix-core schedule (1..kMaxBatchValu + 1)
     int mm_min_batch = kMaxBatchValu + 1;
+    // row blocks per matrix-core expert tile: 0 = mm_row_blocks(), else 1..kMmMaxRowBlocks
+    int mm_row_blocks = 0;
     // timing model used to place tiles on workgroups
     double model_bw_bytes_per_us = 5.6e6;  // whole-device HBM bandwidth
     double model_task_us = 2.5;            // fixed cost of a task after its inputs are ready
@@ -58,6 +60,7 @@ struct Plan {
     int n_wg = 0;
     int B = 0;
     bool mm = false;                  // the matrix-core schedule (else the one- and two-token tiles)
+    int rb = 1;                       // row blocks per matrix-core expert tile
     int chunk = 0;
     int n_levels = 0;
     std::vector<Task> tasks;          // grouped per workgroup (CSR)
@@ -77,9 +80,11 @@ struct Plan {
 // after them. Otherwise the configured sizes.
 void expert_rows(const ModelShape& s, const TileConfig& cfg, int n_wg, int S, int* rows_gu, int* rows_down);
 
-// Batches of 3+: slot groups of the gate/up tiles (8-row blocks of the
-// expert width) and of the down tiles (16-row blocks of the hidden size).
-void expert_groups_mm(const ModelShape& s, int n_wg, int S, int* gu_groups, int* down_groups);
+// Batches of 3+: row blocks per expert tile (1 or 2), then the slot groups
+// of the gate/up tiles (rb 8-row blocks of the expert width) and of the down
+// tiles (rb 16-row blocks of the hidden size).
+int mm_row_blocks(const ModelShape& s, int n_wg, int B);
+void expert_groups_mm(const ModelShape& s, int n_wg, int S, int rb, int* gu_groups, int* down_groups);
 
 // For each task of P (by index), the tasks whose outputs it reads: the
 // relation validate_plan proves covered by waits, as task indices (used by

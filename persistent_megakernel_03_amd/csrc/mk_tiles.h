@@ -949,7 +949,8 @@ __device__ __forceinline__ bool bad_task(const Task& t, TileCtx& cx) {
 // batches of 3 or more (attention, its merge and the embedding are shared).
 template <class S, int NB>
 __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
-    if constexpr (NB == 0) {
+    if constexpr (NB == 0 || NB == kNbMmWide) {
+        constexpr int RBK = NB == kNbMmWide ? kMmMaxRowBlocks : 1;
         switch (t.op) {
             case OP_EMBED: return tile_embed(t, cx);
             case OP_QKV: return tile_qkv_mm(t, cx);
@@ -958,8 +959,8 @@ __device__ __forceinline__ bool dispatch_tile(const Task& t, TileCtx& cx) {
             case OP_OPROJ: return tile_oproj_mm(t, cx);
             case OP_ROUTER: return tile_router_mm(t, cx);
             case OP_ROUTE: return tile_route<4 * S::NE>(t, cx);
-            case OP_GATEUP: return tile_gateup_mm(t, cx);
-            case OP_DOWN: return tile_down_mm(t, cx);
+            case OP_GATEUP: return tile_gateup_mm<RBK>(t, cx);
+            case OP_DOWN: return tile_down_mm<RBK>(t, cx);
             case OP_MOESUM: return tile_moesum(t, cx);
             case OP_FNORM: return tile_fnorm(t, cx);
             case OP_LMHEAD: return tile_lmhead_mm(t, cx);

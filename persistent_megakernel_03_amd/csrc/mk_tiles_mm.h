@@ -644,6 +644,19 @@ __device__ __forceinline__ void load_slot_tables(const Params& p, const int32_t*
     __syncthreads();
 }
 
+// Row blocks a wave multiplies per load of its activations, in a kernel
+// built for tiles of RBK row blocks, and k-steps per batch, by the number of
+// 8-token column blocks: the weights and the activations of two batches in
+// flight fill about the same registers.
+template <int NC8, int RBK>
+struct MmRb {
+    static constexpr int v = NC8 <= 2 ? RBK : 1;
+};
+template <int NC8, int R>
+struct MmPfR {
+    static constexpr int v = R == 1 ? MmPfS<NC8>::v : (NC8 == 1 ? 6 : 4);
+};
+
 // One wave's slots (chunk indices wave, wave + 4, ...; mw of them) as one
 // stream of nsteps k-steps each: acc[cb] += A x B over the slot, then
 // flush(i, acc) at its end (acc: hi + lo summed on even columns; i: chunk
@@ -713,6 +726,94 @@ __device__ __forceinline__ void slot_stream(int mw, int nsteps, APtr&& a_ptr, XP
     }
 }
 
+// slot_stream over tiles of several row blocks: one stream of batches of
+// k-steps per wave, items (slot, pass)
+// for its slots (chunk indices wave, wave + 4, ...; mw of them), each pass
+// covering R row blocks of the tile (blocks R ps .. R ps + R - 1) over
+// nsteps k-steps: acc[r][cb] += A_r x B over the slot, then flush(i, blk0,
+// acc) at the item's end (acc: hi + lo summed on even columns; i: chunk
+// index; blk0: the pass's first block). a_ptr(i, blk, k) / x_ptr(i, cb, k):
+// this lane's A row of block blk and B operand (null: zero) at k-step k of
+// slot i; one B load serves the R blocks.
+template <int NC8, int R, class APtr, class XPtr, class Flush>
+__device__ __forceinline__ void slot_stream_rb(int mw, int npass, int nsteps, APtr&& a_ptr, XPtr&& x_ptr,
+                                               Flush&& flush) {
+    constexpr int PF = MmPfR<NC8, R>::v;
+    const int wave = tid_() >> 6;
+    int spb = PF;   // k-steps per batch: the largest divisor of nsteps <= PF
+    while (nsteps % spb) --spb;
+    const int nbps = nsteps / spb, nbt = mw * npass * nbps;
+    uint4 a0[PF][R], a1[PF][R], x0[PF][NC8], x1[PF][NC8];
+    auto loadA = [&](uint4(&a)[PF][R], int b) {
+        const int it = b / nbps, j = it / npass, ps = it - j * npass;
+        const int k0 = spb * (b - it * nbps);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint16_t* ap = a_ptr(wave + NWAVES * j, R * ps + r, k0);
+#pragma unroll
+            for (int q = 0; q < PF; ++q)
+                if (q < spb) a[q][r] = ld16s(ap + 32 * q);
+        }
+    };
+    auto loadX = [&](uint4(&x)[PF][NC8], int b) {
+        const int it = b / nbps, j = it / npass;
+        const int k0 = spb * (b - it * nbps);
+#pragma unroll
+        for (int cb = 0; cb < NC8; ++cb) {
+            const uint4* xp = x_ptr(wave + NWAVES * j, cb, k0);
+#pragma unroll
+            for (int q = 0; q < PF; ++q)
+                x[q][cb] = (q < spb && xp != nullptr) ? ld16(xp + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    f32x4_t acc[R][NC8];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int cb = 0; cb < NC8; ++cb) acc[r][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const uint4(&a)[PF][R], const uint4(&x)[PF][NC8], int b) {
+#pragma unroll
+        for (int q = 0; q < PF; ++q)
+            if (q < spb) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int cb = 0; cb < NC8; ++cb) acc[r][cb] = mfma16x16x32(a[q][r], x[q][cb], acc[r][cb]);
+            }
+        if ((b + 1) % nbps == 0) {
+            const int it = b / nbps, j = it / npass, ps = it - j * npass;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int cb = 0; cb < NC8; ++cb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[r][cb][q] += dpp_mov<0xB1>(acc[r][cb][q]);
+            flush(wave + NWAVES * j, R * ps, acc);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int cb = 0; cb < NC8; ++cb) acc[r][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    if (nbt > 0) {
+        loadA(a0, 0);
+        if (nbt > 1) loadA(a1, 1);
+        loadX(x0, 0);
+        for (int bt = 0; bt < nbt; bt += 2) {
+            if (bt + 1 < nbt) loadX(x1, bt + 1);
+            compute(a0, x0, bt);
+            if (bt + 2 < nbt) {
+                loadA(a0, bt + 2);
+                loadX(x0, bt + 2);
+            }
+            if (bt + 1 < nbt) {
+                compute(a1, x1, bt + 1);
+                if (bt + 3 < nbt) loadA(a1, bt + 3);
+            }
+        }
+    }
+}
+
 // Runs body(tables, c0, mc, NC8 tag) per LDS chunk of this tile's slots, NC8
 // sized for the chunk's widest slot. Block-uniform.
 template <class Body>
@@ -735,12 +836,14 @@ __device__ __forceinline__ void for_slot_chunks(const Params& p, const int32_t* 
 
 // ---------------------------------------------------------- expert gate/up
 
-// Rows a0..a0+8 of the expert width, slots a2, a2 + a3, ... of the routing
-// table: a = SiLU(W_gate h2) * (W_up h2) for the tokens routed to each slot's
-// expert, h2 = RMSNorm(x_mid) * g (split, from the router tiles), written
-// split to the (token, rank) row of the activations. One MFMA block holds
-// the 8 gate rows (A rows 0-7) and the 8 up rows (A rows 8-15) of the slot's
-// expert, so SwiGLU pairs meet in one wave.
+// Rows a0..a1 (whole 8-row blocks) of the expert width, slots a2, a2 + a3,
+// ... of the routing table: a = SiLU(W_gate h2) * (W_up h2) for the tokens
+// routed to each slot's expert, h2 = RMSNorm(x_mid) * g (split, from the
+// router tiles), written split to the (token, rank) row of the activations.
+// One MFMA block holds the 8 gate rows (A rows 0-7) and the 8 up rows (A rows
+// 8-15) of an 8-row block of the slot's expert, so SwiGLU pairs meet in one
+// wave.
+template <int RBK>
 __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, r0 = t.a0, q0 = t.a2, Q = t.a3, H = p.H, K = p.K, I = p.I;
@@ -753,46 +856,66 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
     const float* h2 = h2s_at(p, l);
     float* act = act_at(p, l);
     const int wave = tid_() >> 6;
+    // 8-row blocks of this tile (one in a kernel built for one, where the
+    // plan gives every gate/up tile 8 rows)
+    const int nrb = RBK == 1 ? 1 : (t.a1 - r0 + 7) >> 3;
     for_slot_chunks(p, rt, q0, Q, cx.lds, [&](const SlotTables& s, int mc, auto nn) {
         constexpr int NC8 = decltype(nn)::v;
         const int mw = mc > wave ? (mc - wave + NWAVES - 1) / NWAVES : 0;
         const uint16_t* Wrow = (col < 8 ? Wg : Wu) + (int64_t)(r0 + (col & 7)) * H + 8 * g4;
-        slot_stream<NC8>(
-            mw, H >> 5,
-            [&](int i, int k) { return Wrow + (int64_t)s.e[i] * I * H + 32 * k; },
-            [&](int i, int cb, int k) -> const uint4* {
-                const int c = 8 * cb + (col >> 1);
-                if (c >= s.n[i]) return nullptr;
-                return split_ptr(h2 + (int64_t)(s.ent[i * p.max_batch + c] & 0xffff) * H, 8 * g4 + 32 * k, col & 1);
-            },
-            [&](int i, f32x4_t(&acc)[NC8]) {
-                // lane (col, g4): rows 4 g4 + q; gate rows 0-7 in g4 0-1, up rows 8-15 in g4 2-3
+        auto x_ptr = [&](int i, int cb, int k) -> const uint4* {
+            const int c = 8 * cb + (col >> 1);
+            if (c >= s.n[i]) return nullptr;
+            return split_ptr(h2 + (int64_t)(s.ent[i * p.max_batch + c] & 0xffff) * H, 8 * g4 + 32 * k, col & 1);
+        };
+        // block blk of slot i: lane (col, g4) holds rows 4 g4 + q; gate rows
+        // 0-7 in g4 0-1, up rows 8-15 in g4 2-3 (wave-uniform call)
+        auto store = [&](int i, int blk, const f32x4_t(&acc)[NC8]) {
 #pragma unroll
-                for (int cb = 0; cb < NC8; ++cb) {
-                    float a4[4];
+            for (int cb = 0; cb < NC8; ++cb) {
+                float a4[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float up = __shfl_xor(acc[cb][q], 32);
-                        const float g = acc[cb][q];
-                        a4[q] = (g / (1.0f + expf(-g))) * up;
-                    }
-                    const int c = 8 * cb + (col >> 1);
-                    if ((col & 1) == 0 && g4 < 2 && c < s.n[i]) {
-                        const int ent = s.ent[i * p.max_batch + c];
-                        // elements 4 g4 .. 4 g4 + 3 of the row's 8-group: half of its hi and of its lo half
-                        uint32_t hi0, lo0, hi1, lo1;
-                        split_pair(a4[0], a4[1], hi0, lo0);
-                        split_pair(a4[2], a4[3], hi1, lo1);
-                        uint32_t* d = reinterpret_cast<uint32_t*>(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I + r0);
-                        uint64_t* dh = reinterpret_cast<uint64_t*>(d + 2 * g4);
-                        uint64_t* dl = reinterpret_cast<uint64_t*>(d + 4 + 2 * g4);
-                        __hip_atomic_store(dh, (uint64_t)hi0 | ((uint64_t)hi1 << 32), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(dl, (uint64_t)lo0 | ((uint64_t)lo1 << 32), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const float up = __shfl_xor(acc[cb][q], 32);
+                    const float g = acc[cb][q];
+                    a4[q] = (g / (1.0f + expf(-g))) * up;
                 }
-            });
+                const int c = 8 * cb + (col >> 1);
+                if ((col & 1) == 0 && g4 < 2 && c < s.n[i]) {
+                    const int ent = s.ent[i * p.max_batch + c];
+                    // elements 4 g4 .. 4 g4 + 3 of the row's 8-group: half of its hi and of its lo half
+                    uint32_t hi0, lo0, hi1, lo1;
+                    split_pair(a4[0], a4[1], hi0, lo0);
+                    split_pair(a4[2], a4[3], hi1, lo1);
+                    uint32_t* d = reinterpret_cast<uint32_t*>(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I +
+                                                              r0 + 8 * blk);
+                    uint64_t* dh = reinterpret_cast<uint64_t*>(d + 2 * g4);
+                    uint64_t* dl = reinterpret_cast<uint64_t*>(d + 4 + 2 * g4);
+                    __hip_atomic_store(dh, (uint64_t)hi0 | ((uint64_t)hi1 << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(dl, (uint64_t)lo0 | ((uint64_t)lo1 << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        };
+        if constexpr (RBK == 1) {
+            slot_stream<NC8>(
+                mw, H >> 5, [&](int i, int k) { return Wrow + (int64_t)s.e[i] * I * H + 32 * k; }, x_ptr,
+                [&](int i, f32x4_t(&acc)[NC8]) { store(i, 0, acc); });
+        } else {
+            constexpr int R = MmRb<NC8, RBK>::v;
+            slot_stream_rb<NC8, R>(
+                mw, (nrb + R - 1) / R, H >> 5,
+                [&](int i, int blk, int k) {
+                    return Wrow + (int64_t)s.e[i] * I * H + (int64_t)8 * (blk < nrb ? blk : nrb - 1) * H + 32 * k;
+                },
+                x_ptr,
+                [&](int i, int blk0, f32x4_t(&acc)[R][NC8]) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (blk0 + r < nrb) store(i, blk0 + r, acc[r]);
+                });
+        }
     });
     mark(cx, 1);
     block_signal(p, t.signal);
@@ -801,10 +924,12 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
 
 // ------------------------------------------------------------ expert down
 
-// Rows a0..a1 (<= 16) of the hidden size, slots a2, a2 + a3, ... of the
-// routing table: y = W_down a (a split, from the gate/up tiles) for each
+// Rows a0..a1 (16-row blocks, the last one possibly partial) of the hidden
+// size, slots a2, a2 + a3, ... of the routing table: y = W_down a (a split,
+// from the gate/up tiles) for each
 // token routed to the slot's expert, written to that token's (token, rank)
 // row of the expert outputs.
+template <int RBK>
 __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, q0 = t.a2, Q = t.a3;
@@ -816,33 +941,56 @@ __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const uint16_t* Wd = wptr(p, l, W_DOWN);
     const float* act = act_at(p, l);
     float* y = ybuf_at(p, l);
-    const int rsel = col < nrows ? col : nrows - 1;
+    // 16-row blocks of this tile (one in a kernel built for one, where the
+    // plan gives every down tile at most 16 rows)
+    const int nrb = RBK == 1 ? 1 : (nrows + 15) >> 4;
     for_slot_chunks(p, rt, q0, Q, cx.lds, [&](const SlotTables& s, int mc, auto nn) {
         constexpr int NC8 = decltype(nn)::v;
         const int mw = mc > wave ? (mc - wave + NWAVES - 1) / NWAVES : 0;
-        const uint16_t* Wrow = Wd + (int64_t)(h0 + rsel) * I + 8 * g4;
-        slot_stream<NC8>(
-            mw, I >> 5,
-            [&](int i, int k) { return Wrow + (int64_t)s.e[i] * H * I + 32 * k; },
-            [&](int i, int cb, int k) -> const uint4* {
+        auto x_ptr = [&](int i, int cb, int k) -> const uint4* {
+            const int c = 8 * cb + (col >> 1);
+            if (c >= s.n[i]) return nullptr;
+            const int ent = s.ent[i * p.max_batch + c];
+            return split_ptr(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I, 8 * g4 + 32 * k, col & 1);
+        };
+        // block blk of slot i: rows 16 blk + 4 g4 + q of the tile
+        auto store = [&](int i, int blk, const f32x4_t(&acc)[NC8]) {
+#pragma unroll
+            for (int cb = 0; cb < NC8; ++cb) {
                 const int c = 8 * cb + (col >> 1);
-                if (c >= s.n[i]) return nullptr;
-                const int ent = s.ent[i * p.max_batch + c];
-                return split_ptr(act + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * I, 8 * g4 + 32 * k, col & 1);
-            },
-            [&](int i, f32x4_t(&acc)[NC8]) {
+                if ((col & 1) == 0 && c < s.n[i]) {
+                    const int ent = s.ent[i * p.max_batch + c];
+                    float* yr = y + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * H + h0 + 16 * blk;
 #pragma unroll
-                for (int cb = 0; cb < NC8; ++cb) {
-                    const int c = 8 * cb + (col >> 1);
-                    if ((col & 1) == 0 && c < s.n[i]) {
-                        const int ent = s.ent[i * p.max_batch + c];
-                        float* yr = y + ((int64_t)(ent & 0xffff) * K + (ent >> 16)) * H + h0;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
-                    }
+                    for (int q = 0; q < 4; ++q)
+                        if (16 * blk + 4 * g4 + q < nrows) st_dev(yr + 4 * g4 + q, acc[cb][q]);
                 }
-            });
+            }
+        };
+        if constexpr (RBK == 1) {
+            const int rsel = col < nrows ? col : nrows - 1;
+            const uint16_t* Wrow = Wd + (int64_t)(h0 + rsel) * I + 8 * g4;
+            slot_stream<NC8>(
+                mw, I >> 5, [&](int i, int k) { return Wrow + (int64_t)s.e[i] * H * I + 32 * k; }, x_ptr,
+                [&](int i, f32x4_t(&acc)[NC8]) { store(i, 0, acc); });
+        } else {
+            constexpr int R = MmRb<NC8, RBK>::v;
+            slot_stream_rb<NC8, R>(
+                mw, (nrb + R - 1) / R, I >> 5,
+                [&](int i, int blk, int k) {
+                    // rows past the tile's end re-read its last row (their products are not stored)
+                    const int b = blk < nrb ? blk : nrb - 1;
+                    const int rb = min(16, nrows - 16 * b);
+                    const int rsel = 16 * b + (col < rb ? col : rb - 1);
+                    return Wd + ((int64_t)s.e[i] * H + h0 + rsel) * I + 8 * g4 + 32 * k;
+                },
+                x_ptr,
+                [&](int i, int blk0, f32x4_t(&acc)[R][NC8]) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (blk0 + r < nrb) store(i, blk0 + r, acc[r]);
+                });
+        }
     });
     mark(cx, 1);
     block_signal(p, t.signal);

@@ -71,7 +71,8 @@ class mk_options(ctypes.Structure):
                 ("wg_per_cu", ctypes.c_int32), ("split_kv_tokens", ctypes.c_int32),
                 ("n_cu_override", ctypes.c_int32), ("time_kernels", ctypes.c_int32),
                 ("shared_levels", ctypes.c_int32), ("validate_plans", ctypes.c_int32),
-                ("mfma_min_batch", ctypes.c_int32), ("poison_exchange", ctypes.c_int32)]
+                ("mfma_min_batch", ctypes.c_int32), ("poison_exchange", ctypes.c_int32),
+                ("mm_row_blocks", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
 
 
 class mk_debug_ptrs(ctypes.Structure):
@@ -186,7 +187,7 @@ def make_dims(cfg: dict, max_batch: int, max_pages_per_seq: int, n_pages: int) -
 def make_options(mode: int = MK_MODE_MEGAKERNEL, trace: bool = False, watchdog_ns: int = 0, wg_per_cu: int = 0,
                  split_kv_tokens: int = 0, n_cu_override: int = 0, time_kernels: bool = False,
                  shared_levels: int = 0, validate_plans: bool = False, mfma_min_batch: int = 0,
-                 poison_exchange: bool = False) -> mk_options:
+                 poison_exchange: bool = False, mm_row_blocks: int = 0) -> mk_options:
     o = mk_options()
     o.mode, o.trace, o.watchdog_ns = mode, int(bool(trace)), watchdog_ns
     o.wg_per_cu, o.split_kv_tokens, o.n_cu_override = wg_per_cu, split_kv_tokens, n_cu_override
@@ -195,6 +196,7 @@ def make_options(mode: int = MK_MODE_MEGAKERNEL, trace: bool = False, watchdog_n
     o.validate_plans = int(bool(validate_plans))
     o.mfma_min_batch = int(mfma_min_batch)
     o.poison_exchange = int(bool(poison_exchange))
+    o.mm_row_blocks = int(mm_row_blocks)
     return o
 
 
@@ -370,12 +372,12 @@ class Decoder:
                  max_pages_per_seq: int, mode: int = MK_MODE_MEGAKERNEL, trace: bool = False,
                  watchdog_ns: int = 0, wg_per_cu: int = 0, split_kv_tokens: int = 0, device: int = 0,
                  time_kernels: bool = False, shared_levels: int = 0, validate_plans: bool = False,
-                 mfma_min_batch: int = 0, poison_exchange: bool = False):
+                 mfma_min_batch: int = 0, poison_exchange: bool = False, mm_row_blocks: int = 0):
         import torch
         self.cfg = dict(cfg)
         self.dims = make_dims(cfg, max_batch, max_pages_per_seq, k_pool.shape[1])
         self.opts = make_options(mode, trace, watchdog_ns, wg_per_cu, split_kv_tokens, 0, time_kernels, shared_levels,
-                                 validate_plans, mfma_min_batch, poison_exchange)
+                                 validate_plans, mfma_min_batch, poison_exchange, mm_row_blocks)
         L = cfg["n_layers"]
         self._keep: List = [weights, k_pool, v_pool]
 

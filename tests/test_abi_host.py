@@ -169,8 +169,12 @@ def test_plan_counts_for_the_30b_shape():
 @pytest.mark.parametrize("batch", [4, 16, 64])
 def test_plan_counts_for_30b_batches(batch):
     # batches of 3+: every weight product in 16-row matrix-core blocks, one
-    # routing tile; gate/up tiles are (8 rows, one of 8 slot groups) pairs;
-    # router tiles are (8 expert rows, one 16-token block) pairs
+    # routing tile; router tiles are (8 expert rows, one 16-token block)
+    # pairs. Gate/up tiles are (rb 8-row blocks, slot group) pairs and down
+    # tiles (rb 16-row blocks, slot group): rb = 2 where the expected distinct
+    # experts, 128 (1 - (120/128)^B), reach 7 per gate/up slot group (126 at
+    # B = 64 over 16 groups), else 1 (83 at B = 16 over 8 groups)
+    rb = 2 if batch == 64 else 1
     d = mk.make_dims(configs.A3B, batch, 520, 520 * batch)
     info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192] * batch)
     ops = np.bincount(tasks[:, 0], minlength=13)
@@ -183,8 +187,8 @@ def test_plan_counts_for_30b_batches(batch):
     assert set((rt[:, 4] >> 16).tolist()) == set(range(-(-batch // 16)))   # token blocks
     assert set((rt[:, 4] & 0xffff).tolist()) == set(range(0, 256, 16))   # 8-element groups of the expert input
     assert ops[OP_ROUTE] == 48
-    assert ops[OP_GATEUP] == 48 * 96 * 8
-    assert ops[OP_DOWN] == 48 * 128 * 4        # 16-row blocks x 4 slot groups
+    assert ops[OP_GATEUP] == 48 * (96 // rb) * (8 * rb)     # 8 rb rows per tile x 8 rb slot groups
+    assert ops[OP_DOWN] == 48 * (128 // rb) * (4 * rb)      # 16 rb rows per tile x 4 rb slot groups
     assert ops[OP_MOESUM] == 48 * 128
     assert ops[OP_FNORM] == batch                  # the final norm, one tile per token
     assert ops[OP_LMHEAD] == -(-151936 // 32)
@@ -192,7 +196,35 @@ def test_plan_counts_for_30b_batches(batch):
     assert len(att) == 48 * batch * 4 * att[0, 5]
     # down slot groups: every slot in exactly one group
     dn = tasks[(tasks[:, 0] == OP_DOWN) & (tasks[:, 1] == 0)]
-    assert set(dn[:, 5]) == {4} and set(dn[:, 4]) == {0, 1, 2, 3}
+    assert set(dn[:, 5]) == {4 * rb} and set(dn[:, 4]) == set(range(4 * rb))
+    assert set((dn[:, 3] - dn[:, 2]).tolist()) == {16 * rb}
+    gu = tasks[(tasks[:, 0] == OP_GATEUP) & (tasks[:, 1] == 0)]
+    assert set(gu[:, 5]) == {8 * rb} and set(gu[:, 4]) == set(range(8 * rb))
+    assert set((gu[:, 3] - gu[:, 2]).tolist()) == {8 * rb}
+
+
+@pytest.mark.parametrize("rb", [1, 2])
+def test_plan_row_blocks_option(rb):
+    # forced row blocks per matrix-core expert tile: gate/up tiles of 8 rb
+    # rows, down tiles of 16 rb rows (the last one partial where the size is
+    # not a multiple), every tile still covering each slot group exactly once
+    d = mk.make_dims(configs.TINY, 8, 8, 64)
+    pos = [5, 9, 33, 70, 1, 0, 2, 3]
+    o = mk.make_options(mm_row_blocks=rb)
+    info, tasks, offs, targets = mk.mk_plan_build(d, o, 64, pos)
+    gu = tasks[(tasks[:, 0] == OP_GATEUP) & (tasks[:, 1] == 0)]
+    dn = tasks[(tasks[:, 0] == OP_DOWN) & (tasks[:, 1] == 0)]
+    assert set((gu[:, 3] - gu[:, 2]).tolist()) == {8 * rb}
+    assert set((dn[:, 3] - dn[:, 2]).tolist()) == {16 * rb}
+    mk.mk_plan_check(d, o, 64, pos, tasks, offs)
+
+
+def test_plan_rejects_bad_row_blocks():
+    d = mk.make_dims(configs.TINY, 8, 8, 64)
+    for bad in (-1, 3):
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_plan_build(d, mk.make_options(mm_row_blocks=bad), 64, [5] * 8)
+        assert e.value.status == mk.MK_ERR_INVALID
 
 
 def test_plan_rejects_bad_input():

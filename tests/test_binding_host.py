@@ -62,5 +62,7 @@ def test_plan_validation_option_is_in_the_options_struct():
     o = mk.make_options(validate_plans=True)
     assert o.validate_plans == 1 and o.mfma_min_batch == 0 and o.poison_exchange == 0
     assert mk.make_options(poison_exchange=True).poison_exchange == 1
-    # the debug word took the place of the reserved one: the struct's size is unchanged
-    assert ctypes.sizeof(mk.mk_options) == 48
+    assert o.mm_row_blocks == 0 and mk.make_options(mm_row_blocks=2).mm_row_blocks == 2
+    # the C struct: 8-byte watchdog after two words, ten more words (the last one padding)
+    assert ctypes.sizeof(mk.mk_options) == 56
+    assert mk.mk_options.mm_row_blocks.offset == 48

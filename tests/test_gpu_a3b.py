@@ -330,7 +330,9 @@ def test_a3b_batch_matches_oracle(weights, B):
     """The batch sweep's shape: B sequences at 8192 cached tokens each, pages
     from a shuffled pool, per-sequence seeded first tokens. Rows 0 and B-1
     are checked end to end against the oracle as above; B = 2 (the two-token
-    schedule) and B = 4 also megakernel == per-op bit for bit."""
+    schedule) and B = 4 also megakernel == per-op bit for bit; B = 16 and 64
+    also the step with the other number of row blocks per expert tile (two at
+    B = 16, one at B = 64) bit for bit."""
     ctx = 8192
     pages = ctx // P + 2
     n_pages = B * pages + 7
@@ -339,22 +341,24 @@ def test_a3b_batch_matches_oracle(weights, B):
     bts = [[int(x) for x in r] for r in synth.make_block_tables(B, pages, n_pages, seed=B, shuffle=True)]
     toks = [int(t) for t in synth.make_tokens(B, CFG["vocab"], seed=100 + B)]
     outs = []
-    for mode in ([mk.MK_MODE_MEGAKERNEL, mk.MK_MODE_PEROP] if B <= 4 else [mk.MK_MODE_MEGAKERNEL]):
+    runs = [(mk.MK_MODE_MEGAKERNEL, 0)]
+    runs.append((mk.MK_MODE_PEROP, 0) if B <= 4 else (mk.MK_MODE_MEGAKERNEL, 1 if B == 64 else 2))
+    for mode, rb in runs:
         k, v = s.fresh_pools()
-        dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=B, max_pages_per_seq=pages, mode=mode)
+        dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=B, max_pages_per_seq=pages, mode=mode, mm_row_blocks=rb)
         tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
         logits = torch.empty(B, CFG["vocab"], dtype=torch.float32, device="cuda")
-        print(f"a3b batch {B}: one step, mode {mode}", flush=True)
+        print(f"a3b batch {B}: one step, mode {mode}, row blocks {rb}", flush=True)
         dec.step([ctx] * B, bts, tokens, logits)
         assert dec.sync_check() == mk.MK_OK
         outs.append(dict(logits=logits.cpu().numpy(), xs=x_layers(dec).cpu().numpy(),
                          ids=route_ids(dec).cpu().numpy(), k=k, v=v))
         dec.close()
-    if len(outs) == 2:
-        a, b = outs
-        assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["xs"], b["xs"])
-        assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
-        del outs[1]
+    a, b = outs
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["xs"], b["xs"])
+    assert np.array_equal(a["ids"], b["ids"])
+    assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+    del outs[1], a, b
     g = outs[0]
     written = {(bts[b][ctx // P], ctx % P) for b in range(B)}
     for b in (0, B - 1):

@@ -46,14 +46,16 @@ def _batch(B, seed):
     return positions, bts, toks
 
 
-def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=0, mfma_min_batch=0):
+def _run(s, positions, bts, toks, mode=mk.MK_MODE_MEGAKERNEL, steps=1, shared=0, mfma_min_batch=0, row_blocks=0):
     B = len(positions)
     k, v = s.fresh_pools()
     dec = mk.Decoder(CFG, s.w_dev, k, v, max_batch=max(B, 3), max_pages_per_seq=PAGES_PER_SEQ, mode=mode,
-                     shared_levels=shared, validate_plans=True, mfma_min_batch=mfma_min_batch)
+                     shared_levels=shared, validate_plans=True, mfma_min_batch=mfma_min_batch,
+                     mm_row_blocks=row_blocks)
     tokens = torch.tensor(toks, dtype=torch.int32, device="cuda")
     logits = torch.empty(B, CFG["vocab"], device="cuda")
-    print(f"batch B={B} mode={mode} shared={shared} steps={steps} mfma_min_batch={mfma_min_batch}", flush=True)
+    print(f"batch B={B} mode={mode} shared={shared} steps={steps} mfma_min_batch={mfma_min_batch} "
+          f"row_blocks={row_blocks}", flush=True)
     for st in range(steps):
         dec.step([p + st for p in positions], bts, tokens, logits, seq_ids=list(range(100, 100 + B)))
         assert dec.sync_check() == mk.MK_OK
@@ -123,6 +125,21 @@ def test_batch_megakernel_equals_perop_bitwise(setup):
     assert np.array_equal(a["xs"], b["xs"])
     assert np.array_equal(a["ids"], b["ids"])
     assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
+
+
+@pytest.mark.parametrize("B", [3, 17, 64])
+def test_expert_row_blocks_bitwise(setup, B):
+    """Expert tiles of two row blocks per activation load (gate/up: 16 rows,
+    down: 32 rows) sum each output row's products in the same order as tiles
+    of one block, so the step is the same bit for bit, in both modes."""
+    positions, bts, toks = _batch(B, 13)
+    a = _run(setup, positions, bts, toks, mk.MK_MODE_MEGAKERNEL, steps=2, row_blocks=1)
+    for mode in (mk.MK_MODE_MEGAKERNEL, mk.MK_MODE_PEROP):
+        b = _run(setup, positions, bts, toks, mode, steps=2, row_blocks=2)
+        assert np.array_equal(a["logits"], b["logits"])
+        assert np.array_equal(a["xs"], b["xs"])
+        assert np.array_equal(a["ids"], b["ids"])
+        assert torch.equal(a["k"], b["k"]) and torch.equal(a["v"], b["v"])
 
 
 @pytest.mark.parametrize("B", [8, 64])
