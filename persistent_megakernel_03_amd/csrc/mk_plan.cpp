@@ -371,7 +371,7 @@ static void build_levels_mm(const ModelShape& s, const TileConfig& cfg, int n_wg
         for (int q = 0; q < Q; ++q)
             for (int i = 0; i < nblk; ++i) {
                 const int r0 = i * 16 * rb, r1 = std::min(s.H, r0 + 16 * rb);
-                add(make_task(OP_DOWN, l, r0, r1, q, Q, -1, 0, cl.gateup(l), ngu, cl.down(l), lv + 7),
+                add(make_task(OP_DOWN, l, r0, r1, q, Q, cl.route(l), 1, cl.gateup(l), ngu, cl.down(l), lv + 7),
                     2.0 * ceil_div(S - q, Q) * (r1 - r0) * s.I, kRouted);
             }
         P.targets[cl.down(l)] = nd;

@@ -661,9 +661,12 @@ struct MmPfR {
 // stream of nsteps k-steps each: acc[cb] += A x B over the slot, then
 // flush(i, acc) at its end (acc: hi + lo summed on even columns; i: chunk
 // index). a_ptr(i, k) / x_ptr(i, cb, k): this lane's A row and B operand
-// (null: zero) at k-step k of slot i.
-template <int NC8, class APtr, class XPtr, class Flush>
-__device__ __forceinline__ void slot_stream(int mw, int nsteps, APtr&& a_ptr, XPtr&& x_ptr, Flush&& flush) {
+// (null: zero) at k-step k of slot i. ready() is called by every wave once
+// the first two batches of A are requested and before any B is (it may wait
+// on a counter at block level).
+template <int NC8, class APtr, class XPtr, class Flush, class Ready>
+__device__ __forceinline__ void slot_stream(int mw, int nsteps, APtr&& a_ptr, XPtr&& x_ptr, Flush&& flush,
+                                            Ready&& ready) {
     constexpr int PF = MmPfS<NC8>::v;
     const int wave = tid_() >> 6;
     int spb = PF;   // k-steps per batch: the largest divisor of nsteps <= PF
@@ -710,6 +713,9 @@ __device__ __forceinline__ void slot_stream(int mw, int nsteps, APtr&& a_ptr, XP
     if (nbt > 0) {
         loadA(a0, 0);
         if (nbt > 1) loadA(a1, 1);
+    }
+    ready();
+    if (nbt > 0) {
         loadX(x0, 0);
         for (int bt = 0; bt < nbt; bt += 2) {
             if (bt + 1 < nbt) loadX(x1, bt + 1);
@@ -901,7 +907,7 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
         if constexpr (RBK == 1) {
             slot_stream<NC8>(
                 mw, H >> 5, [&](int i, int k) { return Wrow + (int64_t)s.e[i] * I * H + 32 * k; }, x_ptr,
-                [&](int i, f32x4_t(&acc)[NC8]) { store(i, 0, acc); });
+                [&](int i, f32x4_t(&acc)[NC8]) { store(i, 0, acc); }, [] {});
         } else {
             constexpr int R = MmRb<NC8, RBK>::v;
             slot_stream_rb<NC8, R>(
@@ -928,15 +934,26 @@ __device__ __forceinline__ bool tile_gateup_mm(const Task& t, TileCtx& cx) {
 // size, slots a2, a2 + a3, ... of the routing table: y = W_down a (a split,
 // from the gate/up tiles) for each
 // token routed to the slot's expert, written to that token's (token, rank)
-// row of the expert outputs.
+// row of the expert outputs. The routing (pre counter) fixes the tile's
+// expert rows, so with one row block the first weight batches are
+// requested before the wait on the gate/up tiles (main counter) that the
+// activations need.
 template <int RBK>
 __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     const Params& p = cx.p;
     const int l = t.layer, h0 = t.a0, nrows = t.a1 - t.a0, q0 = t.a2, Q = t.a3;
     const int H = p.H, K = p.K, I = p.I;
     const int lane = tid_() & 63, col = lane & 15, g4 = lane >> 4, wave = tid_() >> 6;
-    if (!block_wait(p, t.ctr, t.target, cx.t_wait)) return false;
-    mark(cx, 0);
+    if (!block_wait(p, t.pre_ctr, t.pre_target, cx.t_wait)) return false;
+    // the wait on the gate/up tiles, once, by every wave at the same point
+    // (inside the first slot chunk, or after the chunks if there is none)
+    bool ok = true, waited = false;
+    auto ready = [&]() {
+        if (waited) return;
+        waited = true;
+        ok = block_wait(p, t.ctr, t.target, cx.t_wait);
+        mark(cx, 0);
+    };
     const int32_t* rt = rtab_at(p, l);
     const uint16_t* Wd = wptr(p, l, W_DOWN);
     const float* act = act_at(p, l);
@@ -944,6 +961,9 @@ __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
     // 16-row blocks of this tile (one in a kernel built for one, where the
     // plan gives every down tile at most 16 rows)
     const int nrb = RBK == 1 ? 1 : (nrows + 15) >> 4;
+    // the two-block stream waits before its first request (holding its
+    // first batches across the wait spills that kernel's registers)
+    if constexpr (RBK > 1) ready();
     for_slot_chunks(p, rt, q0, Q, cx.lds, [&](const SlotTables& s, int mc, auto nn) {
         constexpr int NC8 = decltype(nn)::v;
         const int mw = mc > wave ? (mc - wave + NWAVES - 1) / NWAVES : 0;
@@ -972,7 +992,7 @@ __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
             const uint16_t* Wrow = Wd + (int64_t)(h0 + rsel) * I + 8 * g4;
             slot_stream<NC8>(
                 mw, I >> 5, [&](int i, int k) { return Wrow + (int64_t)s.e[i] * H * I + 32 * k; }, x_ptr,
-                [&](int i, f32x4_t(&acc)[NC8]) { store(i, 0, acc); });
+                [&](int i, f32x4_t(&acc)[NC8]) { store(i, 0, acc); }, ready);
         } else {
             constexpr int R = MmRb<NC8, RBK>::v;
             slot_stream_rb<NC8, R>(
@@ -992,6 +1012,8 @@ __device__ __forceinline__ bool tile_down_mm(const Task& t, TileCtx& cx) {
                 });
         }
     });
+    ready();
+    if (!ok) return false;  // block-uniform (block_wait)
     mark(cx, 1);
     block_signal(p, t.signal);
     return true;
