@@ -219,6 +219,20 @@ def test_plan_row_blocks_option(rb):
     mk.mk_plan_check(d, o, 64, pos, tasks, offs)
 
 
+@pytest.mark.parametrize("batch,rb", [(32, 1), (33, 2)])
+def test_row_block_choice_at_its_threshold(batch, rb):
+    # two row blocks per gate/up tile once the expected distinct experts,
+    # 128 (1 - (120/128)^B), reach 7 per slot group of the two-block plan
+    # (16 groups): 111.77 at B = 32, 112.79 at B = 33
+    expected = 128 * (1 - (120 / 128) ** batch)
+    assert (expected >= 7 * 16) == (rb == 2)
+    d = mk.make_dims(configs.A3B, batch, 520, 520 * batch)
+    info, tasks, offs, targets = mk.mk_plan_build(d, mk.make_options(), 512, [8192] * batch)
+    gu = tasks[(tasks[:, 0] == OP_GATEUP) & (tasks[:, 1] == 0)]
+    assert set((gu[:, 3] - gu[:, 2]).tolist()) == {8 * rb}
+    assert len(gu) == (96 // rb) * (8 * rb)
+
+
 def test_plan_rejects_bad_row_blocks():
     d = mk.make_dims(configs.TINY, 8, 8, 64)
     for bad in (-1, 3):
